@@ -1,0 +1,242 @@
+/*
+ * safe.h -- C ABI of libsafe, the MI355X (gfx950) hot path of SAFE-DiT
+ * ("SAFE-DiT: Semantics-Aware Fast-path Execution for High-Resolution
+ * Diffusion Transformers", arXiv 2606.29360).
+ *
+ * Four operations, each enqueued on a caller-supplied HIP stream:
+ *   safe_mask_classify  Eq. 6-8   is an attention mask in the row-constant class R?
+ *   safe_pcsp_select    Eq. 9-12  image->text sensitivity scores and the top-k set S
+ *   safe_kv_assemble    Eq. 14,16 global K/V: fresh rows of S over cached context rows
+ *   safe_attn_fwd       Eq. 2,16-18 attention on all rows (dense anchor pass) or on the
+ *                       gathered rows of S, with optional per-sample valid key lengths
+ *
+ * Common conventions
+ *   - Tensors are DEVICE pointers owned by the caller; the library never allocates,
+ *     frees or retains device memory.  Scratch space, where an operation needs it,
+ *     is a caller-provided workspace whose size is queried first (see each call).
+ *   - Activations are token-major [B, N, H, d] with d contiguous; the three other
+ *     strides are given in ELEMENTS as stride[0] = batch, stride[1] = token,
+ *     stride[2] = head.  bf16 tensors are passed as 16-bit storage.
+ *   - Every argument is validated on the host before any HIP call; a failed check
+ *     returns a negative status and enqueues nothing.  Values that live in device
+ *     memory (index lists, key lengths) are NOT read by the host unless
+ *     SAFE_FLAG_CHECK is set; the kernels bound every such value before using it
+ *     as an address, so a bad value yields a documented result, never a stray
+ *     access.
+ *   - No call throws; no call keeps state between calls; calls on different
+ *     streams with separate outputs and workspaces may run concurrently.
+ *   - `stream` is a hipStream_t (NULL = the default stream).
+ */
+#ifndef SAFE_DIT_SAFE_H
+#define SAFE_DIT_SAFE_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+#define SAFE_ABI_VERSION 1
+
+/* ---- status codes (negative = error) ----------------------------------- */
+enum {
+  SAFE_OK = 0,
+  SAFE_ERR_NULL = -1,        /* a required pointer is NULL                          */
+  SAFE_ERR_SHAPE = -2,       /* sizes/strides inconsistent or out of range          */
+  SAFE_ERR_DTYPE = -3,       /* unknown dtype code                                  */
+  SAFE_ERR_RANGE = -4,       /* a scalar argument, or (with SAFE_FLAG_CHECK) a device
+                                value such as an index or a key length, out of range */
+  SAFE_ERR_UNSUPPORTED = -5, /* valid request the library does not implement (e.g. d) */
+  SAFE_ERR_WORKSPACE = -6,   /* workspace missing or too small                      */
+  SAFE_ERR_HIP = -7,         /* a HIP runtime call failed                            */
+  SAFE_ERR_ALIGN = -8        /* a pointer or stride breaks the 16-byte vector access */
+};
+
+/* ---- flags ------------------------------------------------------------- */
+#define SAFE_FLAG_CHECK        (1u << 0)  /* copy device index/length inputs to the host,
+                                             check them, return SAFE_ERR_RANGE on a bad
+                                             value (synchronises the stream)            */
+#define SAFE_ATTN_SCATTER_OUT  (1u << 1)  /* safe_attn_fwd: write row r at token q_rows[r]
+                                             of an [B, Nq, H, d] output instead of the
+                                             compact [B, n_rows, H, d] layout           */
+#define SAFE_CLASSIFY_ASYNC    (1u << 2)  /* safe_mask_classify: do not wait; `info` is
+                                             not written (it may be NULL); the summary is
+                                             left in the workspace's first 32 bytes as a
+                                             safe_mask_info                             */
+#define SAFE_PCSP_ACCUM        (1u << 3)  /* safe_pcsp_select: add Eq. 9-10 scores to acc */
+#define SAFE_PCSP_SELECT       (1u << 4)  /* safe_pcsp_select: Eq. 11-12 from acc         */
+
+/* ---- element types ----------------------------------------------------- */
+enum {
+  SAFE_DT_BOOL = 0,  /* uint8: nonzero = attend, 0 = blocked              */
+  SAFE_DT_BF16 = 1,  /* additive bias, bfloat16                           */
+  SAFE_DT_F16 = 2,   /* additive bias, IEEE half                          */
+  SAFE_DT_F32 = 3    /* additive bias, IEEE single                        */
+};
+
+/* ---- mask row classes (ordered: the overall class is the maximum) ------- */
+enum {
+  SAFE_MASK_ALL_VALID = 0,   /* Boolean row, every entry attends          } class R:   */
+  SAFE_MASK_ZERO = 1,        /* additive row of zeros (-0 == +0)          } removable  */
+  SAFE_MASK_ROW_CONST = 2,   /* additive row, one finite nonzero constant } (Eq. 6)    */
+  SAFE_MASK_KEY_PADDING = 3, /* keys [0,L) valid and equal, [L,Nk) blocked, 1 <= L < Nk */
+  SAFE_MASK_NONCONST = 4,    /* finite, not all equal                                  */
+  SAFE_MASK_BLOCKED = 5,     /* any other row with -inf / false entries (incl. L = 0)  */
+  SAFE_MASK_NONFINITE = 6    /* a NaN or +inf entry                                    */
+};
+
+typedef struct {
+  int32_t verdict;        /* 1: every stored row is in R, so the mask may be dropped   */
+  int32_t mask_class;     /* overall class (max over rows; KEY_PADDING only if every
+                             row of each stored batch index has the same L, rows in R
+                             counting as L = Nk; otherwise BLOCKED)                    */
+  int64_t first_bad_row;  /* lowest flat stored row (b,h,i row-major) not in R, or -1  */
+  int64_t rows;           /* number of stored rows = size[0]*size[1]*size[2]           */
+} safe_mask_info;
+
+/*
+ * safe_mask_classify -- certify whether an attention mask is removable.
+ *
+ * Defined by the paper's Eq. 6 (the row-constant class R), the rule that
+ * batched or head-specific masks are judged on every broadcast query row, the
+ * statements after Eq. 7 (all-valid Boolean and all-zero additive masks are in
+ * R; finite non-uniform biases and masks with blocked positions are kept) and
+ * the Eq. 8 rewrite (drop the mask iff it is in R).  A mask whose rows are all
+ * KEY_PADDING with one L per sample is the text-padding mask of Eq. 4/17 and is
+ * reported with kv_len_out[b] = L, so the caller can run safe_attn_fwd with
+ * per-sample key lengths instead of the mask.
+ *
+ * mask       device; 4-D [size0, size1, size2, size3] = [B, H, Nq, Nk] as STORED
+ *            (broadcast dims stored with size 1); element type `dtype`.
+ * stride     element strides of the four dims, >= 0; stride[3] must be 1 when
+ *            size[3] > 1.  Any alignment is accepted (rows whose start is 16-byte
+ *            aligned are scanned with vector loads).
+ * info       host; written on return unless SAFE_CLASSIFY_ASYNC.
+ * row_class  device, optional: uint8 [rows] class of every stored row.
+ * kv_len_out device, optional: int32 [size0]; L per stored batch index when the
+ *            overall class is KEY_PADDING, else -1.
+ * workspace  device scratch of *workspace_bytes; call first with workspace == NULL
+ *            to have the required size written to *workspace_bytes (returns SAFE_OK).
+ * Blocking unless SAFE_CLASSIFY_ASYNC: waits for the stream and reads 32 bytes back.
+ * A mask with zero rows is removable (class ALL_VALID for bool, ZERO otherwise).
+ */
+int safe_mask_classify(const void* mask, int32_t dtype, const int64_t size[4], const int64_t stride[4],
+                       uint32_t flags, safe_mask_info* info, uint8_t* row_class, int32_t* kv_len_out,
+                       void* workspace, size_t* workspace_bytes, void* stream);
+
+/*
+ * safe_pcsp_select -- Prompt-Conditioned Sensitivity Partitioning.
+ *
+ * SAFE_PCSP_ACCUM (Eq. 9-10): for every image token i and head h in the head set,
+ *   A_h[i, j] = softmax over j < kv_len[b] of scale * q[b,i,h,:] . k_text[b,j,h,:]
+ *   acc[b, i] += sum_h sum_{j < kv_len[b]} w[b, j] * A_h[i, j]
+ * Call once per warm-up step and layer; the 1/(|W||L||H|) factor of Eq. 10 is a
+ * positive constant and is left out (it changes neither order nor Norm).
+ * SAFE_PCSP_SELECT (Eq. 11-12): s_bar = G_sigma * acc on the grid_h x grid_w
+ * row-major raster (token i = row*grid_w + col): separable Gaussian taps
+ * exp(-t^2/(2 sigma^2)), |t| <= ceil(3 sigma), renormalised over the taps inside
+ * the grid; sigma == 0 leaves acc unchanged.  score_out (optional) receives
+ * Norm(s_bar) = (s_bar - min)/(max - min) (0 for a constant field).  idx_out
+ * receives the k tokens ranking highest by s_bar (descending value, ties to the
+ * lower index, -0 == +0, NaN last), in ASCENDING token order.  Norm is
+ * increasing, so ranking s_bar selects the same set as ranking Norm(s_bar).
+ * Both flags may be given in one call (accumulate, then select).
+ *
+ * Workspace: query with workspace == NULL; needed only for SAFE_PCSP_SELECT.
+ * Limits: H <= 64 when head_mask != 0; d in {32, 64, 96, 128}; M <= 1024;
+ * 0 <= k <= N; acc is caller-zeroed before the first accumulation.
+ */
+typedef struct {
+  uint32_t flags;                  /* SAFE_PCSP_ACCUM | SAFE_PCSP_SELECT                */
+  int32_t B, N, M, H, d;
+  const void* q;      int64_t q_stride[3];   /* [B, N, H, d] bf16 image queries (ACCUM) */
+  const void* k_text; int64_t k_stride[3];   /* [B, M, H, d] bf16 text keys (ACCUM)     */
+  const int32_t* kv_len;           /* device [B] valid text keys (suffix padding); NULL = M;
+                                      values are clamped to [0, M]                      */
+  const float* w;                  /* device [B, M] content weights (ACCUM): 0 on padding
+                                      and special tokens, summing to 1 over content     */
+  uint64_t head_mask;              /* bit h set = head h is in the head set; 0 = all    */
+  float scale;                     /* logit scale; <= 0 means 1/sqrt(d)                 */
+  float* acc;                      /* device [B, N] fp32 (ACCUM adds; SELECT reads)     */
+  int32_t grid_h, grid_w;          /* SELECT: grid_h * grid_w == N                      */
+  float sigma;                     /* SELECT: Gaussian width in tokens, >= 0, <= 32     */
+  int32_t k;                       /* SELECT: 0 <= k <= N                               */
+  float* score_out;                /* device [B, N], optional (SELECT)                  */
+  int32_t* idx_out;                /* device [B, k] (SELECT)                            */
+} safe_pcsp_args;
+
+int safe_pcsp_select(const safe_pcsp_args* a, void* workspace, size_t* workspace_bytes, void* stream);
+
+/*
+ * safe_kv_assemble -- global keys and values for SRSU (Eq. 14, 16).
+ *
+ *   k_out[b, j] = k_fresh[b, r]  if idx[b, r] == j
+ *               = k_cache[b, j]  otherwise          (same for v)
+ * i.e. the fresh rows of the sensitive set S placed, in the original token order,
+ * over the cached context rows of the last anchor.  idx holds nsel ascending
+ * distinct token indices per sample (shared by all samples when idx_bstride == 0).
+ * Out of place: every output row is read once from its source and written once.
+ * In place (k_out == k_cache, v_out == v_cache, equal strides): only the nsel
+ * fresh rows are written (the cache refresh of Eq. 19 with S = all rows is the
+ * same call with nsel == N and idx = 0..N-1).
+ * Index entries outside [0, N) are skipped (no write); with SAFE_FLAG_CHECK they
+ * return SAFE_ERR_RANGE instead.  Elements are 16-bit (bf16 / fp16); every
+ * pointer and stride must give 16-byte aligned rows, and d % 8 == 0.
+ */
+typedef struct {
+  int32_t B, N, H, d, nsel;
+  const void* k_fresh; const void* v_fresh; int64_t fresh_stride[3]; /* [B, nsel, H, d] */
+  const int32_t* idx; int64_t idx_bstride;                           /* [B, nsel] int32  */
+  const void* k_cache; const void* v_cache; int64_t cache_stride[3]; /* [B, N, H, d]     */
+  void* k_out; void* v_out; int64_t out_stride[3];                   /* [B, N, H, d]     */
+  uint32_t flags;                                                    /* SAFE_FLAG_CHECK  */
+} safe_kv_args;
+
+int safe_kv_assemble(const safe_kv_args* a, void* stream);
+
+/*
+ * safe_attn_fwd -- scaled dot-product attention without a mask tensor.
+ *
+ * For each sample b, head h and output row r (query token i = q_rows[b][r], or
+ * i = r when q_rows is NULL), with L = kv_len[b] (or Nk):
+ *   O[b, r, h, :] = sum_{j < L} softmax_j(scale * q[b,i,h,:] . k[b,j,h,:]) v[b,j,h,:]
+ *   lse[b, h, r]  = natural-log log-sum-exp of those scaled logits
+ * This is Eq. 2 with m = empty (also the Eq. 8 rewrite of a removable mask), the
+ * SRSU row-selective forms Eq. 16 (self-attention: every key visible) and Eq. 17
+ * (cross-attention: text padding kept as the valid length L), and the dense anchor
+ * pass of Eq. 18 (q_rows == NULL).  L == 0 gives O = 0 and lse = -inf.
+ * Inputs bf16; softmax and accumulation in fp32; O is written as bf16.
+ *
+ * q_rows        device int32 [B, n_rows] (sample stride q_rows_bstride; 0 = one list
+ *               shared by every sample) or NULL (n_rows must then equal Nq).  Entries
+ *               outside [0, Nq) read a zero query row (SAFE_FLAG_CHECK: error).
+ * kv_len        device int32 [B] or NULL; values are clamped to [0, Nk].
+ * lse           device fp32 [B, H, n_rows], optional.
+ * o             bf16; compact [B, n_rows, H, d] unless SAFE_ATTN_SCATTER_OUT.
+ * Limits: d in {32, 64, 96, 128}; pointers and strides give 16-byte aligned rows.
+ */
+typedef struct {
+  int32_t B, H, Nq, Nk, d;
+  const void* q; int64_t q_stride[3];     /* [B, Nq, H, d] bf16 */
+  const void* k; int64_t k_stride[3];     /* [B, Nk, H, d] bf16 */
+  const void* v; int64_t v_stride[3];     /* [B, Nk, H, d] bf16 */
+  void* o;       int64_t o_stride[3];     /* bf16, see above    */
+  const int32_t* q_rows; int32_t n_rows; int64_t q_rows_bstride;
+  const int32_t* kv_len;
+  float scale;                            /* <= 0 means 1/sqrt(d) (Eq. 2) */
+  float* lse;
+  uint32_t flags;                         /* SAFE_ATTN_SCATTER_OUT | SAFE_FLAG_CHECK */
+} safe_attn_args;
+
+int safe_attn_fwd(const safe_attn_args* a, void* stream);
+
+/* Human-readable name of a status code (static storage). */
+const char* safe_status_str(int status);
+/* SAFE_ABI_VERSION of the built library. */
+int safe_abi_version(void);
+
+#ifdef __cplusplus
+}
+#endif
+#endif /* SAFE_DIT_SAFE_H */

@@ -1,0 +1,300 @@
+"""Python binding of libsafe, the MI355X (gfx950) SAFE-DiT attention hot path.
+
+Argument marshalling only: every step runs in the HIP kernels of libsafe.so;
+PyTorch supplies device memory and the current HIP stream.  There is no CPU
+fallback: importing the package fails loudly when the library is missing.
+
+Entry points (same names as the C ABI in include/safe.h):
+  mask_classify  -- Eq. 6-8 row-constant certification of an attention mask
+  pcsp_select    -- Eq. 9-12 sensitivity accumulation / smoothing / top-k
+  kv_assemble    -- Eq. 14, 16 global K/V from fresh rows over cached rows
+  attn_fwd       -- Eq. 2, 16-18 attention, dense or on gathered rows, with kv_len
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+from typing import Optional
+
+import torch
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(_HERE, "libsafe.so")
+
+SAFE_OK = 0
+STATUS = {0: "SAFE_OK", -1: "SAFE_ERR_NULL", -2: "SAFE_ERR_SHAPE", -3: "SAFE_ERR_DTYPE", -4: "SAFE_ERR_RANGE",
+          -5: "SAFE_ERR_UNSUPPORTED", -6: "SAFE_ERR_WORKSPACE", -7: "SAFE_ERR_HIP", -8: "SAFE_ERR_ALIGN"}
+
+FLAG_CHECK = 1 << 0
+ATTN_SCATTER_OUT = 1 << 1
+CLASSIFY_ASYNC = 1 << 2
+PCSP_ACCUM = 1 << 3
+PCSP_SELECT = 1 << 4
+
+DT_BOOL, DT_BF16, DT_F16, DT_F32 = 0, 1, 2, 3
+MASK_CLASS_NAMES = ("ALL_VALID", "ZERO", "ROW_CONST", "KEY_PADDING", "NONCONST", "BLOCKED", "NONFINITE")
+
+_i64x3 = ctypes.c_int64 * 3
+_i64x4 = ctypes.c_int64 * 4
+
+
+class MaskInfo(ctypes.Structure):
+    _fields_ = [("verdict", ctypes.c_int32), ("mask_class", ctypes.c_int32),
+                ("first_bad_row", ctypes.c_int64), ("rows", ctypes.c_int64)]
+
+
+class PcspArgs(ctypes.Structure):
+    _fields_ = [("flags", ctypes.c_uint32), ("B", ctypes.c_int32), ("N", ctypes.c_int32), ("M", ctypes.c_int32),
+                ("H", ctypes.c_int32), ("d", ctypes.c_int32),
+                ("q", ctypes.c_void_p), ("q_stride", _i64x3),
+                ("k_text", ctypes.c_void_p), ("k_stride", _i64x3),
+                ("kv_len", ctypes.c_void_p), ("w", ctypes.c_void_p), ("head_mask", ctypes.c_uint64),
+                ("scale", ctypes.c_float), ("acc", ctypes.c_void_p),
+                ("grid_h", ctypes.c_int32), ("grid_w", ctypes.c_int32), ("sigma", ctypes.c_float),
+                ("k", ctypes.c_int32), ("score_out", ctypes.c_void_p), ("idx_out", ctypes.c_void_p)]
+
+
+class KvArgs(ctypes.Structure):
+    _fields_ = [("B", ctypes.c_int32), ("N", ctypes.c_int32), ("H", ctypes.c_int32), ("d", ctypes.c_int32),
+                ("nsel", ctypes.c_int32),
+                ("k_fresh", ctypes.c_void_p), ("v_fresh", ctypes.c_void_p), ("fresh_stride", _i64x3),
+                ("idx", ctypes.c_void_p), ("idx_bstride", ctypes.c_int64),
+                ("k_cache", ctypes.c_void_p), ("v_cache", ctypes.c_void_p), ("cache_stride", _i64x3),
+                ("k_out", ctypes.c_void_p), ("v_out", ctypes.c_void_p), ("out_stride", _i64x3),
+                ("flags", ctypes.c_uint32)]
+
+
+class AttnArgs(ctypes.Structure):
+    _fields_ = [("B", ctypes.c_int32), ("H", ctypes.c_int32), ("Nq", ctypes.c_int32), ("Nk", ctypes.c_int32),
+                ("d", ctypes.c_int32),
+                ("q", ctypes.c_void_p), ("q_stride", _i64x3),
+                ("k", ctypes.c_void_p), ("k_stride", _i64x3),
+                ("v", ctypes.c_void_p), ("v_stride", _i64x3),
+                ("o", ctypes.c_void_p), ("o_stride", _i64x3),
+                ("q_rows", ctypes.c_void_p), ("n_rows", ctypes.c_int32), ("q_rows_bstride", ctypes.c_int64),
+                ("kv_len", ctypes.c_void_p), ("scale", ctypes.c_float), ("lse", ctypes.c_void_p),
+                ("flags", ctypes.c_uint32)]
+
+
+def _load():
+    if not os.path.exists(LIB_PATH):
+        raise ImportError(f"libsafe.so not found at {LIB_PATH}: build it with "
+                          "`python -m sparse_query_sdpa_amd.build` (no CPU fallback exists)")
+    lib = ctypes.CDLL(LIB_PATH)
+    lib.safe_abi_version.restype = ctypes.c_int
+    lib.safe_status_str.restype = ctypes.c_char_p
+    lib.safe_status_str.argtypes = [ctypes.c_int]
+    lib.safe_attn_fwd.restype = ctypes.c_int
+    lib.safe_attn_fwd.argtypes = [ctypes.POINTER(AttnArgs), ctypes.c_void_p]
+    lib.safe_kv_assemble.restype = ctypes.c_int
+    lib.safe_kv_assemble.argtypes = [ctypes.POINTER(KvArgs), ctypes.c_void_p]
+    lib.safe_pcsp_select.restype = ctypes.c_int
+    lib.safe_pcsp_select.argtypes = [ctypes.POINTER(PcspArgs), ctypes.c_void_p, ctypes.POINTER(ctypes.c_size_t),
+                                     ctypes.c_void_p]
+    lib.safe_mask_classify.restype = ctypes.c_int
+    lib.safe_mask_classify.argtypes = [ctypes.c_void_p, ctypes.c_int32, ctypes.POINTER(ctypes.c_int64),
+                                       ctypes.POINTER(ctypes.c_int64), ctypes.c_uint32, ctypes.POINTER(MaskInfo),
+                                       ctypes.c_void_p, ctypes.c_void_p, ctypes.c_void_p,
+                                       ctypes.POINTER(ctypes.c_size_t), ctypes.c_void_p]
+    return lib
+
+
+lib = _load()
+
+
+class SafeError(RuntimeError):
+    def __init__(self, fn: str, status: int):
+        super().__init__(f"{fn} failed: {lib.safe_status_str(status).decode()} ({status})")
+        self.status = status
+
+
+def _check(fn: str, status: int):
+    if status != SAFE_OK:
+        raise SafeError(fn, status)
+
+
+def _stream(stream=None) -> int:
+    s = stream if stream is not None else torch.cuda.current_stream()
+    return int(s.cuda_stream)
+
+
+def _ptr(t: Optional[torch.Tensor]) -> Optional[int]:
+    return None if t is None else t.data_ptr()
+
+
+def _bnhd(t: torch.Tensor, name: str):
+    if t.dim() != 4:
+        raise ValueError(f"{name} must be 4-D [B, N, H, d]")
+    if t.shape[3] > 1 and t.stride(3) != 1:
+        raise ValueError(f"{name}: the head dimension d must be contiguous")
+    return _i64x3(t.stride(0), t.stride(1), t.stride(2))
+
+
+def _bits16(t: torch.Tensor, name: str):
+    if t.dtype not in (torch.bfloat16, torch.float16, torch.int16, torch.uint16):
+        raise TypeError(f"{name} must be a 16-bit tensor (bf16 storage)")
+    if not t.is_cuda:
+        raise ValueError(f"{name} must be a device tensor")
+
+
+def _i32(t: Optional[torch.Tensor], name: str):
+    if t is None:
+        return None
+    if t.dtype != torch.int32 or not t.is_cuda:
+        raise TypeError(f"{name} must be an int32 device tensor")
+    return t
+
+
+# ---------------------------------------------------------------------------------
+def attn_fwd(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, q_rows: Optional[torch.Tensor] = None,
+             kv_len: Optional[torch.Tensor] = None, scale: Optional[float] = None, out: Optional[torch.Tensor] = None,
+             return_lse: bool = False, scatter_out: bool = False, check: bool = False, stream=None):
+    """Attention on all rows (q_rows None) or on gathered rows q_rows [n] / [B, n]; see safe.h."""
+    for t, n in ((q, "q"), (k, "k"), (v, "v")):
+        _bits16(t, n)
+    B, Nq, H, d = q.shape
+    Nk = k.shape[1]
+    if k.shape != (B, Nk, H, d) or v.shape != k.shape:
+        raise ValueError("k and v must be [B, Nk, H, d] matching q")
+    q_rows = _i32(q_rows, "q_rows")
+    kv_len = _i32(kv_len, "kv_len")
+    if q_rows is not None:
+        if q_rows.dim() == 1:
+            n_rows, bstride = q_rows.shape[0], 0
+        else:
+            if q_rows.shape[0] != B or q_rows.stride(1) != 1:
+                raise ValueError("q_rows must be [n] or [B, n] with contiguous rows")
+            n_rows, bstride = q_rows.shape[1], q_rows.stride(0)
+    else:
+        n_rows, bstride = Nq, 0
+    if out is None:
+        out = torch.empty((B, Nq if scatter_out else n_rows, H, d), dtype=q.dtype, device=q.device)
+    lse = torch.empty((B, H, n_rows), dtype=torch.float32, device=q.device) if return_lse else None
+    if q_rows is not None and n_rows == 0:   # an empty row list has no storage pointer: nothing to compute
+        return (out, lse) if return_lse else out
+    a = AttnArgs(B, H, Nq, Nk, d, _ptr(q), _bnhd(q, "q"), _ptr(k), _bnhd(k, "k"), _ptr(v), _bnhd(v, "v"),
+                 _ptr(out), _bnhd(out, "out"), _ptr(q_rows), n_rows, bstride, _ptr(kv_len),
+                 0.0 if scale is None else float(scale), _ptr(lse),
+                 (ATTN_SCATTER_OUT if scatter_out else 0) | (FLAG_CHECK if check else 0))
+    _check("safe_attn_fwd", lib.safe_attn_fwd(ctypes.byref(a), _stream(stream)))
+    return (out, lse) if return_lse else out
+
+
+def kv_assemble(k_fresh: torch.Tensor, v_fresh: torch.Tensor, idx: torch.Tensor, k_cache: torch.Tensor,
+                v_cache: torch.Tensor, k_out: Optional[torch.Tensor] = None, v_out: Optional[torch.Tensor] = None,
+                in_place: bool = False, check: bool = False, stream=None):
+    """Global K/V = fresh rows (token idx) over cached rows; see safe.h.  Returns (k_out, v_out)."""
+    for t, n in ((k_fresh, "k_fresh"), (v_fresh, "v_fresh"), (k_cache, "k_cache"), (v_cache, "v_cache")):
+        _bits16(t, n)
+    B, N, H, d = k_cache.shape
+    idx = _i32(idx, "idx")
+    if idx.dim() == 1:
+        nsel, ibs = idx.shape[0], 0
+    else:
+        nsel, ibs = idx.shape[1], idx.stride(0)
+    if k_fresh.shape != (B, nsel, H, d) or v_fresh.shape != k_fresh.shape or v_cache.shape != k_cache.shape:
+        raise ValueError("shape mismatch: fresh [B, nsel, H, d], cache [B, N, H, d]")
+    if in_place:
+        k_out, v_out = k_cache, v_cache
+    else:
+        if k_out is None:
+            k_out = torch.empty_like(k_cache)
+        if v_out is None:
+            v_out = torch.empty_like(v_cache)
+    a = KvArgs(B, N, H, d, nsel, _ptr(k_fresh), _ptr(v_fresh), _bnhd(k_fresh, "k_fresh"), _ptr(idx), ibs,
+               _ptr(k_cache), _ptr(v_cache), _bnhd(k_cache, "k_cache"), _ptr(k_out), _ptr(v_out),
+               _bnhd(k_out, "k_out"), FLAG_CHECK if check else 0)
+    if _bnhd(v_fresh, "v_fresh")[:] != a.fresh_stride[:] or _bnhd(v_cache, "v_cache")[:] != a.cache_stride[:] \
+            or _bnhd(v_out, "v_out")[:] != a.out_stride[:]:
+        raise ValueError("k and v tensors must share strides")
+    _check("safe_kv_assemble", lib.safe_kv_assemble(ctypes.byref(a), _stream(stream)))
+    return k_out, v_out
+
+
+_MASK_DT = {torch.bool: DT_BOOL, torch.uint8: DT_BOOL, torch.bfloat16: DT_BF16, torch.float16: DT_F16,
+            torch.float32: DT_F32}
+
+
+def mask_classify(mask: torch.Tensor, row_class: bool = False, kv_len: bool = False, workspace=None,
+                  asynchronous: bool = False, stream=None) -> dict:
+    """Certify a [B, H, Nq, Nk] mask (as stored); returns a dict with verdict, class, first bad row, rows."""
+    if mask.dim() != 4:
+        raise ValueError("mask must be 4-D [B, H, Nq, Nk] (broadcast dims stored with size 1)")
+    if mask.dtype not in _MASK_DT:
+        raise TypeError(f"unsupported mask dtype {mask.dtype}")
+    if not mask.is_cuda:
+        raise ValueError("mask must be a device tensor")
+    dt = _MASK_DT[mask.dtype]
+    size = _i64x4(*mask.shape)
+    stride = _i64x4(*mask.stride())
+    need = ctypes.c_size_t(0)
+    s = _stream(stream)
+    _check("safe_mask_classify", lib.safe_mask_classify(None, dt, size, stride, 0, None, None, None, None,
+                                                        ctypes.byref(need), s))
+    if workspace is None or workspace.numel() < need.value:
+        workspace = torch.empty(need.value, dtype=torch.uint8, device=mask.device)
+    rc = torch.empty(mask.shape[0] * mask.shape[1] * mask.shape[2], dtype=torch.uint8, device=mask.device) \
+        if row_class else None
+    kl = torch.empty(mask.shape[0], dtype=torch.int32, device=mask.device) if kv_len else None
+    info = MaskInfo()
+    flags = CLASSIFY_ASYNC if asynchronous else 0
+    # torch.bool storage is one byte per element (0/1): read as uint8
+    _check("safe_mask_classify", lib.safe_mask_classify(_ptr(mask), dt, size, stride, flags, ctypes.byref(info),
+                                                        _ptr(rc), _ptr(kl), _ptr(workspace), ctypes.byref(need), s))
+    out = {"row_class": rc, "kv_len": kl, "workspace": workspace}
+    if not asynchronous:
+        out.update(verdict=info.verdict, mask_class=info.mask_class, first_bad_row=info.first_bad_row,
+                   rows=info.rows, class_name=MASK_CLASS_NAMES[info.mask_class])
+    return out
+
+
+def pcsp_accumulate(q_c: torch.Tensor, k_txt: torch.Tensor, w: torch.Tensor, acc: torch.Tensor,
+                    kv_len: Optional[torch.Tensor] = None, head_mask: int = 0, scale: Optional[float] = None,
+                    stream=None) -> torch.Tensor:
+    """acc[b, i] += sum_h sum_j w[b, j] softmax_j(scale q_c[b,i,h] . k_txt[b,j,h])  (Eq. 9-10)."""
+    _bits16(q_c, "q_c")
+    _bits16(k_txt, "k_txt")
+    B, N, H, d = q_c.shape
+    M = k_txt.shape[1]
+    if w.dtype != torch.float32 or w.shape != (B, M) or not w.is_contiguous():
+        raise ValueError("w must be contiguous float32 [B, M]")
+    if acc.dtype != torch.float32 or acc.shape != (B, N) or not acc.is_contiguous():
+        raise ValueError("acc must be contiguous float32 [B, N]")
+    kv_len = _i32(kv_len, "kv_len")
+    a = PcspArgs()
+    a.flags = PCSP_ACCUM
+    a.B, a.N, a.M, a.H, a.d = B, N, M, H, d
+    a.q, a.q_stride = _ptr(q_c), _bnhd(q_c, "q_c")
+    a.k_text, a.k_stride = _ptr(k_txt), _bnhd(k_txt, "k_txt")
+    a.kv_len, a.w, a.head_mask = _ptr(kv_len), _ptr(w), head_mask
+    a.scale = 0.0 if scale is None else float(scale)
+    a.acc = _ptr(acc)
+    _check("safe_pcsp_select", lib.safe_pcsp_select(ctypes.byref(a), None, None, _stream(stream)))
+    return acc
+
+
+def pcsp_select(acc: torch.Tensor, grid_h: int, grid_w: int, sigma: float, k: int, score_out: bool = False,
+                workspace=None, stream=None):
+    """Eq. 11-12: smoothed field, optional Norm output, ascending top-k indices [B, k] int32."""
+    if acc.dtype != torch.float32 or acc.dim() != 2 or not acc.is_contiguous():
+        raise ValueError("acc must be contiguous float32 [B, N]")
+    B, N = acc.shape
+    a = PcspArgs()
+    a.flags = PCSP_SELECT
+    a.B, a.N = B, N
+    a.acc = _ptr(acc)
+    a.grid_h, a.grid_w, a.sigma, a.k = grid_h, grid_w, float(sigma), k
+    idx = torch.empty((B, k), dtype=torch.int32, device=acc.device)
+    so = torch.empty_like(acc) if score_out else None
+    a.score_out, a.idx_out = _ptr(so), _ptr(idx)
+    need = ctypes.c_size_t(0)
+    s = _stream(stream)
+    _check("safe_pcsp_select", lib.safe_pcsp_select(ctypes.byref(a), None, ctypes.byref(need), s))
+    if workspace is None or workspace.numel() < need.value:
+        workspace = torch.empty(max(need.value, 1), dtype=torch.uint8, device=acc.device)
+    _check("safe_pcsp_select", lib.safe_pcsp_select(ctypes.byref(a), _ptr(workspace), ctypes.byref(need), s))
+    return (idx, so) if score_out else idx
+
+
+__all__ = ["attn_fwd", "kv_assemble", "mask_classify", "pcsp_accumulate", "pcsp_select", "lib", "SafeError",
+           "LIB_PATH", "MASK_CLASS_NAMES"]

@@ -1,0 +1,214 @@
+// libsafe C ABI: argument validation (host only, before any HIP call) and dispatch.
+#include <math.h>
+#include <string.h>
+
+#include <vector>
+
+#include "common.h"
+
+namespace safe {
+int attn_fwd_launch(const safe_attn_args* a, float scale, hipStream_t stream);
+int kv_assemble_launch(const safe_kv_args* a, bool in_place, hipStream_t stream);
+int mask_classify_launch(const void* mask, int32_t dtype, const int64_t size[4], const int64_t stride[4],
+                         uint32_t flags, safe_mask_info* info, uint8_t* row_class, int32_t* kv_len_out,
+                         void* workspace, hipStream_t stream);
+size_t mask_classify_workspace(const int64_t size[4]);
+int pcsp_launch(const safe_pcsp_args* a, float scale, void* workspace, hipStream_t stream);
+size_t pcsp_workspace(const safe_pcsp_args* a);
+}  // namespace safe
+
+using namespace safe;
+
+namespace {
+
+bool supported_head_dim(int d) { return d == 32 || d == 64 || d == 96 || d == 128; }
+
+bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
+
+// A [B, N, H, d] 16-bit tensor read or written in 16-byte chunks: every row start
+// must be 16-byte aligned (strides multiples of 8 elements) and strides >= 0.
+int check_bnhd(const void* p, const int64_t st[3], bool need) {
+  if (p == nullptr) return need ? SAFE_ERR_NULL : SAFE_OK;
+  for (int i = 0; i < 3; ++i) {
+    if (st[i] < 0) return SAFE_ERR_SHAPE;
+    if (st[i] % 8 != 0) return SAFE_ERR_ALIGN;
+  }
+  if (!aligned16(p)) return SAFE_ERR_ALIGN;
+  return SAFE_OK;
+}
+
+float resolve_scale(float scale, int d) { return scale > 0.f ? scale : 1.0f / sqrtf((float)d); }
+
+template <typename T>
+int copy_to_host(std::vector<T>& dst, const T* src, size_t n, hipStream_t s) {
+  dst.resize(n);
+  if (n == 0) return SAFE_OK;
+  if (hipMemcpyAsync(dst.data(), src, n * sizeof(T), hipMemcpyDeviceToHost, s) != hipSuccess) return SAFE_ERR_HIP;
+  if (hipStreamSynchronize(s) != hipSuccess) return SAFE_ERR_HIP;
+  return SAFE_OK;
+}
+
+// SAFE_FLAG_CHECK: index lists ascending? (attention only needs range; assembly
+// needs range and distinctness, which ascending order guarantees.)
+int check_rows(const int32_t* rows, int B, int n, int64_t bstride, int limit, bool ascending, hipStream_t s) {
+  const int nb = bstride == 0 ? 1 : B;
+  for (int b = 0; b < nb; ++b) {
+    std::vector<int32_t> h;
+    int st = copy_to_host(h, rows + (int64_t)b * bstride, (size_t)n, s);
+    if (st != SAFE_OK) return st;
+    for (int i = 0; i < n; ++i) {
+      if (h[i] < 0 || h[i] >= limit) return SAFE_ERR_RANGE;
+      if (ascending && i > 0 && h[i] <= h[i - 1]) return SAFE_ERR_RANGE;
+    }
+  }
+  return SAFE_OK;
+}
+
+int check_lengths(const int32_t* len, int B, int limit, hipStream_t s) {
+  std::vector<int32_t> h;
+  int st = copy_to_host(h, len, (size_t)B, s);
+  if (st != SAFE_OK) return st;
+  for (int b = 0; b < B; ++b)
+    if (h[b] < 0 || h[b] > limit) return SAFE_ERR_RANGE;
+  return SAFE_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+int safe_abi_version(void) { return SAFE_ABI_VERSION; }
+
+const char* safe_status_str(int status) {
+  switch (status) {
+    case SAFE_OK: return "SAFE_OK";
+    case SAFE_ERR_NULL: return "SAFE_ERR_NULL: a required pointer is NULL";
+    case SAFE_ERR_SHAPE: return "SAFE_ERR_SHAPE: sizes or strides inconsistent or out of range";
+    case SAFE_ERR_DTYPE: return "SAFE_ERR_DTYPE: unknown dtype code";
+    case SAFE_ERR_RANGE: return "SAFE_ERR_RANGE: a scalar or device value is out of range";
+    case SAFE_ERR_UNSUPPORTED: return "SAFE_ERR_UNSUPPORTED: valid request the library does not implement";
+    case SAFE_ERR_WORKSPACE: return "SAFE_ERR_WORKSPACE: workspace missing or too small";
+    case SAFE_ERR_HIP: return "SAFE_ERR_HIP: a HIP runtime call failed";
+    case SAFE_ERR_ALIGN: return "SAFE_ERR_ALIGN: pointer or stride breaks 16-byte alignment";
+    default: return "unknown status";
+  }
+}
+
+int safe_attn_fwd(const safe_attn_args* a, void* stream) {
+  if (a == nullptr) return SAFE_ERR_NULL;
+  if (a->B < 0 || a->H < 0 || a->Nq < 0 || a->Nk < 0 || a->n_rows < 0) return SAFE_ERR_SHAPE;
+  if (!supported_head_dim(a->d)) return SAFE_ERR_UNSUPPORTED;
+  if (!(isfinite(a->scale))) return SAFE_ERR_RANGE;
+  if (a->q_rows == nullptr && a->n_rows != a->Nq) return SAFE_ERR_SHAPE;
+  if (a->q_rows == nullptr && (a->flags & SAFE_ATTN_SCATTER_OUT)) return SAFE_ERR_SHAPE;
+  if (a->q_rows != nullptr && a->q_rows_bstride < 0) return SAFE_ERR_SHAPE;
+  if (a->q_rows != nullptr && a->q_rows_bstride != 0 && a->q_rows_bstride < a->n_rows) return SAFE_ERR_SHAPE;
+  if (a->flags & ~(SAFE_ATTN_SCATTER_OUT | SAFE_FLAG_CHECK)) return SAFE_ERR_RANGE;
+  const bool work = (int64_t)a->B * a->H * a->n_rows > 0;
+  int st;
+  if ((st = check_bnhd(a->q, a->q_stride, work)) != SAFE_OK) return st;
+  if ((st = check_bnhd(a->k, a->k_stride, work && a->Nk > 0)) != SAFE_OK) return st;
+  if ((st = check_bnhd(a->v, a->v_stride, work && a->Nk > 0)) != SAFE_OK) return st;
+  if ((st = check_bnhd(a->o, a->o_stride, work)) != SAFE_OK) return st;
+  if (!work) return SAFE_OK;
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  if (a->flags & SAFE_FLAG_CHECK) {
+    if (a->q_rows != nullptr &&
+        (st = check_rows(a->q_rows, a->B, a->n_rows, a->q_rows_bstride, a->Nq, false, s)) != SAFE_OK)
+      return st;
+    if (a->kv_len != nullptr && (st = check_lengths(a->kv_len, a->B, a->Nk, s)) != SAFE_OK) return st;
+  }
+  return attn_fwd_launch(a, resolve_scale(a->scale, a->d), s);
+}
+
+int safe_kv_assemble(const safe_kv_args* a, void* stream) {
+  if (a == nullptr) return SAFE_ERR_NULL;
+  if (a->B < 0 || a->N < 0 || a->H < 0 || a->d < 0 || a->nsel < 0) return SAFE_ERR_SHAPE;
+  if (a->d % 8 != 0) return SAFE_ERR_ALIGN;
+  if (a->nsel > a->N) return SAFE_ERR_SHAPE;
+  if (a->idx_bstride < 0 || (a->idx_bstride != 0 && a->idx_bstride < a->nsel)) return SAFE_ERR_SHAPE;
+  if (a->flags & ~SAFE_FLAG_CHECK) return SAFE_ERR_RANGE;
+  const bool any = (int64_t)a->B * a->N * a->H * a->d > 0;
+  const bool sel = any && a->nsel > 0;
+  int st;
+  if ((st = check_bnhd(a->k_cache, a->cache_stride, any)) != SAFE_OK) return st;
+  if ((st = check_bnhd(a->v_cache, a->cache_stride, any)) != SAFE_OK) return st;
+  if ((st = check_bnhd(a->k_out, a->out_stride, any)) != SAFE_OK) return st;
+  if ((st = check_bnhd(a->v_out, a->out_stride, any)) != SAFE_OK) return st;
+  if ((st = check_bnhd(a->k_fresh, a->fresh_stride, sel)) != SAFE_OK) return st;
+  if ((st = check_bnhd(a->v_fresh, a->fresh_stride, sel)) != SAFE_OK) return st;
+  if (sel && a->idx == nullptr) return SAFE_ERR_NULL;
+  if (!any) return SAFE_OK;
+  const bool k_same = a->k_out == a->k_cache, v_same = a->v_out == a->v_cache;
+  const bool same_strides = memcmp(a->out_stride, a->cache_stride, sizeof(a->out_stride)) == 0;
+  if (k_same != v_same) return SAFE_ERR_SHAPE;            // half in place is not supported
+  if (k_same && !same_strides) return SAFE_ERR_SHAPE;     // aliasing with different strides
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  if ((a->flags & SAFE_FLAG_CHECK) && sel &&
+      (st = check_rows(a->idx, a->B, a->nsel, a->idx_bstride, a->N, true, s)) != SAFE_OK)
+    return st;
+  return kv_assemble_launch(a, k_same, s);
+}
+
+int safe_mask_classify(const void* mask, int32_t dtype, const int64_t size[4], const int64_t stride[4],
+                       uint32_t flags, safe_mask_info* info, uint8_t* row_class, int32_t* kv_len_out,
+                       void* workspace, size_t* workspace_bytes, void* stream) {
+  if (size == nullptr || stride == nullptr) return SAFE_ERR_NULL;
+  if (dtype < SAFE_DT_BOOL || dtype > SAFE_DT_F32) return SAFE_ERR_DTYPE;
+  for (int i = 0; i < 4; ++i)
+    if (size[i] < 0 || stride[i] < 0) return SAFE_ERR_SHAPE;
+  if (size[3] > 1 && stride[3] != 1) return SAFE_ERR_SHAPE;
+  if (size[0] > 0x7fffffff || size[3] > 0x7fffffff) return SAFE_ERR_SHAPE;
+  if (flags & ~SAFE_CLASSIFY_ASYNC) return SAFE_ERR_RANGE;
+  const size_t need = mask_classify_workspace(size);
+  if (workspace == nullptr) {
+    if (workspace_bytes == nullptr) return SAFE_ERR_WORKSPACE;
+    *workspace_bytes = need;
+    return SAFE_OK;
+  }
+  if (workspace_bytes != nullptr && *workspace_bytes < need) return SAFE_ERR_WORKSPACE;
+  if (!(flags & SAFE_CLASSIFY_ASYNC) && info == nullptr) return SAFE_ERR_NULL;
+  const int64_t rows = size[0] * size[1] * size[2];
+  if (rows > 0 && size[3] > 0 && mask == nullptr) return SAFE_ERR_NULL;
+  if ((reinterpret_cast<uintptr_t>(workspace) & 15u) != 0) return SAFE_ERR_ALIGN;
+  return mask_classify_launch(mask, dtype, size, stride, flags, info, row_class, kv_len_out, workspace,
+                              static_cast<hipStream_t>(stream));
+}
+
+int safe_pcsp_select(const safe_pcsp_args* a, void* workspace, size_t* workspace_bytes, void* stream) {
+  if (a == nullptr) return SAFE_ERR_NULL;
+  const uint32_t ops = a->flags & (SAFE_PCSP_ACCUM | SAFE_PCSP_SELECT);
+  if (ops == 0 || (a->flags & ~(SAFE_PCSP_ACCUM | SAFE_PCSP_SELECT))) return SAFE_ERR_RANGE;
+  if (a->B < 0 || a->N < 0 || a->M < 0 || a->H < 0) return SAFE_ERR_SHAPE;
+  const bool sel = (a->flags & SAFE_PCSP_SELECT) != 0;
+  const bool accum = (a->flags & SAFE_PCSP_ACCUM) != 0;
+  if (sel) {
+    const size_t need = pcsp_workspace(a);
+    if (workspace == nullptr && need > 0) {
+      if (workspace_bytes == nullptr) return SAFE_ERR_WORKSPACE;
+      *workspace_bytes = need;
+      return SAFE_OK;
+    }
+    if (workspace_bytes != nullptr && *workspace_bytes < need) return SAFE_ERR_WORKSPACE;
+    if (a->grid_h < 0 || a->grid_w < 0 || (int64_t)a->grid_h * a->grid_w != a->N) return SAFE_ERR_SHAPE;
+    if (!(a->sigma >= 0.f && a->sigma <= 32.f)) return SAFE_ERR_RANGE;
+    if (a->k < 0 || a->k > a->N) return SAFE_ERR_RANGE;
+    if (a->B > 0 && a->N > 0 && a->acc == nullptr) return SAFE_ERR_NULL;
+    if (a->B > 0 && a->k > 0 && a->idx_out == nullptr) return SAFE_ERR_NULL;
+  }
+  if (accum) {
+    if (!supported_head_dim(a->d)) return SAFE_ERR_UNSUPPORTED;
+    if (a->M > 1024) return SAFE_ERR_UNSUPPORTED;
+    if (a->head_mask != 0 && a->H > 64) return SAFE_ERR_RANGE;
+    if (a->head_mask != 0 && a->H < 64 && (a->head_mask >> a->H) != 0) return SAFE_ERR_RANGE;
+    if (!isfinite(a->scale)) return SAFE_ERR_RANGE;
+    const bool work = (int64_t)a->B * a->N * a->H > 0 && a->M > 0;
+    int st;
+    if ((st = check_bnhd(a->q, a->q_stride, work)) != SAFE_OK) return st;
+    if ((st = check_bnhd(a->k_text, a->k_stride, work)) != SAFE_OK) return st;
+    if (work && (a->w == nullptr || a->acc == nullptr)) return SAFE_ERR_NULL;
+  }
+  return pcsp_launch(a, accum ? resolve_scale(a->scale, a->d) : 0.f, workspace, static_cast<hipStream_t>(stream));
+}
+
+}  // extern "C"

@@ -1,0 +1,45 @@
+// Internal helpers shared by the libsafe kernels (gfx950 / CDNA4, wave64).
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+#include "../../include/safe.h"
+
+namespace safe {
+
+typedef unsigned short u16;
+typedef unsigned int u32;
+typedef u32 u32x2 __attribute__((ext_vector_type(2)));
+typedef u32 u32x4 __attribute__((ext_vector_type(4)));
+typedef float f32x4 __attribute__((ext_vector_type(4)));
+typedef float f32x16 __attribute__((ext_vector_type(16)));
+typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+
+constexpr int kWave = 64;
+constexpr int kNumXcd = 8;  // MI355X: 8 accelerator complex dies, workgroups dealt round-robin
+
+// Workgroup id -> logical id such that consecutive logical ids run on the same XCD.
+// The dispatcher places workgroup L on XCD L % 8; XCD x receives ceil/floor(total/8)
+// workgroups, and its s-th one gets logical id (first id of x) + s.
+__device__ __forceinline__ int xcd_remap(int L, int total) {
+  const int per = total / kNumXcd, rem = total % kNumXcd;
+  const int x = L % kNumXcd, s = L / kNumXcd;
+  return x * per + (x < rem ? x : rem) + s;
+}
+
+__device__ __forceinline__ u32x4 ld16(const void* p) { return *reinterpret_cast<const u32x4*>(p); }
+__device__ __forceinline__ void st16(void* p, u32x4 v) { *reinterpret_cast<u32x4*>(p) = v; }
+__device__ __forceinline__ void st8(void* p, u32x2 v) { *reinterpret_cast<u32x2*>(p) = v; }
+
+__device__ __forceinline__ bf16x8 as_bf16x8(u32x4 v) { return __builtin_bit_cast(bf16x8, v); }
+
+// Round-to-nearest-even float -> bfloat16 bits (finite and infinite inputs; NaN stays NaN).
+__device__ __forceinline__ u32 pack_bf16x2(float lo, float hi) {
+  __bf16 a = (__bf16)lo, b = (__bf16)hi;
+  return (u32)__builtin_bit_cast(u16, a) | ((u32)__builtin_bit_cast(u16, b) << 16);
+}
+
+inline int64_t ceil_div64(int64_t a, int64_t b) { return (a + b - 1) / b; }
+
+}  // namespace safe

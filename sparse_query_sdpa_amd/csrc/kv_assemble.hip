@@ -1,0 +1,157 @@
+// Global K/V assembly for SRSU ("SAFE-DiT" Eq. 14 and 16): the fresh rows of the
+// sensitive set S are placed, in the original token order, over the cached
+// context rows of the last anchor.
+//
+// Out of place: a workgroup owns 32 consecutive tokens of one sample.  It finds
+// which of them are in S with one binary search of the ascending index list
+// (lower bound of the first token) plus a 32-entry map in LDS, then streams each
+// token's K and V rows from their single source to the output in 16-byte chunks.
+// Every output byte is read once and written once.
+// In place (output == cache): a workgroup copies 32 fresh rows to their tokens;
+// context rows are not touched.
+// Index entries outside [0, N) are skipped, so no index value can address
+// memory outside the tensors.
+#include "common.h"
+
+namespace safe {
+namespace {
+
+constexpr int TOK = 32;
+constexpr int NT = 256;
+
+struct KvParams {
+  const u16* kf; const u16* vf; int64_t fs0, fs1, fs2;
+  const int32_t* idx; int64_t ibs;
+  const u16* kc; const u16* vc; int64_t cs0, cs1, cs2;
+  u16* ko; u16* vo; int64_t os0, os1, os2;
+  int B, N, H, d8, nsel, blocks_per_b;
+};
+
+__global__ __launch_bounds__(NT) void kv_assemble_kernel(KvParams p) {
+  __shared__ int src_row[TOK];
+  const int tid = threadIdx.x;
+  const int b = blockIdx.x / p.blocks_per_b;
+  const int j0 = (blockIdx.x % p.blocks_per_b) * TOK;
+  const int32_t* idx = p.idx + (int64_t)b * p.ibs;
+
+  if (tid < TOK) src_row[tid] = -1;
+  __syncthreads();
+  if (p.nsel > 0 && tid < TOK) {
+    // lower bound of j0 in the ascending list (each of the 32 threads searches; cheap)
+    int lo = 0, hi = p.nsel;
+    while (lo < hi) {
+      const int mid = (lo + hi) >> 1;
+      if (idx[mid] < j0) lo = mid + 1; else hi = mid;
+    }
+    const int r = lo + tid;
+    if (r < p.nsel) {
+      const int j = idx[r];
+      if (j >= j0 && j < j0 + TOK && j < p.N) src_row[j - j0] = r;
+    }
+  }
+  __syncthreads();
+
+  const int ntok = min(TOK, p.N - j0);
+  const int cpr = p.H * p.d8;  // 16-byte chunks per token row
+  for (int c = tid; c < cpr; c += NT) {
+    const int hh = c / p.d8, part = c % p.d8;
+    const int64_t fo = (int64_t)b * p.fs0 + (int64_t)hh * p.fs2 + part * 8;
+    const int64_t co = (int64_t)b * p.cs0 + (int64_t)hh * p.cs2 + part * 8;
+    const int64_t oo = (int64_t)b * p.os0 + (int64_t)hh * p.os2 + part * 8;
+    constexpr int U = 8;
+    for (int t0 = 0; t0 < ntok; t0 += U) {
+      u32x4 kv[U], vv[U];
+#pragma unroll
+      for (int u = 0; u < U; ++u) {
+        const int t = t0 + u;
+        if (t < ntok) {
+          const int r = src_row[t];
+          const u16* ks = r >= 0 ? p.kf + fo + (int64_t)r * p.fs1 : p.kc + co + (int64_t)(j0 + t) * p.cs1;
+          const u16* vs = r >= 0 ? p.vf + fo + (int64_t)r * p.fs1 : p.vc + co + (int64_t)(j0 + t) * p.cs1;
+          kv[u] = ld16(ks);
+          vv[u] = ld16(vs);
+        }
+      }
+#pragma unroll
+      for (int u = 0; u < U; ++u) {
+        const int t = t0 + u;
+        if (t < ntok) {
+          st16(p.ko + oo + (int64_t)(j0 + t) * p.os1, kv[u]);
+          st16(p.vo + oo + (int64_t)(j0 + t) * p.os1, vv[u]);
+        }
+      }
+    }
+  }
+}
+
+__global__ __launch_bounds__(NT) void kv_scatter_kernel(KvParams p) {
+  const int tid = threadIdx.x;
+  const int b = blockIdx.x / p.blocks_per_b;
+  const int r0 = (blockIdx.x % p.blocks_per_b) * TOK;
+  const int32_t* idx = p.idx + (int64_t)b * p.ibs;
+  const int nr = min(TOK, p.nsel - r0);
+  const int cpr = p.H * p.d8;
+  for (int c = tid; c < cpr; c += NT) {
+    const int hh = c / p.d8, part = c % p.d8;
+    const int64_t fo = (int64_t)b * p.fs0 + (int64_t)hh * p.fs2 + part * 8;
+    const int64_t oo = (int64_t)b * p.os0 + (int64_t)hh * p.os2 + part * 8;
+    constexpr int U = 8;
+    for (int t0 = 0; t0 < nr; t0 += U) {
+      u32x4 kv[U], vv[U];
+      int dst[U];
+#pragma unroll
+      for (int u = 0; u < U; ++u) {
+        const int r = r0 + t0 + u;
+        dst[u] = -1;
+        if (t0 + u < nr) {
+          const int j = idx[r];
+          if (j >= 0 && j < p.N) {
+            dst[u] = j;
+            kv[u] = ld16(p.kf + fo + (int64_t)r * p.fs1);
+            vv[u] = ld16(p.vf + fo + (int64_t)r * p.fs1);
+          }
+        }
+      }
+#pragma unroll
+      for (int u = 0; u < U; ++u) {
+        if (dst[u] >= 0) {
+          st16(p.ko + oo + (int64_t)dst[u] * p.os1, kv[u]);
+          st16(p.vo + oo + (int64_t)dst[u] * p.os1, vv[u]);
+        }
+      }
+    }
+  }
+}
+
+}  // namespace
+
+int kv_assemble_launch(const safe_kv_args* a, bool in_place, hipStream_t s) {
+  KvParams p;
+  p.kf = static_cast<const u16*>(a->k_fresh);
+  p.vf = static_cast<const u16*>(a->v_fresh);
+  p.fs0 = a->fresh_stride[0]; p.fs1 = a->fresh_stride[1]; p.fs2 = a->fresh_stride[2];
+  p.idx = a->idx;
+  p.ibs = a->idx_bstride;
+  p.kc = static_cast<const u16*>(a->k_cache);
+  p.vc = static_cast<const u16*>(a->v_cache);
+  p.cs0 = a->cache_stride[0]; p.cs1 = a->cache_stride[1]; p.cs2 = a->cache_stride[2];
+  p.ko = static_cast<u16*>(a->k_out);
+  p.vo = static_cast<u16*>(a->v_out);
+  p.os0 = a->out_stride[0]; p.os1 = a->out_stride[1]; p.os2 = a->out_stride[2];
+  p.B = a->B; p.N = a->N; p.H = a->H; p.d8 = a->d / 8; p.nsel = a->nsel;
+  if (in_place) {
+    if (a->nsel == 0) return SAFE_OK;
+    p.blocks_per_b = (a->nsel + TOK - 1) / TOK;
+    const int64_t grid = (int64_t)p.blocks_per_b * a->B;
+    if (grid > 0x7fffffff) return SAFE_ERR_SHAPE;
+    hipLaunchKernelGGL(kv_scatter_kernel, dim3((unsigned)grid), dim3(NT), 0, s, p);
+  } else {
+    p.blocks_per_b = (a->N + TOK - 1) / TOK;
+    const int64_t grid = (int64_t)p.blocks_per_b * a->B;
+    if (grid > 0x7fffffff) return SAFE_ERR_SHAPE;
+    hipLaunchKernelGGL(kv_assemble_kernel, dim3((unsigned)grid), dim3(NT), 0, s, p);
+  }
+  return hipGetLastError() == hipSuccess ? SAFE_OK : SAFE_ERR_HIP;
+}
+
+}  // namespace safe

@@ -1,0 +1,349 @@
+// Prompt-Conditioned Sensitivity Partitioning ("SAFE-DiT" Eq. 9-12).
+//
+// ACCUM (Eq. 9-10): acc[b,i] += sum_{h in head set} sum_{j<L_b} w[b,j] softmax_j(scale q_i.k_j).
+//   A workgroup owns 128 image tokens of one sample (4 waves x 32).  For each head
+//   the text keys stream through LDS in tiles of 64; S^T = K_txt Q^T runs on
+//   v_mfma_f32_32x32x16_bf16 exactly as in the attention kernel (each lane owns one
+//   image token), and instead of a P V product each lane keeps an online softmax
+//   numerator sum_j w_j p_j and denominator sum_j p_j.  The probabilities are never
+//   stored: only the N-vector acc is kept, as the paper's instrumentation does.
+// SELECT (Eq. 11-12): one workgroup per sample (1024 threads).
+//   Separable Gaussian (rows, then columns) with the in-grid taps renormalised,
+//   min-max normalisation for the optional score output, then an exact top-k:
+//   order-preserving 32-bit keys (-0 folded to +0, NaN lowest), a 4 x 8-bit radix
+//   select of the k-th key, and an ordered compaction that keeps every key above
+//   it plus the lowest-index ties, so the result is a deterministic ascending list.
+#include <limits.h>
+
+#include "common.h"
+
+namespace safe {
+namespace {
+
+// ============================== ACCUM ========================================
+constexpr int ABM = 128;
+constexpr int ABN = 64;
+constexpr int ANT = 256;
+
+struct AccParams {
+  const u16* q; int64_t qs0, qs1, qs2;
+  const u16* kt; int64_t ks0, ks1, ks2;
+  const int32_t* kv_len;
+  const float* w;
+  float* acc;
+  uint64_t head_mask;
+  int B, N, M, H, tiles_per_b;
+  float scale_log2;
+};
+
+template <int D>
+__global__ __launch_bounds__(ANT) void pcsp_accum_kernel(AccParams p) {
+  constexpr int KS = D / 16;
+  constexpr int PARTS = D / 8;
+  constexpr int KCH = ABN * PARTS;
+  __shared__ __attribute__((aligned(16))) u16 Ks[ABN][D + 8];
+  __shared__ float Ws[ABN];
+
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int col = lane & 31, half = lane >> 5;
+  const int b = blockIdx.x / p.tiles_per_b;
+  const int tile = blockIdx.x % p.tiles_per_b;
+  const int i = tile * ABM + wave * 32 + col;
+  const bool ok = i < p.N;
+
+  int L = p.kv_len ? p.kv_len[b] : p.M;
+  L = L < 0 ? 0 : (L > p.M ? p.M : L);
+  const int ntiles = (L + ABN - 1) / ABN;
+  const float sl2 = p.scale_log2;
+
+  float total = 0.f;
+  for (int h = 0; h < p.H; ++h) {
+    if (p.head_mask != 0 && !((p.head_mask >> h) & 1ull)) continue;
+    bf16x8 qf[KS];
+    const u16* qp = p.q + (int64_t)b * p.qs0 + (int64_t)(ok ? i : 0) * p.qs1 + (int64_t)h * p.qs2 + half * 8;
+#pragma unroll
+    for (int s = 0; s < KS; ++s) {
+      u32x4 v = {0u, 0u, 0u, 0u};
+      if (ok) v = ld16(qp + s * 16);
+      qf[s] = as_bf16x8(v);
+    }
+    float m = -INFINITY, num = 0.f, den = 0.f;
+    const u16* kb = p.kt + (int64_t)b * p.ks0 + (int64_t)h * p.ks2;
+    for (int it = 0; it < ntiles; ++it) {
+      const int j0 = it * ABN;
+      __syncthreads();  // previous tile consumed
+      for (int c = tid; c < KCH; c += ANT) {
+        const int key = c / PARTS, part = c % PARTS;
+        u32x4 v = {0u, 0u, 0u, 0u};
+        if (j0 + key < L) v = ld16(kb + (int64_t)(j0 + key) * p.ks1 + part * 8);
+        st16(&Ks[key][part * 8], v);
+      }
+      if (tid < ABN) Ws[tid] = (j0 + tid < L) ? p.w[(int64_t)b * p.M + j0 + tid] : 0.f;
+      __syncthreads();
+      f32x16 sacc[2];
+#pragma unroll
+      for (int blk = 0; blk < 2; ++blk) {
+        f32x16 a = f32x16{};
+#pragma unroll
+        for (int s = 0; s < KS; ++s) {
+          const bf16x8 kf = as_bf16x8(ld16(&Ks[blk * 32 + col][s * 16 + half * 8]));
+          a = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kf, qf[s], a, 0, 0, 0);
+        }
+        sacc[blk] = a;
+      }
+      float mt = -INFINITY;
+#pragma unroll
+      for (int blk = 0; blk < 2; ++blk)
+#pragma unroll
+        for (int r = 0; r < 16; ++r) {
+          const int kk = blk * 32 + 8 * (r >> 2) + 4 * half + (r & 3);
+          if (j0 + kk >= L) sacc[blk][r] = -INFINITY;
+          mt = fmaxf(mt, sacc[blk][r]);
+        }
+      mt = fmaxf(mt, __shfl_xor(mt, 32)) * sl2;
+      const float m_new = fmaxf(m, mt);
+      const float alpha = __builtin_amdgcn_exp2f(m - m_new);
+      num *= alpha;
+      den *= alpha;
+      m = m_new;
+#pragma unroll
+      for (int blk = 0; blk < 2; ++blk)
+#pragma unroll
+        for (int r = 0; r < 16; ++r) {
+          const int kk = blk * 32 + 8 * (r >> 2) + 4 * half + (r & 3);
+          const float pr = __builtin_amdgcn_exp2f(__builtin_fmaf(sacc[blk][r], sl2, -m));
+          den += pr;
+          num = __builtin_fmaf(pr, Ws[kk], num);
+        }
+    }
+    const float num_t = num + __shfl_xor(num, 32);
+    const float den_t = den + __shfl_xor(den, 32);
+    if (den_t > 0.f) total += num_t / den_t;
+  }
+  if (ok && half == 0 && L > 0) p.acc[(int64_t)b * p.N + i] += total;
+}
+
+// ============================== SELECT =======================================
+constexpr int SNT = 1024;
+constexpr int MAX_TAPS = 2 * 96 + 1;  // sigma <= 32 -> radius <= 96
+
+struct SelParams {
+  const float* acc;
+  float* score_out;
+  int32_t* idx_out;
+  float* ws;           // per sample: tmp[N], sbar[N]
+  int N, gh, gw, k, radius;
+  float sigma;
+};
+
+__device__ __forceinline__ u32 order_key(float f) {
+  u32 u = __builtin_bit_cast(u32, f);
+  if ((u & 0x7FFFFFFFu) > 0x7F800000u) return 0u;      // NaN: lowest
+  if (u == 0x80000000u) u = 0u;                          // -0 -> +0
+  return (u & 0x80000000u) ? ~u : (u | 0x80000000u);
+}
+
+// Exclusive prefix sum over the block (1024 threads); returns the block total in *total.
+__device__ int block_exclusive_scan(int v, int* sh, int* total) {
+  const int t = threadIdx.x;
+  sh[t] = v;
+  __syncthreads();
+  for (int off = 1; off < SNT; off <<= 1) {
+    const int add = t >= off ? sh[t - off] : 0;
+    __syncthreads();
+    sh[t] += add;
+    __syncthreads();
+  }
+  const int incl = sh[t];
+  *total = sh[SNT - 1];
+  __syncthreads();
+  return incl - v;
+}
+
+__global__ __launch_bounds__(SNT) void pcsp_select_kernel(SelParams p) {
+  __shared__ float taps[MAX_TAPS];
+  __shared__ int hist[256];
+  __shared__ int scan_buf[SNT];
+  __shared__ float red_min[SNT / 64], red_max[SNT / 64];
+  __shared__ u32 sh_prefix;
+  __shared__ int sh_krem;
+
+  const int t = threadIdx.x;
+  const int b = blockIdx.x;
+  const int N = p.N;
+  const float* acc = p.acc + (int64_t)b * N;
+  float* tmp = p.ws + (int64_t)b * 2 * N;
+  float* sbar = tmp + N;
+  const int R = p.radius;
+
+  // ---- Eq. 11: separable Gaussian, renormalised at the borders ---------------
+  const float* src = acc;
+  if (p.sigma > 0.f) {
+    const float inv2s2 = 1.0f / (2.0f * p.sigma * p.sigma);
+    for (int i = t; i <= 2 * R; i += SNT) {
+      const float d = (float)(i - R);
+      taps[i] = expf(-d * d * inv2s2);
+    }
+    __syncthreads();
+    for (int pos = t; pos < N; pos += SNT) {  // along grid rows
+      const int y = pos / p.gw, x = pos % p.gw;
+      const int lo = max(-R, -x), hi = min(R, p.gw - 1 - x);
+      float num = 0.f, den = 0.f;
+      for (int d = lo; d <= hi; ++d) {
+        num = __builtin_fmaf(taps[d + R], acc[y * p.gw + x + d], num);
+        den += taps[d + R];
+      }
+      tmp[pos] = num / den;
+    }
+    __syncthreads();
+    for (int pos = t; pos < N; pos += SNT) {  // along grid columns
+      const int y = pos / p.gw, x = pos % p.gw;
+      const int lo = max(-R, -y), hi = min(R, p.gh - 1 - y);
+      float num = 0.f, den = 0.f;
+      for (int d = lo; d <= hi; ++d) {
+        num = __builtin_fmaf(taps[d + R], tmp[(y + d) * p.gw + x], num);
+        den += taps[d + R];
+      }
+      sbar[pos] = num / den;
+    }
+    __syncthreads();
+    src = sbar;
+  }
+
+  // ---- Norm: min-max scaling (optional output) --------------------------------
+  if (p.score_out != nullptr) {
+    float lo = INFINITY, hi = -INFINITY;
+    for (int pos = t; pos < N; pos += SNT) {
+      const float v = src[pos];
+      lo = fminf(lo, v);
+      hi = fmaxf(hi, v);
+    }
+#pragma unroll
+    for (int off = 32; off > 0; off >>= 1) {
+      lo = fminf(lo, __shfl_xor(lo, off));
+      hi = fmaxf(hi, __shfl_xor(hi, off));
+    }
+    if ((t & 63) == 0) { red_min[t >> 6] = lo; red_max[t >> 6] = hi; }
+    __syncthreads();
+    lo = red_min[0]; hi = red_max[0];
+    for (int w = 1; w < SNT / 64; ++w) { lo = fminf(lo, red_min[w]); hi = fmaxf(hi, red_max[w]); }
+    const float span = hi - lo;
+    float* so = p.score_out + (int64_t)b * N;
+    for (int pos = t; pos < N; pos += SNT) so[pos] = span > 0.f ? (src[pos] - lo) / span : 0.f;
+  }
+
+  // ---- Eq. 12: exact top-k ------------------------------------------------------
+  const int k = p.k;
+  if (k == 0) return;
+  int32_t* out = p.idx_out + (int64_t)b * k;
+  // radix select of the k-th largest key
+  if (t == 0) { sh_prefix = 0u; sh_krem = k; }
+  for (int pass = 0; pass < 4; ++pass) {
+    const int shift = 24 - 8 * pass;
+    if (t < 256) hist[t] = 0;
+    __syncthreads();
+    const u32 prefix = sh_prefix;
+    const u32 hmask = pass == 0 ? 0u : (0xFFFFFFFFu << (shift + 8));
+    for (int pos = t; pos < N; pos += SNT) {
+      const u32 key = order_key(src[pos]);
+      if ((key & hmask) == prefix) atomicAdd(&hist[(key >> shift) & 255u], 1);
+    }
+    __syncthreads();
+    if (t == 0) {
+      int rem = sh_krem, bin = 255;
+      for (; bin > 0; --bin) {
+        if (hist[bin] >= rem) break;
+        rem -= hist[bin];
+      }
+      sh_prefix = prefix | ((u32)bin << shift);
+      sh_krem = rem;  // how many to take from within this bin (and deeper)
+    }
+    __syncthreads();
+  }
+  const u32 T = sh_prefix;
+  const int need_eq = sh_krem;  // keys equal to T to keep (lowest indices first)
+
+  // ordered compaction: each thread owns a contiguous segment
+  const int seg = (N + SNT - 1) / SNT;
+  const int beg = min(N, t * seg), end = min(N, beg + seg);
+  int n_eq = 0;
+  for (int pos = beg; pos < end; ++pos) n_eq += order_key(src[pos]) == T;
+  int tot;
+  const int eq_base = block_exclusive_scan(n_eq, scan_buf, &tot);
+  int n_sel = 0;
+  {
+    int r = eq_base;
+    for (int pos = beg; pos < end; ++pos) {
+      const u32 key = order_key(src[pos]);
+      if (key > T) ++n_sel;
+      else if (key == T) { if (r < need_eq) ++n_sel; ++r; }
+    }
+  }
+  const int sel_base = block_exclusive_scan(n_sel, scan_buf, &tot);
+  {
+    int r = eq_base, o = sel_base;
+    for (int pos = beg; pos < end; ++pos) {
+      const u32 key = order_key(src[pos]);
+      bool take = false;
+      if (key > T) take = true;
+      else if (key == T) { take = r < need_eq; ++r; }
+      if (take && o < k) out[o++] = pos;
+    }
+  }
+}
+
+}  // namespace
+
+size_t pcsp_workspace(const safe_pcsp_args* a) {
+  if (!(a->flags & SAFE_PCSP_SELECT)) return 0;
+  const size_t n = (size_t)(a->B > 0 ? a->B : 0) * 2 * (size_t)(a->N > 0 ? a->N : 0) * sizeof(float);
+  return (n + 255) & ~(size_t)255;
+}
+
+int pcsp_launch(const safe_pcsp_args* a, float scale, void* workspace, hipStream_t s) {
+  if (a->flags & SAFE_PCSP_ACCUM) {
+    if ((int64_t)a->B * a->N * a->H > 0 && a->M > 0) {
+      AccParams p;
+      p.q = static_cast<const u16*>(a->q);
+      p.qs0 = a->q_stride[0]; p.qs1 = a->q_stride[1]; p.qs2 = a->q_stride[2];
+      p.kt = static_cast<const u16*>(a->k_text);
+      p.ks0 = a->k_stride[0]; p.ks1 = a->k_stride[1]; p.ks2 = a->k_stride[2];
+      p.kv_len = a->kv_len;
+      p.w = a->w;
+      p.acc = a->acc;
+      p.head_mask = a->head_mask;
+      p.B = a->B; p.N = a->N; p.M = a->M; p.H = a->H;
+      p.tiles_per_b = (a->N + ABM - 1) / ABM;
+      p.scale_log2 = scale * 1.4426950408889634f;
+      const int64_t grid = (int64_t)p.tiles_per_b * a->B;
+      if (grid > 0x7fffffff) return SAFE_ERR_SHAPE;
+      switch (a->d) {
+        case 32: hipLaunchKernelGGL(pcsp_accum_kernel<32>, dim3((unsigned)grid), dim3(ANT), 0, s, p); break;
+        case 64: hipLaunchKernelGGL(pcsp_accum_kernel<64>, dim3((unsigned)grid), dim3(ANT), 0, s, p); break;
+        case 96: hipLaunchKernelGGL(pcsp_accum_kernel<96>, dim3((unsigned)grid), dim3(ANT), 0, s, p); break;
+        case 128: hipLaunchKernelGGL(pcsp_accum_kernel<128>, dim3((unsigned)grid), dim3(ANT), 0, s, p); break;
+        default: return SAFE_ERR_UNSUPPORTED;
+      }
+      if (hipGetLastError() != hipSuccess) return SAFE_ERR_HIP;
+    }
+  }
+  if (a->flags & SAFE_PCSP_SELECT) {
+    if (a->B > 0 && a->N > 0) {
+      SelParams p;
+      p.acc = a->acc;
+      p.score_out = a->score_out;
+      p.idx_out = a->idx_out;
+      p.ws = static_cast<float*>(workspace);
+      p.N = a->N; p.gh = a->grid_h; p.gw = a->grid_w; p.k = a->k;
+      p.sigma = a->sigma;
+      p.radius = a->sigma > 0.f ? (int)ceilf(3.0f * a->sigma) : 0;
+      if (p.radius > (MAX_TAPS - 1) / 2) return SAFE_ERR_RANGE;
+      if (p.ws == nullptr && a->sigma > 0.f) return SAFE_ERR_WORKSPACE;
+      hipLaunchKernelGGL(pcsp_select_kernel, dim3(a->B), dim3(SNT), 0, s, p);
+      if (hipGetLastError() != hipSuccess) return SAFE_ERR_HIP;
+    }
+  }
+  return SAFE_OK;
+}
+
+}  // namespace safe

@@ -1,0 +1,169 @@
+"""CPU-only checks of the C ABI: the library loads, exports every declared symbol,
+and rejects bad arguments on the host before any HIP call."""
+import ctypes
+import os
+import re
+
+import pytest
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "safe.h")
+
+sq = pytest.importorskip("sparse_query_sdpa_amd", reason="libsafe.so not built")
+
+
+def declared_functions():
+    text = open(HEADER).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"^\s*(?:int|const char\*)\s+(safe_\w+)\s*\(", text, flags=re.M)))
+
+
+def test_header_declares_the_four_entry_points():
+    names = declared_functions()
+    for n in ("safe_mask_classify", "safe_pcsp_select", "safe_kv_assemble", "safe_attn_fwd",
+              "safe_status_str", "safe_abi_version"):
+        assert n in names
+
+
+def test_every_declared_symbol_is_exported():
+    lib = ctypes.CDLL(sq.LIB_PATH)
+    for n in declared_functions():
+        assert hasattr(lib, n), n
+
+
+def test_abi_version_and_status_strings():
+    assert sq.lib.safe_abi_version() == 1
+    for code, name in sq.STATUS.items():
+        assert sq.lib.safe_status_str(code).decode().startswith(name)
+    assert sq.lib.safe_status_str(12345) == b"unknown status"
+
+
+def _attn_args(**kw):
+    a = sq.AttnArgs()
+    a.B, a.H, a.Nq, a.Nk, a.d = 1, 1, 128, 128, 96
+    fake = 0x10000  # never dereferenced: validation fails or returns first
+    a.q = a.k = a.v = a.o = fake
+    for name in ("q_stride", "k_stride", "v_stride", "o_stride"):
+        getattr(a, name)[:] = [128 * 96, 96, 96]
+    a.n_rows = 128
+    for k, v in kw.items():
+        setattr(a, k, v)
+    return a
+
+
+@pytest.mark.parametrize("kw,status", [
+    (dict(d=48), -5), (dict(d=256), -5), (dict(B=-1), -2), (dict(q=None), -1), (dict(o=None), -1),
+    (dict(n_rows=5), -2), (dict(scale=float("nan")), -4), (dict(scale=float("inf")), -4),
+    (dict(q=0x10008), -8), (dict(flags=1 << 7), -4), (dict(flags=2), -2),
+])
+def test_attn_rejects_bad_arguments_without_gpu(kw, status):
+    a = _attn_args(**kw)
+    assert sq.lib.safe_attn_fwd(ctypes.byref(a), None) == status
+
+
+def test_attn_stride_checks():
+    a = _attn_args()
+    a.k_stride[1] = 100  # not a multiple of 8 elements
+    assert sq.lib.safe_attn_fwd(ctypes.byref(a), None) == -8
+    a = _attn_args()
+    a.v_stride[0] = -96
+    assert sq.lib.safe_attn_fwd(ctypes.byref(a), None) == -2
+    a = _attn_args(q_rows=0x20000, n_rows=10, q_rows_bstride=5)  # per-sample lists overlap
+    assert sq.lib.safe_attn_fwd(ctypes.byref(a), None) == -2
+
+
+def test_attn_empty_work_is_ok_without_gpu():
+    a = _attn_args(B=0)
+    assert sq.lib.safe_attn_fwd(ctypes.byref(a), None) == 0
+    a = _attn_args(q_rows=0x20000, n_rows=0)
+    assert sq.lib.safe_attn_fwd(ctypes.byref(a), None) == 0
+    a = _attn_args(B=0, q=None, k=None, v=None, o=None)
+    assert sq.lib.safe_attn_fwd(ctypes.byref(a), None) == 0
+
+
+def _kv_args(**kw):
+    a = sq.KvArgs()
+    a.B, a.N, a.H, a.d, a.nsel = 1, 64, 2, 96, 8
+    fake = 0x10000
+    a.k_fresh = a.v_fresh = a.k_cache = a.v_cache = fake
+    a.k_out, a.v_out = 0x40000, 0x50000
+    a.idx = 0x20000
+    for name in ("fresh_stride", "cache_stride", "out_stride"):
+        getattr(a, name)[:] = [64 * 192, 192, 96]
+    for k, v in kw.items():
+        setattr(a, k, v)
+    return a
+
+
+@pytest.mark.parametrize("kw,status", [
+    (dict(d=12), -8), (dict(nsel=65), -2), (dict(idx=None), -1), (dict(k_cache=None), -1),
+    (dict(k_out=0x10000), -2), (dict(idx_bstride=3), -2), (dict(k_fresh=0x10004), -8), (dict(flags=4), -4),
+])
+def test_kv_rejects_bad_arguments_without_gpu(kw, status):
+    a = _kv_args(**kw)
+    assert sq.lib.safe_kv_assemble(ctypes.byref(a), None) == status
+
+
+def test_kv_in_place_with_other_strides_is_rejected():
+    a = _kv_args(k_out=0x10000, v_out=0x10000)
+    a.out_stride[1] = 200
+    assert sq.lib.safe_kv_assemble(ctypes.byref(a), None) == -2
+
+
+def _classify(size, stride, dtype=1, flags=0, ws=None, need=None, info=True, mask=0x10000):
+    sz = (ctypes.c_int64 * 4)(*size)
+    st = (ctypes.c_int64 * 4)(*stride)
+    inf = sq.MaskInfo()
+    nb = ctypes.c_size_t(0) if need is None else ctypes.c_size_t(need)
+    rc = sq.lib.safe_mask_classify(mask, dtype, sz, st, flags, ctypes.byref(inf) if info else None, None, None, ws,
+                                   ctypes.byref(nb), None)
+    return rc, nb.value
+
+
+def test_classify_workspace_query_and_errors():
+    rc, need = _classify([2, 1, 100, 100], [10000, 10000, 100, 1])
+    assert rc == 0 and need >= 64 + 16 and need % 256 == 0
+    assert _classify([1, 1, 4, 4], [16, 16, 4, 1], dtype=7)[0] == -3
+    assert _classify([1, 1, 4, 4], [16, 16, 4, 2])[0] == -2          # last dim not contiguous
+    assert _classify([1, 1, -4, 4], [16, 16, 4, 1])[0] == -2
+    assert _classify([1, 1, 4, 4], [16, 16, 4, 1], flags=64)[0] == -4
+    assert _classify([1, 1, 4, 4], [16, 16, 4, 1], ws=0x30000, need=1)[0] == -6
+    assert _classify([1, 1, 4, 4], [16, 16, 4, 1], ws=0x30000, need=4096, info=False)[0] == -1
+    assert _classify([1, 1, 4, 4], [16, 16, 4, 1], ws=0x30008, need=4096)[0] == -8
+    assert _classify([1, 1, 4, 4], [16, 16, 4, 1], ws=0x30000, need=4096, mask=None)[0] == -1
+
+
+def _pcsp(**kw):
+    a = sq.PcspArgs()
+    a.flags = sq.PCSP_ACCUM
+    a.B, a.N, a.M, a.H, a.d = 1, 64, 16, 2, 96
+    a.q = a.k_text = 0x10000
+    a.q_stride[:] = [64 * 192, 192, 96]
+    a.k_stride[:] = [16 * 192, 192, 96]
+    a.w = a.acc = 0x20000
+    a.grid_h, a.grid_w, a.k = 8, 8, 4
+    a.idx_out = 0x30000
+    for k, v in kw.items():
+        setattr(a, k, v)
+    need = ctypes.c_size_t(1 << 20)
+    return sq.lib.safe_pcsp_select(ctypes.byref(a), 0x40000, ctypes.byref(need), None)
+
+
+@pytest.mark.parametrize("kw,status", [
+    (dict(flags=0), -4), (dict(flags=1 << 9), -4), (dict(d=40), -5), (dict(M=2048), -5), (dict(w=None), -1),
+    (dict(head_mask=1 << 5), -4), (dict(scale=float("nan")), -4), (dict(q_stride=(ctypes.c_int64 * 3)(1, 2, 3)), -8),
+    (dict(flags=sq.PCSP_SELECT, grid_h=7), -2), (dict(flags=sq.PCSP_SELECT, k=65), -4),
+    (dict(flags=sq.PCSP_SELECT, sigma=-1.0), -4), (dict(flags=sq.PCSP_SELECT, sigma=40.0), -4),
+    (dict(flags=sq.PCSP_SELECT, idx_out=None), -1),
+])
+def test_pcsp_rejects_bad_arguments_without_gpu(kw, status):
+    assert _pcsp(**kw) == status
+
+
+def test_pcsp_select_workspace_query():
+    a = sq.PcspArgs()
+    a.flags = sq.PCSP_SELECT
+    a.B, a.N, a.grid_h, a.grid_w, a.k = 2, 100, 10, 10, 5
+    need = ctypes.c_size_t(0)
+    assert sq.lib.safe_pcsp_select(ctypes.byref(a), None, ctypes.byref(need), None) == 0
+    assert need.value >= 2 * 2 * 100 * 4

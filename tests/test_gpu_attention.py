@@ -1,0 +1,136 @@
+"""GPU parity of safe_attn_fwd against the fp64 oracle (Eq. 2, 16, 17, 18)."""
+import numpy as np
+import pytest
+import torch
+
+import oracle
+import workloads as W
+from gpu_util import assert_attn_close, assert_lse_close, to_dev, to_dev_bf16
+
+pytestmark = pytest.mark.gpu
+
+sq = pytest.importorskip("sparse_query_sdpa_amd")
+
+
+def test_tiny_dense_all_rows():
+    inp = W.workload_inputs(1)
+    q, k, v = (to_dev_bf16(inp[n]) for n in ("q_x", "k_x", "v_x"))
+    o, lse = sq.attn_fwd(q, k, v, return_lse=True)
+    ref, ref_lse = oracle.sdpa(inp["q_x"].value, inp["k_x"].value, inp["v_x"].value)
+    assert_attn_close(o, ref, "tiny dense")
+    assert_lse_close(lse, ref_lse, "tiny dense")
+
+
+def test_tiny_srsu_self_and_cross():
+    inp = W.workload_inputs(1)
+    w = inp["workload"]
+    rows = W.random_rows(W.rng_for(1, stream=2), w.N, w.k_for(25))
+    rows_t = to_dev(rows)
+    q, k, v = (to_dev_bf16(inp[n]) for n in ("q_x", "k_x", "v_x"))
+    o, lse = sq.attn_fwd(q, k, v, q_rows=rows_t, return_lse=True)
+    ref, ref_lse = oracle.sdpa(inp["q_x"].value, inp["k_x"].value, inp["v_x"].value, q_rows=rows)
+    assert_attn_close(o, ref, "tiny srsu")
+    assert_lse_close(lse, ref_lse, "tiny srsu")
+    qc, kt, vt = (to_dev_bf16(inp[n]) for n in ("q_c", "k_txt", "v_txt"))
+    kv = to_dev(inp["kv_len"])
+    o = sq.attn_fwd(qc, kt, vt, q_rows=rows_t, kv_len=kv)
+    ref, _ = oracle.sdpa(inp["q_c"].value, inp["k_txt"].value, inp["v_txt"].value, q_rows=rows, kv_len=inp["kv_len"])
+    assert_attn_close(o, ref, "tiny cross")
+
+
+@pytest.mark.parametrize("d", [32, 64, 96, 128])
+def test_ragged_shapes_rows_lengths(d):
+    B, Nq, Nk, H = 4, 301, 333, 3
+    q, k, v = W.attention_inputs(B, Nq, Nk, H, d, seed=100 + d)
+    rng = np.random.default_rng(d)
+    rows = np.stack([W.random_rows(rng, Nq, 77) for _ in range(B)])
+    kv = np.array([0, 1, 333, 65], dtype=np.int32)
+    qd, kd, vd = to_dev_bf16(q), to_dev_bf16(k), to_dev_bf16(v)
+    # dense, no lengths (tails in both rows and keys)
+    o, lse = sq.attn_fwd(qd, kd, vd, return_lse=True)
+    ref, ref_lse = oracle.sdpa(q.value, k.value, v.value)
+    assert_attn_close(o, ref, f"dense d={d}")
+    assert_lse_close(lse, ref_lse, f"dense d={d}")
+    # gathered per-sample rows with per-sample lengths (including 0 and 1)
+    o, lse = sq.attn_fwd(qd, kd, vd, q_rows=to_dev(rows), kv_len=to_dev(kv), return_lse=True)
+    ref, ref_lse = oracle.sdpa(q.value, k.value, v.value, q_rows=rows, kv_len=kv)
+    assert_attn_close(o, ref, f"rows+len d={d}")
+    assert_lse_close(lse, ref_lse, f"rows+len d={d}")
+    assert torch.all(o[0] == 0), "kv_len 0 must give zero output"
+    # scattered output lands at the query tokens, other tokens untouched
+    out = torch.full((B, Nq, H, d), 7.0, dtype=torch.bfloat16, device=qd.device)
+    sq.attn_fwd(qd, kd, vd, q_rows=to_dev(rows), kv_len=to_dev(kv), out=out, scatter_out=True)
+    g = out.float().cpu().numpy()
+    for b in range(B):
+        assert_attn_close(out[b][torch.from_numpy(rows[b]).long()].unsqueeze(0), ref[b:b + 1], "scatter")
+        mask = np.ones(Nq, bool)
+        mask[rows[b]] = False
+        assert np.all(g[b][mask] == 7.0)
+
+
+def test_shared_rows_and_dense_equivalence_bitwise():
+    B, N, H, d = 2, 1000, 4, 96
+    q, k, v = W.attention_inputs(B, N, N, H, d, seed=7)
+    qd, kd, vd = to_dev_bf16(q), to_dev_bf16(k), to_dev_bf16(v)
+    dense = sq.attn_fwd(qd, kd, vd)
+    all_rows = sq.attn_fwd(qd, kd, vd, q_rows=torch.arange(N, dtype=torch.int32, device=qd.device))
+    assert torch.equal(dense, all_rows), "S = all rows must reproduce the dense pass"
+    rows = W.random_rows(np.random.default_rng(3), N, 250)
+    part = sq.attn_fwd(qd, kd, vd, q_rows=to_dev(rows))
+    assert torch.equal(part, dense[:, torch.from_numpy(rows).long()])
+    again = sq.attn_fwd(qd, kd, vd)
+    assert torch.equal(dense, again), "repeated calls must be bitwise identical"
+
+
+def test_invalid_rows_and_lengths():
+    B, N, H, d = 1, 200, 2, 64
+    q, k, v = W.attention_inputs(B, N, N, H, d, seed=9)
+    qd, kd, vd = to_dev_bf16(q), to_dev_bf16(k), to_dev_bf16(v)
+    bad = to_dev(np.array([3, 250, -1, 7], dtype=np.int32))
+    with pytest.raises(sq.SafeError) as e:
+        sq.attn_fwd(qd, kd, vd, q_rows=bad, check=True)
+    assert e.value.status == -4
+    o = sq.attn_fwd(qd, kd, vd, q_rows=bad)  # out-of-range entries read a zero query row
+    zero_q = np.zeros((1, 1, H, d))
+    ref_zero, _ = oracle.sdpa(zero_q, k.value, v.value)
+    assert_attn_close(o[:, 1:3], np.concatenate([ref_zero, ref_zero], axis=1), "zero-query rows")
+    with pytest.raises(sq.SafeError):
+        sq.attn_fwd(qd, kd, vd, kv_len=to_dev(np.array([201], np.int32)), check=True)
+    o = sq.attn_fwd(qd, kd, vd, kv_len=to_dev(np.array([5000], np.int32)))   # clamped to Nk
+    assert torch.equal(o, sq.attn_fwd(qd, kd, vd))
+    empty = sq.attn_fwd(qd, kd, vd, q_rows=to_dev(np.zeros((0,), np.int32)))
+    assert empty.shape == (1, 0, H, d)
+
+
+def _sample_rows(rng, n, per=24):
+    """Sampled output rows: the first, the last, rows around the 128-row tile edges and random ones."""
+    pick = {0, n - 1, min(n - 1, 127), min(n - 1, 128), max(0, n - 129)}
+    pick.update(rng.choice(n, size=min(n, per), replace=False).tolist())
+    return np.array(sorted(pick))
+
+
+@pytest.mark.parametrize("number", [2, 3, 4, 5])
+def test_full_size_workloads_sampled_rows(number):
+    """Full workload shapes in the bench's launch configuration; oracle on sampled output rows."""
+    inp = W.workload_inputs(number)
+    w = inp["workload"]
+    rng = W.rng_for(number, stream=3)
+    q, k, v = (to_dev_bf16(inp[n]) for n in ("q_x", "k_x", "v_x"))
+    rows = W.random_rows(rng, w.N, w.k_for(w.rho_percent[0]))
+    rows_t = to_dev(rows)
+    # SRSU self-attention (Eq. 16)
+    o = sq.attn_fwd(q, k, v, q_rows=rows_t)
+    samp = _sample_rows(rng, rows.shape[0])
+    ref, _ = oracle.sdpa(inp["q_x"].value, inp["k_x"].value, inp["v_x"].value, q_rows=rows[samp])
+    assert_attn_close(o[:, torch.from_numpy(samp).long()], ref, f"srsu N={w.N}")
+    # SRSU cross-attention with per-sample text lengths (Eq. 17)
+    qc, kt, vt = (to_dev_bf16(inp[n]) for n in ("q_c", "k_txt", "v_txt"))
+    o = sq.attn_fwd(qc, kt, vt, q_rows=rows_t, kv_len=to_dev(inp["kv_len"]))
+    ref, _ = oracle.sdpa(inp["q_c"].value, inp["k_txt"].value, inp["v_txt"].value, q_rows=rows[samp],
+                         kv_len=inp["kv_len"])
+    assert_attn_close(o[:, torch.from_numpy(samp).long()], ref, f"cross N={w.N}")
+    # dense anchor pass (Eq. 18)
+    o = sq.attn_fwd(q, k, v)
+    samp = _sample_rows(rng, w.N)
+    ref, _ = oracle.sdpa(inp["q_x"].value, inp["k_x"].value, inp["v_x"].value, q_rows=samp)
+    assert_attn_close(o[:, torch.from_numpy(samp).long()], ref, f"dense N={w.N}")

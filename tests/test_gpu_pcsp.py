@@ -1,0 +1,112 @@
+"""GPU parity of safe_pcsp_select against the oracle (Eq. 9-12)."""
+import json
+import os
+
+import numpy as np
+import pytest
+import torch
+
+import oracle
+import workloads as W
+from gpu_util import dev, to_dev, to_dev_bf16
+
+pytestmark = pytest.mark.gpu
+
+sq = pytest.importorskip("sparse_query_sdpa_amd")
+
+GOLD = os.path.join(os.path.dirname(__file__), "golden")
+ACC_RTOL = 1e-4
+
+
+@pytest.mark.parametrize("number", [1, 2])
+def test_accumulate_matches_oracle(number):
+    inp = W.workload_inputs(number)
+    w = inp["workload"]
+    wts = W.pcsp_content_weights(inp["kv_len"], w.M)
+    acc = torch.zeros((w.B, w.N), dtype=torch.float32, device=dev())
+    qc, kt = to_dev_bf16(inp["q_c"]), to_dev_bf16(inp["k_txt"])
+    sq.pcsp_accumulate(qc, kt, to_dev(wts), acc, kv_len=to_dev(inp["kv_len"]))
+    ref = oracle.pcsp_accumulate(inp["q_c"].value, inp["k_txt"].value, inp["kv_len"], wts)
+    np.testing.assert_allclose(acc.cpu().numpy(), ref, rtol=ACC_RTOL, atol=1e-7)
+    # a second call adds (two warm-up calls), a head subset picks heads
+    heads = [0, w.H - 1]
+    mask = (1 << 0) | (1 << (w.H - 1))
+    sq.pcsp_accumulate(qc, kt, to_dev(wts), acc, kv_len=to_dev(inp["kv_len"]), head_mask=mask)
+    ref2 = oracle.pcsp_accumulate(inp["q_c"].value, inp["k_txt"].value, inp["kv_len"], wts, heads=heads, acc=ref)
+    np.testing.assert_allclose(acc.cpu().numpy(), ref2, rtol=ACC_RTOL, atol=1e-7)
+
+
+def test_accumulate_ragged_lengths():
+    B, N, M, H, d = 3, 300, 80, 2, 64
+    q, k, _ = W.attention_inputs(B, N, M, H, d, seed=11)
+    kv = np.array([80, 1, 0], np.int32)
+    wts = np.random.default_rng(0).random((B, M)).astype(np.float32)
+    acc = torch.zeros((B, N), dtype=torch.float32, device=dev())
+    sq.pcsp_accumulate(to_dev_bf16(q), to_dev_bf16(k), to_dev(wts), acc, kv_len=to_dev(kv))
+    ref = oracle.pcsp_accumulate(q.value, k.value, kv, wts)
+    np.testing.assert_allclose(acc.cpu().numpy(), ref, rtol=ACC_RTOL, atol=1e-7)
+    assert torch.all(acc[2] == 0)
+
+
+def _select(s: np.ndarray, k: int, gh: int, gw: int, sigma: float = 0.0):
+    acc = to_dev(s.astype(np.float32))
+    return sq.pcsp_select(acc, gh, gw, sigma, k, score_out=True)
+
+
+def test_topk_golden_cases():
+    for case in json.load(open(os.path.join(GOLD, "topk_hand.json")))["cases"]:
+        s = np.asarray([[{"inf": np.inf, "-inf": -np.inf, "nan": np.nan, "-0": -0.0}.get(x, x)
+                         if isinstance(x, str) else x for x in case["s"]]], dtype=np.float32)
+        idx, _ = _select(s, case["k"], 1, s.shape[1])
+        assert idx.cpu().numpy()[0].tolist() == case["idx"], case["why"]
+
+
+@pytest.mark.parametrize("levels", [None, 8, 1])
+@pytest.mark.parametrize("N,grid", [(256, (16, 16)), (4096, (64, 64)), (36864, (192, 192))])
+def test_topk_bit_exact_on_identical_scores(N, grid, levels):
+    """Same fp32 score array on both sides (sigma = 0): identical index sets, lower index wins ties."""
+    rng = np.random.default_rng(N + (levels or 0))
+    s = W.score_field(rng, 2, N, levels=levels)
+    s[0, :5] = [-0.0, 0.0, np.nan, -np.inf, np.inf]
+    for k in sorted({1, N // 4, (3 * N) // 10, N - 1, N}):
+        idx, _ = _select(s, k, *grid)
+        ref = oracle.topk_select(s.astype(np.float64), k)
+        assert np.array_equal(idx.cpu().numpy(), ref), (N, levels, k)
+
+
+def test_smoothing_and_norm_against_oracle():
+    rng = np.random.default_rng(5)
+    gh, gw = 40, 33
+    s = rng.random((2, gh * gw)).astype(np.float32)
+    for sigma in (0.7, 1.0, 2.5):
+        idx, so = _select(s, 300, gh, gw, sigma)
+        sbar = oracle.gaussian_smooth(s.astype(np.float64), gh, gw, sigma)
+        ref_norm = oracle.minmax_normalize(sbar)
+        np.testing.assert_allclose(so.cpu().numpy(), ref_norm, atol=2e-5)
+        # selection: may differ only where the oracle's smoothed score is within a rounding band of the k-th
+        ref_idx = oracle.topk_select(sbar, 300)
+        for b in range(2):
+            got, exp = set(idx[b].cpu().tolist()), set(ref_idx[b].tolist())
+            kth = np.sort(sbar[b])[::-1][299]
+            band = 1e-5 * np.abs(sbar[b]).max()
+            for t in got ^ exp:
+                assert abs(sbar[b, t] - kth) <= band, (sigma, t)
+            assert np.all(np.diff(idx[b].cpu().numpy()) > 0)
+
+
+def test_pipeline_tiny_workload():
+    """Accumulate -> smooth (sigma 1) -> select on the 16x16 workload."""
+    inp = W.workload_inputs(1)
+    w = inp["workload"]
+    wts = W.pcsp_content_weights(inp["kv_len"], w.M)
+    acc = torch.zeros((w.B, w.N), dtype=torch.float32, device=dev())
+    sq.pcsp_accumulate(to_dev_bf16(inp["q_c"]), to_dev_bf16(inp["k_txt"]), to_dev(wts), acc,
+                       kv_len=to_dev(inp["kv_len"]))
+    idx, so = sq.pcsp_select(acc, w.grid_h, w.grid_w, 1.0, w.k_for(25), score_out=True)
+    _, sbar, s_norm, ref_idx = oracle.pcsp_scores(inp["q_c"].value, inp["k_txt"].value, inp["kv_len"], wts,
+                                                  w.grid_h, w.grid_w, 1.0, w.k_for(25))
+    np.testing.assert_allclose(so.cpu().numpy(), s_norm, atol=1e-4)
+    got, exp = set(idx[0].cpu().tolist()), set(ref_idx[0].tolist())
+    kth = np.sort(sbar[0])[::-1][w.k_for(25) - 1]
+    for t in got ^ exp:
+        assert abs(sbar[0, t] - kth) <= 1e-4 * np.abs(sbar).max()
