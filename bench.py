@@ -1,0 +1,275 @@
+#!/usr/bin/env python3
+"""Benchmark of the SAFE-DiT attention hot path on one MI355X.
+
+One step is one pass of the whole hot path on the 2560^2-like workload
+(B=2 CFG pair, 24 heads of d=96, N=25600 image tokens on a 160x160 grid,
+M=256 text tokens with per-sample valid lengths, sensitive fraction 25%):
+  1. certify the [2, 1, N, N] bf16 all-valid additive mask (Eq. 6-8)
+  2. accumulate image->text scores over all heads (Eq. 9-10)
+  3. smooth (sigma 1) and select the top-k sensitive set (Eq. 11-12)
+  4. assemble global K/V: fresh sensitive rows over the cached context (Eq. 16)
+  5. SRSU self-attention on the gathered rows of S (Eq. 16)
+  6. SRSU cross-attention with per-sample text lengths (Eq. 17)
+  7. the dense anchor pass over all rows (Eq. 18)
+Inputs are seeded synthetic bf16 N(0,1) activations already resident in HBM.
+
+The reported value is SRSU self-attention TFLOP/s (algorithmic FLOPs
+4*B*H*k*N*d over the event-timed duration of that kernel); the line also
+carries the dense/SRSU time ratio, each kernel's time and roofline fraction,
+and the fp64 CPU oracle timed on a bounded sample on this host.
+
+  python bench.py [--gpus 1] [--steps 20] [--warmup 3]
+  python bench.py --rocprof-summary <kernel_stats.csv>   # markdown summary of a rocprofv3 run
+  python bench.py --copy-probe                           # plain 1 GiB copy for counter calibration
+"""
+from __future__ import annotations
+
+import argparse
+import json
+import math
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+PEAK_BF16_TFLOPS = 2500.0   # MI355X dense bf16 MFMA
+PEAK_HBM_GBS = 8000.0       # MI355X HBM3E
+
+
+def rocprof_summary(path: str) -> None:
+    """Print a short markdown table of a rocprofv3 --stats kernel_stats.csv."""
+    import csv
+    rows = list(csv.DictReader(open(path)))
+    print("| kernel | calls | avg us | min us | max us | total ms | % |")
+    print("|---|---|---|---|---|---|---|")
+    for r in sorted(rows, key=lambda r: -float(r["TotalDurationNs"])):
+        name = r["Name"]
+        if len(name) > 90:
+            name = name[:87] + "..."
+        print(f"| `{name}` | {r['Calls']} | {float(r['AverageNs']) / 1e3:.1f} | {float(r['MinNs']) / 1e3:.1f} | "
+              f"{float(r['MaxNs']) / 1e3:.1f} | {float(r['TotalDurationNs']) / 1e6:.3f} | {float(r['Percentage']):.1f} |")
+
+
+def copy_probe() -> None:
+    import torch
+    n = 1 << 30
+    a = torch.empty(n, dtype=torch.uint8, device="cuda")
+    b = torch.empty(n, dtype=torch.uint8, device="cuda")
+    a.fill_(1)
+    torch.cuda.synchronize()
+    for _ in range(3):
+        b.copy_(a)
+    torch.cuda.synchronize()
+    print(json.dumps({"copy_probe_bytes_each_way": n, "copies": 3}))
+
+
+def main() -> int:
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=20)
+    ap.add_argument("--warmup", type=int, default=3)
+    ap.add_argument("--rho", type=int, default=25, help="sensitive fraction in percent")
+    ap.add_argument("--sigma", type=float, default=1.0)
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--no-sweep", action="store_true")
+    ap.add_argument("--cpu-rows", type=int, default=512, help="oracle sample: query rows per sample")
+    ap.add_argument("--rocprof-summary", type=str, default=None)
+    ap.add_argument("--copy-probe", action="store_true")
+    args = ap.parse_args()
+
+    if args.rocprof_summary:
+        rocprof_summary(args.rocprof_summary)
+        return 0
+    if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) > 1:
+        print("bench.py measures one GPU only: this build has no multi-GPU path "
+              "(the work shards by (sample, head) with no exchange; see the design notes). "
+              "Run with --gpus 1.", file=sys.stderr)
+        return 2
+    if args.copy_probe:
+        copy_probe()
+        return 0
+
+    import numpy as np
+    import torch
+
+    import sparse_query_sdpa_amd as sq
+    import workloads as W
+
+    dev = torch.device("cuda:0")
+    torch.cuda.set_device(dev)
+    wl = W.WORKLOADS[4]
+    B, N, H, d, M = wl.B, wl.N, wl.H, wl.d, wl.M
+    k = wl.k_for(args.rho)
+    inp = W.workload_inputs(4)
+
+    def dbf16(t):
+        return torch.from_numpy(np.ascontiguousarray(t.bits).view(np.int16)).to(dev).view(torch.bfloat16)
+
+    q, kx, vx = dbf16(inp["q_x"]), dbf16(inp["k_x"]), dbf16(inp["v_x"])
+    qc, kt, vt = dbf16(inp["q_c"]), dbf16(inp["k_txt"]), dbf16(inp["v_txt"])
+    kv_len = torch.from_numpy(inp["kv_len"]).to(dev)
+    wts = torch.from_numpy(W.pcsp_content_weights(inp["kv_len"], M)).to(dev)
+    # context cache = anchor K/V; fresh K/V = drifted K/V of the current step
+    k_fresh_full = dbf16(W.bf16_from_f32(inp["k_x"].value + W.drift((1004, 10), inp["k_x"].value.shape)))
+    v_fresh_full = dbf16(W.bf16_from_f32(inp["v_x"].value + W.drift((1004, 11), inp["v_x"].value.shape)))
+    mask = torch.zeros((B, 1, N, N), dtype=torch.bfloat16, device=dev)    # all-valid additive mask
+    mask_bytes = mask.numel() * mask.element_size()
+    acc = torch.zeros((B, N), dtype=torch.float32, device=dev)
+    k_glob = torch.empty_like(kx)
+    v_glob = torch.empty_like(vx)
+    o_srsu = torch.empty((B, k, H, d), dtype=torch.bfloat16, device=dev)
+    o_cross = torch.empty((B, k, H, d), dtype=torch.bfloat16, device=dev)
+    o_dense = torch.empty_like(q)
+
+    # the sensitive set of this input (fixed after warm-up, Eq. 12); fresh rows of S
+    sq.pcsp_accumulate(qc, kt, wts, acc, kv_len=kv_len)
+    idx0 = sq.pcsp_select(acc, wl.grid_h, wl.grid_w, args.sigma, k)
+    k_fresh = torch.stack([k_fresh_full[b, idx0[b].long()] for b in range(B)]).contiguous()
+    v_fresh = torch.stack([v_fresh_full[b, idx0[b].long()] for b in range(B)]).contiguous()
+    del k_fresh_full, v_fresh_full
+    mws = sq.mask_classify(mask)["workspace"]
+    torch.cuda.synchronize()
+
+    stages = ["classify", "pcsp_accum", "pcsp_select", "kv_assemble", "srsu_self", "srsu_cross", "dense"]
+    stream = torch.cuda.current_stream()
+
+    def step(ev=None):
+        def mark(i):
+            if ev is not None:
+                ev[i].record(stream)
+        mark(0)
+        info = sq.mask_classify(mask, workspace=mws)
+        assert info["verdict"] == 1
+        mark(1)
+        acc.zero_()
+        sq.pcsp_accumulate(qc, kt, wts, acc, kv_len=kv_len)
+        mark(2)
+        idx = sq.pcsp_select(acc, wl.grid_h, wl.grid_w, args.sigma, k)
+        mark(3)
+        sq.kv_assemble(k_fresh, v_fresh, idx, kx, vx, k_out=k_glob, v_out=v_glob)
+        mark(4)
+        sq.attn_fwd(q, k_glob, v_glob, q_rows=idx, out=o_srsu)
+        mark(5)
+        sq.attn_fwd(qc, kt, vt, q_rows=idx, kv_len=kv_len, out=o_cross)
+        mark(6)
+        sq.attn_fwd(q, kx, vx, out=o_dense)
+        mark(7)
+        return idx
+
+    for _ in range(args.warmup):
+        step()
+    torch.cuda.synchronize()
+    events = [[torch.cuda.Event(enable_timing=True) for _ in range(len(stages) + 1)] for _ in range(args.steps)]
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for s in range(args.steps):
+        idx = step(events[s])
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    ms_step = wall * 1e3 / args.steps
+    stage_ms = {name: float(np.mean([events[s][i].elapsed_time(events[s][i + 1]) for s in range(args.steps)]))
+                for i, name in enumerate(stages)}
+    assert torch.equal(idx, idx0), "the sensitive set must not change across steps"
+    assert torch.isfinite(o_dense.float()).all() and torch.isfinite(o_srsu.float()).all()
+
+    fl_srsu = 4.0 * B * H * k * N * d
+    fl_dense = 4.0 * B * H * N * N * d
+    Lsum = int(inp["kv_len"].sum())
+    fl_cross = 4.0 * H * d * k * Lsum
+    kv_bytes = 4.0 * B * N * H * d * 2
+    tf = lambda fl, ms: fl / (ms * 1e-3) / 1e12
+    srsu_tf = tf(fl_srsu, stage_ms["srsu_self"])
+    dense_tf = tf(fl_dense, stage_ms["dense"])
+    out = {
+        "metric": "SRSU attention TFLOP/s (bf16 MFMA) at N=25600; dense/SRSU time ratio",
+        "value": round(srsu_tf, 2),
+        "unit": "TFLOP/s",
+        "n_gpus": 1, "steps": args.steps, "warmup": args.warmup,
+        "ms_per_step": round(ms_step, 4),
+        "higher_is_better": True, "scaling": "weak", "vs_baseline": None,
+        "dtype": "bf16", "data": "synthetic",
+        "config": {"workload": "2560sq-like: B=2 (CFG pair) H=24 d=96 N=25600 (160x160) M=256, rho=%d%%" % args.rho,
+                   "B": B, "H": H, "d": d, "N": N, "M": M, "k": k, "sigma": args.sigma,
+                   "kv_len": inp["kv_len"].tolist(), "mask": "[2,1,N,N] bf16 zeros (%.2f GB)" % (mask_bytes / 1e9),
+                   "parallelism": "single GPU"},
+        "srsu_pct_bf16_peak": round(100 * srsu_tf / PEAK_BF16_TFLOPS, 2),
+        "dense_tflops": round(dense_tf, 2),
+        "dense_pct_bf16_peak": round(100 * dense_tf / PEAK_BF16_TFLOPS, 2),
+        "dense_srsu_ratio": round(stage_ms["dense"] / stage_ms["srsu_self"], 3),
+        "dense_srsu_step_ratio": round(stage_ms["dense"] / (stage_ms["srsu_self"] + stage_ms["kv_assemble"]), 3),
+        "ideal_ratio_N_over_k": round(N / k, 3),
+        "stage_ms": {kk: round(v, 4) for kk, v in stage_ms.items()},
+        "cross_tflops": round(tf(fl_cross, stage_ms["srsu_cross"]), 2),
+        "classify_gbs": round(mask_bytes / (stage_ms["classify"] * 1e-3) / 1e9, 1),
+        "classify_pct_hbm": round(100 * mask_bytes / (stage_ms["classify"] * 1e-3) / 1e9 / PEAK_HBM_GBS, 2),
+        "kv_assemble_gbs": round(kv_bytes / (stage_ms["kv_assemble"] * 1e-3) / 1e9, 1),
+        "kv_assemble_pct_hbm": round(100 * kv_bytes / (stage_ms["kv_assemble"] * 1e-3) / 1e9 / PEAK_HBM_GBS, 2),
+        "roofline": {"bound": "mfma", "kernel": "attn_fwd_kernel<96,false,false> (dense anchor pass)",
+                     "achieved": round(dense_tf, 2), "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s",
+                     "frac": round(dense_tf / PEAK_BF16_TFLOPS, 4), "traffic": None,
+                     "algorithmic_flops_per_launch": fl_dense, "avg_launch_ms": round(stage_ms["dense"], 4)},
+        "roofline_srsu": {"bound": "mfma", "kernel": "attn_fwd_kernel<96,true,false> (SRSU self-attention)",
+                          "achieved": round(srsu_tf, 2), "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s",
+                          "frac": round(srsu_tf / PEAK_BF16_TFLOPS, 4), "traffic": None,
+                          "algorithmic_flops_per_launch": fl_srsu, "avg_launch_ms": round(stage_ms["srsu_self"], 4)},
+        "peak_mem_gb": round(torch.cuda.max_memory_allocated() / 1e9, 2),
+        "pages_context": "PyTorch SDPA stack on unstated hardware: masked SDPA 4.1-5.8x slower than mask-free; "
+                         "end-to-end 2.69x at 1024^2 and 5.09x at 2560^2; peak memory 94.1 -> 27.9 GB",
+    }
+
+    if not args.no_sweep:
+        sweep = {}
+        for rho in wl.rho_percent:
+            kk = wl.k_for(rho)
+            ids = sq.pcsp_select(acc, wl.grid_h, wl.grid_w, args.sigma, kk)
+            o = torch.empty((B, kk, H, d), dtype=torch.bfloat16, device=dev)
+            for _ in range(2):
+                sq.attn_fwd(q, k_glob, v_glob, q_rows=ids, out=o)
+            e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            reps = 5
+            e0.record(stream)
+            for _ in range(reps):
+                sq.attn_fwd(q, k_glob, v_glob, q_rows=ids, out=o)
+            e1.record(stream)
+            torch.cuda.synchronize()
+            ms = e0.elapsed_time(e1) / reps
+            t = tf(4.0 * B * H * kk * N * d, ms)
+            sweep[f"rho{rho}"] = {"k": kk, "ms": round(ms, 4), "tflops": round(t, 2),
+                                  "pct_peak": round(100 * t / PEAK_BF16_TFLOPS, 2),
+                                  "dense_ratio": round(stage_ms["dense"] / ms, 3), "ideal": round(N / kk, 3)}
+        out["rho_sweep"] = sweep
+
+    if not args.no_cpu_baseline:
+        out["cpu_baseline"] = cpu_baseline(inp, args.cpu_rows)
+
+    print(json.dumps(out), flush=True)
+    return 0
+
+
+def cpu_baseline(inp, rows_per_bh: int):
+    """The fp64 oracle timed on a bounded sample of the SRSU self-attention (rows_per_bh rows per sample)."""
+    import numpy as np
+
+    import oracle
+    import workloads as W
+    try:
+        from threadpoolctl import threadpool_info
+        cores = max([i.get("num_threads", 1) for i in threadpool_info()] or [1])
+    except Exception:  # pragma: no cover
+        cores = len(os.sched_getaffinity(0))
+    B, N, H, d = inp["q_x"].shape
+    rng = W.rng_for(4, stream=7)
+    rows = np.stack([W.random_rows(rng, N, rows_per_bh) for _ in range(B)])
+    t0 = time.perf_counter()
+    oracle.sdpa(inp["q_x"].value, inp["k_x"].value, inp["v_x"].value, q_rows=rows)
+    secs = time.perf_counter() - t0
+    flops = 4.0 * B * H * rows_per_bh * N * d
+    return {"value": round(flops / secs / 1e12, 6), "unit": "TFLOP/s", "cores": int(cores), "kind": "oracle",
+            "sample": f"SRSU self-attention on {rows_per_bh} query rows per sample x {H} heads against all {N} keys "
+                      f"(B={B}, d={d}): {flops / 1e9:.1f} GFLOP in fp64, {secs:.1f} s"}
+
+
+if __name__ == "__main__":
+    sys.exit(main())

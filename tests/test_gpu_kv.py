@@ -79,8 +79,8 @@ def test_multistep_cache_workload():
     cache_k, cache_v = to_dev_bf16(inp["k_x"]), to_dev_bf16(inp["v_x"])   # anchor: cache <- dense K/V (Eq. 19)
     ref_k, ref_v = inp["k_x"].bits.copy(), inp["v_x"].bits.copy()
     for step in range(3):
-        k_t = k_t + W.drift(rng, k_t.shape)
-        v_t = v_t + W.drift(rng, v_t.shape)
+        k_t = k_t + W.drift((1002, 10, step), k_t.shape)
+        v_t = v_t + W.drift((1002, 11, step), v_t.shape)
         kb, vb = W.bf16_from_f32(k_t), W.bf16_from_f32(v_t)
         fk = W.Bf16Tensor(kb.bits[:, S], kb.value[:, S])
         fv = W.Bf16Tensor(vb.bits[:, S], vb.value[:, S])

@@ -18,7 +18,6 @@ integers; the drift between steps N(0, 0.05) (0.05 is a standard deviation).
 from __future__ import annotations
 
 import dataclasses
-import math
 from typing import Dict, Optional
 
 import numpy as np
@@ -32,16 +31,24 @@ def f32_to_bf16_bits(x: np.ndarray) -> np.ndarray:
     """Round float32 values to bfloat16 (nearest, ties to even); return uint16 bits.
 
     Finite inputs only (the generators never draw NaN/inf; mask cases that need
-    them write the bit patterns directly).
+    them write the bit patterns directly).  In 32-bit arithmetic the sum cannot
+    wrap for finite values (the largest, 0xFF7FFFFF, plus 0x8000 < 2^32).
     """
-    u = np.ascontiguousarray(x, dtype=np.float32).view(np.uint32).astype(np.uint64)
-    bias = ((u >> np.uint64(16)) & np.uint64(1)) + np.uint64(0x7FFF)
-    return ((u + bias) >> np.uint64(16)).astype(np.uint16)
+    u = np.array(x, dtype=np.float32, copy=True).view(np.uint32)
+    t = u >> np.uint32(16)
+    t &= np.uint32(1)
+    t += np.uint32(0x7FFF)
+    u += t
+    u >>= np.uint32(16)
+    return u.astype(np.uint16)
 
 
 def bf16_bits_to_f32(bits: np.ndarray) -> np.ndarray:
     """Exact widening of bfloat16 bit patterns to float32 values."""
-    return (np.ascontiguousarray(bits, dtype=np.uint16).astype(np.uint32) << np.uint32(16)).view(np.float32)
+    b = np.ascontiguousarray(bits, dtype=np.uint16)
+    out = np.zeros(b.shape + (2,), dtype=np.uint16)   # little-endian: high half holds the bf16 bits
+    out[..., 1] = b
+    return out.view(np.float32).reshape(b.shape)
 
 
 BF16_NEG_INF = np.uint16(0xFF80)
@@ -95,36 +102,69 @@ def rng_for(number: int, stream: int = 0) -> np.random.Generator:
 # activations
 # ----------------------------------------------------------------------------
 
-@dataclasses.dataclass
 class Bf16Tensor:
-    """A bfloat16 tensor: the bit pattern handed to the GPU and its exact value."""
-    bits: np.ndarray      # uint16, shape as the tensor
-    value: np.ndarray     # float32, exactly the bf16 value of `bits`
+    """A bfloat16 tensor: the bit pattern handed to the GPU and its exact value.
+
+    `bits` is uint16; `value` (float32, exactly the bf16 value of `bits`) is
+    widened on first use.
+    """
+
+    def __init__(self, bits: np.ndarray, value: Optional[np.ndarray] = None):
+        self.bits = bits
+        self._value = value
+
+    @property
+    def value(self) -> np.ndarray:
+        if self._value is None:
+            self._value = bf16_bits_to_f32(self.bits)
+        return self._value
 
     @property
     def shape(self):
         return self.bits.shape
 
 
-def bf16_normal(rng: np.random.Generator, shape, std: float = 1.0) -> Bf16Tensor:
-    x = rng.standard_normal(size=shape, dtype=np.float32)
+def _seed_of(key) -> int:
+    """A 63-bit seed derived from a tuple of ints."""
+    return int(np.random.SeedSequence(list(key)).generate_state(1, dtype=np.uint64)[0] >> np.uint64(1))
+
+
+def normal_f32(key, shape, std: float = 1.0) -> np.ndarray:
+    """float32 N(0, std^2) draws of `shape`, deterministic in `key` (a tuple of ints).
+
+    Drawn with torch's CPU generator (Mersenne Twister, seeded from `key`),
+    whose output does not depend on the number of threads.
+    """
+    import torch
+    g = torch.Generator().manual_seed(_seed_of(key))
+    x = torch.randn(int(np.prod(shape)), generator=g, dtype=torch.float32)
     if std != 1.0:
-        x = (x * np.float32(std)).astype(np.float32)
-    bits = f32_to_bf16_bits(x)
-    return Bf16Tensor(bits, bf16_bits_to_f32(bits))
+        x.mul_(std)
+    return x.numpy().reshape(shape)
+
+
+def _to_bf16_parallel(x: np.ndarray) -> Bf16Tensor:
+    """Round to bfloat16 (nearest even) with torch's cast: identical to f32_to_bf16_bits, faster."""
+    import torch
+    t = torch.from_numpy(np.ascontiguousarray(x, dtype=np.float32))
+    bits = t.to(torch.bfloat16).view(torch.int16).numpy().view(np.uint16)
+    return Bf16Tensor(bits)
+
+
+def bf16_normal(key, shape, std: float = 1.0) -> Bf16Tensor:
+    """bf16 tensor of N(0, std^2) draws (rounded to nearest even), deterministic in `key`."""
+    return _to_bf16_parallel(normal_f32(key, shape, std))
 
 
 def bf16_from_f32(x: np.ndarray) -> Bf16Tensor:
-    bits = f32_to_bf16_bits(x)
-    return Bf16Tensor(bits, bf16_bits_to_f32(bits))
+    return _to_bf16_parallel(np.ascontiguousarray(x, dtype=np.float32))
 
 
 def attention_inputs(B: int, Nq: int, Nk: int, H: int, d: int, seed: int, std: float = 1.0):
     """q [B,Nq,H,d], k and v [B,Nk,H,d]: bf16 N(0, std^2)."""
-    rng = np.random.Generator(np.random.PCG64(seed))
-    q = bf16_normal(rng, (B, Nq, H, d), std)
-    k = bf16_normal(rng, (B, Nk, H, d), std)
-    v = bf16_normal(rng, (B, Nk, H, d), std)
+    q = bf16_normal((seed, 0), (B, Nq, H, d), std)
+    k = bf16_normal((seed, 1), (B, Nk, H, d), std)
+    v = bf16_normal((seed, 2), (B, Nk, H, d), std)
     return q, k, v
 
 
@@ -141,19 +181,20 @@ def text_lengths(rng: np.random.Generator, B: int, M: int, lo: int = 32) -> np.n
 def workload_inputs(number: int) -> dict:
     """All activations of one workload, drawn in a fixed order.
 
-    Order: q_x, k_x, v_x, q_c, k_txt, v_txt, kv_len, then three drift draws
-    for k and v (used by the multi-step cache workload).
+    Tensor keys (1000 + number, i) for i = 0..5 in the order q_x, k_x, v_x,
+    q_c, k_txt, v_txt; the per-sample text lengths come from rng_for(number).
     """
     w = WORKLOADS[number]
     rng = rng_for(number)
     B, N, H, d, M = w.B, w.N, w.H, w.d, w.M
+    base = 1000 + number
     out = {"workload": w}
-    out["q_x"] = bf16_normal(rng, (B, N, H, d))
-    out["k_x"] = bf16_normal(rng, (B, N, H, d))
-    out["v_x"] = bf16_normal(rng, (B, N, H, d))
-    out["q_c"] = bf16_normal(rng, (B, N, H, d))
-    out["k_txt"] = bf16_normal(rng, (B, M, H, d))
-    out["v_txt"] = bf16_normal(rng, (B, M, H, d))
+    out["q_x"] = bf16_normal((base, 0), (B, N, H, d))
+    out["k_x"] = bf16_normal((base, 1), (B, N, H, d))
+    out["v_x"] = bf16_normal((base, 2), (B, N, H, d))
+    out["q_c"] = bf16_normal((base, 3), (B, N, H, d))
+    out["k_txt"] = bf16_normal((base, 4), (B, M, H, d))
+    out["v_txt"] = bf16_normal((base, 5), (B, M, H, d))
     if w.kv_len_fixed is not None:
         out["kv_len"] = np.full((B,), w.kv_len_fixed, dtype=np.int32)
     else:
@@ -161,9 +202,9 @@ def workload_inputs(number: int) -> dict:
     return out
 
 
-def drift(rng: np.random.Generator, shape, std: float = 0.05) -> np.ndarray:
-    """float32 N(0, std^2) drift added to cached activations between steps."""
-    return (rng.standard_normal(size=shape, dtype=np.float32) * np.float32(std)).astype(np.float32)
+def drift(key, shape, std: float = 0.05) -> np.ndarray:
+    """float32 N(0, std^2) drift added to cached activations between steps (deterministic in key)."""
+    return normal_f32(key, shape, std)
 
 
 # ----------------------------------------------------------------------------
