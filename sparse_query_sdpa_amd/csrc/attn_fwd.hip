@@ -6,22 +6,29 @@
 // padding kept as a per-sample valid key count; Eq. 18 dense anchor pass).
 //
 // Work decomposition
-//   workgroup = 4 waves = 128 query rows of one (b, h); each wave owns 32 rows.
-//   Keys stream in tiles of 64 through LDS (double buffered, one barrier per tile).
+//   workgroup = 4 waves = 128 query rows of one (b, h); each wave owns 32 rows;
+//   two workgroups per CU (<= 256 registers per lane) so one wave's MFMAs overlap
+//   the other wave's softmax on every SIMD.
+//   Keys stream in tiles of 64 through LDS, double buffered, one barrier per tile.
+//   K and V tiles are copied global -> LDS by the direct-to-LDS loads
+//   (global_load_lds_dwordx4): no staging registers, no LDS store instructions.
+//   Both tiles keep the natural [key][d] layout with one 16-byte pad chunk per row.
 //   Per wave and tile:
 //     S^T[64 keys x 32 queries] = K_tile . Q^T     (v_mfma_f32_32x32x16_bf16)
-//       A = K rows straight from LDS (d contiguous), B = the wave's Q^T held in
-//       registers for the whole loop.  In the 32x32 accumulator layout lane l
-//       holds query column l%32 and 16 keys, so every lane owns one query and
-//       the row max / row sum need only the partner lane l^32.
+//       A = K rows from LDS (ds_read_b128, d contiguous); B = the wave's Q^T,
+//       held in registers for the whole loop.  In the 32x32 accumulator layout
+//       lane l holds query column l%32 and 16 keys, so each lane owns one query
+//       and the row max / row sum need only the partner lane l^32.
 //     O^T[d x 32 queries] += V^T . P^T             (same MFMA)
-//       B = P^T: the lane's own probabilities, converted to bf16 in registers
-//       (no LDS round trip); A = V^T rows from LDS.  V is written to LDS
-//       transposed ([d][key]) with keys permuted inside each group of 16 so the
-//       A operand's k-slots line up with the accumulator rows of S^T.
+//       B = P^T: the lane's own probabilities packed to bf16 in registers.
+//       A = V^T, read with the LDS transpose load ds_read_b64_tr_b16: in each
+//       16-lane group, output lane i element j comes from source lane 4j + i/4,
+//       element i%4; pointing source lane s at V[key0 + s/4][d0 + 4(s%4)] gives
+//       output lane i the four keys key0..key0+3 of column d0 + i, which are
+//       exactly the k-slots the S^T accumulator layout assigns to P^T.
 //   Online softmax in the log2 domain with a lazily moved reference max: the
-//   reference only moves (and O, l are rescaled) when a tile's max exceeds it
-//   by more than 2^8, so probabilities stay <= 256 and rescaling is rare.
+//   reference only moves (and O, l are rescaled) when a tile's max exceeds it by
+//   more than 2^8, so probabilities stay <= 256 and rescaling is rare.
 //   Workgroups are remapped so all row tiles of one (b, h) sit on one XCD and
 //   share its L2 for the K/V stream.
 #include "common.h"
@@ -32,6 +39,7 @@ namespace {
 constexpr int BM = 128;       // query rows per workgroup
 constexpr int BN = 64;        // keys per tile
 constexpr int NTHREADS = 256;
+constexpr int NWAVES = NTHREADS / 64;
 constexpr float kRescaleThreshold = 8.0f;  // log2 units
 
 struct AttnParams {
@@ -49,81 +57,33 @@ struct AttnParams {
   int scatter;
 };
 
-// Slot of key-subgroup sg (4 keys) inside a 16-key group of the transposed V tile:
-// storage order is keys {0-3, 8-11, 4-7, 12-15}.
-__device__ __forceinline__ int vslot(int kg) {
-  const int sg = kg & 3;
-  return (kg & ~3) * 4 + (((sg & 1) << 1) | (sg >> 1)) * 4;
-}
-
 template <int D>
-struct TileRegs {
-  static constexpr int KCH = BN * D / 8;                       // 16-byte K chunks per tile
-  static constexpr int KPT = (KCH + NTHREADS - 1) / NTHREADS;   // per thread
-  static constexpr int VTASKS = (BN / 4) * (D / 8);             // 4 keys x 8 d tasks
-  u32x4 kr[KPT];
-  u32x4 vr[4];
+struct Tile {
+  static constexpr int CH = D / 8;               // 16-byte chunks of a row
+  static constexpr int SLOTS = CH + 1;           // plus one pad chunk
+  static constexpr int ROWB = SLOTS * 16;        // LDS bytes per row
+  static constexpr int BYTES = BN * ROWB;        // LDS bytes per tile and tensor
+  static constexpr int NI = BN * SLOTS / 64;     // wave-wide copies per tile and tensor (= SLOTS)
+  static constexpr int PER_WAVE = (2 * NI + NWAVES - 1) / NWAVES;
 };
 
-template <int D>
-__device__ __forceinline__ void load_tile(TileRegs<D>& t, const u16* kbase, const u16* vbase, int64_t ks1,
-                                          int64_t vs1, int j0, int nvalid, int tid) {
-  constexpr int PARTS = D / 8;
-#pragma unroll
-  for (int c = 0; c < TileRegs<D>::KPT; ++c) {
-    const int chunk = tid + c * NTHREADS;
-    const int key = chunk / PARTS, part = chunk % PARTS;
-    u32x4 val = {0u, 0u, 0u, 0u};
-    if (chunk < TileRegs<D>::KCH && j0 + key < nvalid) val = ld16(kbase + (int64_t)(j0 + key) * ks1 + part * 8);
-    t.kr[c] = val;
-  }
-  if (tid < TileRegs<D>::VTASKS) {
-    const int kg = tid / PARTS, part = tid % PARTS;
-#pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      const int key = kg * 4 + i;
-      u32x4 val = {0u, 0u, 0u, 0u};
-      if (j0 + key < nvalid) val = ld16(vbase + (int64_t)(j0 + key) * vs1 + part * 8);
-      t.vr[i] = val;
-    }
-  }
+typedef __attribute__((address_space(3))) void lds_void;
+typedef short i16x4 __attribute__((ext_vector_type(4)));
+
+__device__ __forceinline__ void copy16_to_lds(const u16* src, char* lds_dst) {
+  __builtin_amdgcn_global_load_lds(src, (lds_void*)lds_dst, 16, 0, 0);
 }
 
-template <int D>
-__device__ __forceinline__ void store_tile(const TileRegs<D>& t, u16 (*Ks)[D + 8], u16 (*Vs)[BN + 8], int tid) {
-  constexpr int PARTS = D / 8;
-#pragma unroll
-  for (int c = 0; c < TileRegs<D>::KPT; ++c) {
-    const int chunk = tid + c * NTHREADS;
-    if (chunk < TileRegs<D>::KCH) {
-      const int key = chunk / PARTS, part = chunk % PARTS;
-      st16(&Ks[key][part * 8], t.kr[c]);
-    }
-  }
-  if (tid < TileRegs<D>::VTASKS) {
-    const int kg = tid / PARTS, part = tid % PARTS;
-    const int slot = vslot(kg);
-#pragma unroll
-    for (int w = 0; w < 4; ++w) {
-      // d = part*8 + 2w (low halves) and + 2w + 1 (high halves), keys kg*4 + 0..3
-      const u32 a0 = t.vr[0][w], a1 = t.vr[1][w], a2 = t.vr[2][w], a3 = t.vr[3][w];
-      u32x2 lo, hi;
-      lo[0] = (a0 & 0xFFFFu) | (a1 << 16);
-      lo[1] = (a2 & 0xFFFFu) | (a3 << 16);
-      hi[0] = (a0 >> 16) | (a1 & 0xFFFF0000u);
-      hi[1] = (a2 >> 16) | (a3 & 0xFFFF0000u);
-      st8(&Vs[part * 8 + 2 * w][slot], lo);
-      st8(&Vs[part * 8 + 2 * w + 1][slot], hi);
-    }
-  }
+__device__ __forceinline__ i16x4 lds_read_tr(const char* p) {
+  return __builtin_amdgcn_ds_read_tr16_b64_v4i16((__attribute__((address_space(3))) i16x4*)p);
 }
 
 template <int D, bool GATHER, bool KVLEN>
-__global__ __launch_bounds__(NTHREADS) void attn_fwd_kernel(AttnParams p) {
+__global__ __launch_bounds__(NTHREADS, 2) void attn_fwd_kernel(AttnParams p) {
+  using T = Tile<D>;
   constexpr int KS = D / 16;   // k-steps of the Q K^T product
   constexpr int DB = D / 32;   // 32-row blocks of O^T
-  __shared__ __attribute__((aligned(16))) u16 Ks[2][BN][D + 8];
-  __shared__ __attribute__((aligned(16))) u16 Vs[2][D][BN + 8];
+  __shared__ __attribute__((aligned(1024))) char smem[2][2][T::BYTES];  // [stage][K, V]
 
   const int tid = threadIdx.x;
   const int lane = tid & 63;
@@ -162,28 +122,63 @@ __global__ __launch_bounds__(NTHREADS) void attn_fwd_kernel(AttnParams p) {
   }
   const int ntiles = (nkeys + BN - 1) / BN;
 
+  // ---- per-lane copy plan: which row/chunk of a tile this lane fetches ----------
+  // Copy gi in [0, 2*NI) of a tile: tensor gi / NI (0 = K, 1 = V), wave-wide part
+  // gi % NI; this wave issues gi = wave + NWAVES * m.
+  const u16* kbase = p.k + (int64_t)b * p.ks0 + (int64_t)h * p.ks2;
+  const u16* vbase = p.v + (int64_t)b * p.vs0 + (int64_t)h * p.vs2;
+  uint32_t coff[T::PER_WAVE];   // element offset of this lane's chunk inside a tile
+  int crow[T::PER_WAVE];        // its row (key) inside the tile; -1: pad slot
+#pragma unroll
+  for (int m = 0; m < T::PER_WAVE; ++m) {
+    const int gi = wave + NWAVES * m;
+    const int t = gi % T::NI;
+    const int slot = t * 64 + lane;
+    const int row = slot / T::SLOTS, chunk = slot % T::SLOTS;
+    const int64_t sn = gi < T::NI ? p.ks1 : p.vs1;
+    coff[m] = (uint32_t)(row * sn + chunk * 8);
+    crow[m] = (gi < 2 * T::NI && chunk < T::CH) ? row : -1;
+  }
+  auto issue_tile = [&](int j0, int stage) {
+    const bool tail = j0 + BN > nkeys;
+#pragma unroll
+    for (int m = 0; m < T::PER_WAVE; ++m) {
+      const int gi = wave + NWAVES * m;
+      if (gi < 2 * T::NI) {
+        const bool isk = gi < T::NI;
+        const int t = gi % T::NI;
+        const u16* base = (isk ? kbase : vbase) + (int64_t)j0 * (isk ? p.ks1 : p.vs1);
+        char* dst = smem[stage][isk ? 0 : 1] + t * 1024;
+        uint32_t off = coff[m];
+        if (tail && crow[m] >= 0 && j0 + crow[m] >= nkeys) off -= (uint32_t)(crow[m] * (isk ? p.ks1 : p.vs1));
+        if (crow[m] >= 0) copy16_to_lds(base + off, dst);
+      }
+    }
+  };
+
   f32x16 oacc[DB];
 #pragma unroll
   for (int i = 0; i < DB; ++i) oacc[i] = f32x16{};
   float m_ref = -INFINITY;  // reference max, log2 domain
   float l_run = 0.f;        // this lane's share of the row sum
-
-  const u16* kbase = p.k + (int64_t)b * p.ks0 + (int64_t)h * p.ks2;
-  const u16* vbase = p.v + (int64_t)b * p.vs0 + (int64_t)h * p.vs2;
   const float sl2 = p.scale_log2;
 
-  TileRegs<D> tr;
-  if (ntiles > 0) {
-    load_tile<D>(tr, kbase, vbase, p.ks1, p.vs1, 0, nkeys, tid);
-    store_tile<D>(tr, Ks[0], Vs[0], tid);
-  }
-  __syncthreads();
+  // LDS addresses of this lane's operand reads (byte offsets inside a tile)
+  const int k_lane = col * T::ROWB + half * 16;
+  const int grp = (lane >> 4) & 3, src = lane & 15;
+  const int v_lane = (4 * (grp >> 1) + (src >> 2)) * T::ROWB + (16 * (grp & 1) + 4 * (src & 3)) * 2;
+
+  if (ntiles > 0) issue_tile(0, 0);
 
   for (int it = 0; it < ntiles; ++it) {
     const int buf = it & 1;
     const int j0 = it * BN;
-    const bool has_next = it + 1 < ntiles;
-    if (has_next) load_tile<D>(tr, kbase, vbase, p.ks1, p.vs1, j0 + BN, nkeys, tid);
+    __builtin_amdgcn_s_waitcnt(0x0F70);  // vmcnt(0): this wave's copies of tile `it` landed
+    __syncthreads();                     // ... everyone's, and tile it-1 is no longer read
+    if (it + 1 < ntiles) issue_tile(j0 + BN, buf ^ 1);
+
+    const char* Kt = smem[buf][0];
+    const char* Vt = smem[buf][1];
 
     // ---- S^T = K Q^T for 64 keys (two 32-key blocks) -------------------------
     f32x16 sacc[2];
@@ -192,7 +187,7 @@ __global__ __launch_bounds__(NTHREADS) void attn_fwd_kernel(AttnParams p) {
       f32x16 acc = f32x16{};
 #pragma unroll
       for (int s = 0; s < KS; ++s) {
-        const bf16x8 kf = as_bf16x8(ld16(&Ks[buf][blk * 32 + col][s * 16 + half * 8]));
+        const bf16x8 kf = as_bf16x8(ld16(Kt + k_lane + blk * 32 * T::ROWB + s * 32));
         acc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kf, qf[s], acc, 0, 0, 0);
       }
       sacc[blk] = acc;
@@ -229,7 +224,7 @@ __global__ __launch_bounds__(NTHREADS) void attn_fwd_kernel(AttnParams p) {
       m_ref = m_new;
     }
 
-    // ---- probabilities, row-sum share, bf16 B operands ------------------------
+    // ---- probabilities (bf16 B operands) and the row-sum share ---------------
     bf16x8 pb[2][2];
 #pragma unroll
     for (int blk = 0; blk < 2; ++blk) {
@@ -240,8 +235,8 @@ __global__ __launch_bounds__(NTHREADS) void attn_fwd_kernel(AttnParams p) {
         for (int e = 0; e < 4; ++e) {
           const float p0 = __builtin_amdgcn_exp2f(__builtin_fmaf(sacc[blk][8 * t + 2 * e], sl2, -m_ref));
           const float p1 = __builtin_amdgcn_exp2f(__builtin_fmaf(sacc[blk][8 * t + 2 * e + 1], sl2, -m_ref));
-          l_run += p0 + p1;
           packed[e] = pack_bf16x2(p0, p1);
+          l_run += p0 + p1;
         }
         pb[blk][t] = as_bf16x8(packed);
       }
@@ -254,13 +249,13 @@ __global__ __launch_bounds__(NTHREADS) void attn_fwd_kernel(AttnParams p) {
       for (int blk = 0; blk < 2; ++blk)
 #pragma unroll
         for (int t = 0; t < 2; ++t) {
-          const bf16x8 vf = as_bf16x8(ld16(&Vs[buf][db * 32 + col][blk * 32 + t * 16 + half * 8]));
+          const char* vp = Vt + v_lane + (blk * 32 + t * 16) * T::ROWB + db * 64;
+          const i16x4 lo = lds_read_tr(vp);
+          const i16x4 hi = lds_read_tr(vp + 8 * T::ROWB);
+          const bf16x8 vf = __builtin_bit_cast(bf16x8, __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7));
           oacc[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(vf, pb[blk][t], oacc[db], 0, 0, 0);
         }
     }
-
-    if (has_next) store_tile<D>(tr, Ks[buf ^ 1], Vs[buf ^ 1], tid);
-    __syncthreads();
   }
 
   // ---- epilogue: normalise, store O (bf16) and LSE ------------------------------
