@@ -12,7 +12,8 @@
 //   Keys stream in tiles of 64 through LDS, double buffered, one barrier per tile.
 //   K and V tiles are copied global -> LDS by the direct-to-LDS loads
 //   (global_load_lds_dwordx4): no staging registers, no LDS store instructions.
-//   Both tiles keep the natural [key][d] layout with one 16-byte pad chunk per row.
+//   Both tiles keep the natural [key][d] layout; row strides are chosen for
+//   conflict-free LDS reads (see Tile).
 //   Per wave and tile:
 //     S^T[64 keys x 32 queries] = K_tile . Q^T     (v_mfma_f32_32x32x16_bf16)
 //       A = K rows from LDS (ds_read_b128, d contiguous); B = the wave's Q^T,
@@ -57,14 +58,24 @@ struct AttnParams {
   int scatter;
 };
 
+// LDS tile geometry.  K rows are read 16 bytes per lane, 16 lanes on 16 rows at once:
+// conflict-free on the 64 four-byte banks when the row stride is an odd number of
+// 16-byte chunks.  V rows are read by the transpose load, 4 rows x 32 bytes per
+// 16-lane group: conflict-free when the stride is 64 or 192 bytes modulo 256.
 template <int D>
 struct Tile {
-  static constexpr int CH = D / 8;               // 16-byte chunks of a row
-  static constexpr int SLOTS = CH + 1;           // plus one pad chunk
-  static constexpr int ROWB = SLOTS * 16;        // LDS bytes per row
-  static constexpr int BYTES = BN * ROWB;        // LDS bytes per tile and tensor
-  static constexpr int NI = BN * SLOTS / 64;     // wave-wide copies per tile and tensor (= SLOTS)
-  static constexpr int PER_WAVE = (2 * NI + NWAVES - 1) / NWAVES;
+  static constexpr int CH = D / 8;                                   // 16-byte chunks of a row
+  static constexpr int K_SLOTS = CH | 1;                             // odd chunk count
+  static constexpr int V_SLOTS = (CH % 16 == 4 || CH % 16 == 12) ? CH : (CH | 3) + (((CH | 3) % 16 == 7 || (CH | 3) % 16 == 15) ? 5 : 1);
+  static constexpr int K_ROWB = K_SLOTS * 16;
+  static constexpr int V_ROWB = V_SLOTS * 16;
+  static constexpr int K_BYTES = BN * K_ROWB;
+  static constexpr int V_BYTES = BN * V_ROWB;
+  static constexpr int STAGE = K_BYTES + V_BYTES;
+  static constexpr int NCOPY = K_SLOTS + V_SLOTS;                    // wave-wide 1 KB copies per tile
+  static constexpr int PER_WAVE = (NCOPY + NWAVES - 1) / NWAVES;
+  static_assert((V_SLOTS % 16) == 4 || (V_SLOTS % 16) == 12, "V stride must be 64 or 192 mod 256 bytes");
+  static_assert(V_SLOTS >= CH && K_SLOTS >= CH, "rows must fit");
 };
 
 typedef __attribute__((address_space(3))) void lds_void;
@@ -83,7 +94,7 @@ __global__ __launch_bounds__(NTHREADS, 2) void attn_fwd_kernel(AttnParams p) {
   using T = Tile<D>;
   constexpr int KS = D / 16;   // k-steps of the Q K^T product
   constexpr int DB = D / 32;   // 32-row blocks of O^T
-  __shared__ __attribute__((aligned(1024))) char smem[2][2][T::BYTES];  // [stage][K, V]
+  __shared__ __attribute__((aligned(1024))) char smem[2][T::STAGE];  // [stage]: K tile, then V tile
 
   const int tid = threadIdx.x;
   const int lane = tid & 63;
@@ -122,36 +133,59 @@ __global__ __launch_bounds__(NTHREADS, 2) void attn_fwd_kernel(AttnParams p) {
   }
   const int ntiles = (nkeys + BN - 1) / BN;
 
-  // ---- per-lane copy plan: which row/chunk of a tile this lane fetches ----------
-  // Copy gi in [0, 2*NI) of a tile: tensor gi / NI (0 = K, 1 = V), wave-wide part
-  // gi % NI; this wave issues gi = wave + NWAVES * m.
-  const u16* kbase = p.k + (int64_t)b * p.ks0 + (int64_t)h * p.ks2;
-  const u16* vbase = p.v + (int64_t)b * p.vs0 + (int64_t)h * p.vs2;
-  uint32_t coff[T::PER_WAVE];   // element offset of this lane's chunk inside a tile
-  int crow[T::PER_WAVE];        // its row (key) inside the tile; -1: pad slot
+  // ---- per-lane copy plan ------------------------------------------------------
+  // A tile is NCOPY wave-wide copies of 1 KB: copy c < K_SLOTS fills K slots
+  // [64c, 64c + 64), the rest fill V.  Slot sigma is row sigma / SLOTS, chunk
+  // sigma % SLOTS; pad chunks fetch chunk 0 of their row (never read back), so every
+  // lane is active.  This wave issues copies c = wave + NWAVES * m.
+  const char* kbase = reinterpret_cast<const char*>(p.k + (int64_t)b * p.ks0 + (int64_t)h * p.ks2);
+  const char* vbase = reinterpret_cast<const char*>(p.v + (int64_t)b * p.vs0 + (int64_t)h * p.vs2);
+  const int64_t krow_b = p.ks1 * 2, vrow_b = p.vs1 * 2;   // bytes between consecutive keys
+  uint32_t coff[T::PER_WAVE];                               // byte offset of this lane's chunk in a tile
 #pragma unroll
   for (int m = 0; m < T::PER_WAVE; ++m) {
-    const int gi = wave + NWAVES * m;
-    const int t = gi % T::NI;
-    const int slot = t * 64 + lane;
-    const int row = slot / T::SLOTS, chunk = slot % T::SLOTS;
-    const int64_t sn = gi < T::NI ? p.ks1 : p.vs1;
-    coff[m] = (uint32_t)(row * sn + chunk * 8);
-    crow[m] = (gi < 2 * T::NI && chunk < T::CH) ? row : -1;
+    const int c = wave + NWAVES * m;
+    const bool isk = c < T::K_SLOTS;
+    const int slots = isk ? T::K_SLOTS : T::V_SLOTS;
+    const int sigma = (isk ? c : c - T::K_SLOTS) * 64 + lane;
+    const int row = sigma / slots;
+    int chunk = sigma % slots;
+    if (chunk >= T::CH) chunk = 0;
+    coff[m] = (uint32_t)(row * (isk ? krow_b : vrow_b) + chunk * 16);
   }
+  // rows of the last (partial) tile past the valid keys fetch key j0 instead
+  auto tail_off = [&](int m, int nrow_valid) -> uint32_t {
+    const int c = wave + NWAVES * m;
+    const bool isk = c < T::K_SLOTS;
+    const int slots = isk ? T::K_SLOTS : T::V_SLOTS;
+    const int sigma = (isk ? c : c - T::K_SLOTS) * 64 + lane;
+    const int row = sigma / slots;
+    int chunk = sigma % slots;
+    if (chunk >= T::CH) chunk = 0;
+    return (uint32_t)((row < nrow_valid ? row : 0) * (isk ? krow_b : vrow_b) + chunk * 16);
+  };
   auto issue_tile = [&](int j0, int stage) {
-    const bool tail = j0 + BN > nkeys;
+    const char* kb = kbase + (int64_t)j0 * krow_b;
+    const char* vb = vbase + (int64_t)j0 * vrow_b;
+    const int nrow_valid = nkeys - j0;
+    if (nrow_valid >= BN) {
 #pragma unroll
-    for (int m = 0; m < T::PER_WAVE; ++m) {
-      const int gi = wave + NWAVES * m;
-      if (gi < 2 * T::NI) {
-        const bool isk = gi < T::NI;
-        const int t = gi % T::NI;
-        const u16* base = (isk ? kbase : vbase) + (int64_t)j0 * (isk ? p.ks1 : p.vs1);
-        char* dst = smem[stage][isk ? 0 : 1] + t * 1024;
-        uint32_t off = coff[m];
-        if (tail && crow[m] >= 0 && j0 + crow[m] >= nkeys) off -= (uint32_t)(crow[m] * (isk ? p.ks1 : p.vs1));
-        if (crow[m] >= 0) copy16_to_lds(base + off, dst);
+      for (int m = 0; m < T::PER_WAVE; ++m) {
+        const int c = wave + NWAVES * m;
+        if (c < T::NCOPY) {
+          const bool isk = c < T::K_SLOTS;
+          copy16_to_lds(reinterpret_cast<const u16*>((isk ? kb : vb) + coff[m]), smem[stage] + c * 1024);
+        }
+      }
+    } else {
+#pragma unroll
+      for (int m = 0; m < T::PER_WAVE; ++m) {
+        const int c = wave + NWAVES * m;
+        if (c < T::NCOPY) {
+          const bool isk = c < T::K_SLOTS;
+          copy16_to_lds(reinterpret_cast<const u16*>((isk ? kb : vb) + tail_off(m, nrow_valid)),
+                        smem[stage] + c * 1024);
+        }
       }
     }
   };
@@ -164,9 +198,9 @@ __global__ __launch_bounds__(NTHREADS, 2) void attn_fwd_kernel(AttnParams p) {
   const float sl2 = p.scale_log2;
 
   // LDS addresses of this lane's operand reads (byte offsets inside a tile)
-  const int k_lane = col * T::ROWB + half * 16;
+  const int k_lane = col * T::K_ROWB + half * 16;
   const int grp = (lane >> 4) & 3, src = lane & 15;
-  const int v_lane = (4 * (grp >> 1) + (src >> 2)) * T::ROWB + (16 * (grp & 1) + 4 * (src & 3)) * 2;
+  const int v_lane = (4 * (grp >> 1) + (src >> 2)) * T::V_ROWB + (16 * (grp & 1) + 4 * (src & 3)) * 2;
 
   if (ntiles > 0) issue_tile(0, 0);
 
@@ -177,8 +211,8 @@ __global__ __launch_bounds__(NTHREADS, 2) void attn_fwd_kernel(AttnParams p) {
     __syncthreads();                     // ... everyone's, and tile it-1 is no longer read
     if (it + 1 < ntiles) issue_tile(j0 + BN, buf ^ 1);
 
-    const char* Kt = smem[buf][0];
-    const char* Vt = smem[buf][1];
+    const char* Kt = smem[buf];
+    const char* Vt = smem[buf] + T::K_BYTES;
 
     // ---- S^T = K Q^T for 64 keys (two 32-key blocks) -------------------------
     f32x16 sacc[2];
@@ -187,7 +221,7 @@ __global__ __launch_bounds__(NTHREADS, 2) void attn_fwd_kernel(AttnParams p) {
       f32x16 acc = f32x16{};
 #pragma unroll
       for (int s = 0; s < KS; ++s) {
-        const bf16x8 kf = as_bf16x8(ld16(Kt + k_lane + blk * 32 * T::ROWB + s * 32));
+        const bf16x8 kf = as_bf16x8(ld16(Kt + k_lane + blk * 32 * T::K_ROWB + s * 32));
         acc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kf, qf[s], acc, 0, 0, 0);
       }
       sacc[blk] = acc;
@@ -249,9 +283,9 @@ __global__ __launch_bounds__(NTHREADS, 2) void attn_fwd_kernel(AttnParams p) {
       for (int blk = 0; blk < 2; ++blk)
 #pragma unroll
         for (int t = 0; t < 2; ++t) {
-          const char* vp = Vt + v_lane + (blk * 32 + t * 16) * T::ROWB + db * 64;
+          const char* vp = Vt + v_lane + (blk * 32 + t * 16) * T::V_ROWB + db * 64;
           const i16x4 lo = lds_read_tr(vp);
-          const i16x4 hi = lds_read_tr(vp + 8 * T::ROWB);
+          const i16x4 hi = lds_read_tr(vp + 8 * T::V_ROWB);
           const bf16x8 vf = __builtin_bit_cast(bf16x8, __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7));
           oacc[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(vf, pb[blk][t], oacc[db], 0, 0, 0);
         }
