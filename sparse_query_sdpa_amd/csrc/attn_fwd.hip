@@ -9,7 +9,8 @@
 //   workgroup = 4 waves = 128 query rows of one (b, h); each wave owns 32 rows;
 //   two workgroups per CU (<= 256 registers per lane) so one wave's MFMAs overlap
 //   the other wave's softmax on every SIMD.
-//   Keys stream in tiles of 64 through LDS, double buffered, one barrier per tile.
+//   Keys stream in tiles of 64 through LDS, double buffered (two separate LDS
+//   objects, loop unrolled by two), one barrier per tile.
 //   K and V tiles are copied global -> LDS by the direct-to-LDS loads
 //   (global_load_lds_dwordx4): no staging registers, no LDS store instructions.
 //   Both tiles keep the natural [key][d] layout; row strides are chosen for
@@ -94,7 +95,10 @@ __global__ __launch_bounds__(NTHREADS, 2) void attn_fwd_kernel(AttnParams p) {
   using T = Tile<D>;
   constexpr int KS = D / 16;   // k-steps of the Q K^T product
   constexpr int DB = D / 32;   // 32-row blocks of O^T
-  __shared__ __attribute__((aligned(1024))) char smem[2][T::STAGE];  // [stage]: K tile, then V tile
+  // two stages as separate objects: the compiler can then tell a copy into one stage
+  // from reads of the other and does not wait for the copy before those reads
+  __shared__ __attribute__((aligned(1024))) char stage0[T::STAGE];  // K tile, then V tile
+  __shared__ __attribute__((aligned(1024))) char stage1[T::STAGE];
 
   const int tid = threadIdx.x;
   const int lane = tid & 63;
@@ -164,7 +168,7 @@ __global__ __launch_bounds__(NTHREADS, 2) void attn_fwd_kernel(AttnParams p) {
     if (chunk >= T::CH) chunk = 0;
     return (uint32_t)((row < nrow_valid ? row : 0) * (isk ? krow_b : vrow_b) + chunk * 16);
   };
-  auto issue_tile = [&](int j0, int stage) {
+  auto issue_tile = [&](int j0, char* stage) {
     const char* kb = kbase + (int64_t)j0 * krow_b;
     const char* vb = vbase + (int64_t)j0 * vrow_b;
     const int nrow_valid = nkeys - j0;
@@ -174,7 +178,7 @@ __global__ __launch_bounds__(NTHREADS, 2) void attn_fwd_kernel(AttnParams p) {
         const int c = wave + NWAVES * m;
         if (c < T::NCOPY) {
           const bool isk = c < T::K_SLOTS;
-          copy16_to_lds(reinterpret_cast<const u16*>((isk ? kb : vb) + coff[m]), smem[stage] + c * 1024);
+          copy16_to_lds(reinterpret_cast<const u16*>((isk ? kb : vb) + coff[m]), stage + c * 1024);
         }
       }
     } else {
@@ -184,7 +188,7 @@ __global__ __launch_bounds__(NTHREADS, 2) void attn_fwd_kernel(AttnParams p) {
         if (c < T::NCOPY) {
           const bool isk = c < T::K_SLOTS;
           copy16_to_lds(reinterpret_cast<const u16*>((isk ? kb : vb) + tail_off(m, nrow_valid)),
-                        smem[stage] + c * 1024);
+                        stage + c * 1024);
         }
       }
     }
@@ -202,17 +206,16 @@ __global__ __launch_bounds__(NTHREADS, 2) void attn_fwd_kernel(AttnParams p) {
   const int grp = (lane >> 4) & 3, src = lane & 15;
   const int v_lane = (4 * (grp >> 1) + (src >> 2)) * T::V_ROWB + (16 * (grp & 1) + 4 * (src & 3)) * 2;
 
-  if (ntiles > 0) issue_tile(0, 0);
-
-  for (int it = 0; it < ntiles; ++it) {
-    const int buf = it & 1;
+  // One tile: wait for its copies, start the next tile's copies into the other
+  // stage, then compute from this stage.
+  auto tile_step = [&](int it, const char* cur, char* nxt) {
     const int j0 = it * BN;
     __builtin_amdgcn_s_waitcnt(0x0F70);  // vmcnt(0): this wave's copies of tile `it` landed
     __syncthreads();                     // ... everyone's, and tile it-1 is no longer read
-    if (it + 1 < ntiles) issue_tile(j0 + BN, buf ^ 1);
+    if (it + 1 < ntiles) issue_tile(j0 + BN, nxt);
 
-    const char* Kt = smem[buf];
-    const char* Vt = smem[buf] + T::K_BYTES;
+    const char* Kt = cur;
+    const char* Vt = cur + T::K_BYTES;
 
     // ---- S^T = K Q^T for 64 keys (two 32-key blocks) -------------------------
     f32x16 sacc[2];
@@ -290,6 +293,12 @@ __global__ __launch_bounds__(NTHREADS, 2) void attn_fwd_kernel(AttnParams p) {
           oacc[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(vf, pb[blk][t], oacc[db], 0, 0, 0);
         }
     }
+  };
+
+  if (ntiles > 0) issue_tile(0, stage0);
+  for (int it = 0; it < ntiles; it += 2) {
+    tile_step(it, stage0, stage1);
+    if (it + 1 < ntiles) tile_step(it + 1, stage1, stage0);
   }
 
   // ---- epilogue: normalise, store O (bf16) and LSE ------------------------------

@@ -38,10 +38,12 @@ __device__ __forceinline__ void st8(void* p, u32x2 v) { *reinterpret_cast<u32x2*
 
 __device__ __forceinline__ bf16x8 as_bf16x8(u32x4 v) { return __builtin_bit_cast(bf16x8, v); }
 
-// Round-to-nearest-even float -> bfloat16 bits (finite and infinite inputs; NaN stays NaN).
+typedef float f32x2 __attribute__((ext_vector_type(2)));
+
+// Round-to-nearest-even float pair -> packed bfloat16 (one v_cvt_pk_bf16_f32).
 __device__ __forceinline__ u32 pack_bf16x2(float lo, float hi) {
-  __bf16 a = (__bf16)lo, b = (__bf16)hi;
-  return (u32)__builtin_bit_cast(u16, a) | ((u32)__builtin_bit_cast(u16, b) << 16);
+  const f32x2 f = {lo, hi};
+  return __builtin_bit_cast(u32, __builtin_convertvector(f, bf16x2));
 }
 
 inline int64_t ceil_div64(int64_t a, int64_t b) { return (a + b - 1) / b; }
