@@ -21,13 +21,21 @@ and the fp64 CPU oracle timed on a bounded sample on this host.
   python bench.py [--gpus 1] [--steps 20] [--warmup 3]
   python bench.py --rocprof-summary <kernel_stats.csv>   # markdown summary of a rocprofv3 run
   python bench.py --copy-probe                           # plain 1 GiB copy for counter calibration
+  python bench.py --pmc-summary F.csv Fcopy.csv W.csv Wcopy.csv  # HBM traffic per attention launch
+
+HBM traffic (the roofline's `traffic`) comes from two rocprofv3 --pmc runs of
+this script (FETCH_SIZE, then WRITE_SIZE) scaled by what the same counters read
+for the copy probe; --pmc-summary writes it with a hash of the kernel source,
+and the bench reports it only while the source still has that hash.
 """
 from __future__ import annotations
 
 import argparse
+import csv
+import hashlib
 import json
-import math
 import os
+import re
 import sys
 import time
 
@@ -36,11 +44,65 @@ sys.path.insert(0, ROOT)
 
 PEAK_BF16_TFLOPS = 2500.0   # MI355X dense bf16 MFMA
 PEAK_HBM_GBS = 8000.0       # MI355X HBM3E
+COPY_PROBE_BYTES = 1 << 30  # bytes read and bytes written by one copy-probe launch
+ATTN_SOURCES = ("sparse_query_sdpa_amd/csrc/attn_fwd.hip", "sparse_query_sdpa_amd/csrc/common.h")
+TRAFFIC_FILE = os.path.join(ROOT, "profiles", "attn_fwd_hbm_traffic_2560sq.md")
+KERNELS = {"dense": "attn_fwd_kernel<96, false, false>", "srsu": "attn_fwd_kernel<96, true, false>"}
+
+
+def attn_source_hash() -> str:
+    h = hashlib.sha256()
+    for rel in ATTN_SOURCES:
+        h.update(open(os.path.join(ROOT, rel), "rb").read())
+    return h.hexdigest()[:16]
+
+
+def recorded_traffic() -> dict:
+    """Per-launch HBM bytes recorded by --pmc-summary, if the kernel source is unchanged."""
+    if not os.path.exists(TRAFFIC_FILE):
+        return {}
+    out, cur = {}, attn_source_hash()
+    for m in re.finditer(r"^traffic (\w+) bytes=(\d+) fetch=(\d+) write=(\d+) source=(\w+)$",
+                         open(TRAFFIC_FILE).read(), flags=re.M):
+        if m.group(5) == cur:
+            out[m.group(1)] = {"bytes": int(m.group(2)), "fetch": int(m.group(3)), "write": int(m.group(4))}
+    return out
+
+
+def _pmc_rows(path: str, counter: str):
+    return [r for r in csv.DictReader(open(path)) if r["Counter_Name"] == counter]
+
+
+def pmc_summary(fetch_csv: str, fetch_copy_csv: str, write_csv: str, write_copy_csv: str) -> None:
+    """Markdown of per-launch HBM traffic from FETCH_SIZE / WRITE_SIZE runs (KiB per dispatch) of the
+    bench, each scaled by the same counter's reading for the copy probe (1 GiB read + 1 GiB written)."""
+
+    def mean_of(rows, pred):
+        vals = [float(r["Counter_Value"]) * 1024 for r in rows if pred(r["Kernel_Name"])]
+        return (sum(vals) / len(vals) if vals else float("nan")), len(vals)
+
+    is_copy = lambda name: "elementwise" in name and "Fill" not in name
+    copy_f, _ = mean_of(_pmc_rows(fetch_copy_csv, "FETCH_SIZE"), is_copy)
+    copy_w, _ = mean_of(_pmc_rows(write_copy_csv, "WRITE_SIZE"), is_copy)
+    ff, fw = COPY_PROBE_BYTES / copy_f, COPY_PROBE_BYTES / copy_w
+    print(f"copy probe (1 GiB read + 1 GiB written per launch): FETCH_SIZE reads {copy_f / 2**30:.4f} GiB, "
+          f"WRITE_SIZE reads {copy_w / 2**30:.4f} GiB -> scale factors fetch {ff:.4f}, write {fw:.4f}\n")
+    print("| kernel | launches | FETCH_SIZE MB (raw) | WRITE_SIZE MB (raw) | HBM bytes per launch (scaled) |")
+    print("|---|---|---|---|---|")
+    fetch, write = _pmc_rows(fetch_csv, "FETCH_SIZE"), _pmc_rows(write_csv, "WRITE_SIZE")
+    lines, src = [], attn_source_hash()
+    for key, needle in KERNELS.items():
+        f, nf = mean_of(fetch, lambda n: needle in n)
+        w, _ = mean_of(write, lambda n: needle in n)
+        total = int(f * ff + w * fw)
+        print(f"| `{needle}` ({key}) | {nf} | {f / 1e6:.1f} | {w / 1e6:.1f} | {total / 1e6:.1f} MB |")
+        lines.append(f"traffic {key} bytes={total} fetch={int(f * ff)} write={int(w * fw)} source={src}")
+    print()
+    print("\n".join(lines))
 
 
 def rocprof_summary(path: str) -> None:
     """Print a short markdown table of a rocprofv3 --stats kernel_stats.csv."""
-    import csv
     rows = list(csv.DictReader(open(path)))
     print("| kernel | calls | avg us | min us | max us | total ms | % |")
     print("|---|---|---|---|---|---|---|")
@@ -53,16 +115,16 @@ def rocprof_summary(path: str) -> None:
 
 
 def copy_probe() -> None:
+    """A plain elementwise kernel of known traffic: 1 GiB read, 1 GiB written per launch."""
     import torch
-    n = 1 << 30
-    a = torch.empty(n, dtype=torch.uint8, device="cuda")
-    b = torch.empty(n, dtype=torch.uint8, device="cuda")
-    a.fill_(1)
+    n = COPY_PROBE_BYTES // 4
+    a = torch.ones(n, dtype=torch.float32, device="cuda")
+    b = torch.empty_like(a)
     torch.cuda.synchronize()
     for _ in range(3):
-        b.copy_(a)
+        torch.add(a, 0.0, out=b)
     torch.cuda.synchronize()
-    print(json.dumps({"copy_probe_bytes_each_way": n, "copies": 3}))
+    print(json.dumps({"copy_probe_bytes_each_way": COPY_PROBE_BYTES, "launches": 3}))
 
 
 def main() -> int:
@@ -74,13 +136,18 @@ def main() -> int:
     ap.add_argument("--sigma", type=float, default=1.0)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-sweep", action="store_true")
-    ap.add_argument("--cpu-rows", type=int, default=512, help="oracle sample: query rows per sample")
+    ap.add_argument("--cpu-rows", type=int, default=3072, help="oracle sample: query rows per sample")
     ap.add_argument("--rocprof-summary", type=str, default=None)
     ap.add_argument("--copy-probe", action="store_true")
+    ap.add_argument("--pmc-summary", nargs=4, metavar=("FETCH_CSV", "FETCH_COPY_CSV", "WRITE_CSV", "WRITE_COPY_CSV"),
+                    default=None)
     args = ap.parse_args()
 
     if args.rocprof_summary:
         rocprof_summary(args.rocprof_summary)
+        return 0
+    if args.pmc_summary:
+        pmc_summary(*args.pmc_summary)
         return 0
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) > 1:
         print("bench.py measures one GPU only: this build has no multi-GPU path "
@@ -180,6 +247,7 @@ def main() -> int:
     fl_cross = 4.0 * H * d * k * Lsum
     kv_bytes = 4.0 * B * N * H * d * 2
     tf = lambda fl, ms: fl / (ms * 1e-3) / 1e12
+    traffic = recorded_traffic()
     srsu_tf = tf(fl_srsu, stage_ms["srsu_self"])
     dense_tf = tf(fl_dense, stage_ms["dense"])
     out = {
@@ -208,11 +276,13 @@ def main() -> int:
         "kv_assemble_pct_hbm": round(100 * kv_bytes / (stage_ms["kv_assemble"] * 1e-3) / 1e9 / PEAK_HBM_GBS, 2),
         "roofline": {"bound": "mfma", "kernel": "attn_fwd_kernel<96,false,false> (dense anchor pass)",
                      "achieved": round(dense_tf, 2), "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s",
-                     "frac": round(dense_tf / PEAK_BF16_TFLOPS, 4), "traffic": None,
+                     "frac": round(dense_tf / PEAK_BF16_TFLOPS, 4),
+                     "traffic": traffic.get("dense", {}).get("bytes"),
                      "algorithmic_flops_per_launch": fl_dense, "avg_launch_ms": round(stage_ms["dense"], 4)},
         "roofline_srsu": {"bound": "mfma", "kernel": "attn_fwd_kernel<96,true,false> (SRSU self-attention)",
                           "achieved": round(srsu_tf, 2), "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s",
-                          "frac": round(srsu_tf / PEAK_BF16_TFLOPS, 4), "traffic": None,
+                          "frac": round(srsu_tf / PEAK_BF16_TFLOPS, 4),
+                          "traffic": traffic.get("srsu", {}).get("bytes"),
                           "algorithmic_flops_per_launch": fl_srsu, "avg_launch_ms": round(stage_ms["srsu_self"], 4)},
         "peak_mem_gb": round(torch.cuda.max_memory_allocated() / 1e9, 2),
         "pages_context": "PyTorch SDPA stack on unstated hardware: masked SDPA 4.1-5.8x slower than mask-free; "
