@@ -109,7 +109,7 @@ __global__ __launch_bounds__(NT) void mask_scan_kernel(ScanParams p) {
       const bool first_blocked = is_blocked<T>(first);
       const int nchunks = Nk / EPC;
       const u32x4* rv = reinterpret_cast<const u32x4*>(row);
-      constexpr int UNR = 4;
+      constexpr int UNR = 8;
       for (int c0 = 0; c0 < nchunks; c0 += kWave * UNR) {
         u32x4 buf[UNR];
 #pragma unroll
