@@ -7,8 +7,8 @@
 //
 // Work decomposition
 //   workgroup = 4 waves = 128 query rows of one (b, h); each wave owns 32 rows;
-//   two workgroups per CU (<= 256 registers per lane) so one wave's MFMAs overlap
-//   the other wave's softmax on every SIMD.
+//   three workgroups per CU (<= 168 registers per lane; two for the key-length
+//   variant) so the waves on a SIMD overlap one another's MFMA and softmax work.
 //   Keys stream in tiles of 64 through LDS, double buffered (two separate LDS
 //   objects, loop unrolled by two), one barrier per tile.
 //   K and V tiles are copied global -> LDS by the direct-to-LDS loads
@@ -91,7 +91,7 @@ __device__ __forceinline__ i16x4 lds_read_tr(const char* p) {
 }
 
 template <int D, bool GATHER, bool KVLEN>
-__global__ __launch_bounds__(NTHREADS, 2) void attn_fwd_kernel(AttnParams p) {
+__global__ __launch_bounds__(NTHREADS, KVLEN ? 2 : 3) void attn_fwd_kernel(AttnParams p) {
   using T = Tile<D>;
   constexpr int KS = D / 16;   // k-steps of the Q K^T product
   constexpr int DB = D / 32;   // 32-row blocks of O^T
