@@ -214,7 +214,8 @@ int safe_kv_assemble(const safe_kv_args* a, void* stream);
  * kv_len        device int32 [B] or NULL; values are clamped to [0, Nk].
  * lse           device fp32 [B, H, n_rows], optional.
  * o             bf16; compact [B, n_rows, H, d] unless SAFE_ATTN_SCATTER_OUT.
- * Limits: d in {32, 64, 96, 128}; pointers and strides give 16-byte aligned rows.
+ * Limits: d in {32, 64, 96, 128}; pointers and strides give 16-byte aligned rows;
+ * k and v token strides (stride[1]) below 2^25 elements (else SAFE_ERR_UNSUPPORTED).
  */
 typedef struct {
   int32_t B, H, Nq, Nk, d;

@@ -111,8 +111,9 @@ int safe_attn_fwd(const safe_attn_args* a, void* stream) {
   if ((st = check_bnhd(a->v, a->v_stride, work && a->Nk > 0)) != SAFE_OK) return st;
   if ((st = check_bnhd(a->o, a->o_stride, work)) != SAFE_OK) return st;
   if (!work) return SAFE_OK;
-  // key/value token strides: a 64-key tile must span < 2^32 elements (32-bit lane offsets)
-  if (a->k_stride[1] >= (int64_t(1) << 26) || a->v_stride[1] >= (int64_t(1) << 26)) return SAFE_ERR_UNSUPPORTED;
+  // key/value token strides: the kernel addresses a 64-key tile with 32-bit byte offsets
+  // (63 rows of 2 * stride bytes plus a row), so strides stay below 2^25 elements
+  if (a->k_stride[1] >= (int64_t(1) << 25) || a->v_stride[1] >= (int64_t(1) << 25)) return SAFE_ERR_UNSUPPORTED;
   hipStream_t s = static_cast<hipStream_t>(stream);
   if (a->flags & SAFE_FLAG_CHECK) {
     if (a->q_rows != nullptr &&

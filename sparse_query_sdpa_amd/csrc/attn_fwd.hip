@@ -82,7 +82,7 @@ struct Tile {
 typedef __attribute__((address_space(3))) void lds_void;
 typedef short i16x4 __attribute__((ext_vector_type(4)));
 
-__device__ __forceinline__ void copy16_to_lds(const u16* src, char* lds_dst) {
+__device__ __forceinline__ void copy16_to_lds(const char* src, char* lds_dst) {
   __builtin_amdgcn_global_load_lds(src, (lds_void*)lds_dst, 16, 0, 0);
 }
 
@@ -91,7 +91,7 @@ __device__ __forceinline__ i16x4 lds_read_tr(const char* p) {
 }
 
 template <int D, bool GATHER, bool KVLEN>
-__global__ __launch_bounds__(NTHREADS, KVLEN ? 2 : 3) void attn_fwd_kernel(AttnParams p) {
+__global__ __launch_bounds__(NTHREADS, D >= 128 ? 2 : 3) void attn_fwd_kernel(AttnParams p) {
   using T = Tile<D>;
   constexpr int KS = D / 16;   // k-steps of the Q K^T product
   constexpr int DB = D / 32;   // 32-row blocks of O^T
@@ -102,7 +102,7 @@ __global__ __launch_bounds__(NTHREADS, KVLEN ? 2 : 3) void attn_fwd_kernel(AttnP
 
   const int tid = threadIdx.x;
   const int lane = tid & 63;
-  const int wave = tid >> 6;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);  // uniform: scalar copy bookkeeping
   const int col = lane & 31;   // query column owned by this lane
   const int half = lane >> 5;  // which 8-wide k slice / 4-row group this lane holds
 
@@ -141,7 +141,12 @@ __global__ __launch_bounds__(NTHREADS, KVLEN ? 2 : 3) void attn_fwd_kernel(AttnP
   // A tile is NCOPY wave-wide copies of 1 KB: copy c < K_SLOTS fills K slots
   // [64c, 64c + 64), the rest fill V.  Slot sigma is row sigma / SLOTS, chunk
   // sigma % SLOTS; pad chunks fetch chunk 0 of their row (never read back), so every
-  // lane is active.  This wave issues copies c = wave + NWAVES * m.
+  // lane is active.  Wave w issues copies c = w + NWAVES * m.  Rounds m < FULL are
+  // issued by every wave and whether a round is K, V or mixed is a compile-time
+  // fact, so a full tile costs one scalar select per mixed round and one uniform
+  // branch for the partial last round: no per-copy branches (a taken branch
+  // refetches the wave's instructions).
+  constexpr int FULL = T::NCOPY / NWAVES;
   const char* kbase = reinterpret_cast<const char*>(p.k + (int64_t)b * p.ks0 + (int64_t)h * p.ks2);
   const char* vbase = reinterpret_cast<const char*>(p.v + (int64_t)b * p.vs0 + (int64_t)h * p.vs2);
   const int64_t krow_b = p.ks1 * 2, vrow_b = p.vs1 * 2;   // bytes between consecutive keys
@@ -157,38 +162,39 @@ __global__ __launch_bounds__(NTHREADS, KVLEN ? 2 : 3) void attn_fwd_kernel(AttnP
     if (chunk >= T::CH) chunk = 0;
     coff[m] = (uint32_t)(row * (isk ? krow_b : vrow_b) + chunk * 16);
   }
-  // rows of the last (partial) tile past the valid keys fetch key j0 instead
-  auto tail_off = [&](int m, int nrow_valid) -> uint32_t {
-    const int c = wave + NWAVES * m;
-    const bool isk = c < T::K_SLOTS;
-    const int slots = isk ? T::K_SLOTS : T::V_SLOTS;
-    const int sigma = (isk ? c : c - T::K_SLOTS) * 64 + lane;
-    const int row = sigma / slots;
-    int chunk = sigma % slots;
-    if (chunk >= T::CH) chunk = 0;
-    return (uint32_t)((row < nrow_valid ? row : 0) * (isk ? krow_b : vrow_b) + chunk * 16);
-  };
   auto issue_tile = [&](int j0, char* stage) {
     const char* kb = kbase + (int64_t)j0 * krow_b;
     const char* vb = vbase + (int64_t)j0 * vrow_b;
     const int nrow_valid = nkeys - j0;
     if (nrow_valid >= BN) {
+      // The empty asm statements redefine the offsets in place each tile: the 32-bit
+      // lane offsets are then not widened and hoisted out of the loop (the copy keeps
+      // the scalar-base form, base in SGPRs + 32-bit lane offset), and the LDS
+      // destinations are one scalar add each instead of precomputed registers.
+      int wlds = wave * 1024;
+      asm volatile("" : "+s"(wlds));
 #pragma unroll
       for (int m = 0; m < T::PER_WAVE; ++m) {
         const int c = wave + NWAVES * m;
-        if (c < T::NCOPY) {
-          const bool isk = c < T::K_SLOTS;
-          copy16_to_lds(reinterpret_cast<const u16*>((isk ? kb : vb) + coff[m]), stage + c * 1024);
-        }
+        const bool all_k = NWAVES * m + NWAVES - 1 < T::K_SLOTS;  // compile-time per unrolled m
+        const bool all_v = NWAVES * m >= T::K_SLOTS;
+        const char* base = all_k ? kb : (all_v ? vb : (c < T::K_SLOTS ? kb : vb));
+        asm volatile("" : "+v"(coff[m]));
+        if (m < FULL || c < T::NCOPY) copy16_to_lds(base + coff[m], stage + wlds + m * NWAVES * 1024);
       }
     } else {
+      // last, partial tile: rows past the valid keys fetch row 0 of the tile instead
+      // (lane laundered so none of this is hoisted into registers live across the loop)
+      int ln = lane, wv = wave;
+      asm volatile("" : "+v"(ln), "+s"(wv));
 #pragma unroll
       for (int m = 0; m < T::PER_WAVE; ++m) {
-        const int c = wave + NWAVES * m;
+        const int c = wv + NWAVES * m;
         if (c < T::NCOPY) {
           const bool isk = c < T::K_SLOTS;
-          copy16_to_lds(reinterpret_cast<const u16*>((isk ? kb : vb) + tail_off(m, nrow_valid)),
-                        stage + c * 1024);
+          const int row = ((isk ? c : c - T::K_SLOTS) * 64 + ln) / (isk ? T::K_SLOTS : T::V_SLOTS);
+          const uint32_t off = row < nrow_valid ? coff[m] : coff[m] - (uint32_t)(row * (isk ? krow_b : vrow_b));
+          copy16_to_lds((isk ? kb : vb) + off, stage + c * 1024);
         }
       }
     }

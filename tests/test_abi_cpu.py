@@ -70,6 +70,11 @@ def test_attn_stride_checks():
     assert sq.lib.safe_attn_fwd(ctypes.byref(a), None) == -2
     a = _attn_args(q_rows=0x20000, n_rows=10, q_rows_bstride=5)  # per-sample lists overlap
     assert sq.lib.safe_attn_fwd(ctypes.byref(a), None) == -2
+    # a 64-key tile is addressed with 32-bit byte offsets: 63 * 2 * 2^25 + row > 2^32
+    for name in ("k_stride", "v_stride"):
+        a = _attn_args()
+        getattr(a, name)[1] = 1 << 25
+        assert sq.lib.safe_attn_fwd(ctypes.byref(a), None) == -5
 
 
 def test_attn_empty_work_is_ok_without_gpu():
