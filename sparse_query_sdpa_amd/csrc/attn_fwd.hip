@@ -28,9 +28,14 @@
 //       element i%4; pointing source lane s at V[key0 + s/4][d0 + 4(s%4)] gives
 //       output lane i the four keys key0..key0+3 of column d0 + i, which are
 //       exactly the k-slots the S^T accumulator layout assigns to P^T.
-//   Online softmax in the log2 domain with a lazily moved reference max: the
-//   reference only moves (and O, l are rescaled) when a tile's max exceeds it by
-//   more than 2^8, so probabilities stay <= 256 and rescaling is rare.
+//   Online softmax in the log2 domain with a lazily moved reference max.  A tile's
+//   probabilities are first computed against the current reference, with no tile
+//   max at all; only when some lane's share of the tile sum exceeds 2^16 or is not
+//   finite (always on the first tile, whose reference is -inf) does the wave take
+//   the exact pair max, move the reference of the rows whose max exceeds it by more
+//   than 2^8 (rescaling O and l), and recompute the tile.  Probabilities stay below
+//   2^16, far inside the range of bf16 P and the fp32 accumulators, and the common
+//   path skips the 32-value max reduction.
 //   Workgroups are remapped so all row tiles of one (b, h) sit on one XCD and
 //   share its L2 for the K/V stream.
 #include "common.h"
@@ -43,6 +48,7 @@ constexpr int BN = 64;        // keys per tile
 constexpr int NTHREADS = 256;
 constexpr int NWAVES = NTHREADS / 64;
 constexpr float kRescaleThreshold = 8.0f;  // log2 units
+constexpr float kSumLimit = 65536.0f;          // a lane's tile-sum share above this moves the reference
 
 struct AttnParams {
   const u16* q;
@@ -247,43 +253,48 @@ __global__ __launch_bounds__(NTHREADS, D >= 128 ? 2 : 3) void attn_fwd_kernel(At
         }
     }
 
-    // ---- tile max (raw scores) over the lane pair ---------------------------
-    float mt = sacc[0][0];
+    // ---- probabilities (bf16 B operands) against the current reference -------
+    bf16x8 pb[2][2];
+    float ts = 0.f;  // this lane's share of the tile's row sum
+    auto probs = [&]() {
 #pragma unroll
-    for (int r = 1; r < 16; ++r) mt = fmaxf(mt, sacc[0][r]);
+      for (int blk = 0; blk < 2; ++blk) {
 #pragma unroll
-    for (int r = 0; r < 16; ++r) mt = fmaxf(mt, sacc[1][r]);
-    mt = fmaxf(mt, __shfl_xor(mt, 32));
-    const float mt2 = mt * sl2;
-
-    // ---- lazy reference move + rescale (wave-uniform branch) ----------------
-    const bool move = mt2 > m_ref + kRescaleThreshold;
-    if (__any(move)) {
+        for (int t = 0; t < 2; ++t) {
+          u32x4 packed;
+#pragma unroll
+          for (int e = 0; e < 4; ++e) {
+            const float p0 = __builtin_amdgcn_exp2f(__builtin_fmaf(sacc[blk][8 * t + 2 * e], sl2, -m_ref));
+            const float p1 = __builtin_amdgcn_exp2f(__builtin_fmaf(sacc[blk][8 * t + 2 * e + 1], sl2, -m_ref));
+            packed[e] = pack_bf16x2(p0, p1);
+            ts += p0 + p1;
+          }
+          pb[blk][t] = as_bf16x8(packed);
+        }
+      }
+    };
+    probs();
+    // ---- reference move (rare, wave-uniform): the first tile (reference -inf gives
+    // +inf), or a tile whose probabilities grew past 2^16 / 32 somewhere ---------
+    if (__any(!(ts <= kSumLimit))) {
+      float mt = sacc[0][0];
+#pragma unroll
+      for (int r = 1; r < 16; ++r) mt = fmaxf(mt, sacc[0][r]);
+#pragma unroll
+      for (int r = 0; r < 16; ++r) mt = fmaxf(mt, sacc[1][r]);
+      mt = fmaxf(mt, __shfl_xor(mt, 32));
+      const float mt2 = mt * sl2;
+      const bool move = mt2 > m_ref + kRescaleThreshold;
       const float m_new = move ? mt2 : m_ref;
       const float alpha = __builtin_amdgcn_exp2f(m_ref - m_new);  // exp2(-inf) = 0 on the first tile
       l_run *= alpha;
 #pragma unroll
       for (int i = 0; i < DB; ++i) oacc[i] *= alpha;
       m_ref = m_new;
+      ts = 0.f;
+      probs();
     }
-
-    // ---- probabilities (bf16 B operands) and the row-sum share ---------------
-    bf16x8 pb[2][2];
-#pragma unroll
-    for (int blk = 0; blk < 2; ++blk) {
-#pragma unroll
-      for (int t = 0; t < 2; ++t) {
-        u32x4 packed;
-#pragma unroll
-        for (int e = 0; e < 4; ++e) {
-          const float p0 = __builtin_amdgcn_exp2f(__builtin_fmaf(sacc[blk][8 * t + 2 * e], sl2, -m_ref));
-          const float p1 = __builtin_amdgcn_exp2f(__builtin_fmaf(sacc[blk][8 * t + 2 * e + 1], sl2, -m_ref));
-          packed[e] = pack_bf16x2(p0, p1);
-          l_run += p0 + p1;
-        }
-        pb[blk][t] = as_bf16x8(packed);
-      }
-    }
+    l_run += ts;
 
     // ---- O^T += V^T P^T --------------------------------------------------------
 #pragma unroll

@@ -102,6 +102,33 @@ def test_invalid_rows_and_lengths():
     assert empty.shape == (1, 0, H, d)
 
 
+@pytest.mark.parametrize("d", [64, 96])
+def test_logits_growing_along_keys_and_a_late_spike(d):
+    """Rows whose scores keep growing across key tiles, so the running reference max has
+    to move again and again mid-row (and O, l be rescaled), plus rows where one key in a
+    middle tile dwarfs everything before it."""
+    B, N, H = 1, 700, 2
+    rng = np.random.default_rng(40 + d)
+    u = rng.standard_normal(d)
+    q = u[None, None, None, :] + 0.3 * rng.standard_normal((B, N, H, d))
+    alpha = np.linspace(0.0, 5.0, N)[None, :, None, None]          # scores rise by ~5 |u|^2
+    k = alpha * u[None, None, None, :] + 0.3 * rng.standard_normal((B, N, H, d))
+    v = rng.standard_normal((B, N, H, d))
+    qb, kb, vb = (W.bf16_from_f32(x.astype(np.float32)) for x in (q, k, v))
+    o, lse = sq.attn_fwd(to_dev_bf16(qb), to_dev_bf16(kb), to_dev_bf16(vb), return_lse=True)
+    ref, ref_lse = oracle.sdpa(qb.value, kb.value, vb.value)
+    assert_attn_close(o, ref, f"growing d={d}")
+    assert_lse_close(lse, ref_lse, f"growing d={d}")
+    # flat scores with one spike key at 400 (tile 6 of 11)
+    k2 = 0.05 * rng.standard_normal((B, N, H, d))
+    k2[:, 400] = 4.0 * u
+    k2b = W.bf16_from_f32(k2.astype(np.float32))
+    o, lse = sq.attn_fwd(to_dev_bf16(qb), to_dev_bf16(k2b), to_dev_bf16(vb), return_lse=True)
+    ref, ref_lse = oracle.sdpa(qb.value, k2b.value, vb.value)
+    assert_attn_close(o, ref, f"spike d={d}")
+    assert_lse_close(lse, ref_lse, f"spike d={d}")
+
+
 def _sample_rows(rng, n, per=24):
     """Sampled output rows: the first, the last, rows around the 128-row tile edges and random ones."""
     pick = {0, n - 1, min(n - 1, 127), min(n - 1, 128), max(0, n - 129)}
