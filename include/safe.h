@@ -37,7 +37,7 @@
 extern "C" {
 #endif
 
-#define SAFE_ABI_VERSION 1
+#define SAFE_ABI_VERSION 2
 
 /* ---- status codes (negative = error) ----------------------------------- */
 enum {
@@ -216,6 +216,17 @@ int safe_kv_assemble(const safe_kv_args* a, void* stream);
  * o             bf16; compact [B, n_rows, H, d] unless SAFE_ATTN_SCATTER_OUT.
  * Limits: d in {32, 64, 96, 128}; pointers and strides give 16-byte aligned rows;
  * k and v token strides (stride[1]) below 2^25 elements (else SAFE_ERR_UNSUPPORTED).
+ *
+ * workspace     optional device scratch of workspace_bytes bytes (16-byte aligned),
+ *               owned by the caller and not retained.  The rows are processed in
+ *               128-row tiles, one workgroup each; when the tile count leaves the last
+ *               round of workgroups on the GPU partly empty, the tiles of that round
+ *               are split along the keys into partial results (unnormalised fp32 O,
+ *               running max and sum per row) kept in the workspace and merged by a
+ *               second kernel on the same stream.  The result is the same attention,
+ *               rounded differently for those rows.  With workspace NULL or smaller
+ *               than safe_attn_workspace_bytes() reports, no tile is split.  Calls that
+ *               share a workspace must be ordered on one stream.
  */
 typedef struct {
   int32_t B, H, Nq, Nk, d;
@@ -228,9 +239,16 @@ typedef struct {
   float scale;                            /* <= 0 means 1/sqrt(d) (Eq. 2) */
   float* lse;
   uint32_t flags;                         /* SAFE_ATTN_SCATTER_OUT | SAFE_FLAG_CHECK */
+  void* workspace; int64_t workspace_bytes;   /* optional, see above */
 } safe_attn_args;
 
 int safe_attn_fwd(const safe_attn_args* a, void* stream);
+
+/* Workspace bytes that let safe_attn_fwd split the last round of tiles for these
+ * arguments on the current device (0: this shape gains nothing from a split, the
+ * key-length form is never split, or no device is visible).  The pointer fields are
+ * not read.  Negative: the SAFE_ERR_* status safe_attn_fwd would return for the sizes. */
+int64_t safe_attn_workspace_bytes(const safe_attn_args* a);
 
 /* Human-readable name of a status code (static storage). */
 const char* safe_status_str(int status);

@@ -73,19 +73,21 @@ class AttnArgs(ctypes.Structure):
                 ("o", ctypes.c_void_p), ("o_stride", _i64x3),
                 ("q_rows", ctypes.c_void_p), ("n_rows", ctypes.c_int32), ("q_rows_bstride", ctypes.c_int64),
                 ("kv_len", ctypes.c_void_p), ("scale", ctypes.c_float), ("lse", ctypes.c_void_p),
-                ("flags", ctypes.c_uint32)]
+                ("flags", ctypes.c_uint32), ("workspace", ctypes.c_void_p), ("workspace_bytes", ctypes.c_int64)]
 
 
 def _load():
     if not os.path.exists(LIB_PATH):
         raise ImportError(f"libsafe.so not found at {LIB_PATH}: build it with "
-                          "`python -m sparse_query_sdpa_amd.build` (no CPU fallback exists)")
+                          "`python sparse_query_sdpa_amd/build.py` (no CPU fallback exists)")
     lib = ctypes.CDLL(LIB_PATH)
     lib.safe_abi_version.restype = ctypes.c_int
     lib.safe_status_str.restype = ctypes.c_char_p
     lib.safe_status_str.argtypes = [ctypes.c_int]
     lib.safe_attn_fwd.restype = ctypes.c_int
     lib.safe_attn_fwd.argtypes = [ctypes.POINTER(AttnArgs), ctypes.c_void_p]
+    lib.safe_attn_workspace_bytes.restype = ctypes.c_int64
+    lib.safe_attn_workspace_bytes.argtypes = [ctypes.POINTER(AttnArgs)]
     lib.safe_kv_assemble.restype = ctypes.c_int
     lib.safe_kv_assemble.argtypes = [ctypes.POINTER(KvArgs), ctypes.c_void_p]
     lib.safe_pcsp_select.restype = ctypes.c_int
@@ -146,10 +148,31 @@ def _i32(t: Optional[torch.Tensor], name: str):
 
 
 # ---------------------------------------------------------------------------------
+_ATTN_WS = {}  # (device index, stream handle) -> uint8 workspace tensor, grown on demand
+
+
+def _attn_workspace(a: AttnArgs, device: torch.device, stream_handle) -> Optional[torch.Tensor]:
+    need = lib.safe_attn_workspace_bytes(ctypes.byref(a))
+    if need < 0:
+        _check("safe_attn_workspace_bytes", int(need))
+    if need <= 0:
+        return None
+    key = (device.index, stream_handle)
+    ws = _ATTN_WS.get(key)
+    if ws is None or ws.numel() < need:
+        ws = torch.empty(int(need), dtype=torch.uint8, device=device)
+        _ATTN_WS[key] = ws
+    return ws
+
+
 def attn_fwd(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, q_rows: Optional[torch.Tensor] = None,
              kv_len: Optional[torch.Tensor] = None, scale: Optional[float] = None, out: Optional[torch.Tensor] = None,
-             return_lse: bool = False, scatter_out: bool = False, check: bool = False, stream=None):
-    """Attention on all rows (q_rows None) or on gathered rows q_rows [n] / [B, n]; see safe.h."""
+             return_lse: bool = False, scatter_out: bool = False, check: bool = False, stream=None,
+             workspace="auto"):
+    """Attention on all rows (q_rows None) or on gathered rows q_rows [n] / [B, n]; see safe.h.
+
+    workspace: "auto" (a buffer cached per device and stream, sized by
+    safe_attn_workspace_bytes), None (no tail split), or a uint8 device tensor."""
     for t, n in ((q, "q"), (k, "k"), (v, "v")):
         _bits16(t, n)
     B, Nq, H, d = q.shape
@@ -175,9 +198,34 @@ def attn_fwd(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, q_rows: Optional
     a = AttnArgs(B, H, Nq, Nk, d, _ptr(q), _bnhd(q, "q"), _ptr(k), _bnhd(k, "k"), _ptr(v), _bnhd(v, "v"),
                  _ptr(out), _bnhd(out, "out"), _ptr(q_rows), n_rows, bstride, _ptr(kv_len),
                  0.0 if scale is None else float(scale), _ptr(lse),
-                 (ATTN_SCATTER_OUT if scatter_out else 0) | (FLAG_CHECK if check else 0))
-    _check("safe_attn_fwd", lib.safe_attn_fwd(ctypes.byref(a), _stream(stream)))
+                 (ATTN_SCATTER_OUT if scatter_out else 0) | (FLAG_CHECK if check else 0), None, 0)
+    st = _stream(stream)
+    if isinstance(workspace, str):
+        if workspace != "auto":
+            raise ValueError("workspace must be 'auto', None or a device tensor")
+        workspace = _attn_workspace(a, q.device, st)
+    if workspace is not None:
+        a.workspace, a.workspace_bytes = _ptr(workspace), workspace.numel() * workspace.element_size()
+    _check("safe_attn_fwd", lib.safe_attn_fwd(ctypes.byref(a), st))
     return (out, lse) if return_lse else out
+
+
+def attn_workspace_bytes(q: torch.Tensor, k: torch.Tensor, q_rows: Optional[torch.Tensor] = None,
+                         kv_len: Optional[torch.Tensor] = None) -> int:
+    """Workspace bytes attn_fwd would use on the current device for these shapes (0: no split)."""
+    B, Nq, H, d = q.shape
+    if q_rows is None:
+        n_rows = Nq
+    else:
+        n_rows = q_rows.shape[-1]
+    a = AttnArgs()
+    a.B, a.H, a.Nq, a.Nk, a.d, a.n_rows = B, H, Nq, k.shape[1], d, n_rows
+    a.q_rows = None if q_rows is None else _ptr(q_rows)
+    a.kv_len = None if kv_len is None else _ptr(kv_len)
+    n = lib.safe_attn_workspace_bytes(ctypes.byref(a))
+    if n < 0:
+        _check("safe_attn_workspace_bytes", int(n))
+    return int(n)
 
 
 def kv_assemble(k_fresh: torch.Tensor, v_fresh: torch.Tensor, idx: torch.Tensor, k_cache: torch.Tensor,

@@ -1,6 +1,7 @@
 """Build libsafe.so (HIP for gfx950) in-tree with hipcc.
 
-Usage: python -m sparse_query_sdpa_amd.build [-v]
+Usage: python sparse_query_sdpa_amd/build.py [-v]   (run by path: importing the package
+loads the library, which may be missing or older than the sources)
 """
 from __future__ import annotations
 

@@ -8,6 +8,7 @@
 
 namespace safe {
 int attn_fwd_launch(const safe_attn_args* a, float scale, hipStream_t stream);
+int64_t attn_workspace_bytes(const safe_attn_args* a);
 int kv_assemble_launch(const safe_kv_args* a, bool in_place, hipStream_t stream);
 int mask_classify_launch(const void* mask, int32_t dtype, const int64_t size[4], const int64_t stride[4],
                          uint32_t flags, safe_mask_info* info, uint8_t* row_class, int32_t* kv_len_out,
@@ -94,7 +95,8 @@ const char* safe_status_str(int status) {
   }
 }
 
-int safe_attn_fwd(const safe_attn_args* a, void* stream) {
+// Size, scale and flag checks shared by the call and its workspace query (no pointers read).
+static int check_attn_sizes(const safe_attn_args* a) {
   if (a == nullptr) return SAFE_ERR_NULL;
   if (a->B < 0 || a->H < 0 || a->Nq < 0 || a->Nk < 0 || a->n_rows < 0) return SAFE_ERR_SHAPE;
   if (!supported_head_dim(a->d)) return SAFE_ERR_UNSUPPORTED;
@@ -104,8 +106,21 @@ int safe_attn_fwd(const safe_attn_args* a, void* stream) {
   if (a->q_rows != nullptr && a->q_rows_bstride < 0) return SAFE_ERR_SHAPE;
   if (a->q_rows != nullptr && a->q_rows_bstride != 0 && a->q_rows_bstride < a->n_rows) return SAFE_ERR_SHAPE;
   if (a->flags & ~(SAFE_ATTN_SCATTER_OUT | SAFE_FLAG_CHECK)) return SAFE_ERR_RANGE;
+  if (a->workspace_bytes < 0) return SAFE_ERR_WORKSPACE;
+  return SAFE_OK;
+}
+
+int64_t safe_attn_workspace_bytes(const safe_attn_args* a) {
+  const int st = check_attn_sizes(a);
+  if (st != SAFE_OK) return st;
+  return attn_workspace_bytes(a);
+}
+
+int safe_attn_fwd(const safe_attn_args* a, void* stream) {
+  int st = check_attn_sizes(a);
+  if (st != SAFE_OK) return st;
+  if (a->workspace != nullptr && !aligned16(a->workspace)) return SAFE_ERR_ALIGN;
   const bool work = (int64_t)a->B * a->H * a->n_rows > 0;
-  int st;
   if ((st = check_bnhd(a->q, a->q_stride, work)) != SAFE_OK) return st;
   if ((st = check_bnhd(a->k, a->k_stride, work && a->Nk > 0)) != SAFE_OK) return st;
   if ((st = check_bnhd(a->v, a->v_stride, work && a->Nk > 0)) != SAFE_OK) return st;

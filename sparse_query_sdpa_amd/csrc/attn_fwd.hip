@@ -40,6 +40,9 @@
 //   share its L2 for the K/V stream.
 #include "common.h"
 
+#include <algorithm>
+#include <atomic>
+
 namespace safe {
 namespace {
 
@@ -63,6 +66,12 @@ struct AttnParams {
   int B, H, Nq, Nk, n_rows, n_row_tiles, total_wg;
   float scale_log2;
   int scatter;
+  // Tail split: workgroups [0, n_full) take whole row tiles (logical tiles 0..n_full-1);
+  // workgroup n_full + t takes key range t % nsplit (split_tiles key tiles each) of
+  // logical tile n_full + t / nsplit and leaves unnormalised partials in `part`:
+  // O as fp32 [n_slots][BM][D], then (max, sum) as fp32 [n_slots][BM][2].
+  int n_full, nsplit, split_tiles, n_slots;
+  float* part;
 };
 
 // LDS tile geometry.  K rows are read 16 bytes per lane, 16 lanes on 16 rows at once:
@@ -112,7 +121,15 @@ __global__ __launch_bounds__(NTHREADS, D >= 128 ? 2 : 3) void attn_fwd_kernel(At
   const int col = lane & 31;   // query column owned by this lane
   const int half = lane >> 5;  // which 8-wide k slice / 4-row group this lane holds
 
-  const int logical = xcd_remap(blockIdx.x, p.total_wg);
+  // whole row tile (slot < 0), or key range [kb0, kb0 + split_tiles * BN) of a tail tile
+  int logical, slot = -1, kb0 = 0;
+  if ((int)blockIdx.x < p.n_full) {
+    logical = xcd_remap(blockIdx.x, p.n_full);
+  } else {
+    slot = (int)blockIdx.x - p.n_full;
+    logical = p.n_full + slot / p.nsplit;
+    kb0 = (slot % p.nsplit) * p.split_tiles * BN;
+  }
   const int tile = logical % p.n_row_tiles;
   const int bh = logical / p.n_row_tiles;
   const int h = bh % p.H;
@@ -141,7 +158,8 @@ __global__ __launch_bounds__(NTHREADS, D >= 128 ? 2 : 3) void attn_fwd_kernel(At
     int L = p.kv_len[b];
     nkeys = L < 0 ? 0 : (L > p.Nk ? p.Nk : L);
   }
-  const int ntiles = (nkeys + BN - 1) / BN;
+  const int kend = slot < 0 ? nkeys : min(nkeys, kb0 + p.split_tiles * BN);
+  const int ntiles = (kend - kb0 + BN - 1) / BN;   // key ranges of splits are never empty
 
   // ---- per-lane copy plan ------------------------------------------------------
   // A tile is NCOPY wave-wide copies of 1 KB: copy c < K_SLOTS fills K slots
@@ -221,7 +239,7 @@ __global__ __launch_bounds__(NTHREADS, D >= 128 ? 2 : 3) void attn_fwd_kernel(At
   // One tile: wait for its copies, start the next tile's copies into the other
   // stage, then compute from this stage.
   auto tile_step = [&](int it, const char* cur, char* nxt) {
-    const int j0 = it * BN;
+    const int j0 = kb0 + it * BN;
     __builtin_amdgcn_s_waitcnt(0x0F70);  // vmcnt(0): this wave's copies of tile `it` landed
     __syncthreads();                     // ... everyone's, and tile it-1 is no longer read
     if (it + 1 < ntiles) issue_tile(j0 + BN, nxt);
@@ -312,7 +330,7 @@ __global__ __launch_bounds__(NTHREADS, D >= 128 ? 2 : 3) void attn_fwd_kernel(At
     }
   };
 
-  if (ntiles > 0) issue_tile(0, stage0);
+  if (ntiles > 0) issue_tile(kb0, stage0);
   for (int it = 0; it < ntiles; it += 2) {
     tile_step(it, stage0, stage1);
     if (it + 1 < ntiles) tile_step(it + 1, stage1, stage0);
@@ -321,6 +339,23 @@ __global__ __launch_bounds__(NTHREADS, D >= 128 ? 2 : 3) void attn_fwd_kernel(At
   // ---- epilogue: normalise, store O (bf16) and LSE ------------------------------
   const float l_tot = l_run + __shfl_xor(l_run, 32);
   if (!row_ok) return;
+  if (slot >= 0) {  // partial of a split tile: unnormalised O and this range's (max, sum)
+    const int rloc = wave * 32 + col;
+    float* po = p.part + ((int64_t)slot * BM + rloc) * D;
+#pragma unroll
+    for (int db = 0; db < DB; ++db)
+#pragma unroll
+      for (int g = 0; g < 4; ++g) {
+        const f32x4 w = {oacc[db][4 * g + 0], oacc[db][4 * g + 1], oacc[db][4 * g + 2], oacc[db][4 * g + 3]};
+        st16(po + db * 32 + 8 * g + 4 * half, __builtin_bit_cast(u32x4, w));
+      }
+    if (half == 0) {
+      float* pm = p.part + (int64_t)p.n_slots * BM * D + ((int64_t)slot * BM + rloc) * 2;
+      pm[0] = m_ref;
+      pm[1] = l_tot;
+    }
+    return;
+  }
   const float inv = l_tot > 0.f ? 1.0f / l_tot : 0.f;
   const int orow = (GATHER && p.scatter) ? qi : rr;
   if (!GATHER || !p.scatter || q_ok) {
@@ -341,9 +376,70 @@ __global__ __launch_bounds__(NTHREADS, D >= 128 ? 2 : 3) void attn_fwd_kernel(At
   }
 }
 
+// Merge the key-range partials of each split tail tile: M = max of the ranges' maxima,
+// L = sum of their sums scaled by 2^(max - M), O = sum of their O scaled the same way
+// over L; the same output rules as the whole-tile epilogue.  Two threads per row,
+// each owning half of the head dimension.
+template <int D, bool GATHER>
+__global__ __launch_bounds__(256) void attn_merge_kernel(AttnParams p) {
+  constexpr int DH = D / 2;
+  const int ti = blockIdx.x;
+  const int logical = p.n_full + ti;
+  const int tile = logical % p.n_row_tiles;
+  const int bh = logical / p.n_row_tiles;
+  const int h = bh % p.H;
+  const int b = bh / p.H;
+  const int rloc = threadIdx.x >> 1, hf = threadIdx.x & 1;
+  const int rr = tile * BM + rloc;
+  if (rr >= p.n_rows) return;
+  int qi = rr;
+  if (GATHER) qi = p.q_rows[(int64_t)b * p.qr_bs + rr];
+  const bool q_ok = qi >= 0 && qi < p.Nq;
+
+  const float* pml = p.part + (int64_t)p.n_slots * BM * D;
+  float M = -INFINITY;
+  for (int s = 0; s < p.nsplit; ++s) M = fmaxf(M, pml[((int64_t)(ti * p.nsplit + s) * BM + rloc) * 2]);
+  float acc[DH];
+#pragma unroll
+  for (int i = 0; i < DH; ++i) acc[i] = 0.f;
+  float L = 0.f;
+  for (int s = 0; s < p.nsplit; ++s) {
+    const int64_t sl = (int64_t)(ti * p.nsplit + s) * BM + rloc;
+    const float w = M == -INFINITY ? 0.f : __builtin_amdgcn_exp2f(pml[sl * 2] - M);
+    L += w * pml[sl * 2 + 1];
+    const float* po = p.part + sl * D + hf * DH;
+#pragma unroll
+    for (int i = 0; i < DH; i += 4) {
+      const f32x4 v = __builtin_bit_cast(f32x4, ld16(po + i));
+      acc[i] += w * v[0]; acc[i + 1] += w * v[1]; acc[i + 2] += w * v[2]; acc[i + 3] += w * v[3];
+    }
+  }
+  const float inv = L > 0.f ? 1.0f / L : 0.f;
+  const int orow = (GATHER && p.scatter) ? qi : rr;
+  if (!GATHER || !p.scatter || q_ok) {
+    u16* op = p.o + (int64_t)b * p.os0 + (int64_t)orow * p.os1 + (int64_t)h * p.os2 + hf * DH;
+#pragma unroll
+    for (int i = 0; i < DH; i += 8) {
+      u32x4 w;
+      w[0] = pack_bf16x2(acc[i] * inv, acc[i + 1] * inv);
+      w[1] = pack_bf16x2(acc[i + 2] * inv, acc[i + 3] * inv);
+      w[2] = pack_bf16x2(acc[i + 4] * inv, acc[i + 5] * inv);
+      w[3] = pack_bf16x2(acc[i + 6] * inv, acc[i + 7] * inv);
+      st16(op + i, w);
+    }
+  }
+  if (p.lse != nullptr && hf == 0) {
+    const float lse = L > 0.f ? (M + __builtin_log2f(L)) * 0.69314718055994530942f : -INFINITY;
+    p.lse[((int64_t)b * p.H + h) * p.n_rows + rr] = lse;
+  }
+}
+
 template <int D, bool G, bool KV>
 hipError_t launch(const AttnParams& p, hipStream_t s) {
   hipLaunchKernelGGL((attn_fwd_kernel<D, G, KV>), dim3(p.total_wg), dim3(NTHREADS), 0, s, p);
+  hipError_t e = hipGetLastError();
+  if (e != hipSuccess || p.n_slots == 0) return e;
+  hipLaunchKernelGGL((attn_merge_kernel<D, G>), dim3(p.n_slots / p.nsplit), dim3(256), 0, s, p);
   return hipGetLastError();
 }
 
@@ -353,9 +449,77 @@ hipError_t dispatch_flags(const AttnParams& p, bool gather, bool kvlen, hipStrea
   return kvlen ? launch<D, false, true>(p, s) : launch<D, false, false>(p, s);
 }
 
+// Workgroups of one kernel instance resident on the whole device (0 if unknown).
+// Cached per device and instance; racing first calls store the same value.
+template <int D, bool G>
+int resident_workgroups() {
+  constexpr int kMaxDev = 64;
+  static std::atomic<int> cache[kMaxDev];
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= kMaxDev) return 0;
+  int v = cache[dev].load(std::memory_order_relaxed);
+  if (v > 0) return v;
+  int per_cu = 0, cus = 0;
+  if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, attn_fwd_kernel<D, G, false>, NTHREADS, 0) != hipSuccess ||
+      hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess)
+    return 0;
+  v = per_cu * cus;
+  if (v > 0) cache[dev].store(v, std::memory_order_relaxed);
+  return v;
+}
+
+int resident_for(int d, bool gather) {
+  switch (d) {
+    case 32: return gather ? resident_workgroups<32, true>() : resident_workgroups<32, false>();
+    case 64: return gather ? resident_workgroups<64, true>() : resident_workgroups<64, false>();
+    case 96: return gather ? resident_workgroups<96, true>() : resident_workgroups<96, false>();
+    case 128: return gather ? resident_workgroups<128, true>() : resident_workgroups<128, false>();
+    default: return 0;
+  }
+}
+
+// Tail split plan.  With S workgroups resident, T whole tiles run in rounds of S; the
+// last round holds tail = T mod S tiles (all of them when T < S).  Splitting each of
+// those along the keys into up to S / tail ranges (at least kMinSplitTiles key tiles
+// each, at most kMaxSplit ranges) fills that round with short workgroups instead.
+struct SplitPlan {
+  int n_full = 0, nsplit = 1, split_tiles = 0, tail = 0;
+  int64_t bytes = 0;
+};
+constexpr int kMinSplitTiles = 4;
+constexpr int kMaxSplit = 16;
+
+SplitPlan plan_split(const safe_attn_args* a, int64_t total_tiles) {
+  SplitPlan pl;
+  pl.n_full = (int)total_tiles;
+  if (a->kv_len != nullptr || total_tiles <= 0 || a->Nk <= 0) return pl;
+  const int S = resident_for(a->d, a->q_rows != nullptr);
+  if (S <= 0) return pl;
+  const int64_t tail = total_tiles % S;
+  if (tail == 0) return pl;
+  const int nk_tiles = (a->Nk + BN - 1) / BN;
+  int nsplit = (int)std::min<int64_t>(S / tail, kMaxSplit);
+  nsplit = std::min(nsplit, nk_tiles / kMinSplitTiles);
+  if (nsplit < 2) return pl;
+  pl.split_tiles = (nk_tiles + nsplit - 1) / nsplit;
+  pl.nsplit = (nk_tiles + pl.split_tiles - 1) / pl.split_tiles;   // every range non-empty
+  if (pl.nsplit < 2) return SplitPlan{(int)total_tiles};
+  pl.tail = (int)tail;
+  pl.n_full = (int)(total_tiles - tail);
+  pl.bytes = (int64_t)pl.tail * pl.nsplit * BM * ((int64_t)a->d * 4 + 8);
+  return pl;
+}
+
 }  // namespace
 
-// Enqueue the attention kernel.  Arguments were validated by the caller.
+int64_t attn_workspace_bytes(const safe_attn_args* a) {
+  const int64_t total = (int64_t)((a->n_rows + BM - 1) / BM) * a->H * a->B;
+  if (a->n_rows == 0 || total == 0 || total > 0x7fffffff) return 0;
+  return plan_split(a, total).bytes;
+}
+
+// Enqueue the attention kernel (and the merge of split tiles).  Arguments were validated
+// by the caller.
 int attn_fwd_launch(const safe_attn_args* a, float scale, hipStream_t stream) {
   if (a->n_rows == 0) return SAFE_OK;
   AttnParams p;
@@ -375,9 +539,20 @@ int attn_fwd_launch(const safe_attn_args* a, float scale, hipStream_t stream) {
   p.n_row_tiles = (a->n_rows + BM - 1) / BM;
   const int64_t total = (int64_t)p.n_row_tiles * a->H * a->B;
   if (total > 0x7fffffff) return SAFE_ERR_SHAPE;
-  p.total_wg = (int)total;
   p.scale_log2 = scale * 1.4426950408889634f;
   p.scatter = (a->flags & SAFE_ATTN_SCATTER_OUT) ? 1 : 0;
+  SplitPlan pl;
+  pl.n_full = (int)total;
+  if (a->workspace != nullptr && a->workspace_bytes > 0) {
+    pl = plan_split(a, total);
+    if (pl.tail == 0 || a->workspace_bytes < pl.bytes) pl = SplitPlan{(int)total};
+  }
+  p.n_full = pl.n_full;
+  p.nsplit = pl.nsplit;
+  p.split_tiles = pl.split_tiles;
+  p.n_slots = pl.tail * pl.nsplit;
+  p.part = pl.tail > 0 ? static_cast<float*>(a->workspace) : nullptr;
+  p.total_wg = pl.n_full + p.n_slots;
   const bool gather = a->q_rows != nullptr;
   const bool kvlen = a->kv_len != nullptr;
   hipError_t e;

@@ -13,8 +13,13 @@ def _ensure_library():
     lib = os.path.join(ROOT, "sparse_query_sdpa_amd", "libsafe.so")
     if not os.path.exists(lib):
         try:
-            from sparse_query_sdpa_amd.build import build
-            build()
+            # loaded by path: importing the package would try to load the missing library
+            import importlib.util
+            spec = importlib.util.spec_from_file_location(
+                "_libsafe_build", os.path.join(ROOT, "sparse_query_sdpa_amd", "build.py"))
+            mod = importlib.util.module_from_spec(spec)
+            spec.loader.exec_module(mod)
+            mod.build()
         except Exception as e:  # pragma: no cover - reported by the tests that need it
             print(f"libsafe build failed: {e}")
 

@@ -15,13 +15,13 @@ sq = pytest.importorskip("sparse_query_sdpa_amd", reason="libsafe.so not built")
 def declared_functions():
     text = open(HEADER).read()
     text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
-    return sorted(set(re.findall(r"^\s*(?:int|const char\*)\s+(safe_\w+)\s*\(", text, flags=re.M)))
+    return sorted(set(re.findall(r"^\s*(?:int64_t|int|const char\*)\s+(safe_\w+)\s*\(", text, flags=re.M)))
 
 
 def test_header_declares_the_four_entry_points():
     names = declared_functions()
     for n in ("safe_mask_classify", "safe_pcsp_select", "safe_kv_assemble", "safe_attn_fwd",
-              "safe_status_str", "safe_abi_version"):
+              "safe_attn_workspace_bytes", "safe_status_str", "safe_abi_version"):
         assert n in names
 
 
@@ -32,7 +32,7 @@ def test_every_declared_symbol_is_exported():
 
 
 def test_abi_version_and_status_strings():
-    assert sq.lib.safe_abi_version() == 1
+    assert sq.lib.safe_abi_version() == 2
     for code, name in sq.STATUS.items():
         assert sq.lib.safe_status_str(code).decode().startswith(name)
     assert sq.lib.safe_status_str(12345) == b"unknown status"
@@ -75,6 +75,16 @@ def test_attn_stride_checks():
         a = _attn_args()
         getattr(a, name)[1] = 1 << 25
         assert sq.lib.safe_attn_fwd(ctypes.byref(a), None) == -5
+
+
+def test_attn_workspace_arguments_without_gpu():
+    # the size query validates like the call and reads no pointer
+    assert sq.lib.safe_attn_workspace_bytes(ctypes.byref(_attn_args(d=48))) == -5
+    assert sq.lib.safe_attn_workspace_bytes(ctypes.byref(_attn_args(n_rows=5))) == -2
+    assert sq.lib.safe_attn_workspace_bytes(ctypes.byref(_attn_args(q=None, k=None, v=None, o=None))) >= 0
+    assert sq.lib.safe_attn_workspace_bytes(ctypes.byref(_attn_args(kv_len=0x30000))) == 0  # never split
+    assert sq.lib.safe_attn_fwd(ctypes.byref(_attn_args(workspace_bytes=-1)), None) == -6
+    assert sq.lib.safe_attn_fwd(ctypes.byref(_attn_args(workspace=0x40004, workspace_bytes=64)), None) == -8
 
 
 def test_attn_empty_work_is_ok_without_gpu():

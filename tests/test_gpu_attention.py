@@ -69,17 +69,59 @@ def test_ragged_shapes_rows_lengths(d):
 
 
 def test_shared_rows_and_dense_equivalence_bitwise():
+    """Without tail splitting every row is computed the same way whatever the row set."""
     B, N, H, d = 2, 1000, 4, 96
     q, k, v = W.attention_inputs(B, N, N, H, d, seed=7)
     qd, kd, vd = to_dev_bf16(q), to_dev_bf16(k), to_dev_bf16(v)
-    dense = sq.attn_fwd(qd, kd, vd)
-    all_rows = sq.attn_fwd(qd, kd, vd, q_rows=torch.arange(N, dtype=torch.int32, device=qd.device))
+    dense = sq.attn_fwd(qd, kd, vd, workspace=None)
+    all_rows = sq.attn_fwd(qd, kd, vd, q_rows=torch.arange(N, dtype=torch.int32, device=qd.device), workspace=None)
     assert torch.equal(dense, all_rows), "S = all rows must reproduce the dense pass"
     rows = W.random_rows(np.random.default_rng(3), N, 250)
-    part = sq.attn_fwd(qd, kd, vd, q_rows=to_dev(rows))
+    part = sq.attn_fwd(qd, kd, vd, q_rows=to_dev(rows), workspace=None)
     assert torch.equal(part, dense[:, torch.from_numpy(rows).long()])
-    again = sq.attn_fwd(qd, kd, vd)
-    assert torch.equal(dense, again), "repeated calls must be bitwise identical"
+    assert torch.equal(dense, sq.attn_fwd(qd, kd, vd, workspace=None)), "repeated calls must be bitwise identical"
+    split = sq.attn_fwd(qd, kd, vd)   # workspace chosen by the binding: split schedule
+    assert torch.equal(split, sq.attn_fwd(qd, kd, vd)), "repeated split calls must be bitwise identical"
+
+
+def test_tail_split_against_oracle_and_unsplit():
+    """Fewer row tiles than resident workgroups: every tile is split along the keys into
+    partials (fp32 O, max, sum) that the merge kernel combines."""
+    B, Nq, Nk, H, d = 2, 300, 3000, 3, 96
+    q, k, v = W.attention_inputs(B, Nq, Nk, H, d, seed=21)
+    qd, kd, vd = to_dev_bf16(q), to_dev_bf16(k), to_dev_bf16(v)
+    need = sq.attn_workspace_bytes(qd, kd)
+    assert need > 0, "this shape must be split"
+    o, lse = sq.attn_fwd(qd, kd, vd, return_lse=True)
+    ref, ref_lse = oracle.sdpa(q.value, k.value, v.value)
+    assert_attn_close(o, ref, "split dense")
+    assert_lse_close(lse, ref_lse, "split dense")
+    plain, plain_lse = sq.attn_fwd(qd, kd, vd, return_lse=True, workspace=None)
+    assert (o.float() - plain.float()).abs().max().item() <= 2e-2
+    # a workspace one byte short runs unsplit
+    short = torch.empty(need - 1, dtype=torch.uint8, device=qd.device)
+    assert torch.equal(sq.attn_fwd(qd, kd, vd, workspace=short), plain)
+    exact = torch.empty(need, dtype=torch.uint8, device=qd.device)
+    assert torch.equal(sq.attn_fwd(qd, kd, vd, workspace=exact), o)
+    # gathered per-sample rows, scattered output and LSE through the merge
+    rng = np.random.default_rng(5)
+    rows = np.stack([W.random_rows(rng, Nq, 111) for _ in range(B)])
+    rows[1, 7] = Nq + 5   # out of range: reads a zero query, not written when scattering
+    assert sq.attn_workspace_bytes(qd, kd, q_rows=to_dev(rows)) > 0
+    out = torch.full((B, Nq, H, d), 3.0, dtype=torch.bfloat16, device=qd.device)
+    _, lse = sq.attn_fwd(qd, kd, vd, q_rows=to_dev(rows), out=out, scatter_out=True, return_lse=True)
+    ok_rows = np.where(rows < Nq, rows, 0)
+    ref, ref_lse = oracle.sdpa(q.value, k.value, v.value, q_rows=ok_rows)
+    g = out.float().cpu().numpy()
+    for b in range(B):
+        valid = rows[b] < Nq
+        got = out[b][torch.from_numpy(rows[b][valid]).long()].unsqueeze(0)
+        assert_attn_close(got, ref[b:b + 1, valid], "split scatter")
+        assert_lse_close(lse.cpu()[b:b + 1][:, :, torch.from_numpy(valid)], ref_lse[b:b + 1][:, :, valid],
+                         "split scatter lse")
+        untouched = np.ones(Nq, bool)
+        untouched[rows[b][valid]] = False
+        assert np.all(g[b][untouched] == 3.0)
 
 
 def test_invalid_rows_and_lengths():
