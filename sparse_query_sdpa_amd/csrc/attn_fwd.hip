@@ -42,6 +42,7 @@
 
 #include <algorithm>
 #include <atomic>
+#include <type_traits>
 
 namespace safe {
 namespace {
@@ -236,70 +237,44 @@ __global__ __launch_bounds__(NTHREADS, D >= 128 ? 2 : 3) void attn_fwd_kernel(At
   const int grp = (lane >> 4) & 3, src = lane & 15;
   const int v_lane = (4 * (grp >> 1) + (src >> 2)) * T::V_ROWB + (16 * (grp & 1) + 4 * (src & 3)) * 2;
 
-  // One tile: wait for its copies, start the next tile's copies into the other
-  // stage, then compute from this stage.
-  auto tile_step = [&](int it, const char* cur, char* nxt) {
-    const int j0 = kb0 + it * BN;
-    __builtin_amdgcn_s_waitcnt(0x0F70);  // vmcnt(0): this wave's copies of tile `it` landed
-    __syncthreads();                     // ... everyone's, and tile it-1 is no longer read
-    if (it + 1 < ntiles) issue_tile(j0 + BN, nxt);
-
-    const char* Kt = cur;
-    const char* Vt = cur + T::K_BYTES;
-
-    // ---- S^T = K Q^T for 64 keys (two 32-key blocks) -------------------------
-    f32x16 sacc[2];
+  // Per-lane pieces of a tile.  A tile's two 32-key halves are independent once
+  // scores exist: probabilities are taken against the current reference, so the
+  // softmax of one half can run between the MFMAs of the other half.
+  auto s_half = [&](const char* Kt, int blk) -> f32x16 {   // S^T rows blk*32.. of the tile
+    f32x16 acc = f32x16{};
 #pragma unroll
-    for (int blk = 0; blk < 2; ++blk) {
-      f32x16 acc = f32x16{};
-#pragma unroll
-      for (int s = 0; s < KS; ++s) {
-        const bf16x8 kf = as_bf16x8(ld16(Kt + k_lane + blk * 32 * T::K_ROWB + s * 32));
-        acc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kf, qf[s], acc, 0, 0, 0);
-      }
-      sacc[blk] = acc;
+    for (int s = 0; s < KS; ++s) {
+      const bf16x8 kf = as_bf16x8(ld16(Kt + k_lane + blk * 32 * T::K_ROWB + s * 32));
+      acc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kf, qf[s], acc, 0, 0, 0);
     }
-
-    // ---- mask keys past the valid length (last tile only) -------------------
-    if (j0 + BN > nkeys) {
+    return acc;
+  };
+  // bf16 P^T operands of one half and this lane's share of its sum
+  auto probs_half = [&](const f32x16& sc, bf16x8 (&pb)[2]) -> float {
+    float ts = 0.f;
 #pragma unroll
-      for (int blk = 0; blk < 2; ++blk)
+    for (int t = 0; t < 2; ++t) {
+      u32x4 packed;
 #pragma unroll
-        for (int r = 0; r < 16; ++r) {
-          const int key = j0 + blk * 32 + 8 * (r >> 2) + 4 * half + (r & 3);
-          if (key >= nkeys) sacc[blk][r] = -INFINITY;
-        }
-    }
-
-    // ---- probabilities (bf16 B operands) against the current reference -------
-    bf16x8 pb[2][2];
-    float ts = 0.f;  // this lane's share of the tile's row sum
-    auto probs = [&]() {
-#pragma unroll
-      for (int blk = 0; blk < 2; ++blk) {
-#pragma unroll
-        for (int t = 0; t < 2; ++t) {
-          u32x4 packed;
-#pragma unroll
-          for (int e = 0; e < 4; ++e) {
-            const float p0 = __builtin_amdgcn_exp2f(__builtin_fmaf(sacc[blk][8 * t + 2 * e], sl2, -m_ref));
-            const float p1 = __builtin_amdgcn_exp2f(__builtin_fmaf(sacc[blk][8 * t + 2 * e + 1], sl2, -m_ref));
-            packed[e] = pack_bf16x2(p0, p1);
-            ts += p0 + p1;
-          }
-          pb[blk][t] = as_bf16x8(packed);
-        }
+      for (int e = 0; e < 4; ++e) {
+        const float p0 = __builtin_amdgcn_exp2f(__builtin_fmaf(sc[8 * t + 2 * e], sl2, -m_ref));
+        const float p1 = __builtin_amdgcn_exp2f(__builtin_fmaf(sc[8 * t + 2 * e + 1], sl2, -m_ref));
+        packed[e] = pack_bf16x2(p0, p1);
+        ts += p0 + p1;
       }
-    };
-    probs();
-    // ---- reference move (rare, wave-uniform): the first tile (reference -inf gives
-    // +inf), or a tile whose probabilities grew past 2^16 / 32 somewhere ---------
+      pb[t] = as_bf16x8(packed);
+    }
+    return ts;
+  };
+  // Reference move (rare, wave-uniform): the first half-tile (reference -inf gives
+  // +inf), or a half whose probabilities grew past 2^16 / 16 somewhere.  The rows
+  // whose pair max exceeds the reference by more than 2^8 move it; O and l (which
+  // hold every earlier half) are rescaled and the half is recomputed.
+  auto settle_half = [&](const f32x16& sc, bf16x8 (&pb)[2], float ts) -> float {
     if (__any(!(ts <= kSumLimit))) {
-      float mt = sacc[0][0];
+      float mt = sc[0];
 #pragma unroll
-      for (int r = 1; r < 16; ++r) mt = fmaxf(mt, sacc[0][r]);
-#pragma unroll
-      for (int r = 0; r < 16; ++r) mt = fmaxf(mt, sacc[1][r]);
+      for (int r = 1; r < 16; ++r) mt = fmaxf(mt, sc[r]);
       mt = fmaxf(mt, __shfl_xor(mt, 32));
       const float mt2 = mt * sl2;
       const bool move = mt2 > m_ref + kRescaleThreshold;
@@ -309,32 +284,79 @@ __global__ __launch_bounds__(NTHREADS, D >= 128 ? 2 : 3) void attn_fwd_kernel(At
 #pragma unroll
       for (int i = 0; i < DB; ++i) oacc[i] *= alpha;
       m_ref = m_new;
-      ts = 0.f;
-      probs();
+      ts = probs_half(sc, pb);
     }
-    l_run += ts;
-
-    // ---- O^T += V^T P^T --------------------------------------------------------
+    return ts;
+  };
+  auto pv_half = [&](const char* Vt, int blk, const bf16x8 (&pb)[2]) {   // O^T += V^T P^T, one half
 #pragma unroll
-    for (int db = 0; db < DB; ++db) {
+    for (int db = 0; db < DB; ++db)
 #pragma unroll
-      for (int blk = 0; blk < 2; ++blk)
+      for (int t = 0; t < 2; ++t) {
+        const char* vp = Vt + v_lane + (blk * 32 + t * 16) * T::V_ROWB + db * 64;
+        const i16x4 lo = lds_read_tr(vp);
+        const i16x4 hi = lds_read_tr(vp + 8 * T::V_ROWB);
+        const bf16x8 vf = __builtin_bit_cast(bf16x8, __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7));
+        oacc[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(vf, pb[t], oacc[db], 0, 0, 0);
+      }
+  };
+  // keys past the valid length get -inf (the partial last tile only)
+  auto mask_half = [&](f32x16& sc, int j0, int blk) {
 #pragma unroll
-        for (int t = 0; t < 2; ++t) {
-          const char* vp = Vt + v_lane + (blk * 32 + t * 16) * T::V_ROWB + db * 64;
-          const i16x4 lo = lds_read_tr(vp);
-          const i16x4 hi = lds_read_tr(vp + 8 * T::V_ROWB);
-          const bf16x8 vf = __builtin_bit_cast(bf16x8, __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7));
-          oacc[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(vf, pb[blk][t], oacc[db], 0, 0, 0);
-        }
+    for (int r = 0; r < 16; ++r) {
+      const int key = j0 + blk * 32 + 8 * (r >> 2) + 4 * half + (r & 3);
+      if (key >= nkeys) sc[r] = -INFINITY;
     }
   };
 
+  // One tile: wait for its copies, start the next tile's copies into the other stage,
+  // then S^T half 0; [S^T half 1 | softmax half 0]; [PV half 0 | softmax half 1]; PV
+  // half 1.  Each bracket is one basic block, so the scheduler interleaves the MFMAs
+  // of one half with the VALU work of the other; the rare reference moves sit between
+  // them.  MASKED is the partial last tile: it masks and issues no copies.
+  auto tile_step = [&](auto masked, int it, const char* cur, char* nxt) {
+    constexpr bool MASKED = decltype(masked)::value;
+    const int j0 = kb0 + it * BN;
+    __builtin_amdgcn_s_waitcnt(0x0F70);  // vmcnt(0): this wave's copies of tile `it` landed
+    __syncthreads();                     // ... everyone's, and tile it-1 is no longer read
+    if constexpr (!MASKED) {
+      if (it + 1 < ntiles) issue_tile(j0 + BN, nxt);
+    }
+    const char* Kt = cur;
+    const char* Vt = cur + T::K_BYTES;
+
+    f32x16 s0 = s_half(Kt, 0);
+    if constexpr (MASKED) mask_half(s0, j0, 0);
+    bf16x8 pb0[2], pb1[2];
+    __builtin_amdgcn_sched_barrier(0);
+    f32x16 s1 = s_half(Kt, 1);
+    if constexpr (MASKED) mask_half(s1, j0, 1);
+    float ts0 = probs_half(s0, pb0);
+    __builtin_amdgcn_sched_barrier(0);
+    ts0 = settle_half(s0, pb0, ts0);
+    l_run += ts0;
+    pv_half(Vt, 0, pb0);
+    float ts1 = probs_half(s1, pb1);
+    __builtin_amdgcn_sched_barrier(0);
+    ts1 = settle_half(s1, pb1, ts1);
+    l_run += ts1;
+    pv_half(Vt, 1, pb1);
+  };
+
+  const std::integral_constant<bool, false> kFull;
+  const std::integral_constant<bool, true> kMasked;
+  const int nfull = (kend - kb0) / BN;   // tiles whose 64 keys are all valid
   if (ntiles > 0) issue_tile(kb0, stage0);
-  for (int it = 0; it < ntiles; it += 2) {
-    tile_step(it, stage0, stage1);
-    if (it + 1 < ntiles) tile_step(it + 1, stage1, stage0);
+  int it = 0;
+  for (; it + 2 <= nfull; it += 2) {
+    tile_step(kFull, it, stage0, stage1);
+    tile_step(kFull, it + 1, stage1, stage0);
   }
+  if (it < nfull) {
+    tile_step(kFull, it, stage0, stage1);
+    ++it;
+  }
+  if (it < ntiles) tile_step(kMasked, it, (it & 1) ? stage1 : stage0, nullptr);
 
   // ---- epilogue: normalise, store O (bf16) and LSE ------------------------------
   const float l_tot = l_run + __shfl_xor(l_run, 32);
