@@ -143,7 +143,13 @@ int safe_mask_classify(const void* mask, int32_t dtype, const int64_t size[4], c
  * increasing, so ranking s_bar selects the same set as ranking Norm(s_bar).
  * Both flags may be given in one call (accumulate, then select).
  *
- * Workspace: query with workspace == NULL; needed only for SAFE_PCSP_SELECT.
+ * Workspace: a call with workspace == NULL and workspace_bytes != NULL only writes
+ * the bytes it can use (no launch).  SAFE_PCSP_SELECT needs that much.  For
+ * SAFE_PCSP_ACCUM it is optional: given a workspace of at least that size (the size
+ * passed in *workspace_bytes), the heads are split into groups over more workgroups and
+ * the group sums are added to acc in group order by a second kernel; with workspace
+ * and workspace_bytes both NULL the accumulation runs unsplit.  Accumulation alone
+ * rounds a little differently split and unsplit; each form is deterministic.
  * Limits: H <= 64 when head_mask != 0; d in {32, 64, 96, 128}; M <= 1024;
  * 0 <= k <= N; acc is caller-zeroed before the first accumulation.
  */

@@ -296,10 +296,15 @@ def mask_classify(mask: torch.Tensor, row_class: bool = False, kv_len: bool = Fa
     return out
 
 
+_PCSP_WS = {}  # (device index, stream handle) -> uint8 workspace tensor for the head-group split
+
+
 def pcsp_accumulate(q_c: torch.Tensor, k_txt: torch.Tensor, w: torch.Tensor, acc: torch.Tensor,
                     kv_len: Optional[torch.Tensor] = None, head_mask: int = 0, scale: Optional[float] = None,
-                    stream=None) -> torch.Tensor:
-    """acc[b, i] += sum_h sum_j w[b, j] softmax_j(scale q_c[b,i,h] . k_txt[b,j,h])  (Eq. 9-10)."""
+                    stream=None, workspace="auto") -> torch.Tensor:
+    """acc[b, i] += sum_h sum_j w[b, j] softmax_j(scale q_c[b,i,h] . k_txt[b,j,h])  (Eq. 9-10).
+
+    workspace: "auto" (cached per device and stream), None (unsplit), or a uint8 device tensor."""
     _bits16(q_c, "q_c")
     _bits16(k_txt, "k_txt")
     B, N, H, d = q_c.shape
@@ -317,7 +322,24 @@ def pcsp_accumulate(q_c: torch.Tensor, k_txt: torch.Tensor, w: torch.Tensor, acc
     a.kv_len, a.w, a.head_mask = _ptr(kv_len), _ptr(w), head_mask
     a.scale = 0.0 if scale is None else float(scale)
     a.acc = _ptr(acc)
-    _check("safe_pcsp_select", lib.safe_pcsp_select(ctypes.byref(a), None, None, _stream(stream)))
+    st = _stream(stream)
+    if isinstance(workspace, str):
+        if workspace != "auto":
+            raise ValueError("workspace must be 'auto', None or a device tensor")
+        need = ctypes.c_size_t(0)
+        _check("safe_pcsp_select", lib.safe_pcsp_select(ctypes.byref(a), None, ctypes.byref(need), st))
+        workspace = None
+        if need.value > 0:
+            key = (acc.device.index, st)
+            workspace = _PCSP_WS.get(key)
+            if workspace is None or workspace.numel() < need.value:
+                workspace = torch.empty(need.value, dtype=torch.uint8, device=acc.device)
+                _PCSP_WS[key] = workspace
+    if workspace is None:
+        _check("safe_pcsp_select", lib.safe_pcsp_select(ctypes.byref(a), None, None, st))
+    else:
+        size = ctypes.c_size_t(workspace.numel() * workspace.element_size())
+        _check("safe_pcsp_select", lib.safe_pcsp_select(ctypes.byref(a), _ptr(workspace), ctypes.byref(size), st))
     return acc
 
 

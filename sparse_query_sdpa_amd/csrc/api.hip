@@ -14,8 +14,9 @@ int mask_classify_launch(const void* mask, int32_t dtype, const int64_t size[4],
                          uint32_t flags, safe_mask_info* info, uint8_t* row_class, int32_t* kv_len_out,
                          void* workspace, hipStream_t stream);
 size_t mask_classify_workspace(const int64_t size[4]);
-int pcsp_launch(const safe_pcsp_args* a, float scale, void* workspace, hipStream_t stream);
-size_t pcsp_workspace(const safe_pcsp_args* a);
+int pcsp_launch(const safe_pcsp_args* a, float scale, void* workspace, size_t ws_bytes, hipStream_t stream);
+size_t pcsp_select_workspace(const safe_pcsp_args* a);
+size_t pcsp_accum_workspace(const safe_pcsp_args* a);
 }  // namespace safe
 
 using namespace safe;
@@ -200,14 +201,17 @@ int safe_pcsp_select(const safe_pcsp_args* a, void* workspace, size_t* workspace
   if (a->B < 0 || a->N < 0 || a->M < 0 || a->H < 0) return SAFE_ERR_SHAPE;
   const bool sel = (a->flags & SAFE_PCSP_SELECT) != 0;
   const bool accum = (a->flags & SAFE_PCSP_ACCUM) != 0;
+  // workspace == NULL with a size pointer is a query (both uses share one buffer:
+  // the accumulation's per-head-group sums are consumed before the selection runs)
+  const size_t need_sel = pcsp_select_workspace(a);
+  const size_t need_acc = accum ? pcsp_accum_workspace(a) : 0;
+  if (workspace == nullptr && workspace_bytes != nullptr) {
+    *workspace_bytes = need_sel > need_acc ? need_sel : need_acc;
+    return SAFE_OK;
+  }
   if (sel) {
-    const size_t need = pcsp_workspace(a);
-    if (workspace == nullptr && need > 0) {
-      if (workspace_bytes == nullptr) return SAFE_ERR_WORKSPACE;
-      *workspace_bytes = need;
-      return SAFE_OK;
-    }
-    if (workspace_bytes != nullptr && *workspace_bytes < need) return SAFE_ERR_WORKSPACE;
+    if (workspace == nullptr && need_sel > 0) return SAFE_ERR_WORKSPACE;
+    if (workspace_bytes != nullptr && *workspace_bytes < need_sel) return SAFE_ERR_WORKSPACE;
     if (a->grid_h < 0 || a->grid_w < 0 || (int64_t)a->grid_h * a->grid_w != a->N) return SAFE_ERR_SHAPE;
     if (!(a->sigma >= 0.f && a->sigma <= 32.f)) return SAFE_ERR_RANGE;
     if (a->k < 0 || a->k > a->N) return SAFE_ERR_RANGE;
@@ -226,7 +230,9 @@ int safe_pcsp_select(const safe_pcsp_args* a, void* workspace, size_t* workspace
     if ((st = check_bnhd(a->k_text, a->k_stride, work)) != SAFE_OK) return st;
     if (work && (a->w == nullptr || a->acc == nullptr)) return SAFE_ERR_NULL;
   }
-  return pcsp_launch(a, accum ? resolve_scale(a->scale, a->d) : 0.f, workspace, static_cast<hipStream_t>(stream));
+  if (workspace != nullptr && !aligned16(workspace)) return SAFE_ERR_ALIGN;
+  return pcsp_launch(a, accum ? resolve_scale(a->scale, a->d) : 0.f, workspace,
+                     workspace_bytes != nullptr ? *workspace_bytes : 0, static_cast<hipStream_t>(stream));
 }
 
 }  // extern "C"

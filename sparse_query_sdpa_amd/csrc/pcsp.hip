@@ -1,7 +1,12 @@
 // Prompt-Conditioned Sensitivity Partitioning ("SAFE-DiT" Eq. 9-12).
 //
 // ACCUM (Eq. 9-10): acc[b,i] += sum_{h in head set} sum_{j<L_b} w[b,j] softmax_j(scale q_i.k_j).
-//   A workgroup owns 128 image tokens of one sample (4 waves x 32).  For each head
+//   A workgroup owns 128 image tokens of one sample (4 waves x 32) and one group of
+//   heads: with a workspace the heads are split into groups so the grid holds a few
+//   thousand workgroups, each group's per-token sum goes to its own slice of the
+//   workspace, and pcsp_reduce_kernel adds the slices to acc in group order (the
+//   result does not depend on scheduling); without one, one group holds every head
+//   and the sum is added to acc directly.  For each head
 //   the text keys stream through LDS in tiles of 64; S^T = K_txt Q^T runs on
 //   v_mfma_f32_32x32x16_bf16 exactly as in the attention kernel (each lane owns one
 //   image token), and instead of a P V product each lane keeps an online softmax
@@ -14,6 +19,8 @@
 //   select of the k-th key, and an ordered compaction that keeps every key above
 //   it plus the lowest-index ties, so the result is a deterministic ascending list.
 #include <limits.h>
+
+#include <algorithm>
 
 #include "common.h"
 
@@ -31,8 +38,9 @@ struct AccParams {
   const int32_t* kv_len;
   const float* w;
   float* acc;
+  float* part;        // [groups][B][N] per-group sums, or nullptr: add into acc
   uint64_t head_mask;
-  int B, N, M, H, tiles_per_b;
+  int B, N, M, H, tiles_per_b, heads_per_group;
   float scale_log2;
 };
 
@@ -56,8 +64,10 @@ __global__ __launch_bounds__(ANT) void pcsp_accum_kernel(AccParams p) {
   const int ntiles = (L + ABN - 1) / ABN;
   const float sl2 = p.scale_log2;
 
+  const int g = blockIdx.y;
+  const int h_end = min(p.H, (g + 1) * p.heads_per_group);
   float total = 0.f;
-  for (int h = 0; h < p.H; ++h) {
+  for (int h = g * p.heads_per_group; h < h_end; ++h) {
     if (p.head_mask != 0 && !((p.head_mask >> h) & 1ull)) continue;
     bf16x8 qf[KS];
     const u16* qp = p.q + (int64_t)b * p.qs0 + (int64_t)(ok ? i : 0) * p.qs1 + (int64_t)h * p.qs2 + half * 8;
@@ -120,7 +130,37 @@ __global__ __launch_bounds__(ANT) void pcsp_accum_kernel(AccParams p) {
     const float den_t = den + __shfl_xor(den, 32);
     if (den_t > 0.f) total += num_t / den_t;
   }
-  if (ok && half == 0 && L > 0) p.acc[(int64_t)b * p.N + i] += total;
+  if (p.part != nullptr) {
+    if (ok && half == 0) p.part[((int64_t)g * p.B + b) * p.N + i] = total;
+  } else if (ok && half == 0 && L > 0) {
+    p.acc[(int64_t)b * p.N + i] += total;
+  }
+}
+
+// acc[x] += sum over head groups of part[g][x], in group order
+__global__ __launch_bounds__(256) void pcsp_reduce_kernel(const float* part, float* acc, int64_t n, int groups) {
+  const int64_t x = (int64_t)blockIdx.x * 256 + threadIdx.x;
+  if (x >= n) return;
+  float s = 0.f;
+  for (int g = 0; g < groups; ++g) s += part[(int64_t)g * n + x];
+  acc[x] += s;
+}
+
+// Head groups for the accumulation: enough workgroups to fill the GPU several times.
+struct AccPlan {
+  int groups = 1, heads_per_group = 0;
+};
+AccPlan plan_accum(const safe_pcsp_args* a) {
+  AccPlan pl;
+  pl.heads_per_group = a->H;
+  const int64_t items = (int64_t)a->B * ((a->N + ABM - 1) / ABM);
+  if (items <= 0 || a->H <= 1) return pl;
+  const int64_t want = (2400 + items - 1) / items;
+  if (want <= 1) return pl;
+  const int g = (int)std::min<int64_t>(want, a->H);
+  pl.heads_per_group = (a->H + g - 1) / g;
+  pl.groups = (a->H + pl.heads_per_group - 1) / pl.heads_per_group;
+  return pl;
 }
 
 // ============================== SELECT =======================================
@@ -294,13 +334,23 @@ __global__ __launch_bounds__(SNT) void pcsp_select_kernel(SelParams p) {
 
 }  // namespace
 
-size_t pcsp_workspace(const safe_pcsp_args* a) {
+size_t pcsp_select_workspace(const safe_pcsp_args* a) {
   if (!(a->flags & SAFE_PCSP_SELECT)) return 0;
   const size_t n = (size_t)(a->B > 0 ? a->B : 0) * 2 * (size_t)(a->N > 0 ? a->N : 0) * sizeof(float);
   return (n + 255) & ~(size_t)255;
 }
 
-int pcsp_launch(const safe_pcsp_args* a, float scale, void* workspace, hipStream_t s) {
+size_t pcsp_accum_workspace(const safe_pcsp_args* a) {
+  if (!(a->flags & SAFE_PCSP_ACCUM) || a->B <= 0 || a->N <= 0) return 0;
+  const AccPlan pl = plan_accum(a);
+  if (pl.groups <= 1) return 0;
+  const size_t n = (size_t)pl.groups * (size_t)a->B * (size_t)a->N * sizeof(float);
+  return (n + 255) & ~(size_t)255;
+}
+
+// ws_bytes: usable workspace bytes (0 when unknown); the accumulation is split only
+// when its partial sums fit.
+int pcsp_launch(const safe_pcsp_args* a, float scale, void* workspace, size_t ws_bytes, hipStream_t s) {
   if (a->flags & SAFE_PCSP_ACCUM) {
     if ((int64_t)a->B * a->N * a->H > 0 && a->M > 0) {
       AccParams p;
@@ -315,16 +365,28 @@ int pcsp_launch(const safe_pcsp_args* a, float scale, void* workspace, hipStream
       p.B = a->B; p.N = a->N; p.M = a->M; p.H = a->H;
       p.tiles_per_b = (a->N + ABM - 1) / ABM;
       p.scale_log2 = scale * 1.4426950408889634f;
+      AccPlan pl = plan_accum(a);
+      const size_t need = pcsp_accum_workspace(a);
+      if (pl.groups > 1 && (workspace == nullptr || need == 0 || ws_bytes < need)) pl = AccPlan{1, a->H};
+      p.heads_per_group = pl.heads_per_group;
+      p.part = pl.groups > 1 ? static_cast<float*>(workspace) : nullptr;
       const int64_t grid = (int64_t)p.tiles_per_b * a->B;
       if (grid > 0x7fffffff) return SAFE_ERR_SHAPE;
+      const dim3 g3((unsigned)grid, (unsigned)pl.groups);
       switch (a->d) {
-        case 32: hipLaunchKernelGGL(pcsp_accum_kernel<32>, dim3((unsigned)grid), dim3(ANT), 0, s, p); break;
-        case 64: hipLaunchKernelGGL(pcsp_accum_kernel<64>, dim3((unsigned)grid), dim3(ANT), 0, s, p); break;
-        case 96: hipLaunchKernelGGL(pcsp_accum_kernel<96>, dim3((unsigned)grid), dim3(ANT), 0, s, p); break;
-        case 128: hipLaunchKernelGGL(pcsp_accum_kernel<128>, dim3((unsigned)grid), dim3(ANT), 0, s, p); break;
+        case 32: hipLaunchKernelGGL(pcsp_accum_kernel<32>, g3, dim3(ANT), 0, s, p); break;
+        case 64: hipLaunchKernelGGL(pcsp_accum_kernel<64>, g3, dim3(ANT), 0, s, p); break;
+        case 96: hipLaunchKernelGGL(pcsp_accum_kernel<96>, g3, dim3(ANT), 0, s, p); break;
+        case 128: hipLaunchKernelGGL(pcsp_accum_kernel<128>, g3, dim3(ANT), 0, s, p); break;
         default: return SAFE_ERR_UNSUPPORTED;
       }
       if (hipGetLastError() != hipSuccess) return SAFE_ERR_HIP;
+      if (pl.groups > 1) {
+        const int64_t n = (int64_t)a->B * a->N;
+        hipLaunchKernelGGL(pcsp_reduce_kernel, dim3((unsigned)((n + 255) / 256)), dim3(256), 0, s,
+                           (const float*)p.part, a->acc, n, pl.groups);
+        if (hipGetLastError() != hipSuccess) return SAFE_ERR_HIP;
+      }
     }
   }
   if (a->flags & SAFE_PCSP_SELECT) {

@@ -175,6 +175,20 @@ def test_pcsp_rejects_bad_arguments_without_gpu(kw, status):
     assert _pcsp(**kw) == status
 
 
+def test_pcsp_accumulate_workspace_query():
+    # the head-group split of the accumulation is sized by the query (no launch)
+    a = sq.PcspArgs()
+    a.flags = sq.PCSP_ACCUM
+    a.B, a.N, a.M, a.H, a.d = 2, 25600, 256, 24, 96
+    need = ctypes.c_size_t(0)
+    assert sq.lib.safe_pcsp_select(ctypes.byref(a), None, ctypes.byref(need), None) == 0
+    groups = need.value // (2 * 25600 * 4)
+    assert 2 <= groups <= 24 and need.value >= groups * 2 * 25600 * 4
+    a.H = 1   # nothing to split
+    assert sq.lib.safe_pcsp_select(ctypes.byref(a), None, ctypes.byref(need), None) == 0
+    assert need.value == 0
+
+
 def test_pcsp_select_workspace_query():
     a = sq.PcspArgs()
     a.flags = sq.PCSP_SELECT

@@ -36,6 +36,32 @@ def test_accumulate_matches_oracle(number):
     np.testing.assert_allclose(acc.cpu().numpy(), ref2, rtol=ACC_RTOL, atol=1e-7)
 
 
+def test_accumulate_split_over_head_groups():
+    """With a workspace the heads are split into groups whose sums a second kernel adds
+    in group order: same values as unsplit up to rounding, deterministic, and groups
+    holding no selected head add nothing."""
+    inp = W.workload_inputs(2)
+    w = inp["workload"]
+    wts = to_dev(W.pcsp_content_weights(inp["kv_len"], w.M))
+    qc, kt, kv = to_dev_bf16(inp["q_c"]), to_dev_bf16(inp["k_txt"]), to_dev(inp["kv_len"])
+    ref = oracle.pcsp_accumulate(inp["q_c"].value, inp["k_txt"].value, inp["kv_len"], W.pcsp_content_weights(inp["kv_len"], w.M))
+    split = torch.zeros((w.B, w.N), dtype=torch.float32, device=dev())
+    sq.pcsp_accumulate(qc, kt, wts, split, kv_len=kv)
+    plain = torch.zeros_like(split)
+    sq.pcsp_accumulate(qc, kt, wts, plain, kv_len=kv, workspace=None)
+    np.testing.assert_allclose(split.cpu().numpy(), ref, rtol=ACC_RTOL, atol=1e-7)
+    np.testing.assert_allclose(split.cpu().numpy(), plain.cpu().numpy(), rtol=1e-5, atol=1e-7)
+    again = torch.zeros_like(split)
+    sq.pcsp_accumulate(qc, kt, wts, again, kv_len=kv)
+    assert torch.equal(again, split), "split accumulation must be deterministic"
+    heads = [3, 17]
+    sub = torch.zeros_like(split)
+    sq.pcsp_accumulate(qc, kt, wts, sub, kv_len=kv, head_mask=(1 << 3) | (1 << 17))
+    ref_sub = oracle.pcsp_accumulate(inp["q_c"].value, inp["k_txt"].value, inp["kv_len"],
+                                     W.pcsp_content_weights(inp["kv_len"], w.M), heads=heads)
+    np.testing.assert_allclose(sub.cpu().numpy(), ref_sub, rtol=ACC_RTOL, atol=1e-7)
+
+
 def test_accumulate_ragged_lengths():
     B, N, M, H, d = 3, 300, 80, 2, 64
     q, k, _ = W.attention_inputs(B, N, M, H, d, seed=11)
