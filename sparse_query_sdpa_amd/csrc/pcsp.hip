@@ -12,9 +12,10 @@
 //   image token), and instead of a P V product each lane keeps an online softmax
 //   numerator sum_j w_j p_j and denominator sum_j p_j.  The probabilities are never
 //   stored: only the N-vector acc is kept, as the paper's instrumentation does.
-// SELECT (Eq. 11-12): one workgroup per sample (1024 threads).
-//   Separable Gaussian (rows, then columns) with the in-grid taps renormalised,
-//   min-max normalisation for the optional score output, then an exact top-k:
+// SELECT (Eq. 11-12): the separable Gaussian (rows, then columns, one thread per
+//   token, in-grid taps renormalised) runs as two grid-wide kernels; then one
+//   workgroup per sample (1024 threads, the sample's keys held in LDS when they fit)
+//   does the min-max normalisation for the optional score output and an exact top-k:
 //   order-preserving 32-bit keys (-0 folded to +0, NaN lowest), a 4 x 8-bit radix
 //   select of the k-th key, and an ordered compaction that keeps every key above
 //   it plus the lowest-index ties, so the result is a deterministic ascending list.
@@ -171,7 +172,8 @@ struct SelParams {
   const float* acc;
   float* score_out;
   int32_t* idx_out;
-  float* ws;           // per sample: tmp[N], sbar[N]
+  float* ws;           // smoothed field: sample b at ws + b * ws_bs
+  int64_t ws_bs;
   int N, gh, gw, k, radius;
   float sigma;
 };
@@ -200,70 +202,112 @@ __device__ int block_exclusive_scan(int v, int* sh, int* total) {
   return incl - v;
 }
 
-__global__ __launch_bounds__(SNT) void pcsp_select_kernel(SelParams p) {
+// ---- Eq. 11: separable Gaussian, renormalised at the borders ------------------
+// One thread per token; rows then columns.  Taps exp(-t^2 / (2 sigma^2)) in LDS.
+__device__ __forceinline__ void load_taps(float* taps, int R, float sigma) {
+  const float inv2s2 = 1.0f / (2.0f * sigma * sigma);
+  for (int i = threadIdx.x; i <= 2 * R; i += blockDim.x) {
+    const float d = (float)(i - R);
+    taps[i] = expf(-d * d * inv2s2);
+  }
+  __syncthreads();
+}
+
+template <bool ROWS>
+__global__ __launch_bounds__(256) void pcsp_smooth_kernel(const float* in, float* out, int N, int gh, int gw,
+                                                         int R, float sigma, int64_t in_bs, int64_t out_bs) {
   __shared__ float taps[MAX_TAPS];
+  load_taps(taps, R, sigma);
+  const int b = blockIdx.y;
+  const int pos = blockIdx.x * 256 + threadIdx.x;
+  if (pos >= N) return;
+  const float* src = in + (int64_t)b * in_bs;
+  const int y = pos / gw, x = pos % gw;
+  float num = 0.f, den = 0.f;
+  if (ROWS) {
+    const int lo = max(-R, -x), hi = min(R, gw - 1 - x);
+    for (int d = lo; d <= hi; ++d) {
+      num = __builtin_fmaf(taps[d + R], src[y * gw + x + d], num);
+      den += taps[d + R];
+    }
+  } else {
+    const int lo = max(-R, -y), hi = min(R, gh - 1 - y);
+    for (int d = lo; d <= hi; ++d) {
+      num = __builtin_fmaf(taps[d + R], src[(y + d) * gw + x], num);
+      den += taps[d + R];
+    }
+  }
+  out[(int64_t)b * out_bs + pos] = num / den;
+}
+
+// ---- Norm and Eq. 12: one workgroup per sample --------------------------------
+// KEYS_IN_LDS: the N order keys are loaded into LDS once (N <= kKeyCap) and every
+// radix pass and the compaction read them there; otherwise they are recomputed from
+// the field in global memory.  Histograms aggregate equal bins within a wave first
+// (the leading passes see few distinct bins), and the bin holding the k-th key is
+// found by a suffix scan over the 256 counts on the first wave.
+constexpr int kKeyCap = 32768;
+
+__device__ __forceinline__ void hist_add(int* hist, u32 bin, bool act) {
+  const int lane = threadIdx.x & 63;
+  uint64_t pending = __ballot(act);
+  for (int round = 0; round < 4 && pending != 0; ++round) {
+    const int leader = __builtin_ctzll(pending);
+    const u32 lb = __builtin_amdgcn_readlane(bin, leader);
+    const uint64_t same = __ballot(act && bin == lb);
+    const int n = __builtin_popcountll(same);
+    if (lane == leader) atomicAdd(&hist[lb], n);
+    if (act && bin == lb) act = false;
+    pending &= ~same;
+    if (n < 8) break;   // bins are spread: plain atomics for the rest
+  }
+  if (act) atomicAdd(&hist[bin], 1);
+}
+
+template <bool KEYS_IN_LDS>
+__global__ __launch_bounds__(SNT) void pcsp_select_kernel(SelParams p) {
+  __shared__ u32 kbuf[KEYS_IN_LDS ? kKeyCap : 1];
   __shared__ int hist[256];
   __shared__ int scan_buf[SNT];
   __shared__ float red_min[SNT / 64], red_max[SNT / 64];
+  __shared__ u32 red_kmin[SNT / 64], red_kmax[SNT / 64];
   __shared__ u32 sh_prefix;
   __shared__ int sh_krem;
 
-  const int t = threadIdx.x;
+  const int t = threadIdx.x, lane = t & 63;
   const int b = blockIdx.x;
   const int N = p.N;
-  const float* acc = p.acc + (int64_t)b * N;
-  float* tmp = p.ws + (int64_t)b * 2 * N;
-  float* sbar = tmp + N;
-  const int R = p.radius;
+  const float* src = (p.sigma > 0.f ? p.ws : p.acc) + (int64_t)b * (p.sigma > 0.f ? p.ws_bs : N);
+  auto key_at = [&](int pos) -> u32 {
+    if constexpr (KEYS_IN_LDS) return kbuf[pos];
+    else return order_key(src[pos]);
+  };
 
-  // ---- Eq. 11: separable Gaussian, renormalised at the borders ---------------
-  const float* src = acc;
-  if (p.sigma > 0.f) {
-    const float inv2s2 = 1.0f / (2.0f * p.sigma * p.sigma);
-    for (int i = t; i <= 2 * R; i += SNT) {
-      const float d = (float)(i - R);
-      taps[i] = expf(-d * d * inv2s2);
-    }
-    __syncthreads();
-    for (int pos = t; pos < N; pos += SNT) {  // along grid rows
-      const int y = pos / p.gw, x = pos % p.gw;
-      const int lo = max(-R, -x), hi = min(R, p.gw - 1 - x);
-      float num = 0.f, den = 0.f;
-      for (int d = lo; d <= hi; ++d) {
-        num = __builtin_fmaf(taps[d + R], acc[y * p.gw + x + d], num);
-        den += taps[d + R];
-      }
-      tmp[pos] = num / den;
-    }
-    __syncthreads();
-    for (int pos = t; pos < N; pos += SNT) {  // along grid columns
-      const int y = pos / p.gw, x = pos % p.gw;
-      const int lo = max(-R, -y), hi = min(R, p.gh - 1 - y);
-      float num = 0.f, den = 0.f;
-      for (int d = lo; d <= hi; ++d) {
-        num = __builtin_fmaf(taps[d + R], tmp[(y + d) * p.gw + x], num);
-        den += taps[d + R];
-      }
-      sbar[pos] = num / den;
-    }
-    __syncthreads();
-    src = sbar;
+  float lo = INFINITY, hi = -INFINITY;
+  u32 kmin = 0xFFFFFFFFu, kmax = 0u;
+  for (int pos = t; pos < N; pos += SNT) {
+    const float v = src[pos];
+    const u32 key = order_key(v);
+    if constexpr (KEYS_IN_LDS) kbuf[pos] = key;
+    lo = fminf(lo, v);
+    hi = fmaxf(hi, v);
+    kmin = min(kmin, key);
+    kmax = max(kmax, key);
   }
-
+#pragma unroll
+  for (int off = 32; off > 0; off >>= 1) {
+    kmin = min(kmin, (u32)__shfl_xor((int)kmin, off));
+    kmax = max(kmax, (u32)__shfl_xor((int)kmax, off));
+  }
+  if (lane == 0) { red_kmin[t >> 6] = kmin; red_kmax[t >> 6] = kmax; }
   // ---- Norm: min-max scaling (optional output) --------------------------------
   if (p.score_out != nullptr) {
-    float lo = INFINITY, hi = -INFINITY;
-    for (int pos = t; pos < N; pos += SNT) {
-      const float v = src[pos];
-      lo = fminf(lo, v);
-      hi = fmaxf(hi, v);
-    }
 #pragma unroll
     for (int off = 32; off > 0; off >>= 1) {
       lo = fminf(lo, __shfl_xor(lo, off));
       hi = fmaxf(hi, __shfl_xor(hi, off));
     }
-    if ((t & 63) == 0) { red_min[t >> 6] = lo; red_max[t >> 6] = hi; }
+    if (lane == 0) { red_min[t >> 6] = lo; red_max[t >> 6] = hi; }
     __syncthreads();
     lo = red_min[0]; hi = red_max[0];
     for (int w = 1; w < SNT / 64; ++w) { lo = fminf(lo, red_min[w]); hi = fmaxf(hi, red_max[w]); }
@@ -276,27 +320,65 @@ __global__ __launch_bounds__(SNT) void pcsp_select_kernel(SelParams p) {
   const int k = p.k;
   if (k == 0) return;
   int32_t* out = p.idx_out + (int64_t)b * k;
-  // radix select of the k-th largest key
-  if (t == 0) { sh_prefix = 0u; sh_krem = k; }
-  for (int pass = 0; pass < 4; ++pass) {
-    const int shift = 24 - 8 * pass;
+  // radix select of the k-th largest key, 8-bit digits below the bits that every key
+  // shares (those of the smallest and largest key agree on them)
+  __syncthreads();
+  kmin = red_kmin[0]; kmax = red_kmax[0];
+  for (int w = 1; w < SNT / 64; ++w) { kmin = min(kmin, red_kmin[w]); kmax = max(kmax, red_kmax[w]); }
+  const int free_bits = kmin == kmax ? 0 : 32 - __builtin_clz(kmin ^ kmax);
+  if (t == 0) {
+    sh_prefix = free_bits == 32 ? 0u : (kmax & ~((1u << free_bits) - 1u));
+    sh_krem = k;
+  }
+  __syncthreads();   // also when no pass runs (all keys equal)
+  for (int top = free_bits; top > 0; top -= 8) {
+    const int shift = top > 8 ? top - 8 : 0;
+    const u32 digit_mask = (1u << (top - shift)) - 1u;
     if (t < 256) hist[t] = 0;
     __syncthreads();
     const u32 prefix = sh_prefix;
-    const u32 hmask = pass == 0 ? 0u : (0xFFFFFFFFu << (shift + 8));
-    for (int pos = t; pos < N; pos += SNT) {
-      const u32 key = order_key(src[pos]);
-      if ((key & hmask) == prefix) atomicAdd(&hist[(key >> shift) & 255u], 1);
+    const u32 hmask = top == 32 ? 0u : (0xFFFFFFFFu << top);
+    for (int base = 0; base < N; base += SNT) {   // every lane of a wave runs each step
+      const int pos = base + t;
+      u32 key = 0u;
+      if (pos < N) key = key_at(pos);
+      hist_add(hist, (key >> shift) & digit_mask, pos < N && (key & hmask) == prefix);
     }
     __syncthreads();
-    if (t == 0) {
-      int rem = sh_krem, bin = 255;
-      for (; bin > 0; --bin) {
-        if (hist[bin] >= rem) break;
-        rem -= hist[bin];
+    if (t < 64) {
+      // suffix counts over the 256 bins (lane l owns bins 4l..4l+3), then the bin where
+      // the k-th largest key falls: suffix(bin) >= rem > suffix(bin + 1)
+      const int c0 = hist[4 * lane], c1 = hist[4 * lane + 1], c2 = hist[4 * lane + 2], c3 = hist[4 * lane + 3];
+      int suf = c0 + c1 + c2 + c3;   // becomes the sum over lanes >= lane
+#pragma unroll
+      for (int off = 1; off < 64; off <<= 1) {
+        const int o = __shfl_down(suf, off);
+        if (lane + off < 64) suf += o;
       }
-      sh_prefix = prefix | ((u32)bin << shift);
-      sh_krem = rem;  // how many to take from within this bin (and deeper)
+      const int above = suf - (c0 + c1 + c2 + c3);   // keys in bins above this lane's four
+      const int rem = sh_krem;
+      // lane holding the bin: above < rem <= above + its four counts
+      int bin = -1, left = 0;
+      if (above < rem && rem <= suf) {
+        int acc3 = above + c3;
+        if (rem <= acc3) { bin = 4 * lane + 3; left = rem - above; }
+        else {
+          int acc2 = acc3 + c2;
+          if (rem <= acc2) { bin = 4 * lane + 2; left = rem - acc3; }
+          else {
+            int acc1 = acc2 + c1;
+            if (rem <= acc1) { bin = 4 * lane + 1; left = rem - acc2; }
+            else { bin = 4 * lane; left = rem - acc1; }
+          }
+        }
+      }
+      const uint64_t has = __ballot(bin >= 0);
+      if (has == 0) {
+        if (lane == 0) sh_prefix = prefix;   // fewer than rem keys left (cannot happen for k <= N)
+      } else if (lane == __builtin_ctzll(has)) {
+        sh_prefix = prefix | ((u32)bin << shift);
+        sh_krem = left;  // how many to take from within this bin (and deeper)
+      }
     }
     __syncthreads();
   }
@@ -306,24 +388,20 @@ __global__ __launch_bounds__(SNT) void pcsp_select_kernel(SelParams p) {
   // ordered compaction: each thread owns a contiguous segment
   const int seg = (N + SNT - 1) / SNT;
   const int beg = min(N, t * seg), end = min(N, beg + seg);
-  int n_eq = 0;
-  for (int pos = beg; pos < end; ++pos) n_eq += order_key(src[pos]) == T;
+  int n_eq = 0, n_gt = 0;
+  for (int pos = beg; pos < end; ++pos) {
+    const u32 key = key_at(pos);
+    n_eq += key == T;
+    n_gt += key > T;
+  }
   int tot;
   const int eq_base = block_exclusive_scan(n_eq, scan_buf, &tot);
-  int n_sel = 0;
-  {
-    int r = eq_base;
-    for (int pos = beg; pos < end; ++pos) {
-      const u32 key = order_key(src[pos]);
-      if (key > T) ++n_sel;
-      else if (key == T) { if (r < need_eq) ++n_sel; ++r; }
-    }
-  }
-  const int sel_base = block_exclusive_scan(n_sel, scan_buf, &tot);
+  const int eq_take = max(0, min(n_eq, need_eq - eq_base));
+  const int sel_base = block_exclusive_scan(n_gt + eq_take, scan_buf, &tot);
   {
     int r = eq_base, o = sel_base;
     for (int pos = beg; pos < end; ++pos) {
-      const u32 key = order_key(src[pos]);
+      const u32 key = key_at(pos);
       bool take = false;
       if (key > T) take = true;
       else if (key == T) { take = r < need_eq; ++r; }
@@ -395,13 +473,27 @@ int pcsp_launch(const safe_pcsp_args* a, float scale, void* workspace, size_t ws
       p.acc = a->acc;
       p.score_out = a->score_out;
       p.idx_out = a->idx_out;
-      p.ws = static_cast<float*>(workspace);
+      p.ws = nullptr;
+      p.ws_bs = a->N;
       p.N = a->N; p.gh = a->grid_h; p.gw = a->grid_w; p.k = a->k;
       p.sigma = a->sigma;
       p.radius = a->sigma > 0.f ? (int)ceilf(3.0f * a->sigma) : 0;
       if (p.radius > (MAX_TAPS - 1) / 2) return SAFE_ERR_RANGE;
-      if (p.ws == nullptr && a->sigma > 0.f) return SAFE_ERR_WORKSPACE;
-      hipLaunchKernelGGL(pcsp_select_kernel, dim3(a->B), dim3(SNT), 0, s, p);
+      if (a->sigma > 0.f) {
+        if (workspace == nullptr) return SAFE_ERR_WORKSPACE;
+        // workspace: row-smoothed field [B][N], then the smoothed field [B][N]
+        float* tmp = static_cast<float*>(workspace);
+        float* sbar = tmp + (int64_t)a->B * a->N;
+        const dim3 g((unsigned)((a->N + 255) / 256), (unsigned)a->B);
+        hipLaunchKernelGGL(pcsp_smooth_kernel<true>, g, dim3(256), 0, s, (const float*)a->acc, tmp, a->N,
+                           a->grid_h, a->grid_w, p.radius, p.sigma, (int64_t)a->N, (int64_t)a->N);
+        hipLaunchKernelGGL(pcsp_smooth_kernel<false>, g, dim3(256), 0, s, (const float*)tmp, sbar, a->N,
+                           a->grid_h, a->grid_w, p.radius, p.sigma, (int64_t)a->N, (int64_t)a->N);
+        if (hipGetLastError() != hipSuccess) return SAFE_ERR_HIP;
+        p.ws = sbar;
+      }
+      if (a->N <= kKeyCap) hipLaunchKernelGGL(pcsp_select_kernel<true>, dim3(a->B), dim3(SNT), 0, s, p);
+      else hipLaunchKernelGGL(pcsp_select_kernel<false>, dim3(a->B), dim3(SNT), 0, s, p);
       if (hipGetLastError() != hipSuccess) return SAFE_ERR_HIP;
     }
   }
