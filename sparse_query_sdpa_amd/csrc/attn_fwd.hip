@@ -400,18 +400,21 @@ __global__ __launch_bounds__(NTHREADS, D >= 128 ? 2 : 3) void attn_fwd_kernel(At
 
 // Merge the key-range partials of each split tail tile: M = max of the ranges' maxima,
 // L = sum of their sums scaled by 2^(max - M), O = sum of their O scaled the same way
-// over L; the same output rules as the whole-tile epilogue.  Two threads per row,
-// each owning half of the head dimension.
+// over L; the same output rules as the whole-tile epilogue.  A workgroup takes 32 rows
+// of a tile, eight threads per row, each owning D/8 consecutive columns.
+constexpr int MERGE_ROWS = 32;
+constexpr int MERGE_TPR = 8;
 template <int D, bool GATHER>
-__global__ __launch_bounds__(256) void attn_merge_kernel(AttnParams p) {
-  constexpr int DH = D / 2;
+__global__ __launch_bounds__(MERGE_ROWS * MERGE_TPR) void attn_merge_kernel(AttnParams p) {
+  constexpr int DT = D / MERGE_TPR;   // columns per thread: 4, 8, 12 or 16
   const int ti = blockIdx.x;
   const int logical = p.n_full + ti;
   const int tile = logical % p.n_row_tiles;
   const int bh = logical / p.n_row_tiles;
   const int h = bh % p.H;
   const int b = bh / p.H;
-  const int rloc = threadIdx.x >> 1, hf = threadIdx.x & 1;
+  const int rloc = blockIdx.y * MERGE_ROWS + threadIdx.x / MERGE_TPR;
+  const int part = threadIdx.x % MERGE_TPR;
   const int rr = tile * BM + rloc;
   if (rr >= p.n_rows) return;
   int qi = rr;
@@ -421,17 +424,17 @@ __global__ __launch_bounds__(256) void attn_merge_kernel(AttnParams p) {
   const float* pml = p.part + (int64_t)p.n_slots * BM * D;
   float M = -INFINITY;
   for (int s = 0; s < p.nsplit; ++s) M = fmaxf(M, pml[((int64_t)(ti * p.nsplit + s) * BM + rloc) * 2]);
-  float acc[DH];
+  float acc[DT];
 #pragma unroll
-  for (int i = 0; i < DH; ++i) acc[i] = 0.f;
+  for (int i = 0; i < DT; ++i) acc[i] = 0.f;
   float L = 0.f;
   for (int s = 0; s < p.nsplit; ++s) {
     const int64_t sl = (int64_t)(ti * p.nsplit + s) * BM + rloc;
     const float w = M == -INFINITY ? 0.f : __builtin_amdgcn_exp2f(pml[sl * 2] - M);
     L += w * pml[sl * 2 + 1];
-    const float* po = p.part + sl * D + hf * DH;
+    const float* po = p.part + sl * D + part * DT;
 #pragma unroll
-    for (int i = 0; i < DH; i += 4) {
+    for (int i = 0; i < DT; i += 4) {
       const f32x4 v = __builtin_bit_cast(f32x4, ld16(po + i));
       acc[i] += w * v[0]; acc[i + 1] += w * v[1]; acc[i + 2] += w * v[2]; acc[i + 3] += w * v[3];
     }
@@ -439,18 +442,16 @@ __global__ __launch_bounds__(256) void attn_merge_kernel(AttnParams p) {
   const float inv = L > 0.f ? 1.0f / L : 0.f;
   const int orow = (GATHER && p.scatter) ? qi : rr;
   if (!GATHER || !p.scatter || q_ok) {
-    u16* op = p.o + (int64_t)b * p.os0 + (int64_t)orow * p.os1 + (int64_t)h * p.os2 + hf * DH;
+    u16* op = p.o + (int64_t)b * p.os0 + (int64_t)orow * p.os1 + (int64_t)h * p.os2 + part * DT;
 #pragma unroll
-    for (int i = 0; i < DH; i += 8) {
-      u32x4 w;
+    for (int i = 0; i < DT; i += 4) {
+      u32x2 w;
       w[0] = pack_bf16x2(acc[i] * inv, acc[i + 1] * inv);
       w[1] = pack_bf16x2(acc[i + 2] * inv, acc[i + 3] * inv);
-      w[2] = pack_bf16x2(acc[i + 4] * inv, acc[i + 5] * inv);
-      w[3] = pack_bf16x2(acc[i + 6] * inv, acc[i + 7] * inv);
-      st16(op + i, w);
+      st8(op + i, w);
     }
   }
-  if (p.lse != nullptr && hf == 0) {
+  if (p.lse != nullptr && part == 0) {
     const float lse = L > 0.f ? (M + __builtin_log2f(L)) * 0.69314718055994530942f : -INFINITY;
     p.lse[((int64_t)b * p.H + h) * p.n_rows + rr] = lse;
   }
@@ -461,7 +462,7 @@ hipError_t launch(const AttnParams& p, hipStream_t s) {
   hipLaunchKernelGGL((attn_fwd_kernel<D, G, KV>), dim3(p.total_wg), dim3(NTHREADS), 0, s, p);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess || p.n_slots == 0) return e;
-  hipLaunchKernelGGL((attn_merge_kernel<D, G>), dim3(p.n_slots / p.nsplit), dim3(256), 0, s, p);
+  hipLaunchKernelGGL((attn_merge_kernel<D, G>), dim3(p.n_slots / p.nsplit, BM / MERGE_ROWS), dim3(MERGE_ROWS * MERGE_TPR), 0, s, p);
   return hipGetLastError();
 }
 

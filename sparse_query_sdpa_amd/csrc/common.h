@@ -17,9 +17,6 @@ typedef float f32x16 __attribute__((ext_vector_type(16)));
 typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
 typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
 
-// (1.0, 1.0) as packed bf16: the second operand of a v_dot2 row sum
-#define kOnesBf16x2 (__builtin_bit_cast(bf16x2, 0x3F803F80u))
-
 constexpr int kWave = 64;
 constexpr int kNumXcd = 8;  // MI355X: 8 accelerator complex dies, workgroups dealt round-robin
 
