@@ -237,8 +237,9 @@ def main() -> int:
     torch.cuda.synchronize()
     wall = time.perf_counter() - t0
     ms_step = wall * 1e3 / args.steps
-    stage_ms = {name: float(np.mean([events[s][i].elapsed_time(events[s][i + 1]) for s in range(args.steps)]))
+    per_step = {name: [events[s][i].elapsed_time(events[s][i + 1]) for s in range(args.steps)]
                 for i, name in enumerate(stages)}
+    stage_ms = {name: float(np.mean(v)) for name, v in per_step.items()}
     assert torch.equal(idx, idx0), "the sensitive set must not change across steps"
     verdict = mws[:8].view(torch.int32).cpu().tolist()
     assert verdict == [1, 1], f"the all-zero mask must be certified removable (ZERO), got {verdict}"
@@ -272,6 +273,8 @@ def main() -> int:
         "dense_srsu_step_ratio": round(stage_ms["dense"] / (stage_ms["srsu_self"] + stage_ms["kv_assemble"]), 3),
         "ideal_ratio_N_over_k": round(N / k, 3),
         "stage_ms": {kk: round(v, 4) for kk, v in stage_ms.items()},
+        "stage_ms_median": {kk: round(float(np.median(v)), 4) for kk, v in per_step.items()},
+        "stage_ms_min": {kk: round(float(np.min(v)), 4) for kk, v in per_step.items()},
         "cross_tflops": round(tf(fl_cross, stage_ms["srsu_cross"]), 2),
         "classify_gbs": round(mask_bytes / (stage_ms["classify"] * 1e-3) / 1e9, 1),
         "classify_pct_hbm": round(100 * mask_bytes / (stage_ms["classify"] * 1e-3) / 1e9 / PEAK_HBM_GBS, 2),
@@ -313,12 +316,129 @@ def main() -> int:
                                   "pct_peak": round(100 * t / PEAK_BF16_TFLOPS, 2),
                                   "dense_ratio": round(stage_ms["dense"] / ms, 3), "ideal": round(N / kk, 3)}
         out["rho_sweep"] = sweep
+        out["s_brackets"] = s_brackets(sq, q, k_glob, v_glob, wl, args.rho, stage_ms["dense"], tf)
+        out["configs"] = other_configs(sq, W, tf)
+        clk = clock_under_load(lambda: sq.attn_fwd(q, kx, vx, out=o_dense))
+        out["gfx_clock_mhz_under_dense_load"] = clk
+        if clk is not None:
+            peak_clk = PEAK_BF16_TFLOPS * clk / 2400.0
+            out["roofline"]["peak_at_measured_clock"] = round(peak_clk, 1)
+            out["roofline"]["frac_at_measured_clock"] = round(dense_tf / peak_clk, 4)
+            out["roofline_srsu"]["peak_at_measured_clock"] = round(peak_clk, 1)
+            out["roofline_srsu"]["frac_at_measured_clock"] = round(srsu_tf / peak_clk, 4)
 
     if not args.no_cpu_baseline:
         out["cpu_baseline"] = cpu_baseline(inp, args.cpu_rows)
 
     print(json.dumps(out), flush=True)
     return 0
+
+
+def _time_ms(fn, reps: int) -> float:
+    import torch
+    fn()
+    fn()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record()
+    for _ in range(reps):
+        fn()
+    e1.record()
+    torch.cuda.synchronize()
+    return e0.elapsed_time(e1) / reps
+
+
+def s_brackets(sq, q, k_glob, v_glob, wl, rho: int, dense_ms: float, tf) -> dict:
+    """SRSU self-attention with the same k as the PCSP set but random or contiguous rows."""
+    import torch
+    B, N, H, d = q.shape
+    k = wl.k_for(rho)
+    g = torch.Generator(device="cpu").manual_seed(4242)
+    rand = torch.stack([torch.sort(torch.randperm(N, generator=g)[:k])[0] for _ in range(B)]).to(torch.int32).to(q.device)
+    cont = torch.arange(k, dtype=torch.int32, device=q.device).expand(B, k).contiguous()
+    o = torch.empty((B, k, H, d), dtype=torch.bfloat16, device=q.device)
+    res = {}
+    for name, rows in (("random", rand), ("contiguous", cont)):
+        ms = _time_ms(lambda: sq.attn_fwd(q, k_glob, v_glob, q_rows=rows, out=o), 5)
+        t = tf(4.0 * B * H * k * N * d, ms)
+        res[name] = {"k": k, "ms": round(ms, 4), "tflops": round(t, 2), "pct_peak": round(100 * t / PEAK_BF16_TFLOPS, 2),
+                     "dense_ratio": round(dense_ms / ms, 3)}
+    return res
+
+
+def other_configs(sq, W, tf) -> dict:
+    """SRSU (random sorted rows, k = ceil(rho N)) and dense attention at the 128x128 and 192x192
+    grids on N(0,1) bf16 inputs drawn on the device; at 192x192 also the fp32 row-constant
+    [1,1,N,N] mask (rows c_i ~ U(-3,3)) certified and the peak device memory of that run."""
+    import torch
+    res = {}
+    for num in (3, 5):
+        wl = W.WORKLOADS[num]
+        B, N, H, d = wl.B, wl.N, wl.H, wl.d
+        k = wl.k_for(wl.rho_percent[0])
+        torch.cuda.reset_peak_memory_stats()
+        g = torch.Generator(device="cuda").manual_seed(7000 + num)
+        q, kx, vx = (torch.randn((B, N, H, d), generator=g, device="cuda").to(torch.bfloat16) for _ in range(3))
+        gc = torch.Generator(device="cpu").manual_seed(7100 + num)
+        rows = torch.stack([torch.sort(torch.randperm(N, generator=gc)[:k])[0] for _ in range(B)]).to(torch.int32).cuda()
+        o_s = torch.empty((B, k, H, d), dtype=torch.bfloat16, device="cuda")
+        o_d = torch.empty_like(q)
+        ms_s = _time_ms(lambda: sq.attn_fwd(q, kx, vx, q_rows=rows, out=o_s), 5)
+        ms_d = _time_ms(lambda: sq.attn_fwd(q, kx, vx, out=o_d), 3)
+        ts, td = tf(4.0 * B * H * k * N * d, ms_s), tf(4.0 * B * H * N * N * d, ms_d)
+        entry = {"workload": wl.name, "N": N, "k": k, "srsu_ms": round(ms_s, 4), "srsu_tflops": round(ts, 2),
+                 "srsu_pct_peak": round(100 * ts / PEAK_BF16_TFLOPS, 2), "dense_ms": round(ms_d, 4),
+                 "dense_tflops": round(td, 2), "dense_pct_peak": round(100 * td / PEAK_BF16_TFLOPS, 2),
+                 "dense_srsu_ratio": round(ms_d / ms_s, 3), "ideal": round(N / k, 3)}
+        if num == 5:
+            c = (torch.rand((N, 1), generator=g, device="cuda") * 6.0 - 3.0)
+            mask = c.expand(N, N).contiguous().view(1, 1, N, N)
+            nbytes = mask.numel() * 4
+            info = sq.mask_classify(mask)
+            ws = info["workspace"]
+            ms_c = _time_ms(lambda: sq.mask_classify(mask, workspace=ws, asynchronous=True), 5)
+            entry["classify_f32_row_const"] = {"gb": round(nbytes / 1e9, 2), "ms": round(ms_c, 4),
+                                               "gbs": round(nbytes / (ms_c * 1e-3) / 1e9, 1),
+                                               "pct_hbm": round(100 * nbytes / (ms_c * 1e-3) / 1e9 / PEAK_HBM_GBS, 2),
+                                               "verdict": info["verdict"], "mask_class": info["mask_class"]}
+            del mask, c
+        entry["peak_mem_gb"] = round(torch.cuda.max_memory_allocated() / 1e9, 2)
+        res[f"{wl.grid_h}x{wl.grid_w}"] = entry
+        del q, kx, vx, o_s, o_d
+        torch.cuda.empty_cache()
+    return res
+
+
+def clock_under_load(launch, seconds: float = 1.5):
+    """Mean graphics clock (MHz, over the XCDs) read with amd-smi while `launch` runs in a
+    loop; None when the tool is not available."""
+    import shutil
+    import subprocess
+    import threading
+    import torch
+    tool = shutil.which("amd-smi")
+    if tool is None:
+        return None
+    result = {}
+
+    def sample():
+        try:
+            time.sleep(seconds / 2)
+            txt = subprocess.run([tool, "metric", "-c"], capture_output=True, text=True, timeout=20).stdout
+            result["txt"] = txt
+        except Exception:
+            pass
+
+    th = threading.Thread(target=sample)
+    th.start()
+    t_end = time.perf_counter() + seconds
+    while time.perf_counter() < t_end or th.is_alive():
+        launch()
+        torch.cuda.synchronize()
+        if time.perf_counter() > t_end + 20:
+            break
+    th.join()
+    clks = [int(m) for m in re.findall(r"GFX_\d+:\s*\n\s*CLK:\s*(\d+)\s*MHz", result.get("txt", ""))]
+    return round(sum(clks) / len(clks), 1) if clks else None
 
 
 def cpu_baseline(inp, rows_per_bh: int):
