@@ -317,6 +317,16 @@ def main() -> int:
                                   "dense_ratio": round(stage_ms["dense"] / ms, 3), "ideal": round(N / kk, 3)}
         out["rho_sweep"] = sweep
         out["s_brackets"] = s_brackets(sq, q, k_glob, v_glob, wl, args.rho, stage_ms["dense"], tf)
+        # in place: the fresh rows of S scattered into a copy of the cache (valid while S is fixed
+        # between anchor passes: the context rows stay the anchor's and the rows of S are overwritten
+        # every step)
+        kc2, vc2 = kx.clone(), vx.clone()
+        ms_ip = _time_ms(lambda: sq.kv_assemble(k_fresh, v_fresh, idx, kc2, vc2, in_place=True), 20)
+        ip_bytes = 4.0 * B * k * H * d * 2
+        out["kv_assemble_in_place"] = {"ms": round(ms_ip, 4), "gbs": round(ip_bytes / (ms_ip * 1e-3) / 1e9, 1),
+                                       "pct_hbm": round(100 * ip_bytes / (ms_ip * 1e-3) / 1e9 / PEAK_HBM_GBS, 2),
+                                       "bytes": ip_bytes}
+        del kc2, vc2
         out["configs"] = other_configs(sq, W, tf)
         clk = clock_under_load(lambda: sq.attn_fwd(q, kx, vx, out=o_dense))
         out["gfx_clock_mhz_under_dense_load"] = clk

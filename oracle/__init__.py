@@ -17,6 +17,8 @@ Parts:
                on the latent grid, min-max normalisation, top-k selection.
   kvcache.py   Eq. 14, 16, 19: global K/V assembly in original token order and
                the anchor refresh of the context cache.
+  guidance.py  Eq. 20, 21: sensitivity-weighted classifier-free guidance and its
+               binary variant.
 
 Pinning status (what fixes each function other than itself) is listed in the
 module docstrings; every function is pinned by the CPU tests in
@@ -31,12 +33,14 @@ from .mask import (ALL_VALID, ZERO, ROW_CONST, KEY_PADDING, NONCONST, BLOCKED, N
 from .pcsp import (pcsp_accumulate, gaussian_taps, gaussian_smooth, minmax_normalize,
                    topk_select, pcsp_scores)
 from .kvcache import kv_assemble, car_refresh
+from .guidance import guidance_scales, binary_scales, sw_cfg
 
 __all__ = [
     "sdpa", "sdpa_bruteforce", "lse_from_logits",
     "ALL_VALID", "ZERO", "ROW_CONST", "KEY_PADDING", "NONCONST", "BLOCKED", "NONFINITE",
     "REMOVABLE", "CLASS_NAMES", "classify_row", "classify_rows", "classify_mask", "MaskVerdict",
     "safe_sdpa", "removable_row_witness",
+    "guidance_scales", "binary_scales", "sw_cfg",
     "pcsp_accumulate", "gaussian_taps", "gaussian_smooth", "minmax_normalize", "topk_select",
     "pcsp_scores", "kv_assemble", "car_refresh",
 ]
