@@ -327,6 +327,7 @@ def main() -> int:
                                        "pct_hbm": round(100 * ip_bytes / (ms_ip * 1e-3) / 1e9 / PEAK_HBM_GBS, 2),
                                        "bytes": ip_bytes}
         del kc2, vc2
+        out["sw_cfg"] = sw_cfg_lines(sq, acc, wl, args.sigma, k)
         out["configs"] = other_configs(sq, W, tf)
         clk = clock_under_load(lambda: sq.attn_fwd(q, kx, vx, out=o_dense))
         out["gfx_clock_mhz_under_dense_load"] = clk
@@ -372,6 +373,27 @@ def s_brackets(sq, q, k_glob, v_glob, wl, rho: int, dense_ms: float, tf) -> dict
         t = tf(4.0 * B * H * k * N * d, ms)
         res[name] = {"k": k, "ms": round(ms, 4), "tflops": round(t, 2), "pct_peak": round(100 * t / PEAK_BF16_TFLOPS, 2),
                      "dense_ratio": round(dense_ms / ms, 3)}
+    return res
+
+
+def sw_cfg_lines(sq, acc, wl, sigma: float, k: int) -> dict:
+    """Eq. 20-21 with the normalised score of this input: at the latent size of one image
+    (N tokens x 16 values, fp32: latency-bound) and on 4096 values per token (bandwidth)."""
+    import torch
+    B, N = acc.shape
+    _, s_norm = sq.pcsp_select(acc, wl.grid_h, wl.grid_w, sigma, k, score_out=True)
+    res = {}
+    g = torch.Generator(device="cuda").manual_seed(99)
+    for name, C, reps in (("latent_16", 16, 100), ("wide_4096", 4096, 10)):
+        fc = torch.randn((1, N, C), generator=g, device="cuda")
+        fu = torch.randn((1, N, C), generator=g, device="cuda")
+        o = torch.empty_like(fc)
+        ms = _time_ms(lambda: sq.sw_cfg(fc, fu, 4.0, 7.0, s=s_norm[0], out=o), reps)
+        nbytes = 3 * fc.numel() * 4 + N * 4
+        res[name] = {"shape": [1, N, C], "dtype": "f32", "us": round(ms * 1e3, 2),
+                     "gbs": round(nbytes / (ms * 1e-3) / 1e9, 1),
+                     "pct_hbm": round(100 * nbytes / (ms * 1e-3) / 1e9 / PEAK_HBM_GBS, 2)}
+        del fc, fu, o
     return res
 
 

@@ -37,7 +37,7 @@
 extern "C" {
 #endif
 
-#define SAFE_ABI_VERSION 2
+#define SAFE_ABI_VERSION 3
 
 /* ---- status codes (negative = error) ----------------------------------- */
 enum {
@@ -258,6 +258,39 @@ int64_t safe_attn_workspace_bytes(const safe_attn_args* a);
 
 /* Human-readable name of a status code (static storage). */
 const char* safe_status_str(int status);
+/*
+ * safe_sw_cfg -- sensitivity-weighted classifier-free guidance (Eq. 20, 21).
+ *
+ * For image b, token i and value c (f_c, f_u: conditional and unconditional
+ * predictions, token-major [B, N, C] with C contiguous):
+ *   gamma_i = g_ctx + (g_sens - g_ctx) * s[b, i]     with a score row s (Eq. 20; s is
+ *                                                     the normalised score of Eq. 11)
+ *   gamma_i = g_sens if i is in idx[b], else g_ctx    with an index list (the binary
+ *                                                     variant: S gets g_sens)
+ *   gamma_i = g_ctx                                   with neither (global guidance)
+ *   out[b, i, c] = f_u + gamma_i * (f_c - f_u)        (Eq. 21)
+ * computed in fp32 (one subtraction and one fused multiply-add) and stored in the
+ * tensors' dtype (bf16 rounds to nearest even).  out may alias f_c or f_u.
+ *
+ * dtype         SAFE_DT_BF16 or SAFE_DT_F32 for all three tensors.
+ * stride        element strides of b and i, shared by f_c, f_u and out; C * element
+ *               size must be a multiple of 16 bytes and every row 16-byte aligned.
+ * s             device fp32 [B, N] (sample stride s_bstride; 0 = one row for all).
+ * idx           device int32 [B, k] ascending token indices (sample stride
+ *               idx_bstride; 0 = one list for all); entries outside [0, N) match no
+ *               token.  Give at most one of s and idx.
+ */
+typedef struct {
+  int32_t B, N, C, dtype;
+  const void* f_c; const void* f_u; void* out;   /* [B, N, C] */
+  int64_t stride[2];                            /* b, i (elements) */
+  const float* s; int64_t s_bstride;
+  const int32_t* idx; int32_t k; int64_t idx_bstride;
+  float g_ctx, g_sens;
+} safe_cfg_args;
+
+int safe_sw_cfg(const safe_cfg_args* a, void* stream);
+
 /* SAFE_ABI_VERSION of the built library. */
 int safe_abi_version(void);
 

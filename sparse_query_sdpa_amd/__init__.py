@@ -76,6 +76,15 @@ class AttnArgs(ctypes.Structure):
                 ("flags", ctypes.c_uint32), ("workspace", ctypes.c_void_p), ("workspace_bytes", ctypes.c_int64)]
 
 
+class CfgArgs(ctypes.Structure):
+    _fields_ = [("B", ctypes.c_int32), ("N", ctypes.c_int32), ("C", ctypes.c_int32), ("dtype", ctypes.c_int32),
+                ("f_c", ctypes.c_void_p), ("f_u", ctypes.c_void_p), ("out", ctypes.c_void_p),
+                ("stride", ctypes.c_int64 * 2),
+                ("s", ctypes.c_void_p), ("s_bstride", ctypes.c_int64),
+                ("idx", ctypes.c_void_p), ("k", ctypes.c_int32), ("idx_bstride", ctypes.c_int64),
+                ("g_ctx", ctypes.c_float), ("g_sens", ctypes.c_float)]
+
+
 def _load():
     if not os.path.exists(LIB_PATH):
         raise ImportError(f"libsafe.so not found at {LIB_PATH}: build it with "
@@ -86,6 +95,8 @@ def _load():
     lib.safe_status_str.argtypes = [ctypes.c_int]
     lib.safe_attn_fwd.restype = ctypes.c_int
     lib.safe_attn_fwd.argtypes = [ctypes.POINTER(AttnArgs), ctypes.c_void_p]
+    lib.safe_sw_cfg.restype = ctypes.c_int
+    lib.safe_sw_cfg.argtypes = [ctypes.POINTER(CfgArgs), ctypes.c_void_p]
     lib.safe_attn_workspace_bytes.restype = ctypes.c_int64
     lib.safe_attn_workspace_bytes.argtypes = [ctypes.POINTER(AttnArgs)]
     lib.safe_kv_assemble.restype = ctypes.c_int
@@ -366,5 +377,39 @@ def pcsp_select(acc: torch.Tensor, grid_h: int, grid_w: int, sigma: float, k: in
     return (idx, so) if score_out else idx
 
 
-__all__ = ["attn_fwd", "kv_assemble", "mask_classify", "pcsp_accumulate", "pcsp_select", "lib", "SafeError",
+def sw_cfg(f_c: torch.Tensor, f_u: torch.Tensor, g_ctx: float, g_sens: Optional[float] = None,
+           s: Optional[torch.Tensor] = None, idx: Optional[torch.Tensor] = None,
+           out: Optional[torch.Tensor] = None, stream=None) -> torch.Tensor:
+    """Eq. 20-21: out = f_u + gamma * (f_c - f_u) per token, gamma from the score row s [B, N] (or [N]),
+    from membership in the ascending index list idx [B, k] (or [k]), or g_ctx everywhere."""
+    if f_c.shape != f_u.shape or f_c.dim() != 3 or f_c.dtype != f_u.dtype:
+        raise ValueError("f_c and f_u must be [B, N, C] of one dtype")
+    if f_c.dtype not in (torch.bfloat16, torch.float32):
+        raise ValueError("predictions must be bfloat16 or float32")
+    if f_c.stride() != f_u.stride() or f_c.stride(2) != 1:
+        raise ValueError("f_c and f_u must share strides with C contiguous")
+    B, N, C = f_c.shape
+    if out is None:
+        out = torch.empty_like(f_c)
+    if out.shape != f_c.shape or out.stride() != f_c.stride() or out.dtype != f_c.dtype:
+        raise ValueError("out must match f_c in shape, strides and dtype")
+    a = CfgArgs()
+    a.B, a.N, a.C = B, N, C
+    a.dtype = DT_BF16 if f_c.dtype == torch.bfloat16 else DT_F32
+    a.f_c, a.f_u, a.out = _ptr(f_c), _ptr(f_u), _ptr(out)
+    a.stride[:] = [f_c.stride(0), f_c.stride(1)]
+    if s is not None:
+        if s.dtype != torch.float32 or s.shape[-1] != N or s.stride(-1) != 1:
+            raise ValueError("s must be float32 [B, N] or [N] with contiguous rows")
+        a.s, a.s_bstride = _ptr(s), (s.stride(0) if s.dim() == 2 else 0)
+    idx = _i32(idx, "idx")
+    if idx is not None:
+        a.idx, a.k, a.idx_bstride = _ptr(idx), idx.shape[-1], (idx.stride(0) if idx.dim() == 2 else 0)
+    a.g_ctx = float(g_ctx)
+    a.g_sens = float(g_ctx if g_sens is None else g_sens)
+    _check("safe_sw_cfg", lib.safe_sw_cfg(ctypes.byref(a), _stream(stream)))
+    return out
+
+
+__all__ = ["attn_fwd", "kv_assemble", "mask_classify", "pcsp_accumulate", "pcsp_select", "sw_cfg", "lib", "SafeError",
            "LIB_PATH", "MASK_CLASS_NAMES"]

@@ -9,6 +9,7 @@
 namespace safe {
 int attn_fwd_launch(const safe_attn_args* a, float scale, hipStream_t stream);
 int64_t attn_workspace_bytes(const safe_attn_args* a);
+int sw_cfg_launch(const safe_cfg_args* a, hipStream_t stream);
 int kv_assemble_launch(const safe_kv_args* a, bool in_place, hipStream_t stream);
 int mask_classify_launch(const void* mask, int32_t dtype, const int64_t size[4], const int64_t stride[4],
                          uint32_t flags, safe_mask_info* info, uint8_t* row_class, int32_t* kv_len_out,
@@ -233,6 +234,30 @@ int safe_pcsp_select(const safe_pcsp_args* a, void* workspace, size_t* workspace
   if (workspace != nullptr && !aligned16(workspace)) return SAFE_ERR_ALIGN;
   return pcsp_launch(a, accum ? resolve_scale(a->scale, a->d) : 0.f, workspace,
                      workspace_bytes != nullptr ? *workspace_bytes : 0, static_cast<hipStream_t>(stream));
+}
+
+int safe_sw_cfg(const safe_cfg_args* a, void* stream) {
+  if (a == nullptr) return SAFE_ERR_NULL;
+  if (a->B < 0 || a->N < 0 || a->C < 0) return SAFE_ERR_SHAPE;
+  if (a->dtype != SAFE_DT_BF16 && a->dtype != SAFE_DT_F32) return SAFE_ERR_DTYPE;
+  if (!isfinite(a->g_ctx) || !isfinite(a->g_sens)) return SAFE_ERR_RANGE;
+  if (a->s != nullptr && a->idx != nullptr) return SAFE_ERR_SHAPE;
+  if (a->stride[0] < 0 || a->stride[1] < 0) return SAFE_ERR_SHAPE;
+  if ((int64_t)a->B * a->N * a->C == 0) return SAFE_OK;
+  const int64_t esz = a->dtype == SAFE_DT_BF16 ? 2 : 4;
+  if (a->f_c == nullptr || a->f_u == nullptr || a->out == nullptr) return SAFE_ERR_NULL;
+  if ((a->C * esz) % 16 != 0 || (a->stride[0] * esz) % 16 != 0 || (a->stride[1] * esz) % 16 != 0) return SAFE_ERR_ALIGN;
+  if (!aligned16(a->f_c) || !aligned16(a->f_u) || !aligned16(a->out)) return SAFE_ERR_ALIGN;
+  // token rows and images must not overlap (every row is written once)
+  if (a->N > 1 && a->stride[1] < a->C) return SAFE_ERR_SHAPE;
+  if (a->B > 1 && a->stride[0] < (int64_t)(a->N - 1) * a->stride[1] + a->C) return SAFE_ERR_SHAPE;
+  if (a->s != nullptr && (a->s_bstride < 0 || (a->s_bstride != 0 && a->s_bstride < a->N))) return SAFE_ERR_SHAPE;
+  if (a->idx != nullptr) {
+    if (a->k < 0 || a->idx_bstride < 0 || (a->idx_bstride != 0 && a->idx_bstride < a->k)) return SAFE_ERR_SHAPE;
+  } else if (a->k != 0) {
+    return SAFE_ERR_NULL;
+  }
+  return sw_cfg_launch(a, static_cast<hipStream_t>(stream));
 }
 
 }  // extern "C"

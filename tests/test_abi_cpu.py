@@ -20,7 +20,7 @@ def declared_functions():
 
 def test_header_declares_the_four_entry_points():
     names = declared_functions()
-    for n in ("safe_mask_classify", "safe_pcsp_select", "safe_kv_assemble", "safe_attn_fwd",
+    for n in ("safe_mask_classify", "safe_pcsp_select", "safe_kv_assemble", "safe_attn_fwd", "safe_sw_cfg",
               "safe_attn_workspace_bytes", "safe_status_str", "safe_abi_version"):
         assert n in names
 
@@ -32,7 +32,7 @@ def test_every_declared_symbol_is_exported():
 
 
 def test_abi_version_and_status_strings():
-    assert sq.lib.safe_abi_version() == 2
+    assert sq.lib.safe_abi_version() == 3
     for code, name in sq.STATUS.items():
         assert sq.lib.safe_status_str(code).decode().startswith(name)
     assert sq.lib.safe_status_str(12345) == b"unknown status"
@@ -196,3 +196,28 @@ def test_pcsp_select_workspace_query():
     need = ctypes.c_size_t(0)
     assert sq.lib.safe_pcsp_select(ctypes.byref(a), None, ctypes.byref(need), None) == 0
     assert need.value >= 2 * 2 * 100 * 4
+
+
+def _cfg_args(**kw):
+    a = sq.CfgArgs()
+    a.B, a.N, a.C, a.dtype = 2, 50, 16, sq.DT_F32
+    a.f_c = a.f_u = a.out = 0x10000  # never dereferenced: validation fails or returns first
+    a.stride[:] = [50 * 16, 16]
+    a.g_ctx, a.g_sens = 4.0, 7.0
+    for k, v in kw.items():
+        setattr(a, k, v)
+    return a
+
+
+@pytest.mark.parametrize("kw,status", [
+    (dict(dtype=sq.DT_F16), -3), (dict(B=-1), -2), (dict(f_c=None), -1), (dict(out=None), -1),
+    (dict(C=6), -8), (dict(f_u=0x10008), -8), (dict(g_sens=float("nan")), -4),
+    (dict(s=0x20000, idx=0x30000, k=3), -2), (dict(k=3), -1), (dict(s=0x20000, s_bstride=10), -2),
+    (dict(idx=0x30000, k=5, idx_bstride=2), -2), (dict(stride=(ctypes.c_int64 * 2)(50 * 16, 8)), -2),
+])
+def test_sw_cfg_rejects_bad_arguments_without_gpu(kw, status):
+    assert sq.lib.safe_sw_cfg(ctypes.byref(_cfg_args(**kw)), None) == status
+
+
+def test_sw_cfg_empty_work_is_ok_without_gpu():
+    assert sq.lib.safe_sw_cfg(ctypes.byref(_cfg_args(N=0, f_c=None, f_u=None, out=None)), None) == 0

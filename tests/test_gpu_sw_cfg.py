@@ -1,0 +1,77 @@
+"""GPU parity of safe_sw_cfg against the fp64 oracle (Eq. 20, 21)."""
+import numpy as np
+import pytest
+import torch
+
+import oracle
+import workloads as W
+from gpu_util import dev, to_dev
+
+pytestmark = pytest.mark.gpu
+
+sq = pytest.importorskip("sparse_query_sdpa_amd")
+
+
+def _inputs(B, N, C, seed, dtype):
+    rng = np.random.default_rng(seed)
+    f_c = rng.standard_normal((B, N, C)).astype(np.float32)
+    f_u = rng.standard_normal((B, N, C)).astype(np.float32)
+    if dtype == torch.bfloat16:
+        f_c, f_u = W.bf16_from_f32(f_c).value, W.bf16_from_f32(f_u).value
+    return f_c, f_u, torch.from_numpy(f_c).to(dev()).to(dtype), torch.from_numpy(f_u).to(dev()).to(dtype)
+
+
+def _check(got, ref, dtype):
+    g = got.float().cpu().numpy().astype(np.float64)
+    if dtype == torch.float32:
+        # one fp32 subtraction and one fused multiply-add against exact arithmetic
+        scale = np.abs(ref) + 1.0
+        assert np.all(np.abs(g - ref) <= 4e-6 * scale * 8), float(np.abs(g - ref).max())
+    else:
+        # the fp32 result rounded to bf16 once: within one bf16 step of the exact value
+        ulp = np.maximum(np.abs(ref), 1e-30) * 2.0 ** -7
+        assert np.all(np.abs(g - ref) <= ulp + 1e-6), float((np.abs(g - ref) / ulp).max())
+
+
+@pytest.mark.parametrize("dtype", [torch.bfloat16, torch.float32])
+@pytest.mark.parametrize("B,N,C", [(1, 3, 16), (2, 300, 16), (2, 1000, 64), (3, 77, 8)])
+def test_score_binary_and_global_forms(dtype, B, N, C):
+    if dtype == torch.float32 and C % 4 or dtype == torch.bfloat16 and C % 8:
+        pytest.skip("row not a whole number of 16-byte chunks")
+    f_c, f_u, dc, du = _inputs(B, N, C, 10 + N + C, dtype)
+    rng = np.random.default_rng(N)
+    s = rng.random((B, N)).astype(np.float32)
+    out = sq.sw_cfg(dc, du, 2.0, 7.5, s=to_dev(s))
+    _check(out, oracle.sw_cfg(f_c, f_u, oracle.guidance_scales(s, 2.0, 7.5)), dtype)
+    k = max(1, N // 4)
+    idx = np.stack([np.sort(rng.choice(N, k, replace=False)) for _ in range(B)]).astype(np.int32)
+    out = sq.sw_cfg(dc, du, 2.0, 7.5, idx=to_dev(idx))
+    _check(out, oracle.sw_cfg(f_c, f_u, oracle.binary_scales(idx, B, N, 2.0, 7.5)), dtype)
+    out = sq.sw_cfg(dc, du, 4.5)
+    _check(out, oracle.sw_cfg(f_c, f_u, np.full((B, N), 4.5)), dtype)
+    # shared score row / shared list for every image
+    out = sq.sw_cfg(dc, du, 2.0, 7.5, s=to_dev(s[0]))
+    _check(out, oracle.sw_cfg(f_c, f_u, oracle.guidance_scales(np.broadcast_to(s[0], (B, N)), 2.0, 7.5)), dtype)
+    out = sq.sw_cfg(dc, du, 2.0, 7.5, idx=to_dev(idx[0]))
+    _check(out, oracle.sw_cfg(f_c, f_u, oracle.binary_scales(idx[0], B, N, 2.0, 7.5)), dtype)
+
+
+def test_in_place_strided_and_out_of_range_indices():
+    B, N, C = 2, 129, 16
+    f_c, f_u, dc, du = _inputs(B, N, C, 3, torch.float32)
+    # a padded layout (token stride 24 > C) shared by all three tensors, output over f_c
+    pc = torch.zeros((B, N, 24), device=dev()); pc[..., :C] = dc
+    pu = torch.zeros((B, N, 24), device=dev()); pu[..., :C] = du
+    idx = np.array([-5, 0, 64, 128, 129, 4000], dtype=np.int32)   # out-of-range entries match nothing
+    sq.sw_cfg(pc[..., :C], pu[..., :C], 1.5, 9.0, idx=to_dev(idx), out=pc[..., :C])
+    ref = oracle.sw_cfg(f_c, f_u, oracle.binary_scales(np.array([0, 64, 128]), B, N, 1.5, 9.0))
+    _check(pc[..., :C], ref, torch.float32)
+    assert torch.all(pc[..., C:] == 0), "padding between rows must stay untouched"
+
+
+def test_equal_scales_and_limits_bitwise():
+    B, N, C = 2, 200, 32
+    _, _, dc, du = _inputs(B, N, C, 4, torch.bfloat16)
+    s = torch.rand((B, N), device=dev())
+    assert torch.equal(sq.sw_cfg(dc, du, 3.0, 3.0, s=s), sq.sw_cfg(dc, du, 3.0)), "equal scales = global guidance"
+    assert torch.equal(sq.sw_cfg(dc, du, 0.0), du), "scale 0 gives the unconditional prediction"
