@@ -9,6 +9,8 @@
  *   safe_kv_assemble    Eq. 14,16 global K/V: fresh rows of S over cached context rows
  *   safe_attn_fwd       Eq. 2,16-18 attention on all rows (dense anchor pass) or on the
  *                       gathered rows of S, with optional per-sample valid key lengths
+ *                       (or, for masks the rewrite cannot drop, a dense mask)
+ *   safe_sw_cfg         Eq. 20-21 sensitivity-weighted classifier-free guidance
  *
  * Common conventions
  *   - Tensors are DEVICE pointers owned by the caller; the library never allocates,
@@ -37,7 +39,7 @@
 extern "C" {
 #endif
 
-#define SAFE_ABI_VERSION 3
+#define SAFE_ABI_VERSION 4
 
 /* ---- status codes (negative = error) ----------------------------------- */
 enum {
@@ -202,16 +204,17 @@ typedef struct {
 int safe_kv_assemble(const safe_kv_args* a, void* stream);
 
 /*
- * safe_attn_fwd -- scaled dot-product attention without a mask tensor.
+ * safe_attn_fwd -- scaled dot-product attention, normally without a mask tensor.
  *
  * For each sample b, head h and output row r (query token i = q_rows[b][r], or
  * i = r when q_rows is NULL), with L = kv_len[b] (or Nk):
- *   O[b, r, h, :] = sum_{j < L} softmax_j(scale * q[b,i,h,:] . k[b,j,h,:]) v[b,j,h,:]
+ *   O[b, r, h, :] = sum_{j < L} softmax_j(scale * q[b,i,h,:] . k[b,j,h,:] + m[b,h,i,j]) v[b,j,h,:]
  *   lse[b, h, r]  = natural-log log-sum-exp of those scaled logits
- * This is Eq. 2 with m = empty (also the Eq. 8 rewrite of a removable mask), the
- * SRSU row-selective forms Eq. 16 (self-attention: every key visible) and Eq. 17
- * (cross-attention: text padding kept as the valid length L), and the dense anchor
- * pass of Eq. 18 (q_rows == NULL).  L == 0 gives O = 0 and lse = -inf.
+ * With mask == NULL (m = 0) this is Eq. 2 with m = empty (also the Eq. 8 rewrite of a
+ * removable mask), the SRSU row-selective forms Eq. 16 (self-attention: every key
+ * visible) and Eq. 17 (cross-attention: text padding kept as the valid length L), and
+ * the dense anchor pass of Eq. 18 (q_rows == NULL).  A row with no attended key
+ * (L == 0, or every key blocked by the mask) gives O = 0 and lse = -inf.
  * Inputs bf16; softmax and accumulation in fp32; O is written as bf16.
  *
  * q_rows        device int32 [B, n_rows] (sample stride q_rows_bstride; 0 = one list
@@ -220,8 +223,24 @@ int safe_kv_assemble(const safe_kv_args* a, void* stream);
  * kv_len        device int32 [B] or NULL; values are clamped to [0, Nk].
  * lse           device fp32 [B, H, n_rows], optional.
  * o             bf16; compact [B, n_rows, H, d] unless SAFE_ATTN_SCATTER_OUT.
- * Limits: d in {32, 64, 96, 128}; pointers and strides give 16-byte aligned rows;
+ * Limits: d in {32, 64, 72, 96, 128}; pointers and strides give 16-byte aligned rows;
  * k and v token strides (stride[1]) below 2^25 elements (else SAFE_ERR_UNSUPPORTED).
+ *
+ * mask          optional device mask of Eq. 2 (NULL: none), for masks the Eq. 8 rewrite
+ *               cannot remove and for measuring what the rewrite saves.  Element
+ *               (b, h, i, j) -- i the query TOKEN, not the output row -- is at
+ *               mask + b*mask_stride[0] + h*mask_stride[1] + i*mask_stride[2] + j
+ *               (element strides; 0 broadcasts, e.g. one [Nq, Nk] mask for all b, h
+ *               or a key-only [B, 1, 1, Nk] mask).  mask_dtype: SAFE_DT_BOOL (nonzero
+ *               = attend; blocked keys get -inf), SAFE_DT_BF16, SAFE_DT_F16 or
+ *               SAFE_DT_F32 (additive bias, -inf allowed).  The bias is added in fp32
+ *               as scale * (q . k + bias / scale), so entries beyond about
+ *               FLT_MAX * scale in magnitude act as -inf / +inf.  Strides must be
+ *               multiples of 4 elements and the pointer aligned to 4 elements
+ *               (SAFE_ERR_ALIGN).  Not combinable with kv_len (SAFE_ERR_UNSUPPORTED).
+ *               Rows whose token is outside [0, Nq) read a zero query row and mask
+ *               row 0 of their (b, h).  mask_dtype and mask_stride are ignored when
+ *               mask is NULL.
  *
  * workspace     optional device scratch of workspace_bytes bytes (16-byte aligned),
  *               owned by the caller and not retained.  The rows are processed in
@@ -246,14 +265,16 @@ typedef struct {
   float* lse;
   uint32_t flags;                         /* SAFE_ATTN_SCATTER_OUT | SAFE_FLAG_CHECK */
   void* workspace; int64_t workspace_bytes;   /* optional, see above */
+  const void* mask; int32_t mask_dtype; int64_t mask_stride[3];   /* optional, see above */
 } safe_attn_args;
 
 int safe_attn_fwd(const safe_attn_args* a, void* stream);
 
 /* Workspace bytes that let safe_attn_fwd split the last round of tiles for these
  * arguments on the current device (0: this shape gains nothing from a split, the
- * key-length form is never split, or no device is visible).  The pointer fields are
- * not read.  Negative: the SAFE_ERR_* status safe_attn_fwd would return for the sizes. */
+ * key-length form is never split, or no device is visible).  Of the pointer fields
+ * only whether mask and q_rows are NULL is read.  Negative: the SAFE_ERR_* status
+ * safe_attn_fwd would return for the sizes. */
 int64_t safe_attn_workspace_bytes(const safe_attn_args* a);
 
 /* Human-readable name of a status code (static storage). */

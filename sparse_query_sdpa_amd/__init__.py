@@ -31,6 +31,7 @@ CLASSIFY_ASYNC = 1 << 2
 PCSP_ACCUM = 1 << 3
 PCSP_SELECT = 1 << 4
 
+ABI_VERSION = 4   # struct layouts below match include/safe.h of this version
 DT_BOOL, DT_BF16, DT_F16, DT_F32 = 0, 1, 2, 3
 MASK_CLASS_NAMES = ("ALL_VALID", "ZERO", "ROW_CONST", "KEY_PADDING", "NONCONST", "BLOCKED", "NONFINITE")
 
@@ -73,7 +74,8 @@ class AttnArgs(ctypes.Structure):
                 ("o", ctypes.c_void_p), ("o_stride", _i64x3),
                 ("q_rows", ctypes.c_void_p), ("n_rows", ctypes.c_int32), ("q_rows_bstride", ctypes.c_int64),
                 ("kv_len", ctypes.c_void_p), ("scale", ctypes.c_float), ("lse", ctypes.c_void_p),
-                ("flags", ctypes.c_uint32), ("workspace", ctypes.c_void_p), ("workspace_bytes", ctypes.c_int64)]
+                ("flags", ctypes.c_uint32), ("workspace", ctypes.c_void_p), ("workspace_bytes", ctypes.c_int64),
+                ("mask", ctypes.c_void_p), ("mask_dtype", ctypes.c_int32), ("mask_stride", _i64x3)]
 
 
 class CfgArgs(ctypes.Structure):
@@ -91,6 +93,9 @@ def _load():
                           "`python sparse_query_sdpa_amd/build.py` (no CPU fallback exists)")
     lib = ctypes.CDLL(LIB_PATH)
     lib.safe_abi_version.restype = ctypes.c_int
+    if lib.safe_abi_version() != ABI_VERSION:
+        raise ImportError(f"{LIB_PATH} has ABI version {lib.safe_abi_version()}, this binding needs "
+                          f"{ABI_VERSION}: rebuild with `python sparse_query_sdpa_amd/build.py`")
     lib.safe_status_str.restype = ctypes.c_char_p
     lib.safe_status_str.argtypes = [ctypes.c_int]
     lib.safe_attn_fwd.restype = ctypes.c_int
@@ -176,14 +181,31 @@ def _attn_workspace(a: AttnArgs, device: torch.device, stream_handle) -> Optiona
     return ws
 
 
+def _attn_mask(mask: Optional[torch.Tensor], B: int, H: int, Nq: int, Nk: int):
+    """(pointer, dtype code, element strides of b, h, i) of a [B|1, H|1, Nq|1, Nk] mask."""
+    if mask is None:
+        return None, 0, (0, 0, 0)
+    if mask.dim() != 4 or mask.dtype not in _MASK_DT:
+        raise ValueError("mask must be a 4-D bool/uint8/bfloat16/float16/float32 tensor [B|1, H|1, Nq|1, Nk]")
+    for got, full in zip(mask.shape, (B, H, Nq, Nk)):
+        if got != full and got != 1:
+            raise ValueError(f"mask shape {tuple(mask.shape)} does not broadcast to {(B, H, Nq, Nk)}")
+    if mask.shape[3] != Nk or (Nk > 1 and mask.stride(3) != 1):
+        raise ValueError("mask keys must be the last, contiguous dimension")
+    st = tuple(0 if mask.shape[i] == 1 else mask.stride(i) for i in range(3))
+    return _ptr(mask), _MASK_DT[mask.dtype], st
+
+
 def attn_fwd(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, q_rows: Optional[torch.Tensor] = None,
              kv_len: Optional[torch.Tensor] = None, scale: Optional[float] = None, out: Optional[torch.Tensor] = None,
              return_lse: bool = False, scatter_out: bool = False, check: bool = False, stream=None,
-             workspace="auto"):
+             workspace="auto", mask: Optional[torch.Tensor] = None):
     """Attention on all rows (q_rows None) or on gathered rows q_rows [n] / [B, n]; see safe.h.
 
     workspace: "auto" (a buffer cached per device and stream, sized by
-    safe_attn_workspace_bytes), None (no tail split), or a uint8 device tensor."""
+    safe_attn_workspace_bytes), None (no tail split), or a uint8 device tensor.
+    mask: optional dense mask [B|1, H|1, Nq|1, Nk] (size-1 dims broadcast), indexed by
+    query token; bool/uint8 attend-where-nonzero or an additive bf16/f16/f32 bias."""
     for t, n in ((q, "q"), (k, "k"), (v, "v")):
         _bits16(t, n)
     B, Nq, H, d = q.shape
@@ -210,6 +232,8 @@ def attn_fwd(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, q_rows: Optional
                  _ptr(out), _bnhd(out, "out"), _ptr(q_rows), n_rows, bstride, _ptr(kv_len),
                  0.0 if scale is None else float(scale), _ptr(lse),
                  (ATTN_SCATTER_OUT if scatter_out else 0) | (FLAG_CHECK if check else 0), None, 0)
+    a.mask, a.mask_dtype, ms = _attn_mask(mask, B, H, Nq, Nk)
+    a.mask_stride[:] = ms
     st = _stream(stream)
     if isinstance(workspace, str):
         if workspace != "auto":
@@ -222,7 +246,7 @@ def attn_fwd(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, q_rows: Optional
 
 
 def attn_workspace_bytes(q: torch.Tensor, k: torch.Tensor, q_rows: Optional[torch.Tensor] = None,
-                         kv_len: Optional[torch.Tensor] = None) -> int:
+                         kv_len: Optional[torch.Tensor] = None, mask: Optional[torch.Tensor] = None) -> int:
     """Workspace bytes attn_fwd would use on the current device for these shapes (0: no split)."""
     B, Nq, H, d = q.shape
     if q_rows is None:
@@ -233,6 +257,8 @@ def attn_workspace_bytes(q: torch.Tensor, k: torch.Tensor, q_rows: Optional[torc
     a.B, a.H, a.Nq, a.Nk, a.d, a.n_rows = B, H, Nq, k.shape[1], d, n_rows
     a.q_rows = None if q_rows is None else _ptr(q_rows)
     a.kv_len = None if kv_len is None else _ptr(kv_len)
+    a.mask, a.mask_dtype, ms = _attn_mask(mask, B, a.H, Nq, a.Nk)
+    a.mask_stride[:] = ms
     n = lib.safe_attn_workspace_bytes(ctypes.byref(a))
     if n < 0:
         _check("safe_attn_workspace_bytes", int(n))

@@ -1,0 +1,626 @@
+// Attention forward for gfx950: bf16 MFMA for Q K^T and P V, fp32 online softmax.
+//
+// Computes, per sample b, head h and selected query row, softmax over the valid
+// keys of scale * q . k (+ mask), times V ("SAFE-DiT" Eq. 2; with no mask also the
+// Eq. 8 rewrite of a removable one; Eq. 16 SRSU self-attention on the gathered rows
+// of S; Eq. 17 cross-attention with the text padding kept as a per-sample valid key
+// count; Eq. 18 dense anchor pass).  The masked instances read a dense mask: the
+// call that the rewrite removes, kept for masks outside R.
+//
+// Work decomposition
+//   workgroup = 4 waves = 128 query rows of one (b, h); each wave owns 32 rows;
+//   three workgroups per CU (<= 168 registers per lane; two for d = 128 and for the
+//   masked instances) so the waves on a SIMD overlap one another's MFMA and softmax
+//   work.  Keys stream in tiles of 64 through LDS, double buffered (two separate LDS
+//   objects, loop unrolled by two), one barrier per tile.
+//   K and V tiles are copied global -> LDS by the direct-to-LDS loads
+//   (global_load_lds_dwordx4): no staging registers, no LDS store instructions.
+//   Both tiles keep the natural [key][d] layout; row strides are chosen for
+//   conflict-free LDS reads (see Tile).
+//   Per wave and tile:
+//     S^T[64 keys x 32 queries] = K_tile . Q^T     (v_mfma_f32_32x32x16_bf16)
+//       A = K rows from LDS (ds_read_b128, d contiguous); B = the wave's Q^T,
+//       held in registers for the whole loop.  In the 32x32 accumulator layout
+//       lane l holds query column l%32 and 16 keys, so each lane owns one query
+//       and the row max / row sum need only the partner lane l^32.
+//     O^T[d x 32 queries] += V^T . P^T             (same MFMA)
+//       B = P^T: the lane's own probabilities packed to bf16 in registers.
+//       A = V^T, read with the LDS transpose load ds_read_b64_tr_b16: in each
+//       16-lane group, output lane i element j comes from source lane 4j + i/4,
+//       element i%4; pointing source lane s at V[key0 + s/4][d0 + 4(s%4)] gives
+//       output lane i the four keys key0..key0+3 of column d0 + i, which are
+//       exactly the k-slots the S^T accumulator layout assigns to P^T.
+//   A head dimension that is not a multiple of 16 (d = 72) runs the products on the
+//   next multiples (80 for Q K^T, 96 for P V): the missing Q columns are zero, the
+//   padded K and V columns in LDS hold copies of real data, and O rows past d are
+//   dropped.
+//   Online softmax in the log2 domain with a lazily moved reference max.  A tile's
+//   probabilities are first computed against the current reference, with no tile
+//   max at all; only when some lane's share of the tile sum exceeds 2^16 or is not
+//   finite (always on the first tile, against the initial reference) does the wave take
+//   the exact pair max, move the reference of the rows whose max exceeds it by more
+//   than 2^8 (rescaling O and l), and recompute the tile.  Probabilities stay below
+//   2^16, far inside the range of bf16 P and the fp32 accumulators, and the common
+//   path skips the 32-value max reduction.  The reference starts at -FLT_MAX, not
+//   -inf, so a row whose keys are all masked so far gets exp2(-inf) = 0, not NaN.
+//   The mask, when present, is loaded straight into registers one tile ahead, four
+//   consecutive keys per load (the accumulator layout gives a lane keys in runs of
+//   four), and folded into the scores as s + bias / scale (Boolean: -inf where
+//   blocked) before the softmax.
+//   Workgroups are remapped so all row tiles of one (b, h) sit on one XCD and
+//   share its L2 for the K/V stream.
+#pragma once
+
+#include "common.h"
+
+#include <algorithm>
+#include <atomic>
+#include <cfloat>
+#include <type_traits>
+
+namespace safe {
+
+// mask element type of an instance
+constexpr int kMaskNone = 0, kMaskBool = 1, kMaskBf16 = 2, kMaskF16 = 3, kMaskF32 = 4;
+
+struct AttnParams {
+  const u16* q;
+  const u16* k;
+  const u16* v;
+  u16* o;
+  int64_t qs0, qs1, qs2, ks0, ks1, ks2, vs0, vs1, vs2, os0, os1, os2;
+  const int32_t* q_rows;
+  int64_t qr_bs;
+  const int32_t* kv_len;
+  float* lse;
+  int B, H, Nq, Nk, n_rows, n_row_tiles, total_wg;
+  float scale_log2;
+  int scatter;
+  // Tail split: workgroups [0, n_full) take whole row tiles (logical tiles 0..n_full-1);
+  // workgroup n_full + t takes key range t % nsplit (split_tiles key tiles each) of
+  // logical tile n_full + t / nsplit and leaves unnormalised partials in `part`:
+  // O as fp32 [n_slots][BM][d], then (max, sum) as fp32 [n_slots][BM][2].
+  int n_full, nsplit, split_tiles, n_slots;
+  float* part;
+  // dense mask (masked instances): element (b, h, query token i, key j) at
+  // mask + b*ms0 + h*ms1 + i*ms2 + j elements; bias is added as bias * inv_scale
+  const char* mask;
+  int64_t ms0, ms1, ms2;
+  float inv_scale;
+};
+
+hipError_t attn_masked_dispatch(const AttnParams& p, int d, bool gather, int mt, hipStream_t s);
+int attn_masked_resident(int d, bool gather, int mt);
+
+namespace {
+
+constexpr int BM = 128;       // query rows per workgroup
+constexpr int BN = 64;        // keys per tile
+constexpr int NTHREADS = 256;
+constexpr int NWAVES = NTHREADS / 64;
+constexpr float kRescaleThreshold = 8.0f;  // log2 units
+constexpr float kSumLimit = 65536.0f;          // a lane's tile-sum share above this moves the reference
+
+// LDS tile geometry.  K rows are read 16 bytes per lane, 16 lanes on 16 rows at once:
+// conflict-free on the 64 four-byte banks when the row stride is an odd number of
+// 16-byte chunks.  V rows are read by the transpose load, 4 rows x 32 bytes per
+// 16-lane group: conflict-free when the stride is 64 or 192 bytes modulo 256.
+// K rows hold at least the 2 * KS chunks the Q K^T steps read, V rows the 4 * DB
+// chunks the P V blocks read; chunks past d are padding.
+template <int D>
+struct Tile {
+  static constexpr int CH = D / 8;                                   // 16-byte chunks of a row
+  static constexpr int KS = (D + 15) / 16;                           // k-steps of Q K^T
+  static constexpr int DB = (D + 31) / 32;                           // 32-row blocks of O^T
+  static constexpr int KC = CH > 2 * KS ? CH : 2 * KS;
+  static constexpr int VC = CH > 4 * DB ? CH : 4 * DB;
+  static constexpr int K_SLOTS = KC | 1;                             // odd chunk count
+  static constexpr int V_SLOTS = (VC % 16 == 4 || VC % 16 == 12) ? VC : (VC | 3) + (((VC | 3) % 16 == 7 || (VC | 3) % 16 == 15) ? 5 : 1);
+  static constexpr int K_ROWB = K_SLOTS * 16;
+  static constexpr int V_ROWB = V_SLOTS * 16;
+  static constexpr int K_BYTES = BN * K_ROWB;
+  static constexpr int V_BYTES = BN * V_ROWB;
+  static constexpr int STAGE = K_BYTES + V_BYTES;
+  static constexpr int NCOPY = K_SLOTS + V_SLOTS;                    // wave-wide 1 KB copies per tile
+  static constexpr int PER_WAVE = (NCOPY + NWAVES - 1) / NWAVES;
+  static_assert(D % 8 == 0, "rows are whole 16-byte chunks");
+  static_assert((V_SLOTS % 16) == 4 || (V_SLOTS % 16) == 12, "V stride must be 64 or 192 mod 256 bytes");
+  static_assert(V_SLOTS >= VC && K_SLOTS >= KC, "rows must fit");
+};
+
+// A mask run of four consecutive keys as loaded: 4 bytes (Boolean), 8 (16-bit), 16 (fp32).
+template <int MT> struct MaskRun { typedef u32 type; static constexpr int esz = 1; };
+template <> struct MaskRun<kMaskBf16> { typedef u32x2 type; static constexpr int esz = 2; };
+template <> struct MaskRun<kMaskF16> { typedef u32x2 type; static constexpr int esz = 2; };
+template <> struct MaskRun<kMaskF32> { typedef u32x4 type; static constexpr int esz = 4; };
+
+typedef _Float16 f16x4 __attribute__((ext_vector_type(4)));
+
+// Fold a run into scores sc[4g .. 4g+3]: blocked -> -inf, or + bias * inv_scale.
+// (Whole-vector reinterpretations only.)
+template <int MT>
+__device__ __forceinline__ void fold_run(f32x16& sc, int g, const typename MaskRun<MT>::type& c, float inv_scale) {
+  if constexpr (MT == kMaskBool) {
+#pragma unroll
+    for (int e = 0; e < 4; ++e)
+      if (((c >> (8 * e)) & 0xFFu) == 0u) sc[4 * g + e] = -INFINITY;
+  } else if constexpr (MT == kMaskBf16) {
+    const f32x2 lo = __builtin_bit_cast(f32x2, c << 16);
+    const f32x2 hi = __builtin_bit_cast(f32x2, c & 0xFFFF0000u);
+#pragma unroll
+    for (int k = 0; k < 2; ++k) {
+      sc[4 * g + 2 * k] = __builtin_fmaf(lo[k], inv_scale, sc[4 * g + 2 * k]);
+      sc[4 * g + 2 * k + 1] = __builtin_fmaf(hi[k], inv_scale, sc[4 * g + 2 * k + 1]);
+    }
+  } else if constexpr (MT == kMaskF16) {
+    const f16x4 h = __builtin_bit_cast(f16x4, c);
+#pragma unroll
+    for (int e = 0; e < 4; ++e) sc[4 * g + e] = __builtin_fmaf((float)h[e], inv_scale, sc[4 * g + e]);
+  } else if constexpr (MT == kMaskF32) {
+    const f32x4 f = __builtin_bit_cast(f32x4, c);
+#pragma unroll
+    for (int e = 0; e < 4; ++e) sc[4 * g + e] = __builtin_fmaf(f[e], inv_scale, sc[4 * g + e]);
+  }
+}
+
+typedef __attribute__((address_space(3))) void lds_void;
+typedef short i16x4 __attribute__((ext_vector_type(4)));
+
+__device__ __forceinline__ void copy16_to_lds(const char* src, char* lds_dst) {
+  __builtin_amdgcn_global_load_lds(src, (lds_void*)lds_dst, 16, 0, 0);
+}
+
+__device__ __forceinline__ i16x4 lds_read_tr(const char* p) {
+  return __builtin_amdgcn_ds_read_tr16_b64_v4i16((__attribute__((address_space(3))) i16x4*)p);
+}
+
+template <int D, bool GATHER, bool KVLEN, int MT>
+__global__ __launch_bounds__(NTHREADS, (D >= 128 || MT != kMaskNone) ? 2 : 3) void attn_fwd_kernel(AttnParams p) {
+  using T = Tile<D>;
+  using MR = MaskRun<MT>;
+  typedef typename MR::type MRun;
+  constexpr int KS = T::KS;   // k-steps of the Q K^T product
+  constexpr int DB = T::DB;   // 32-row blocks of O^T
+  constexpr bool HAS_MASK = MT != kMaskNone;
+  // two stages as separate objects: the compiler can then tell a copy into one stage
+  // from reads of the other and does not wait for the copy before those reads
+  __shared__ __attribute__((aligned(1024))) char stage0[T::STAGE];  // K tile, then V tile
+  __shared__ __attribute__((aligned(1024))) char stage1[T::STAGE];
+
+  const int tid = threadIdx.x;
+  const int lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);  // uniform: scalar copy bookkeeping
+  const int col = lane & 31;   // query column owned by this lane
+  const int half = lane >> 5;  // which 8-wide k slice / 4-row group this lane holds
+
+  // whole row tile (slot < 0), or key range [kb0, kb0 + split_tiles * BN) of a tail tile
+  int logical, slot = -1, kb0 = 0;
+  if ((int)blockIdx.x < p.n_full) {
+    logical = xcd_remap(blockIdx.x, p.n_full);
+  } else {
+    slot = (int)blockIdx.x - p.n_full;
+    logical = p.n_full + slot / p.nsplit;
+    kb0 = (slot % p.nsplit) * p.split_tiles * BN;
+  }
+  const int tile = logical % p.n_row_tiles;
+  const int bh = logical / p.n_row_tiles;
+  const int h = bh % p.H;
+  const int b = bh / p.H;
+
+  // ---- this lane's query row --------------------------------------------------
+  const int rr = tile * BM + wave * 32 + col;  // output row (compact index)
+  const bool row_ok = rr < p.n_rows;
+  int qi = rr;
+  if (GATHER) qi = row_ok ? p.q_rows[(int64_t)b * p.qr_bs + rr] : -1;
+  const bool q_ok = row_ok && qi >= 0 && qi < p.Nq;
+
+  bf16x8 qf[KS];
+  {
+    const u16* qp = p.q + (int64_t)b * p.qs0 + (int64_t)(q_ok ? qi : 0) * p.qs1 + (int64_t)h * p.qs2 + half * 8;
+#pragma unroll
+    for (int s = 0; s < KS; ++s) {
+      u32x4 v = {0u, 0u, 0u, 0u};
+      // columns past d (the upper half of the last k-step when d % 16 == 8) stay zero
+      const bool in_row = s * 16 + 16 <= D || half == 0;
+      if (q_ok && in_row) v = ld16(qp + s * 16);
+      qf[s] = as_bf16x8(v);
+    }
+  }
+
+  int nkeys = p.Nk;
+  if (KVLEN) {
+    int L = p.kv_len[b];
+    nkeys = L < 0 ? 0 : (L > p.Nk ? p.Nk : L);
+  }
+  const int kend = slot < 0 ? nkeys : min(nkeys, kb0 + p.split_tiles * BN);
+  const int ntiles = (kend - kb0 + BN - 1) / BN;   // key ranges of splits are never empty
+
+  // ---- per-lane copy plan ------------------------------------------------------
+  // A tile is NCOPY wave-wide copies of 1 KB: copy c < K_SLOTS fills K slots
+  // [64c, 64c + 64), the rest fill V.  Slot sigma is row sigma / SLOTS, chunk
+  // sigma % SLOTS; pad chunks fetch chunk 0 of their row, so every lane is active.
+  // Wave w issues copies c = w + NWAVES * m.  Rounds m < FULL are issued by every
+  // wave and whether a round is K, V or mixed is a compile-time fact, so a full tile
+  // costs one scalar select per mixed round and one uniform branch for the partial
+  // last round: no per-copy branches (a taken branch refetches the wave's
+  // instructions).
+  constexpr int FULL = T::NCOPY / NWAVES;
+  const char* kbase = reinterpret_cast<const char*>(p.k + (int64_t)b * p.ks0 + (int64_t)h * p.ks2);
+  const char* vbase = reinterpret_cast<const char*>(p.v + (int64_t)b * p.vs0 + (int64_t)h * p.vs2);
+  const int64_t krow_b = p.ks1 * 2, vrow_b = p.vs1 * 2;   // bytes between consecutive keys
+  uint32_t coff[T::PER_WAVE];                               // byte offset of this lane's chunk in a tile
+#pragma unroll
+  for (int m = 0; m < T::PER_WAVE; ++m) {
+    const int c = wave + NWAVES * m;
+    const bool isk = c < T::K_SLOTS;
+    const int slots = isk ? T::K_SLOTS : T::V_SLOTS;
+    const int sigma = (isk ? c : c - T::K_SLOTS) * 64 + lane;
+    const int row = sigma / slots;
+    int chunk = sigma % slots;
+    if (chunk >= T::CH) chunk = 0;
+    coff[m] = (uint32_t)(row * (isk ? krow_b : vrow_b) + chunk * 16);
+  }
+  auto issue_tile = [&](int j0, char* stage) {
+    const char* kb = kbase + (int64_t)j0 * krow_b;
+    const char* vb = vbase + (int64_t)j0 * vrow_b;
+    const int nrow_valid = nkeys - j0;
+    if (nrow_valid >= BN) {
+      // The empty asm statements redefine the offsets in place each tile: the 32-bit
+      // lane offsets are then not widened and hoisted out of the loop (the copy keeps
+      // the scalar-base form, base in SGPRs + 32-bit lane offset), and the LDS
+      // destinations are one scalar add each instead of precomputed registers.
+      int wlds = wave * 1024;
+      asm volatile("" : "+s"(wlds));
+#pragma unroll
+      for (int m = 0; m < T::PER_WAVE; ++m) {
+        const int c = wave + NWAVES * m;
+        const bool all_k = NWAVES * m + NWAVES - 1 < T::K_SLOTS;  // compile-time per unrolled m
+        const bool all_v = NWAVES * m >= T::K_SLOTS;
+        const char* base = all_k ? kb : (all_v ? vb : (c < T::K_SLOTS ? kb : vb));
+        asm volatile("" : "+v"(coff[m]));
+        if (m < FULL || c < T::NCOPY) copy16_to_lds(base + coff[m], stage + wlds + m * NWAVES * 1024);
+      }
+    } else {
+      // last, partial tile: rows past the valid keys fetch row 0 of the tile instead
+      // (lane laundered so none of this is hoisted into registers live across the loop)
+      int ln = lane, wv = wave;
+      asm volatile("" : "+v"(ln), "+s"(wv));
+#pragma unroll
+      for (int m = 0; m < T::PER_WAVE; ++m) {
+        const int c = wv + NWAVES * m;
+        if (c < T::NCOPY) {
+          const bool isk = c < T::K_SLOTS;
+          const int row = ((isk ? c : c - T::K_SLOTS) * 64 + ln) / (isk ? T::K_SLOTS : T::V_SLOTS);
+          const uint32_t off = row < nrow_valid ? coff[m] : coff[m] - (uint32_t)(row * (isk ? krow_b : vrow_b));
+          copy16_to_lds((isk ? kb : vb) + off, stage + c * 1024);
+        }
+      }
+    }
+  };
+
+  // ---- mask runs: run i of a tile covers keys 32 (i / 4) + 8 (i % 4) + 4 half + 0..3 ----
+  const char* mrow = nullptr;
+  if constexpr (HAS_MASK)
+    mrow = p.mask + ((int64_t)b * p.ms0 + (int64_t)h * p.ms1 + (int64_t)(q_ok ? qi : 0) * p.ms2 + 4 * half) * MR::esz;
+  auto load_runs = [&](int j0, MRun (&r)[8]) {        // a whole tile: every key valid
+#pragma unroll
+    for (int i = 0; i < 8; ++i)
+      r[i] = *reinterpret_cast<const MRun*>(mrow + (int64_t)(j0 + 32 * (i >> 2) + 8 * (i & 3)) * MR::esz);
+  };
+  auto load_runs_partial = [&](int j0, MRun (&r)[8]) {   // element loads below nkeys
+#pragma unroll
+    for (int i = 0; i < 8; ++i) {
+      MRun c = {};
+      if constexpr (MT == kMaskBool) c = 0x01010101u;   // neutral: attend (masked by length later)
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        const int rel = 32 * (i >> 2) + 8 * (i & 3) + e;
+        if (j0 + 4 * half + rel < nkeys) {
+          const char* ep = mrow + (int64_t)(j0 + rel) * MR::esz;
+          if constexpr (MT == kMaskBool) {
+            c = (c & ~(0xFFu << (8 * e))) | ((u32)*reinterpret_cast<const unsigned char*>(ep) << (8 * e));
+          } else if constexpr (MT != kMaskNone && MR::esz == 2) {
+            c[e >> 1] |= (u32)*reinterpret_cast<const u16*>(ep) << (16 * (e & 1));
+          } else if constexpr (MR::esz == 4) {
+            c[e] = *reinterpret_cast<const u32*>(ep);
+          }
+        }
+      }
+      r[i] = c;
+    }
+  };
+
+  f32x16 oacc[DB];
+#pragma unroll
+  for (int i = 0; i < DB; ++i) oacc[i] = f32x16{};
+  float m_ref = -FLT_MAX;   // reference max, log2 domain (-FLT_MAX: none yet)
+  float l_run = 0.f;        // this lane's share of the row sum
+  const float sl2 = p.scale_log2;
+
+  // LDS addresses of this lane's operand reads (byte offsets inside a tile)
+  const int k_lane = col * T::K_ROWB + half * 16;
+  const int grp = (lane >> 4) & 3, src = lane & 15;
+  const int v_lane = (4 * (grp >> 1) + (src >> 2)) * T::V_ROWB + (16 * (grp & 1) + 4 * (src & 3)) * 2;
+
+  // Per-lane pieces of a tile.  A tile's two 32-key halves are independent once
+  // scores exist: probabilities are taken against the current reference, so the
+  // softmax of one half can run between the MFMAs of the other half.
+  auto s_half = [&](const char* Kt, int blk) -> f32x16 {   // S^T rows blk*32.. of the tile
+    f32x16 acc = f32x16{};
+#pragma unroll
+    for (int s = 0; s < KS; ++s) {
+      const bf16x8 kf = as_bf16x8(ld16(Kt + k_lane + blk * 32 * T::K_ROWB + s * 32));
+      acc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kf, qf[s], acc, 0, 0, 0);
+    }
+    return acc;
+  };
+  auto fold_half = [&](f32x16& sc, int blk, const MRun (&r)[8]) {
+    if constexpr (HAS_MASK) {
+#pragma unroll
+      for (int g = 0; g < 4; ++g) fold_run<MT>(sc, g, r[4 * blk + g], p.inv_scale);
+    }
+  };
+  // bf16 P^T operands of one half and this lane's share of its sum
+  auto probs_half = [&](const f32x16& sc, bf16x8 (&pb)[2]) -> float {
+    float ts = 0.f;
+#pragma unroll
+    for (int t = 0; t < 2; ++t) {
+      u32x4 packed;
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        const float p0 = __builtin_amdgcn_exp2f(__builtin_fmaf(sc[8 * t + 2 * e], sl2, -m_ref));
+        const float p1 = __builtin_amdgcn_exp2f(__builtin_fmaf(sc[8 * t + 2 * e + 1], sl2, -m_ref));
+        packed[e] = pack_bf16x2(p0, p1);
+        ts += p0 + p1;
+      }
+      pb[t] = as_bf16x8(packed);
+    }
+    return ts;
+  };
+  // Reference move (rare, wave-uniform): the first half-tile (reference -FLT_MAX gives
+  // +inf), or a half whose probabilities grew past 2^16 / 16 somewhere.  The rows
+  // whose pair max exceeds the reference by more than 2^8 move it; O and l (which
+  // hold every earlier half) are rescaled and the half is recomputed.  A row whose
+  // keys are all blocked so far (-inf scores) keeps the reference at -FLT_MAX, its
+  // probabilities exp2(-inf) = 0 and O and l zero.
+  auto settle_half = [&](const f32x16& sc, bf16x8 (&pb)[2], float ts) -> float {
+    if (__any(!(ts <= kSumLimit))) {
+      float mt = sc[0];
+#pragma unroll
+      for (int r = 1; r < 16; ++r) mt = fmaxf(mt, sc[r]);
+      mt = fmaxf(mt, __shfl_xor(mt, 32));
+      const float mt2 = mt * sl2;
+      const bool move = mt2 > m_ref + kRescaleThreshold;
+      const float m_new = move ? mt2 : m_ref;
+      const float alpha = __builtin_amdgcn_exp2f(m_ref - m_new);  // 0 on the first move
+      l_run *= alpha;
+#pragma unroll
+      for (int i = 0; i < DB; ++i) oacc[i] *= alpha;
+      m_ref = m_new;
+      ts = probs_half(sc, pb);
+    }
+    return ts;
+  };
+  auto pv_half = [&](const char* Vt, int blk, const bf16x8 (&pb)[2]) {   // O^T += V^T P^T, one half
+#pragma unroll
+    for (int db = 0; db < DB; ++db)
+#pragma unroll
+      for (int t = 0; t < 2; ++t) {
+        const char* vp = Vt + v_lane + (blk * 32 + t * 16) * T::V_ROWB + db * 64;
+        const i16x4 lo = lds_read_tr(vp);
+        const i16x4 hi = lds_read_tr(vp + 8 * T::V_ROWB);
+        const bf16x8 vf = __builtin_bit_cast(bf16x8, __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7));
+        oacc[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(vf, pb[t], oacc[db], 0, 0, 0);
+      }
+  };
+  // keys past the valid length get -inf (the partial last tile only)
+  auto mask_half = [&](f32x16& sc, int j0, int blk) {
+#pragma unroll
+    for (int r = 0; r < 16; ++r) {
+      const int key = j0 + blk * 32 + 8 * (r >> 2) + 4 * half + (r & 3);
+      if (key >= nkeys) sc[r] = -INFINITY;
+    }
+  };
+
+  // One tile: wait for its copies (and mask runs), start the next tile's copies into
+  // the other stage (and its mask runs into the other register set), then S^T half 0;
+  // [S^T half 1 | softmax half 0]; [PV half 0 | softmax half 1]; PV half 1.  Each
+  // bracket is one basic block, so the scheduler interleaves the MFMAs of one half
+  // with the VALU work of the other; the rare reference moves sit between them.
+  // MASKED is the partial last tile: it loads its own mask runs, masks by length and
+  // issues no copies.
+  auto tile_step = [&](auto masked, int it, const char* cur, char* nxt, MRun (&mc)[8], MRun (&mn)[8]) {
+    constexpr bool MASKED = decltype(masked)::value;
+    const int j0 = kb0 + it * BN;
+    __builtin_amdgcn_s_waitcnt(0x0F70);  // vmcnt(0): this wave's copies of tile `it` landed
+    __syncthreads();                     // ... everyone's, and tile it-1 is no longer read
+    if constexpr (!MASKED) {
+      if (it + 1 < ntiles) {
+        issue_tile(j0 + BN, nxt);
+        if constexpr (HAS_MASK) {
+          if (j0 + 2 * BN <= kend) load_runs(j0 + BN, mn);
+        }
+      }
+    } else if constexpr (HAS_MASK) {
+      load_runs_partial(j0, mc);
+    }
+    const char* Kt = cur;
+    const char* Vt = cur + T::K_BYTES;
+
+    f32x16 s0 = s_half(Kt, 0);
+    fold_half(s0, 0, mc);
+    if constexpr (MASKED) mask_half(s0, j0, 0);
+    bf16x8 pb0[2], pb1[2];
+    __builtin_amdgcn_sched_barrier(0);
+    f32x16 s1 = s_half(Kt, 1);
+    fold_half(s1, 1, mc);
+    if constexpr (MASKED) mask_half(s1, j0, 1);
+    float ts0 = probs_half(s0, pb0);
+    __builtin_amdgcn_sched_barrier(0);
+    ts0 = settle_half(s0, pb0, ts0);
+    l_run += ts0;
+    pv_half(Vt, 0, pb0);
+    float ts1 = probs_half(s1, pb1);
+    __builtin_amdgcn_sched_barrier(0);
+    ts1 = settle_half(s1, pb1, ts1);
+    l_run += ts1;
+    pv_half(Vt, 1, pb1);
+  };
+
+  const std::integral_constant<bool, false> kFull;
+  const std::integral_constant<bool, true> kMasked;
+  MRun mA[8], mB[8];   // mask runs of the even / odd tiles (unused without a mask)
+  const int nfull = (kend - kb0) / BN;   // tiles whose 64 keys are all valid
+  if (ntiles > 0) issue_tile(kb0, stage0);
+  if constexpr (HAS_MASK) {
+    if (nfull > 0) load_runs(kb0, mA);
+  }
+  int it = 0;
+  for (; it + 2 <= nfull; it += 2) {
+    tile_step(kFull, it, stage0, stage1, mA, mB);
+    tile_step(kFull, it + 1, stage1, stage0, mB, mA);
+  }
+  if (it < nfull) {
+    tile_step(kFull, it, stage0, stage1, mA, mB);
+    ++it;
+  }
+  if (it < ntiles) tile_step(kMasked, it, (it & 1) ? stage1 : stage0, nullptr, mA, mB);
+
+  // ---- epilogue: normalise, store O (bf16) and LSE ------------------------------
+  const float l_tot = l_run + __shfl_xor(l_run, 32);
+  if (!row_ok) return;
+  if (slot >= 0) {  // partial of a split tile: unnormalised O and this range's (max, sum)
+    const int rloc = wave * 32 + col;
+    float* po = p.part + ((int64_t)slot * BM + rloc) * D;
+#pragma unroll
+    for (int db = 0; db < DB; ++db)
+#pragma unroll
+      for (int g = 0; g < 4; ++g) {
+        if (db * 32 + 8 * g >= D) continue;   // padded O rows (d % 32 != 0)
+        const f32x4 w = {oacc[db][4 * g + 0], oacc[db][4 * g + 1], oacc[db][4 * g + 2], oacc[db][4 * g + 3]};
+        st16(po + db * 32 + 8 * g + 4 * half, __builtin_bit_cast(u32x4, w));
+      }
+    if (half == 0) {
+      float* pm = p.part + (int64_t)p.n_slots * BM * D + ((int64_t)slot * BM + rloc) * 2;
+      pm[0] = m_ref;
+      pm[1] = l_tot;
+    }
+    return;
+  }
+  const float inv = l_tot > 0.f ? 1.0f / l_tot : 0.f;
+  const int orow = (GATHER && p.scatter) ? qi : rr;
+  if (!GATHER || !p.scatter || q_ok) {
+    u16* op = p.o + (int64_t)b * p.os0 + (int64_t)orow * p.os1 + (int64_t)h * p.os2;
+#pragma unroll
+    for (int db = 0; db < DB; ++db)
+#pragma unroll
+      for (int g = 0; g < 4; ++g) {
+        if (db * 32 + 8 * g >= D) continue;   // padded O rows (d % 32 != 0)
+        u32x2 w;
+        w[0] = pack_bf16x2(oacc[db][4 * g + 0] * inv, oacc[db][4 * g + 1] * inv);
+        w[1] = pack_bf16x2(oacc[db][4 * g + 2] * inv, oacc[db][4 * g + 3] * inv);
+        st8(op + db * 32 + 8 * g + 4 * half, w);
+      }
+  }
+  if (p.lse != nullptr && half == 0) {
+    const float lse = l_tot > 0.f ? (m_ref + __builtin_log2f(l_tot)) * 0.69314718055994530942f : -INFINITY;
+    p.lse[((int64_t)b * p.H + h) * p.n_rows + rr] = lse;
+  }
+}
+
+// Merge the key-range partials of each split tail tile: M = max of the ranges' maxima,
+// L = sum of their sums scaled by 2^(max - M), O = sum of their O scaled the same way
+// over L; the same output rules as the whole-tile epilogue.  A workgroup takes 32 rows
+// of a tile, MergeShape<D>::TPR threads per row, each owning DT consecutive columns.
+constexpr int MERGE_ROWS = 32;
+template <int D>
+struct MergeShape {
+  static constexpr int TPR = D % 32 == 0 ? 8 : 6;   // threads per row
+  static constexpr int DT = D / TPR;                // columns per thread: 4, 8, 12 or 16
+  static_assert(D % (4 * TPR) == 0, "whole 4-column groups per thread");
+};
+template <int D, bool GATHER>
+__global__ __launch_bounds__(MERGE_ROWS * 8) void attn_merge_kernel(AttnParams p) {
+  constexpr int TPR = MergeShape<D>::TPR;
+  constexpr int DT = MergeShape<D>::DT;
+  const int ti = blockIdx.x;
+  const int logical = p.n_full + ti;
+  const int tile = logical % p.n_row_tiles;
+  const int bh = logical / p.n_row_tiles;
+  const int h = bh % p.H;
+  const int b = bh / p.H;
+  const int rloc = blockIdx.y * MERGE_ROWS + threadIdx.x / TPR;
+  const int part = threadIdx.x % TPR;
+  const int rr = tile * BM + rloc;
+  if (rr >= p.n_rows) return;
+  int qi = rr;
+  if (GATHER) qi = p.q_rows[(int64_t)b * p.qr_bs + rr];
+  const bool q_ok = qi >= 0 && qi < p.Nq;
+
+  const float* pml = p.part + (int64_t)p.n_slots * BM * D;
+  float M = -INFINITY;
+  for (int s = 0; s < p.nsplit; ++s) M = fmaxf(M, pml[((int64_t)(ti * p.nsplit + s) * BM + rloc) * 2]);
+  float acc[DT];
+#pragma unroll
+  for (int i = 0; i < DT; ++i) acc[i] = 0.f;
+  float L = 0.f;
+  for (int s = 0; s < p.nsplit; ++s) {
+    const int64_t sl = (int64_t)(ti * p.nsplit + s) * BM + rloc;
+    const float w = M == -INFINITY ? 0.f : __builtin_amdgcn_exp2f(pml[sl * 2] - M);
+    L += w * pml[sl * 2 + 1];
+    const float* po = p.part + sl * D + part * DT;
+#pragma unroll
+    for (int i = 0; i < DT; i += 4) {
+      const f32x4 v = __builtin_bit_cast(f32x4, ld16(po + i));
+      acc[i] += w * v[0]; acc[i + 1] += w * v[1]; acc[i + 2] += w * v[2]; acc[i + 3] += w * v[3];
+    }
+  }
+  const float inv = L > 0.f ? 1.0f / L : 0.f;
+  const int orow = (GATHER && p.scatter) ? qi : rr;
+  if (!GATHER || !p.scatter || q_ok) {
+    u16* op = p.o + (int64_t)b * p.os0 + (int64_t)orow * p.os1 + (int64_t)h * p.os2 + part * DT;
+#pragma unroll
+    for (int i = 0; i < DT; i += 4) {
+      u32x2 w;
+      w[0] = pack_bf16x2(acc[i] * inv, acc[i + 1] * inv);
+      w[1] = pack_bf16x2(acc[i + 2] * inv, acc[i + 3] * inv);
+      st8(op + i, w);
+    }
+  }
+  if (p.lse != nullptr && part == 0) {
+    const float lse = L > 0.f ? (M + __builtin_log2f(L)) * 0.69314718055994530942f : -INFINITY;
+    p.lse[((int64_t)b * p.H + h) * p.n_rows + rr] = lse;
+  }
+}
+
+template <int D, bool G, bool KV, int MT>
+hipError_t launch(const AttnParams& p, hipStream_t s) {
+  hipLaunchKernelGGL((attn_fwd_kernel<D, G, KV, MT>), dim3(p.total_wg), dim3(NTHREADS), 0, s, p);
+  hipError_t e = hipGetLastError();
+  if (e != hipSuccess || p.n_slots == 0) return e;
+  hipLaunchKernelGGL((attn_merge_kernel<D, G>), dim3(p.n_slots / p.nsplit, BM / MERGE_ROWS),
+                     dim3(MERGE_ROWS * MergeShape<D>::TPR), 0, s, p);
+  return hipGetLastError();
+}
+
+// Workgroups of one kernel instance resident on the whole device (0 if unknown).
+// Cached per device and instance; racing first calls store the same value.
+template <int D, bool G, bool KV, int MT>
+int resident_workgroups() {
+  constexpr int kMaxDev = 64;
+  static std::atomic<int> cache[kMaxDev];
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= kMaxDev) return 0;
+  int v = cache[dev].load(std::memory_order_relaxed);
+  if (v > 0) return v;
+  int per_cu = 0, cus = 0;
+  if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, attn_fwd_kernel<D, G, KV, MT>, NTHREADS, 0) != hipSuccess ||
+      hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess)
+    return 0;
+  v = per_cu * cus;
+  if (v > 0) cache[dev].store(v, std::memory_order_relaxed);
+  return v;
+}
+
+}  // namespace
+}  // namespace safe

@@ -32,7 +32,7 @@ def test_every_declared_symbol_is_exported():
 
 
 def test_abi_version_and_status_strings():
-    assert sq.lib.safe_abi_version() == 3
+    assert sq.lib.safe_abi_version() == 4 == sq.ABI_VERSION
     for code, name in sq.STATUS.items():
         assert sq.lib.safe_status_str(code).decode().startswith(name)
     assert sq.lib.safe_status_str(12345) == b"unknown status"
@@ -85,6 +85,28 @@ def test_attn_workspace_arguments_without_gpu():
     assert sq.lib.safe_attn_workspace_bytes(ctypes.byref(_attn_args(kv_len=0x30000))) == 0  # never split
     assert sq.lib.safe_attn_fwd(ctypes.byref(_attn_args(workspace_bytes=-1)), None) == -6
     assert sq.lib.safe_attn_fwd(ctypes.byref(_attn_args(workspace=0x40004, workspace_bytes=64)), None) == -8
+
+
+def test_attn_mask_arguments_without_gpu():
+    m = 0x60000
+    assert sq.lib.safe_attn_fwd(ctypes.byref(_attn_args(mask=m, mask_dtype=7)), None) == -3
+    assert sq.lib.safe_attn_fwd(ctypes.byref(_attn_args(mask=m, mask_dtype=-1)), None) == -3
+    assert sq.lib.safe_attn_fwd(ctypes.byref(_attn_args(mask=m, mask_dtype=1, kv_len=0x30000)), None) == -5
+    for i, bad, status in ((2, 130, -8), (0, -4, -2), (1, 2, -8)):
+        a = _attn_args(mask=m, mask_dtype=1)
+        a.mask_stride[:] = [128 * 128, 0, 128]
+        a.mask_stride[i] = bad
+        assert sq.lib.safe_attn_fwd(ctypes.byref(a), None) == status
+    # runs of four elements: pointer aligned to 4 elements of the mask's type
+    for dtype, ptr in ((0, m + 2), (1, m + 4), (2, m + 4), (3, m + 8)):
+        a = _attn_args(mask=ptr, mask_dtype=dtype)
+        a.mask_stride[:] = [0, 0, 128]
+        assert sq.lib.safe_attn_fwd(ctypes.byref(a), None) == -8, dtype
+    # the size query checks the mask fields too; a NULL mask ignores them
+    assert sq.lib.safe_attn_workspace_bytes(ctypes.byref(_attn_args(mask=m, mask_dtype=9))) == -3
+    assert sq.lib.safe_attn_workspace_bytes(ctypes.byref(_attn_args(mask_dtype=9))) >= 0
+    # d = 72 is a supported head dimension (the size query runs without a device)
+    assert sq.lib.safe_attn_workspace_bytes(ctypes.byref(_attn_args(d=72))) >= 0
 
 
 def test_attn_empty_work_is_ok_without_gpu():

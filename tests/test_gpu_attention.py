@@ -38,7 +38,7 @@ def test_tiny_srsu_self_and_cross():
     assert_attn_close(o, ref, "tiny cross")
 
 
-@pytest.mark.parametrize("d", [32, 64, 96, 128])
+@pytest.mark.parametrize("d", [32, 64, 72, 96, 128])
 def test_ragged_shapes_rows_lengths(d):
     B, Nq, Nk, H = 4, 301, 333, 3
     q, k, v = W.attention_inputs(B, Nq, Nk, H, d, seed=100 + d)

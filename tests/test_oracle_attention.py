@@ -13,8 +13,11 @@ import workloads as W
 GOLD = os.path.join(os.path.dirname(__file__), "golden")
 
 
-def torch_sdpa_f64(q, k, v, q_rows=None, kv_len=None, scale=None):
-    """torch's CPU float64 scaled_dot_product_attention on BNHD inputs (library routine)."""
+def torch_sdpa_f64(q, k, v, q_rows=None, kv_len=None, scale=None, attn_mask=None):
+    """torch's CPU float64 scaled_dot_product_attention on BNHD inputs (library routine).
+
+    attn_mask: a [B|1, H|1, Nq, Nk] bool (True = attend) or additive float64 mask over the
+    full query range; it is gathered to the selected rows here."""
     q = torch.from_numpy(np.asarray(q, dtype=np.float64))
     k = torch.from_numpy(np.asarray(k, dtype=np.float64))
     v = torch.from_numpy(np.asarray(v, dtype=np.float64))
@@ -31,6 +34,12 @@ def torch_sdpa_f64(q, k, v, q_rows=None, kv_len=None, scale=None):
     if kv_len is not None:
         mask = torch.arange(Nk)[None, :] < torch.as_tensor(np.asarray(kv_len))[:, None]   # True = attend
         mask = mask[:, None, None, :]
+    if attn_mask is not None:
+        mask = torch.as_tensor(np.asarray(attn_mask))
+        if q_rows is not None:
+            r = np.asarray(q_rows)
+            mask = mask.expand(B, -1, -1, -1)
+            mask = torch.stack([mask[b][:, torch.as_tensor(r if r.ndim == 1 else r[b])] for b in range(B)])
     o = torch.nn.functional.scaled_dot_product_attention(
         q.permute(0, 2, 1, 3), k.permute(0, 2, 1, 3), v.permute(0, 2, 1, 3), attn_mask=mask, scale=scale)
     return o.permute(0, 2, 1, 3).numpy()
@@ -164,3 +173,41 @@ def test_bruteforce_tiny_workload_rows():
     ob, _ = oracle.sdpa_bruteforce(inp["q_c"].value, inp["k_txt"].value, inp["v_txt"].value, q_rows=rows,
                                    kv_len=inp["kv_len"])
     np.testing.assert_allclose(o, np.asarray(ob), rtol=0, atol=1e-12)
+
+
+@pytest.mark.parametrize("seed", [0, 1])
+def test_general_mask_matches_torch_sdpa_f64(seed):
+    """Eq. 2 with a dense mask: additive (finite values and -inf) and Boolean, on all rows
+    and on gathered rows (the mask is indexed by the query token)."""
+    rng = np.random.default_rng(100 + seed)
+    B, Nq, Nk, H, d = 2, 19, 23, 3, 8
+    q = rng.standard_normal((B, Nq, H, d))
+    k = rng.standard_normal((B, Nk, H, d))
+    v = rng.standard_normal((B, Nk, H, d))
+    add = rng.uniform(-4, 4, size=(B, 1, Nq, Nk))
+    add[rng.random(add.shape) < 0.3] = -np.inf
+    add[..., 0] = rng.uniform(-1, 1, size=(B, 1, Nq))   # every row keeps a key (torch gives NaN otherwise)
+    keep = rng.random((1, H, Nq, Nk)) < 0.6
+    keep[..., 5] = True
+    rows = np.sort(rng.choice(Nq, 7, replace=False))
+    for m_oracle, m_torch in ((add, add), (oracle.mask.to_additive(keep, True), keep)):
+        o, _ = oracle.sdpa(q, k, v, mask=m_oracle)
+        np.testing.assert_allclose(o, torch_sdpa_f64(q, k, v, attn_mask=m_torch), rtol=0, atol=1e-12)
+        o, _ = oracle.sdpa(q, k, v, q_rows=rows, mask=m_oracle)
+        np.testing.assert_allclose(o, torch_sdpa_f64(q, k, v, q_rows=rows, attn_mask=m_torch), rtol=0, atol=1e-12)
+
+
+def test_fully_blocked_mask_row_reading():
+    """A row whose every key is blocked has no distribution: output 0 and LSE -inf (the
+    same reading as kv_len = 0); the other rows are untouched."""
+    rng = np.random.default_rng(7)
+    B, N, H, d = 1, 6, 2, 4
+    q, k, v = (rng.standard_normal((B, N, H, d)) for _ in range(3))
+    m = np.zeros((1, 1, N, N))
+    m[0, 0, 2, :] = -np.inf
+    o, lse = oracle.sdpa(q, k, v, mask=m)
+    o0, lse0 = oracle.sdpa(q, k, v)
+    assert np.all(o[:, 2] == 0) and np.all(lse[:, :, 2] == -np.inf)
+    keep = np.ones(N, bool)
+    keep[2] = False
+    assert np.array_equal(o[:, keep], o0[:, keep]) and np.array_equal(lse[..., keep], lse0[..., keep])
