@@ -328,6 +328,7 @@ def main() -> int:
                                        "bytes": ip_bytes}
         del kc2, vc2
         out["sw_cfg"] = sw_cfg_lines(sq, acc, wl, args.sigma, k)
+        out["midt"] = midt_lines(sq, q, kx, vx, mask, idx, stage_ms, tf)
         out["configs"] = other_configs(sq, W, tf)
         clk = clock_under_load(lambda: sq.attn_fwd(q, kx, vx, out=o_dense))
         out["gfx_clock_mhz_under_dense_load"] = clk
@@ -373,6 +374,46 @@ def s_brackets(sq, q, k_glob, v_glob, wl, rho: int, dense_ms: float, tf) -> dict
         t = tf(4.0 * B * H * k * N * d, ms)
         res[name] = {"k": k, "ms": round(ms, 4), "tflops": round(t, 2), "pct_peak": round(100 * t / PEAK_BF16_TFLOPS, 2),
                      "dense_ratio": round(dense_ms / ms, 3)}
+    return res
+
+
+def midt_lines(sq, q, kx, vx, mask, idx, stage_ms: dict, tf) -> dict:
+    """What dropping a removable mask saves on this stack: the masked kernel (reading the
+    [2,1,N,N] bf16 all-valid additive mask, or a [2,1,1,N] Boolean key mask) against the
+    mask-free call, at the workload's d=96/H=24 and at d=72/H=32 (the same model width)."""
+    import torch
+    B, N, H, d = q.shape
+    k = idx.shape[1]
+    res = {"mask": "[%d,1,%d,%d] bf16 zeros, %.2f GB" % (B, N, N, mask.numel() * 2 / 1e9),
+           "classify_ms": round(stage_ms["classify"], 4)}
+    o_d = torch.empty_like(q)
+    o_s = torch.empty((B, k, H, d), dtype=torch.bfloat16, device=q.device)
+    key_mask = torch.ones((B, 1, 1, N), dtype=torch.bool, device=q.device)
+    ms_dm = _time_ms(lambda: sq.attn_fwd(q, kx, vx, mask=mask, out=o_d), 3)
+    ms_dk = _time_ms(lambda: sq.attn_fwd(q, kx, vx, mask=key_mask, out=o_d), 3)
+    ms_sm = _time_ms(lambda: sq.attn_fwd(q, kx, vx, q_rows=idx, mask=mask, out=o_s), 5)
+    fl_d, fl_s = 4.0 * B * H * N * N * d, 4.0 * B * H * k * N * d
+    res["d96_h24"] = {
+        "dense_ms": round(stage_ms["dense"], 4),
+        "dense_masked_ms": round(ms_dm, 4), "dense_masked_tflops": round(tf(fl_d, ms_dm), 2),
+        "dense_tax": round(ms_dm / stage_ms["dense"], 3),
+        "dense_key_mask_ms": round(ms_dk, 4), "dense_key_mask_tax": round(ms_dk / stage_ms["dense"], 3),
+        "srsu_ms": round(stage_ms["srsu_self"], 4), "srsu_masked_ms": round(ms_sm, 4),
+        "srsu_tax": round(ms_sm / stage_ms["srsu_self"], 3),
+        "masked_over_elided_plus_certify": round(ms_dm / (stage_ms["dense"] + stage_ms["classify"]), 3)}
+    del o_d, o_s
+    H2, d2 = 32, 72
+    g = torch.Generator(device="cuda").manual_seed(7272)
+    q2, k2, v2 = (torch.randn((B, N, H2, d2), generator=g, device="cuda").to(torch.bfloat16) for _ in range(3))
+    o2 = torch.empty_like(q2)
+    ms_e = _time_ms(lambda: sq.attn_fwd(q2, k2, v2, out=o2), 3)
+    ms_m = _time_ms(lambda: sq.attn_fwd(q2, k2, v2, mask=mask, out=o2), 3)
+    fl2 = 4.0 * B * H2 * N * N * d2
+    res["d72_h32"] = {"dense_ms": round(ms_e, 4), "dense_tflops": round(tf(fl2, ms_e), 2),
+                      "dense_masked_ms": round(ms_m, 4), "dense_masked_tflops": round(tf(fl2, ms_m), 2),
+                      "dense_tax": round(ms_m / ms_e, 3)}
+    del q2, k2, v2, o2
+    torch.cuda.empty_cache()
     return res
 
 

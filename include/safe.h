@@ -235,9 +235,10 @@ int safe_kv_assemble(const safe_kv_args* a, void* stream);
  *               = attend; blocked keys get -inf), SAFE_DT_BF16, SAFE_DT_F16 or
  *               SAFE_DT_F32 (additive bias, -inf allowed).  The bias is added in fp32
  *               as scale * (q . k + bias / scale), so entries beyond about
- *               FLT_MAX * scale in magnitude act as -inf / +inf.  Strides must be
- *               multiples of 4 elements and the pointer aligned to 4 elements
- *               (SAFE_ERR_ALIGN).  Not combinable with kv_len (SAFE_ERR_UNSUPPORTED).
+ *               FLT_MAX * scale in magnitude act as -inf / +inf.  Rows are read in
+ *               16-byte pieces: the pointer 16-byte aligned and every stride a multiple
+ *               of 16 bytes (SAFE_ERR_ALIGN).  Not combinable with kv_len
+ *               (SAFE_ERR_UNSUPPORTED).
  *               Rows whose token is outside [0, Nq) read a zero query row and mask
  *               row 0 of their (b, h).  mask_dtype and mask_stride are ignored when
  *               mask is NULL.

@@ -112,18 +112,15 @@ static int check_attn_sizes(const safe_attn_args* a) {
   if (a->mask != nullptr) {
     if (a->mask_dtype < SAFE_DT_BOOL || a->mask_dtype > SAFE_DT_F32) return SAFE_ERR_DTYPE;
     if (a->kv_len != nullptr) return SAFE_ERR_UNSUPPORTED;
+    const int esz = a->mask_dtype == SAFE_DT_BOOL ? 1 : (a->mask_dtype == SAFE_DT_F32 ? 4 : 2);
     for (int i = 0; i < 3; ++i) {
       if (a->mask_stride[i] < 0) return SAFE_ERR_SHAPE;
-      if (a->mask_stride[i] % 4 != 0) return SAFE_ERR_ALIGN;
+      if (a->mask_stride[i] * esz % 16 != 0) return SAFE_ERR_ALIGN;
     }
   }
   return SAFE_OK;
 }
 
-// The mask is read in runs of four elements: aligned to four elements.
-static int mask_elem_bytes(int32_t dtype) {
-  return dtype == SAFE_DT_BOOL ? 1 : (dtype == SAFE_DT_F32 ? 4 : 2);
-}
 
 int64_t safe_attn_workspace_bytes(const safe_attn_args* a) {
   const int st = check_attn_sizes(a);
@@ -135,8 +132,7 @@ int safe_attn_fwd(const safe_attn_args* a, void* stream) {
   int st = check_attn_sizes(a);
   if (st != SAFE_OK) return st;
   if (a->workspace != nullptr && !aligned16(a->workspace)) return SAFE_ERR_ALIGN;
-  if (a->mask != nullptr && reinterpret_cast<uintptr_t>(a->mask) % (4 * mask_elem_bytes(a->mask_dtype)) != 0)
-    return SAFE_ERR_ALIGN;
+  if (a->mask != nullptr && !aligned16(a->mask)) return SAFE_ERR_ALIGN;
   const bool work = (int64_t)a->B * a->H * a->n_rows > 0;
   if ((st = check_bnhd(a->q, a->q_stride, work)) != SAFE_OK) return st;
   if ((st = check_bnhd(a->k, a->k_stride, work && a->Nk > 0)) != SAFE_OK) return st;

@@ -43,10 +43,10 @@
 //   2^16, far inside the range of bf16 P and the fp32 accumulators, and the common
 //   path skips the 32-value max reduction.  The reference starts at -FLT_MAX, not
 //   -inf, so a row whose keys are all masked so far gets exp2(-inf) = 0, not NaN.
-//   The mask, when present, is loaded straight into registers one tile ahead, four
-//   consecutive keys per load (the accumulator layout gives a lane keys in runs of
-//   four), and folded into the scores as s + bias / scale (Boolean: -inf where
-//   blocked) before the softmax.
+//   The mask, when present, is loaded one tile ahead -- coalesced into registers and
+//   redistributed through a per-wave LDS area, so each lane ends up with its keys in
+//   runs of four (the accumulator layout's grouping) -- and folded into the scores as
+//   s + bias / scale (Boolean: -inf where blocked) before the softmax.
 //   Workgroups are remapped so all row tiles of one (b, h) sit on one XCD and
 //   share its L2 for the K/V stream.
 #pragma once
@@ -163,6 +163,16 @@ __device__ __forceinline__ void fold_run(f32x16& sc, int g, const typename MaskR
   }
 }
 
+// Logical tile -> (row tile, head, sample): all row tiles of head 0, then head 1, ...
+// Consecutive logical tiles share an XCD (xcd_remap), so the workgroups that run side
+// by side share one head's K/V in L2.
+__device__ __forceinline__ void split_logical(int logical, const AttnParams& p, int& tile, int& h, int& b) {
+  tile = logical % p.n_row_tiles;
+  const int bh = logical / p.n_row_tiles;
+  h = bh % p.H;
+  b = bh / p.H;
+}
+
 typedef __attribute__((address_space(3))) void lds_void;
 typedef short i16x4 __attribute__((ext_vector_type(4)));
 
@@ -202,10 +212,8 @@ __global__ __launch_bounds__(NTHREADS, (D >= 128 || MT != kMaskNone) ? 2 : 3) vo
     logical = p.n_full + slot / p.nsplit;
     kb0 = (slot % p.nsplit) * p.split_tiles * BN;
   }
-  const int tile = logical % p.n_row_tiles;
-  const int bh = logical / p.n_row_tiles;
-  const int h = bh % p.H;
-  const int b = bh / p.H;
+  int tile, h, b;
+  split_logical(logical, p, tile, h, b);
 
   // ---- this lane's query row --------------------------------------------------
   const int rr = tile * BM + wave * 32 + col;  // output row (compact index)
@@ -299,10 +307,61 @@ __global__ __launch_bounds__(NTHREADS, (D >= 128 || MT != kMaskNone) ? 2 : 3) vo
   };
 
   // ---- mask runs: run i of a tile covers keys 32 (i / 4) + 8 (i % 4) + 4 half + 0..3 ----
-  const char* mrow = nullptr;
-  if constexpr (HAS_MASK)
-    mrow = p.mask + ((int64_t)b * p.ms0 + (int64_t)h * p.ms1 + (int64_t)(q_ok ? qi : 0) * p.ms2 + 4 * half) * MR::esz;
-  auto load_runs = [&](int j0, MRun (&r)[8]) {        // a whole tile: every key valid
+  // Whole tiles are loaded one tile ahead.  Staged (when the LDS leaves room for two
+  // workgroups per CU): each of the wave's 32 rows as CPR consecutive 16-byte chunks,
+  // NMI coalesced loads per lane into registers, then written to the wave's own LDS rows
+  // and read back as runs -- a load instruction then touches 8 or fewer cache lines
+  // instead of 32.  Otherwise the runs are loaded directly (8 loads per lane).
+  constexpr int CPR = 4 * MR::esz;                                  // 16-byte chunks per row of a tile
+  constexpr int NMI = HAS_MASK ? 32 * CPR / 64 : 1;                 // staging loads per lane
+  constexpr int MRS = 64 * MR::esz + (MT == kMaskF32 ? 16 : 8);     // LDS row stride: conflict-free run reads
+  constexpr bool STAGED = HAS_MASK && 2 * T::STAGE + NWAVES * 32 * MRS <= 80 * 1024;
+  __shared__ __attribute__((aligned(16))) char mstage[STAGED ? NWAVES * 32 * MRS : 16];
+  char* const mw = mstage + (STAGED ? wave * 32 * MRS : 0);          // this wave's LDS rows
+  const char* mrow = nullptr;   // this lane's own row (and half): direct and partial-tile loads
+  const char* mld[NMI];         // the rows this lane stages, its chunk offset included
+  if constexpr (HAS_MASK) {
+    const char* mbh = p.mask + ((int64_t)b * p.ms0 + (int64_t)h * p.ms1) * MR::esz;
+    const int qrow = q_ok ? qi : 0;
+    mrow = mbh + ((int64_t)qrow * p.ms2 + 4 * half) * MR::esz;
+#pragma unroll
+    for (int i = 0; i < NMI; ++i) {
+      const int q = i * 64 + lane;
+      const int src_row = __shfl(qrow, q / CPR);   // lane r < 32 holds row r's token
+      mld[i] = mbh + (int64_t)src_row * p.ms2 * MR::esz + (q % CPR) * 16;
+    }
+  }
+  typedef u32x4 MStage[STAGED ? NMI : 1];
+  auto stage_load = [&](int j0, MStage& st) {
+    if constexpr (STAGED) {
+#pragma unroll
+      for (int i = 0; i < NMI; ++i) st[i] = ld16(mld[i] + (int64_t)j0 * MR::esz);
+    }
+  };
+  auto stage_runs = [&](const MStage& st, MRun (&r)[8]) {   // registers -> wave LDS rows -> runs
+    if constexpr (STAGED) {
+#pragma unroll
+      for (int i = 0; i < NMI; ++i) {
+        const int q = i * 64 + lane;
+        char* dst = mw + (q / CPR) * MRS + (q % CPR) * 16;
+        if constexpr (MRS % 16 == 0) {
+          st16(dst, st[i]);
+        } else {
+          st8(dst, __builtin_shufflevector(st[i], st[i], 0, 1));
+          st8(dst + 8, __builtin_shufflevector(st[i], st[i], 2, 3));
+        }
+      }
+      // the rows were written by other lanes of this wave (LDS executes a wave's
+      // operations in order; the fences keep the compiler from reordering them)
+      __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+      __builtin_amdgcn_wave_barrier();
+      __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+#pragma unroll
+      for (int i = 0; i < 8; ++i)
+        r[i] = *reinterpret_cast<const MRun*>(mw + col * MRS + (32 * (i >> 2) + 8 * (i & 3) + 4 * half) * MR::esz);
+    }
+  };
+  auto load_runs = [&](int j0, MRun (&r)[8]) {        // direct: a whole tile, every key valid
 #pragma unroll
     for (int i = 0; i < 8; ++i)
       r[i] = *reinterpret_cast<const MRun*>(mrow + (int64_t)(j0 + 32 * (i >> 2) + 8 * (i & 3)) * MR::esz);
@@ -422,23 +481,28 @@ __global__ __launch_bounds__(NTHREADS, (D >= 128 || MT != kMaskNone) ? 2 : 3) vo
     }
   };
 
-  // One tile: wait for its copies (and mask runs), start the next tile's copies into
-  // the other stage (and its mask runs into the other register set), then S^T half 0;
+  // One tile: wait for its copies (and mask data), start the next tile's copies into
+  // the other stage (and its mask loads into the other register set), then S^T half 0;
   // [S^T half 1 | softmax half 0]; [PV half 0 | softmax half 1]; PV half 1.  Each
   // bracket is one basic block, so the scheduler interleaves the MFMAs of one half
   // with the VALU work of the other; the rare reference moves sit between them.
   // MASKED is the partial last tile: it loads its own mask runs, masks by length and
   // issues no copies.
-  auto tile_step = [&](auto masked, int it, const char* cur, char* nxt, MRun (&mc)[8], MRun (&mn)[8]) {
+  auto tile_step = [&](auto masked, int it, const char* cur, char* nxt, MRun (&mc)[8], MRun (&mn)[8],
+                       MStage& sc_, MStage& sn_) {
     constexpr bool MASKED = decltype(masked)::value;
     const int j0 = kb0 + it * BN;
     __builtin_amdgcn_s_waitcnt(0x0F70);  // vmcnt(0): this wave's copies of tile `it` landed
     __syncthreads();                     // ... everyone's, and tile it-1 is no longer read
     if constexpr (!MASKED) {
+      if constexpr (STAGED) stage_runs(sc_, mc);
       if (it + 1 < ntiles) {
         issue_tile(j0 + BN, nxt);
         if constexpr (HAS_MASK) {
-          if (j0 + 2 * BN <= kend) load_runs(j0 + BN, mn);
+          if (j0 + 2 * BN <= kend) {
+            if constexpr (STAGED) stage_load(j0 + BN, sn_);
+            else load_runs(j0 + BN, mn);
+          }
         }
       }
     } else if constexpr (HAS_MASK) {
@@ -469,22 +533,26 @@ __global__ __launch_bounds__(NTHREADS, (D >= 128 || MT != kMaskNone) ? 2 : 3) vo
 
   const std::integral_constant<bool, false> kFull;
   const std::integral_constant<bool, true> kMasked;
-  MRun mA[8], mB[8];   // mask runs of the even / odd tiles (unused without a mask)
+  MRun mA[8], mB[8];        // mask runs of the even / odd tiles (unused without a mask)
+  MStage sA, sB;            // staged mask loads of the even / odd tiles (unused unless STAGED)
   const int nfull = (kend - kb0) / BN;   // tiles whose 64 keys are all valid
   if (ntiles > 0) issue_tile(kb0, stage0);
   if constexpr (HAS_MASK) {
-    if (nfull > 0) load_runs(kb0, mA);
+    if (nfull > 0) {
+      if constexpr (STAGED) stage_load(kb0, sA);
+      else load_runs(kb0, mA);
+    }
   }
   int it = 0;
   for (; it + 2 <= nfull; it += 2) {
-    tile_step(kFull, it, stage0, stage1, mA, mB);
-    tile_step(kFull, it + 1, stage1, stage0, mB, mA);
+    tile_step(kFull, it, stage0, stage1, mA, mB, sA, sB);
+    tile_step(kFull, it + 1, stage1, stage0, mB, mA, sB, sA);
   }
   if (it < nfull) {
-    tile_step(kFull, it, stage0, stage1, mA, mB);
+    tile_step(kFull, it, stage0, stage1, mA, mB, sA, sB);
     ++it;
   }
-  if (it < ntiles) tile_step(kMasked, it, (it & 1) ? stage1 : stage0, nullptr, mA, mB);
+  if (it < ntiles) tile_step(kMasked, it, (it & 1) ? stage1 : stage0, nullptr, mA, mB, sA, sB);
 
   // ---- epilogue: normalise, store O (bf16) and LSE ------------------------------
   const float l_tot = l_run + __shfl_xor(l_run, 32);
@@ -545,10 +613,8 @@ __global__ __launch_bounds__(MERGE_ROWS * 8) void attn_merge_kernel(AttnParams p
   constexpr int DT = MergeShape<D>::DT;
   const int ti = blockIdx.x;
   const int logical = p.n_full + ti;
-  const int tile = logical % p.n_row_tiles;
-  const int bh = logical / p.n_row_tiles;
-  const int h = bh % p.H;
-  const int b = bh / p.H;
+  int tile, h, b;
+  split_logical(logical, p, tile, h, b);
   const int rloc = blockIdx.y * MERGE_ROWS + threadIdx.x / TPR;
   const int part = threadIdx.x % TPR;
   const int rr = tile * BM + rloc;

@@ -97,10 +97,14 @@ def test_attn_mask_arguments_without_gpu():
         a.mask_stride[:] = [128 * 128, 0, 128]
         a.mask_stride[i] = bad
         assert sq.lib.safe_attn_fwd(ctypes.byref(a), None) == status
-    # runs of four elements: pointer aligned to 4 elements of the mask's type
-    for dtype, ptr in ((0, m + 2), (1, m + 4), (2, m + 4), (3, m + 8)):
+    # rows are read in 16-byte pieces: 16-byte aligned pointer, strides of 16 bytes
+    for dtype, ptr in ((0, m + 2), (1, m + 4), (2, m + 8), (3, m + 8)):
         a = _attn_args(mask=ptr, mask_dtype=dtype)
         a.mask_stride[:] = [0, 0, 128]
+        assert sq.lib.safe_attn_fwd(ctypes.byref(a), None) == -8, dtype
+    for dtype, stride in ((0, 8), (1, 4), (2, 12), (3, 2)):   # 8, 8, 24, 8 bytes
+        a = _attn_args(mask=m, mask_dtype=dtype)
+        a.mask_stride[:] = [0, 0, stride]
         assert sq.lib.safe_attn_fwd(ctypes.byref(a), None) == -8, dtype
     # the size query checks the mask fields too; a NULL mask ignores them
     assert sq.lib.safe_attn_workspace_bytes(ctypes.byref(_attn_args(mask=m, mask_dtype=9))) == -3

@@ -15,9 +15,9 @@ sq = pytest.importorskip("sparse_query_sdpa_amd")
 TORCH_DT = {"bool": torch.bool, "bf16": torch.bfloat16, "f16": torch.float16, "f32": torch.float32}
 
 
-def padded_mask(values: np.ndarray, kind: str, pad_to: int = 4) -> torch.Tensor:
+def padded_mask(values: np.ndarray, kind: str, pad_to: int = 16) -> torch.Tensor:
     """A device mask holding `values` [.., Nk] in rows padded to a multiple of `pad_to`
-    elements (the kernel reads runs of four), returned as the [.., :Nk] view."""
+    elements (rows must start 16-byte aligned), returned as the [.., :Nk] view."""
     nk = values.shape[-1]
     width = -(-nk // pad_to) * pad_to
     store = np.zeros(values.shape[:-1] + (width,), dtype=values.dtype)
@@ -78,7 +78,7 @@ def test_removable_masks_are_exact_to_drop():
     """Eq. 7-8 on this kernel: an all-valid Boolean mask and a zero additive mask give
     bit-identical outputs to the mask-free call (same scores, same softmax order); a
     row-constant additive mask stays within tolerance of the oracle's mask-free result."""
-    B, N, H, d = 2, 520, 4, 96
+    B, N, H, d = 2, 528, 4, 96
     q, k, v = W.attention_inputs(B, N, N, H, d, seed=31)
     qd, kd, vd = to_dev_bf16(q), to_dev_bf16(k), to_dev_bf16(v)
     plain = sq.attn_fwd(qd, kd, vd, workspace=None)
@@ -143,7 +143,7 @@ def test_mask_argument_errors():
     with pytest.raises(sq.SafeError) as e:
         sq.attn_fwd(qd, kd, vd, mask=m, kv_len=to_dev(np.array([10], np.int32)))
     assert e.value.status == -5
-    odd = torch.ones((1, 1, N, N + 1), dtype=torch.bool, device=qd.device)[..., :N]   # row stride 65
+    odd = torch.ones((1, 1, N, N + 8), dtype=torch.bool, device=qd.device)[..., :N]   # row stride 72 bytes
     with pytest.raises(sq.SafeError) as e:
         sq.attn_fwd(qd, kd, vd, mask=odd)
     assert e.value.status == -8
