@@ -19,6 +19,8 @@ Parts:
                the anchor refresh of the context cache.
   guidance.py  Eq. 20, 21: sensitivity-weighted classifier-free guidance and its
                binary variant.
+  block.py     Eq. 15-16, 18: the row-selective block around attention (a plain
+               stand-in block with synthetic weights) and its dense form.
 
 Pinning status (what fixes each function other than itself) is listed in the
 module docstrings; every function is pinned by the CPU tests in
@@ -34,6 +36,7 @@ from .pcsp import (pcsp_accumulate, gaussian_taps, gaussian_smooth, minmax_norma
                    topk_select, pcsp_scores)
 from .kvcache import kv_assemble, car_refresh
 from .guidance import guidance_scales, binary_scales, sw_cfg
+from .block import linear, gelu_tanh, block_dense, block_srsu
 
 __all__ = [
     "sdpa", "sdpa_bruteforce", "lse_from_logits",
@@ -43,4 +46,5 @@ __all__ = [
     "guidance_scales", "binary_scales", "sw_cfg",
     "pcsp_accumulate", "gaussian_taps", "gaussian_smooth", "minmax_normalize", "topk_select",
     "pcsp_scores", "kv_assemble", "car_refresh",
+    "linear", "gelu_tanh", "block_dense", "block_srsu",
 ]

@@ -280,3 +280,18 @@ def score_field(rng: np.random.Generator, B: int, N: int, levels: Optional[int] 
 
 
 __all__ = [n for n in dir() if not n.startswith("_") and n not in ("annotations", "dataclasses", "math", "np")]
+
+
+# ----------------------------------------------------------------------------
+# synthetic block weights (the row-selective block around attention)
+# ----------------------------------------------------------------------------
+
+def block_weights(C: int, F: int, seed: int) -> dict:
+    """Random bf16 weights of the stand-in block: Wqkv [3C, C], Wo [C, C], W1 [F, C],
+    W2 [C, F] drawn N(0, 1/fan_in) (unit-variance activations stay unit-variance), and
+    fp32 biases b1 [F], b2 [C] drawn N(0, 0.1^2).  Weights are [out, in] with the input
+    channels contiguous."""
+    def w(i, shape):
+        return bf16_normal((seed, i), shape, std=1.0 / np.sqrt(shape[1]))
+    return {"w_qkv": w(0, (3 * C, C)), "w_o": w(1, (C, C)), "w1": w(2, (F, C)), "w2": w(3, (C, F)),
+            "b1": normal_f32((seed, 4), (F,), std=0.1), "b2": normal_f32((seed, 5), (C,), std=0.1)}
