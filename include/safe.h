@@ -11,6 +11,8 @@
  *                       gathered rows of S, with optional per-sample valid key lengths
  *                       (or, for masks the rewrite cannot drop, a dense mask)
  *   safe_sw_cfg         Eq. 20-21 sensitivity-weighted classifier-free guidance
+ *   safe_linear         Eq. 15    the row-wise linear maps of the block around attention
+ *                                 (projections, residual updates, MLP) on gathered rows
  *
  * Common conventions
  *   - Tensors are DEVICE pointers owned by the caller; the library never allocates,
@@ -39,7 +41,7 @@
 extern "C" {
 #endif
 
-#define SAFE_ABI_VERSION 4
+#define SAFE_ABI_VERSION 5
 
 /* ---- status codes (negative = error) ----------------------------------- */
 enum {
@@ -312,6 +314,49 @@ typedef struct {
 } safe_cfg_args;
 
 int safe_sw_cfg(const safe_cfg_args* a, void* stream);
+
+/*
+ * safe_linear -- the row-wise linear maps of the DiT block around attention.  Eq. 15:
+ * at a non-anchor step the block computes its attention inputs and outputs, residual
+ * updates and row-wise MLP only for the rows of S; this is that computation for any
+ * row list (or all rows, the dense block of Eq. 18).  For batch b and row r < M:
+ *   y[n] = sum_k A[b, ra(r), k] * W[n, k] + bias[n]         ra(r) = a_rows[b][r] or r
+ *   y[n] = gelu_tanh(y[n])                                  if act == SAFE_ACT_GELU_TANH
+ *   y[n] = y[n] + R[b, rr(r), n]                            rr(r) = res_rows[b][r] or r
+ *   out[b, ro(r), n] = bf16(y[n])                           ro(r) = out_rows[b][r] or r
+ * with gelu_tanh(x) = x/2 (1 + tanh(sqrt(2/pi) (x + 0.044715 x^3))); products and sums
+ * in fp32, one rounding to bf16 (nearest even) on store.
+ *
+ * a, res, out   bf16 rows (K values for a, N for res and out); element strides
+ *               stride[0] = batch, stride[1] = row; 16-byte aligned rows.
+ * w             bf16 [N, K]: row n holds output feature n's weights (K contiguous),
+ *               row stride w_stride elements (< 2^24).
+ * bias          fp32 [N] (16-byte aligned) or NULL.
+ * a_rows, res_rows, out_rows  device int32 [batches, M] (batch stride rows_bstride; 0 =
+ *               one list for all) or NULL; entries index rows [0, Ntok).  Out of range:
+ *               an A row reads row 0, a residual row adds nothing, an output row is not
+ *               written (SAFE_FLAG_CHECK: SAFE_ERR_RANGE).  With out_rows the untouched
+ *               output rows keep their contents (e.g. the cached context rows).
+ * Limits: K a multiple of 64, N a multiple of 8 (else SAFE_ERR_UNSUPPORTED /
+ * SAFE_ERR_ALIGN).  out may alias res only row for row (same rows, same strides).
+ */
+#define SAFE_ACT_NONE      0
+#define SAFE_ACT_GELU_TANH 1
+typedef struct {
+  int32_t batches, M, N, K;
+  const void* a; int64_t a_stride[2];
+  const void* w; int64_t w_stride;
+  const float* bias;
+  int32_t act;
+  const void* res; int64_t res_stride[2];
+  void* out; int64_t out_stride[2];
+  const int32_t* a_rows; const int32_t* res_rows; const int32_t* out_rows;
+  int64_t rows_bstride;
+  int32_t Ntok;
+  uint32_t flags;                          /* SAFE_FLAG_CHECK */
+} safe_linear_args;
+
+int safe_linear(const safe_linear_args* a, void* stream);
 
 /* SAFE_ABI_VERSION of the built library. */
 int safe_abi_version(void);

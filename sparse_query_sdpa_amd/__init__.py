@@ -31,7 +31,7 @@ CLASSIFY_ASYNC = 1 << 2
 PCSP_ACCUM = 1 << 3
 PCSP_SELECT = 1 << 4
 
-ABI_VERSION = 4   # struct layouts below match include/safe.h of this version
+ABI_VERSION = 5   # struct layouts below match include/safe.h of this version
 DT_BOOL, DT_BF16, DT_F16, DT_F32 = 0, 1, 2, 3
 MASK_CLASS_NAMES = ("ALL_VALID", "ZERO", "ROW_CONST", "KEY_PADDING", "NONCONST", "BLOCKED", "NONFINITE")
 
@@ -87,6 +87,20 @@ class CfgArgs(ctypes.Structure):
                 ("g_ctx", ctypes.c_float), ("g_sens", ctypes.c_float)]
 
 
+class LinearArgs(ctypes.Structure):
+    _fields_ = [("batches", ctypes.c_int32), ("M", ctypes.c_int32), ("N", ctypes.c_int32), ("K", ctypes.c_int32),
+                ("a", ctypes.c_void_p), ("a_stride", ctypes.c_int64 * 2),
+                ("w", ctypes.c_void_p), ("w_stride", ctypes.c_int64),
+                ("bias", ctypes.c_void_p), ("act", ctypes.c_int32),
+                ("res", ctypes.c_void_p), ("res_stride", ctypes.c_int64 * 2),
+                ("out", ctypes.c_void_p), ("out_stride", ctypes.c_int64 * 2),
+                ("a_rows", ctypes.c_void_p), ("res_rows", ctypes.c_void_p), ("out_rows", ctypes.c_void_p),
+                ("rows_bstride", ctypes.c_int64), ("Ntok", ctypes.c_int32), ("flags", ctypes.c_uint32)]
+
+
+ACT_NONE, ACT_GELU_TANH = 0, 1
+
+
 def _load():
     if not os.path.exists(LIB_PATH):
         raise ImportError(f"libsafe.so not found at {LIB_PATH}: build it with "
@@ -109,6 +123,8 @@ def _load():
     lib.safe_pcsp_select.restype = ctypes.c_int
     lib.safe_pcsp_select.argtypes = [ctypes.POINTER(PcspArgs), ctypes.c_void_p, ctypes.POINTER(ctypes.c_size_t),
                                      ctypes.c_void_p]
+    lib.safe_linear.restype = ctypes.c_int
+    lib.safe_linear.argtypes = [ctypes.POINTER(LinearArgs), ctypes.c_void_p]
     lib.safe_mask_classify.restype = ctypes.c_int
     lib.safe_mask_classify.argtypes = [ctypes.c_void_p, ctypes.c_int32, ctypes.POINTER(ctypes.c_int64),
                                        ctypes.POINTER(ctypes.c_int64), ctypes.c_uint32, ctypes.POINTER(MaskInfo),
@@ -439,3 +455,69 @@ def sw_cfg(f_c: torch.Tensor, f_u: torch.Tensor, g_ctx: float, g_sens: Optional[
 
 __all__ = ["attn_fwd", "kv_assemble", "mask_classify", "pcsp_accumulate", "pcsp_select", "sw_cfg", "lib", "SafeError",
            "LIB_PATH", "MASK_CLASS_NAMES"]
+
+
+def _rows3(t: torch.Tensor, name: str):
+    if t.dim() != 3 or t.stride(2) != 1:
+        raise ValueError(f"{name} must be [batches, rows, features] with features contiguous")
+    _bits16(t, name)
+    return (t.stride(0) if t.shape[0] > 1 else 0, t.stride(1))
+
+
+def linear(a: torch.Tensor, w: torch.Tensor, bias: Optional[torch.Tensor] = None, gelu: bool = False,
+           res: Optional[torch.Tensor] = None, out: Optional[torch.Tensor] = None,
+           a_rows: Optional[torch.Tensor] = None, res_rows: Optional[torch.Tensor] = None,
+           out_rows: Optional[torch.Tensor] = None, check: bool = False, stream=None) -> torch.Tensor:
+    """out[b, ro(r)] = [gelu](a[b, ra(r)] @ w.T + bias) + res[b, rr(r)] in bf16; see safe_linear in safe.h.
+
+    a [B, Ta, K], w [N, K], res [B, Tr, N], out [B, To, N] (bf16, last dim contiguous);
+    the row lists are [B, M] or [M] int32 and index tensors of equal row count."""
+    if w.dim() != 2 or w.stride(1) != 1:
+        raise ValueError("w must be [N, K] with K contiguous")
+    _bits16(w, "w")
+    B, Ta, K = a.shape
+    N = w.shape[0]
+    if w.shape[1] != K:
+        raise ValueError("w must be [N, K] matching a")
+    lists = [_i32(x, n) for x, n in ((a_rows, "a_rows"), (res_rows, "res_rows"), (out_rows, "out_rows"))]
+    given = [x for x in lists if x is not None]
+    M = given[0].shape[-1] if given else Ta
+    bst = 0
+    for x in given:
+        if x.shape[-1] != M or (x.dim() == 2 and (x.shape[0] != B or x.stride(1) != 1)):
+            raise ValueError("row lists must all be [M] or [B, M] with contiguous rows")
+    if given:
+        strides = {x.stride(0) if x.dim() == 2 else 0 for x in given}
+        if len(strides) != 1:
+            raise ValueError("row lists must share one batch stride")
+        bst = strides.pop()
+    ntok = 0
+    for x, t in ((lists[0], a), (lists[1], res), (lists[2], out)):
+        if x is not None:
+            if t is None:
+                raise ValueError("a row list needs its tensor")
+            if ntok and t.shape[1] != ntok:
+                raise ValueError("tensors indexed by row lists must have equal row counts")
+            ntok = t.shape[1]
+    if out is None:
+        if out_rows is not None:
+            raise ValueError("out_rows needs an output tensor holding the other rows")
+        out = torch.empty((B, M, N), dtype=a.dtype, device=a.device)
+    if bias is not None and (bias.dtype != torch.float32 or bias.shape != (N,) or not bias.is_contiguous()):
+        raise ValueError("bias must be contiguous float32 [N]")
+    args = LinearArgs()
+    args.batches, args.M, args.N, args.K = B, M, N, K
+    args.a, args.w, args.w_stride = _ptr(a), _ptr(w), w.stride(0)
+    args.a_stride[:] = _rows3(a, "a")
+    args.bias = _ptr(bias)
+    args.act = ACT_GELU_TANH if gelu else ACT_NONE
+    if res is not None:
+        args.res = _ptr(res)
+        args.res_stride[:] = _rows3(res, "res")
+    args.out = _ptr(out)
+    args.out_stride[:] = _rows3(out, "out")
+    args.a_rows, args.res_rows, args.out_rows = (_ptr(x) for x in lists)
+    args.rows_bstride, args.Ntok = bst, ntok
+    args.flags = FLAG_CHECK if check else 0
+    _check("safe_linear", lib.safe_linear(ctypes.byref(args), _stream(stream)))
+    return out

@@ -17,7 +17,7 @@ CSRC = os.path.join(PKG, "csrc")
 OBJ = os.path.join(PKG, "_build")
 LIB = os.path.join(PKG, "libsafe.so")
 
-SOURCES = ["api.hip", "attn_fwd.hip", "attn_masked.hip", "kv_assemble.hip", "mask_classify.hip", "pcsp.hip", "sw_cfg.hip"]
+SOURCES = ["api.hip", "attn_fwd.hip", "attn_masked.hip", "kv_assemble.hip", "mask_classify.hip", "pcsp.hip", "sw_cfg.hip", "linear.hip"]
 
 # Packed fp32 VALU ops are disabled: the compiler still vectorises ordinary code,
 # but no v_pk_{add,mul,fma}_f32 is emitted.  (The host pass ignores the feature.)

@@ -10,6 +10,7 @@ namespace safe {
 int attn_fwd_launch(const safe_attn_args* a, float scale, hipStream_t stream);
 int64_t attn_workspace_bytes(const safe_attn_args* a);
 int sw_cfg_launch(const safe_cfg_args* a, hipStream_t stream);
+int linear_launch(const safe_linear_args* a, hipStream_t stream);
 int kv_assemble_launch(const safe_kv_args* a, bool in_place, hipStream_t stream);
 int mask_classify_launch(const void* mask, int32_t dtype, const int64_t size[4], const int64_t stride[4],
                          uint32_t flags, safe_mask_info* info, uint8_t* row_class, int32_t* kv_len_out,
@@ -269,6 +270,48 @@ int safe_sw_cfg(const safe_cfg_args* a, void* stream) {
     return SAFE_ERR_NULL;
   }
   return sw_cfg_launch(a, static_cast<hipStream_t>(stream));
+}
+
+// A bf16 row block: 16-byte aligned rows (strides multiples of 8 elements, >= 0).
+static int check_rows2(const void* p, const int64_t st[2], bool need) {
+  if (p == nullptr) return need ? SAFE_ERR_NULL : SAFE_OK;
+  for (int i = 0; i < 2; ++i) {
+    if (st[i] < 0) return SAFE_ERR_SHAPE;
+    if (st[i] % 8 != 0) return SAFE_ERR_ALIGN;
+  }
+  return aligned16(p) ? SAFE_OK : SAFE_ERR_ALIGN;
+}
+
+int safe_linear(const safe_linear_args* a, void* stream) {
+  if (a == nullptr) return SAFE_ERR_NULL;
+  if (a->batches < 0 || a->M < 0 || a->N < 0 || a->K < 0 || a->Ntok < 0) return SAFE_ERR_SHAPE;
+  if (a->K % 64 != 0) return SAFE_ERR_UNSUPPORTED;
+  if (a->N % 8 != 0) return SAFE_ERR_ALIGN;
+  if (a->act != SAFE_ACT_NONE && a->act != SAFE_ACT_GELU_TANH) return SAFE_ERR_RANGE;
+  if (a->flags & ~SAFE_FLAG_CHECK) return SAFE_ERR_RANGE;
+  const bool lists = a->a_rows != nullptr || a->res_rows != nullptr || a->out_rows != nullptr;
+  if (lists && (a->rows_bstride < 0 || (a->rows_bstride != 0 && a->rows_bstride < a->M))) return SAFE_ERR_SHAPE;
+  const bool work = (int64_t)a->batches * a->M * a->N > 0;
+  if (work && a->a_rows != nullptr && a->K > 0 && a->Ntok < 1) return SAFE_ERR_SHAPE;   // row 0 must exist
+  int st;
+  if ((st = check_rows2(a->a, a->a_stride, work && a->K > 0)) != SAFE_OK) return st;
+  if ((st = check_rows2(a->out, a->out_stride, work)) != SAFE_OK) return st;
+  if ((st = check_rows2(a->res, a->res_stride, false)) != SAFE_OK) return st;
+  if (work && a->K > 0) {
+    if (a->w == nullptr) return SAFE_ERR_NULL;
+    if (a->w_stride < a->K || a->w_stride >= (int64_t(1) << 24)) return SAFE_ERR_SHAPE;
+    if (a->w_stride % 8 != 0 || !aligned16(a->w)) return SAFE_ERR_ALIGN;
+  }
+  if (a->bias != nullptr && !aligned16(a->bias)) return SAFE_ERR_ALIGN;
+  if (!work) return SAFE_OK;
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  if (a->flags & SAFE_FLAG_CHECK) {
+    const int32_t* l3[3] = {a->a_rows, a->res_rows, a->out_rows};
+    for (const int32_t* l : l3)
+      if (l != nullptr && (st = check_rows(l, a->batches, a->M, a->rows_bstride, a->Ntok, false, s)) != SAFE_OK)
+        return st;
+  }
+  return linear_launch(a, s);
 }
 
 }  // extern "C"

@@ -20,7 +20,7 @@ def declared_functions():
 
 def test_header_declares_the_four_entry_points():
     names = declared_functions()
-    for n in ("safe_mask_classify", "safe_pcsp_select", "safe_kv_assemble", "safe_attn_fwd", "safe_sw_cfg",
+    for n in ("safe_mask_classify", "safe_pcsp_select", "safe_kv_assemble", "safe_attn_fwd", "safe_sw_cfg", "safe_linear",
               "safe_attn_workspace_bytes", "safe_status_str", "safe_abi_version"):
         assert n in names
 
@@ -32,7 +32,7 @@ def test_every_declared_symbol_is_exported():
 
 
 def test_abi_version_and_status_strings():
-    assert sq.lib.safe_abi_version() == 4 == sq.ABI_VERSION
+    assert sq.lib.safe_abi_version() == 5 == sq.ABI_VERSION
     for code, name in sq.STATUS.items():
         assert sq.lib.safe_status_str(code).decode().startswith(name)
     assert sq.lib.safe_status_str(12345) == b"unknown status"
@@ -247,3 +247,34 @@ def test_sw_cfg_rejects_bad_arguments_without_gpu(kw, status):
 
 def test_sw_cfg_empty_work_is_ok_without_gpu():
     assert sq.lib.safe_sw_cfg(ctypes.byref(_cfg_args(N=0, f_c=None, f_u=None, out=None)), None) == 0
+
+
+def _lin_args(**kw):
+    a = sq.LinearArgs()
+    a.batches, a.M, a.N, a.K = 2, 100, 64, 128
+    a.a, a.w, a.out = 0x10000, 0x20000, 0x30000
+    a.a_stride[:] = [100 * 128, 128]
+    a.out_stride[:] = [100 * 64, 64]
+    a.w_stride = 128
+    for k, v in kw.items():
+        setattr(a, k, v)
+    return a
+
+
+@pytest.mark.parametrize("kw,status", [
+    (dict(K=100), -5), (dict(N=12), -8), (dict(M=-1), -2), (dict(act=5), -4), (dict(flags=1 << 5), -4),
+    (dict(a=None), -1), (dict(out=None), -1), (dict(w=None), -1), (dict(a=0x10008), -8),
+    (dict(w_stride=64), -2), (dict(w_stride=1 << 24), -2), (dict(w_stride=132), -8), (dict(bias=0x40004), -8),
+    (dict(a_rows=0x50000, rows_bstride=50), -2), (dict(a_rows=0x50000, Ntok=0), -2),
+    (dict(res=0x60000), -2),
+])
+def test_linear_rejects_bad_arguments_without_gpu(kw, status):
+    a = _lin_args(**kw)
+    if "res" in kw:
+        a.res_stride[:] = [-64, 64]
+    assert sq.lib.safe_linear(ctypes.byref(a), None) == status
+
+
+def test_linear_empty_work_is_ok_without_gpu():
+    for kw in (dict(M=0), dict(batches=0), dict(N=0, a=None, w=None, out=None)):
+        assert sq.lib.safe_linear(ctypes.byref(_lin_args(**kw)), None) == 0, kw
