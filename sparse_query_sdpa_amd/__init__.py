@@ -521,3 +521,43 @@ def linear(a: torch.Tensor, w: torch.Tensor, bias: Optional[torch.Tensor] = None
     args.flags = FLAG_CHECK if check else 0
     _check("safe_linear", lib.safe_linear(ctypes.byref(args), _stream(stream)))
     return out
+
+
+# ---- the block around attention (Eq. 15-18): sequencing of the entry points above ----
+
+def _heads(t: torch.Tensor, i: int, C: int, H: int) -> torch.Tensor:
+    """Part i (0 = Q, 1 = K, 2 = V) of a [B, n, 3C] projection as a [B, n, H, d] view."""
+    return t[..., i * C:(i + 1) * C].unflatten(-1, (H, C // H))
+
+
+def block_dense(x: torch.Tensor, w: dict, H: int, stream=None):
+    """The dense block (anchor step, Eq. 18) of the stand-in block
+        qkv = x Wqkv^T;  a = SDPA(q, k, v);  y = x + a Wo^T;  z = y + gelu_tanh(y W1^T + b1) W2^T + b2
+    with every map a libsafe call.  Returns (z [B, N, C], qkv [B, N, 3C]); qkv's K and V parts
+    are the key/value cache of the following non-anchor steps (Eq. 14, 19)."""
+    B, N, C = x.shape
+    qkv = linear(x, w["w_qkv"], stream=stream)
+    a = attn_fwd(_heads(qkv, 0, C, H), _heads(qkv, 1, C, H), _heads(qkv, 2, C, H), stream=stream)
+    y = linear(a.view(B, N, C), w["w_o"], res=x, stream=stream)
+    u = linear(y, w["w1"], bias=w["b1"], gelu=True, stream=stream)
+    z = linear(u, w["w2"], bias=w["b2"], res=y, stream=stream)
+    return z, qkv
+
+
+def block_srsu(x: torch.Tensor, idx: torch.Tensor, z: torch.Tensor, qkv_cache: torch.Tensor, w: dict, H: int,
+               stream=None):
+    """The row-selective block (Eq. 15-16) for ascending token lists idx [B, k]: the rows of S
+    are projected from the current state x, their keys and values are written over the cached
+    ones in qkv_cache (in place: global K/V in token order, Eq. 16), their attention, residual
+    and MLP outputs are computed, and their outputs are written over the cached outputs in z
+    (in place: the context rows of z stay the cached ones, Eq. 15).  Returns z."""
+    B, N, C = x.shape
+    k = idx.shape[-1]
+    qkv_s = linear(x, w["w_qkv"], a_rows=idx, stream=stream)
+    kc, vc = _heads(qkv_cache, 1, C, H), _heads(qkv_cache, 2, C, H)
+    kv_assemble(_heads(qkv_s, 1, C, H), _heads(qkv_s, 2, C, H), idx, kc, vc, in_place=True, stream=stream)
+    a_s = attn_fwd(_heads(qkv_s, 0, C, H), kc, vc, stream=stream)
+    y_s = linear(a_s.view(B, k, C), w["w_o"], res=x, res_rows=idx, stream=stream)
+    u_s = linear(y_s, w["w1"], bias=w["b1"], gelu=True, stream=stream)
+    linear(u_s, w["w2"], bias=w["b2"], res=y_s, out=z, out_rows=idx, stream=stream)
+    return z
