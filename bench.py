@@ -330,6 +330,9 @@ def main() -> int:
         del kc2, vc2
         out["sw_cfg"] = sw_cfg_lines(sq, acc, wl, args.sigma, k)
         out["midt"] = midt_lines(sq, q, kx, vx, mask, idx, stage_ms, tf)
+        del mask
+        torch.cuda.empty_cache()
+        out["block"] = block_lines(sq, W, idx, tf)
         out["configs"] = other_configs(sq, W, tf)
         clk = clock_under_load(lambda: sq.attn_fwd(q, kx, vx, out=o_dense))
         out["gfx_clock_mhz_under_dense_load"] = clk
@@ -375,6 +378,51 @@ def s_brackets(sq, q, k_glob, v_glob, wl, rho: int, dense_ms: float, tf) -> dict
         t = tf(4.0 * B * H * k * N * d, ms)
         res[name] = {"k": k, "ms": round(ms, 4), "tflops": round(t, 2), "pct_peak": round(100 * t / PEAK_BF16_TFLOPS, 2),
                      "dense_ratio": round(dense_ms / ms, 3)}
+    return res
+
+
+def block_lines(sq, W, idx, tf) -> dict:
+    """The block around attention at the 2560sq shape (C = H d = 2304, MLP 4C, synthetic
+    N(0, 1/fan_in) weights, N(0,1) state): the dense block (anchor step) against the
+    row-selective block on the PCSP set (k rows per sample), and the row-wise maps alone."""
+    import numpy as np
+    import torch
+    B, k = idx.shape
+    N, H, d = 25600, 24, 96
+    C, Fh = H * d, 4 * H * d
+    wts = W.block_weights(C, Fh, 4242)
+    wd = {n: (torch.from_numpy(v.bits.view(np.int16)).cuda().view(torch.bfloat16) if hasattr(v, "bits")
+              else torch.from_numpy(v).cuda()) for n, v in wts.items()}
+    g = torch.Generator(device="cuda").manual_seed(4243)
+    x = torch.randn((B, N, C), generator=g, device="cuda").to(torch.bfloat16)
+    z, qkv = sq.block_dense(x, wd, H)
+    ms_dense = _time_ms(lambda: sq.block_dense(x, wd, H), 3)
+    ms_srsu = _time_ms(lambda: sq.block_srsu(x, idx, z, qkv, wd, H), 5)
+    # the four row-wise maps alone (dense rows, then the rows of S)
+    a = torch.empty((B, N, C), dtype=torch.bfloat16, device="cuda")
+    y = torch.empty((B, N, C), dtype=torch.bfloat16, device="cuda")
+    u = torch.empty((B, N, Fh), dtype=torch.bfloat16, device="cuda")
+
+    def maps(rows):
+        n = N if rows is None else k
+        sq.linear(x, wd["w_qkv"], a_rows=rows, out=qkv[:, :n])
+        sq.linear(a[:, :n], wd["w_o"], res=x, res_rows=rows, out=y[:, :n])
+        sq.linear(y[:, :n], wd["w1"], bias=wd["b1"], gelu=True, out=u[:, :n])
+        sq.linear(u[:, :n], wd["w2"], bias=wd["b2"], res=y[:, :n], out=z, out_rows=rows)
+    ms_maps_d = _time_ms(lambda: maps(None), 3)
+    ms_maps_s = _time_ms(lambda: maps(idx), 5)
+    fl_maps = lambda n: 2.0 * B * n * C * (3 * C + C + 2 * Fh)
+    fl_attn = lambda n: 4.0 * B * H * n * N * d
+    res = {"shape": {"B": B, "N": N, "C": C, "H": H, "d": d, "mlp": Fh, "k": k},
+           "dense_block_ms": round(ms_dense, 4), "srsu_block_ms": round(ms_srsu, 4),
+           "dense_srsu_block_ratio": round(ms_dense / ms_srsu, 3), "ideal": round(N / k, 3),
+           "dense_block_tflops": round(tf(fl_maps(N) + fl_attn(N), ms_dense), 2),
+           "srsu_block_tflops": round(tf(fl_maps(k) + fl_attn(k), ms_srsu), 2),
+           "maps_dense_ms": round(ms_maps_d, 4), "maps_dense_tflops": round(tf(fl_maps(N), ms_maps_d), 2),
+           "maps_srsu_ms": round(ms_maps_s, 4), "maps_srsu_tflops": round(tf(fl_maps(k), ms_maps_s), 2)}
+    res["maps_srsu_pct_bf16_peak"] = round(100 * res["maps_srsu_tflops"] / PEAK_BF16_TFLOPS, 2)
+    del x, z, qkv, a, y, u, wd
+    torch.cuda.empty_cache()
     return res
 
 

@@ -9,29 +9,44 @@
 //   (tokens m); both are read 16 bytes per lane from LDS rows of k, so neither needs a
 //   transpose, and in the accumulator lane l owns token m = l % 32 and runs of four
 //   consecutive features -- the epilogue stores 8 bytes per run.
-//   Workgroup = 4 waves = a 128 (n) x 128 (m) output tile; each wave 64 x 64 (2 x 2
-//   MFMA blocks).  k advances 64 per stage; A and W tiles are copied global -> LDS with
-//   global_load_lds_dwordx4 (no staging registers), double buffered, one barrier per
-//   stage.  LDS rows are 9 chunks of 16 bytes (8 used): an odd chunk count keeps the
-//   16-lane row reads conflict-free.  Gathered A rows use per-lane 64-bit source
-//   pointers, fixed for the whole k loop; W rows use a scalar base and 32-bit offsets.
+//   Two tile shapes: 256 x 256 (8 waves of 64 features x 128 tokens, one workgroup per
+//   CU: 6 LDS fragment reads feed 8 MFMAs) when the problem fills the GPU at least once,
+//   else 128 x 128 (4 waves of 64 x 64, two workgroups per CU).  k advances 64 per
+//   stage; A and W tiles are copied global -> LDS with global_load_lds_dwordx4 (no
+//   staging registers), double buffered, one barrier per stage.  LDS rows are 9 chunks
+//   of 16 bytes (8 used): an odd chunk count keeps the 16-lane row reads conflict-free.
+//   Gathered A rows use per-lane 64-bit source pointers, fixed for the whole k loop; W
+//   rows use a scalar base and 32-bit offsets.
 #include "common.h"
 
 namespace safe {
 namespace {
 
-constexpr int LT = 128;          // tile edge (tokens and features)
 constexpr int LK = 64;           // k per stage
-constexpr int LTHREADS = 256;
-constexpr int LWAVES = LTHREADS / 64;
 constexpr int LSLOTS = 9;        // 16-byte chunks per LDS row (8 used)
 constexpr int LROWB = LSLOTS * 16;
-constexpr int LTILE_B = LT * LROWB;                // one operand tile: 18 KB
-constexpr int LSTAGE = 2 * LTILE_B;                // A tile then W tile
-constexpr int LCOPY_A = LT * LSLOTS / 64;          // 18 wave-wide copies per operand
-constexpr int LNCOPY = 2 * LCOPY_A;                // 36
-constexpr int LPER_WAVE = LNCOPY / LWAVES;         // 9
-static_assert(LT * LSLOTS % 64 == 0 && LNCOPY % LWAVES == 0, "copy plan");
+
+// Tile shapes: WN x WM waves, each owning BNB x BMB 32 x 32 MFMA blocks (features x tokens).
+template <int WN_, int WM_, int BNB_, int BMB_>
+struct LinCfg {
+  static constexpr int WN = WN_, WM = WM_, BNB = BNB_, BMB = BMB_;
+  static constexpr int WAVES = WN * WM;
+  static constexpr int THREADS = WAVES * 64;
+  static constexpr int TN = WN * BNB * 32;                 // features per tile
+  static constexpr int TM = WM * BMB * 32;                 // tokens per tile
+  static constexpr int COPY_A = TM * LSLOTS / 64;          // wave-wide 1 KB copies per stage
+  static constexpr int COPY_W = TN * LSLOTS / 64;
+  static constexpr int NCOPY = COPY_A + COPY_W;
+  static constexpr int PER_WAVE = NCOPY / WAVES;
+  static constexpr int A_BYTES = TM * LROWB;
+  static constexpr int STAGE = (TM + TN) * LROWB;          // A tile then W tile
+  static constexpr int MIN_BLOCKS = 4 * STAGE <= 160 * 1024 ? 2 : 1;
+  static_assert(TM * LSLOTS % 64 == 0 && TN * LSLOTS % 64 == 0 && NCOPY % WAVES == 0, "copy plan");
+};
+// 128 x 128 tiles, 4 waves of 64 x 64 (two workgroups per CU), and 256 x 256 tiles, 8 waves
+// of 64 x 128 (one workgroup per CU): 6 LDS reads feed 8 MFMAs instead of 4 feeding 4.
+typedef LinCfg<2, 2, 2, 2> LinSmall;
+typedef LinCfg<4, 2, 2, 4> LinLarge;
 
 struct LinParams {
   const char* a; const char* w; const float* bias; const char* res; char* out;
@@ -61,20 +76,23 @@ __device__ __forceinline__ int bounded_row(const int32_t* rows, int64_t bs, int 
   return (v >= 0 && v < limit) ? v : -1;
 }
 
-__global__ __launch_bounds__(LTHREADS, 2) void linear_kernel(LinParams p) {
-  __shared__ __attribute__((aligned(1024))) char st0[LSTAGE];
-  __shared__ __attribute__((aligned(1024))) char st1[LSTAGE];
+template <typename CFG>
+__global__ __launch_bounds__(CFG::THREADS, CFG::MIN_BLOCKS) void linear_kernel(LinParams p) {
+  constexpr int LWAVES = CFG::WAVES, LPER_WAVE = CFG::PER_WAVE, LCOPY_A = CFG::COPY_A;
+  constexpr int BNB = CFG::BNB, BMB = CFG::BMB;
+  __shared__ __attribute__((aligned(1024))) char st0[CFG::STAGE];
+  __shared__ __attribute__((aligned(1024))) char st1[CFG::STAGE];
   const int tid = threadIdx.x, lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int col = lane & 31, half = lane >> 5;
-  const int wn = wave & 1, wm = wave >> 1;       // this wave's 64 x 64 quadrant
+  const int wn = wave % CFG::WN, wm = wave / CFG::WN;       // this wave's block of the tile
   // tiles along m vary fastest and consecutive tiles share an XCD, so the workgroups
   // that run side by side on one XCD share a W tile in its L2
   const int per_b = p.tiles_m * p.tiles_n;
   const int logical = xcd_remap(blockIdx.x, per_b * p.batches);
   const int b = logical / per_b, t = logical - b * per_b;
   const int tm = t % p.tiles_m, tn = t / p.tiles_m;
-  const int m0 = tm * LT, n0 = tn * LT;
+  const int m0 = tm * CFG::TM, n0 = tn * CFG::TN;
 
   // ---- copy plan: copy c < LCOPY_A fills A slots [64c, 64c+64), the rest W slots --
   // slot sigma: row sigma / 9, chunk sigma % 9 (chunk 8 is padding: it fetches chunk 0
@@ -127,29 +145,28 @@ __global__ __launch_bounds__(LTHREADS, 2) void linear_kernel(LinParams p) {
     }
   };
 
-  f32x16 acc[2][2];
+  f32x16 acc[BNB][BMB];
 #pragma unroll
-  for (int i = 0; i < 2; ++i)
+  for (int i = 0; i < BNB; ++i)
 #pragma unroll
-    for (int j = 0; j < 2; ++j) acc[i][j] = f32x16{};
-  const int a_lane = (wm * 64 + col) * LROWB + half * 16;   // B operand: token rows
-  const int w_lane = (wn * 64 + col) * LROWB + half * 16;   // A operand: feature rows
+    for (int j = 0; j < BMB; ++j) acc[i][j] = f32x16{};
+  const int a_lane = (wm * BMB * 32 + col) * LROWB + half * 16;   // B operand: token rows
+  const int w_lane = (wn * BNB * 32 + col) * LROWB + half * 16;   // A operand: feature rows
 
   auto compute = [&](const char* stage) {
     const char* At = stage;
-    const char* Wt = stage + LTILE_B;
+    const char* Wt = stage + CFG::A_BYTES;
 #pragma unroll
     for (int s = 0; s < LK / 16; ++s) {
-      bf16x8 af[2], wf[2];
+      bf16x8 af[BMB], wf[BNB];
 #pragma unroll
-      for (int i = 0; i < 2; ++i) {
-        af[i] = as_bf16x8(ld16(At + a_lane + i * 32 * LROWB + s * 32));
-        wf[i] = as_bf16x8(ld16(Wt + w_lane + i * 32 * LROWB + s * 32));
-      }
+      for (int j = 0; j < BMB; ++j) af[j] = as_bf16x8(ld16(At + a_lane + j * 32 * LROWB + s * 32));
 #pragma unroll
-      for (int i = 0; i < 2; ++i)
+      for (int i = 0; i < BNB; ++i) wf[i] = as_bf16x8(ld16(Wt + w_lane + i * 32 * LROWB + s * 32));
 #pragma unroll
-        for (int j = 0; j < 2; ++j)
+      for (int i = 0; i < BNB; ++i)
+#pragma unroll
+        for (int j = 0; j < BMB; ++j)
           acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(wf[i], af[j], acc[i][j], 0, 0, 0);
     }
   };
@@ -174,9 +191,9 @@ __global__ __launch_bounds__(LTHREADS, 2) void linear_kernel(LinParams p) {
   }
 
   // ---- epilogue: lane owns token m and, per feature block i, four runs of 4 features --
-  const int r = m0 + wm * 64;   // + j * 32 + col
+  const int r = m0 + wm * BMB * 32;   // + j * 32 + col
 #pragma unroll
-  for (int j = 0; j < 2; ++j) {
+  for (int j = 0; j < BMB; ++j) {
     const int rr = r + j * 32 + col;
     if (rr >= p.M) continue;
     int ro = rr, rres = rr;
@@ -186,10 +203,10 @@ __global__ __launch_bounds__(LTHREADS, 2) void linear_kernel(LinParams p) {
     const char* resp = (p.res != nullptr && rres >= 0) ? p.res + (int64_t)b * p.res_bs + (int64_t)rres * p.res_s : nullptr;
     char* op = p.out + (int64_t)b * p.out_bs + (int64_t)ro * p.out_s;
 #pragma unroll
-    for (int i = 0; i < 2; ++i)
+    for (int i = 0; i < BNB; ++i)
 #pragma unroll
       for (int g = 0; g < 4; ++g) {
-        const int n = n0 + wn * 64 + i * 32 + 8 * g + 4 * half;
+        const int n = n0 + wn * BNB * 32 + i * 32 + 8 * g + 4 * half;
         if (n >= p.N) continue;
         float y[4] = {acc[i][j][4 * g], acc[i][j][4 * g + 1], acc[i][j][4 * g + 2], acc[i][j][4 * g + 3]};
         if (p.bias != nullptr) {
@@ -233,12 +250,22 @@ int linear_launch(const safe_linear_args* a, hipStream_t s) {
   p.a_rows = a->a_rows; p.res_rows = a->res_rows; p.out_rows = a->out_rows;
   p.rows_bs = a->rows_bstride;
   p.M = a->M; p.N = a->N; p.K = a->K; p.Ntok = a->Ntok; p.act = a->act;
-  p.tiles_m = (a->M + LT - 1) / LT;
-  p.tiles_n = (a->N + LT - 1) / LT;
   p.batches = a->batches;
+  // Large tiles when they fill the GPU at least once (one workgroup per CU); otherwise the
+  // small ones, whose 4x as many workgroups spread better over a short problem.
+  int cus = 0, dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess ||
+      hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess)
+    cus = 256;
+  const int64_t large_tiles = ceil_div64(a->M, LinLarge::TM) * ceil_div64(a->N, LinLarge::TN) * a->batches;
+  const bool large = large_tiles >= cus;
+  const int TM = large ? LinLarge::TM : LinSmall::TM, TN = large ? LinLarge::TN : LinSmall::TN;
+  p.tiles_m = (a->M + TM - 1) / TM;
+  p.tiles_n = (a->N + TN - 1) / TN;
   const int64_t grid = (int64_t)p.tiles_m * p.tiles_n * a->batches;
   if (grid > 0x7fffffff) return SAFE_ERR_SHAPE;
-  hipLaunchKernelGGL(linear_kernel, dim3((unsigned)grid), dim3(LTHREADS), 0, s, p);
+  if (large) hipLaunchKernelGGL(linear_kernel<LinLarge>, dim3((unsigned)grid), dim3(LinLarge::THREADS), 0, s, p);
+  else hipLaunchKernelGGL(linear_kernel<LinSmall>, dim3((unsigned)grid), dim3(LinSmall::THREADS), 0, s, p);
   return hipGetLastError() == hipSuccess ? SAFE_OK : SAFE_ERR_HIP;
 }
 

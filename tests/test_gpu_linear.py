@@ -122,3 +122,17 @@ def test_block_shapes_sampled_rows():
         a_s = a64[b, rows[b].numpy()[samp]]
         ref = oracle.linear(a_s, w64)
         check(y[b, torch.from_numpy(samp).cuda()], ref, bound(a_s, w64, ref, C), f"block shape b={b}")
+
+
+def test_large_tiles_ragged_edges():
+    """Enough 256 x 256 tiles to take the large-tile kernel, with ragged token and feature
+    edges, a gathered list, GELU and a residual."""
+    B, T, N, K, M = 1, 4100, 4104, 128, 4000
+    a, w, bias, res = inputs(B, T, N, K, 40)
+    rows = np.sort(np.random.default_rng(40).choice(T, M, replace=False)).astype(np.int32)[None]
+    y = sq.linear(to_dev_bf16(a), to_dev_bf16(w), bias=to_dev(bias), gelu=True, res=to_dev_bf16(res),
+                  a_rows=to_dev(rows), res_rows=to_dev(rows))
+    a_s = a.value[:, rows[0]]
+    r_s = res.value[:, rows[0]]
+    ref = oracle.gelu_tanh(oracle.linear(a_s, w.value, bias)) + r_s
+    check(y, ref, bound(a_s, w.value, ref, K, gelu=True, res=r_s), "large tiles")
