@@ -23,6 +23,7 @@ and the fp64 CPU oracle timed on a bounded sample on this host.
   python bench.py --rocprof-summary <kernel_stats.csv>   # markdown summary of a rocprofv3 run
   python bench.py --copy-probe                           # plain 1 GiB copy for counter calibration
   python bench.py --pmc-summary F.csv Fcopy.csv W.csv Wcopy.csv  # HBM traffic per attention launch
+  python bench.py --mfma-busy-summary counters.csv       # MFMA-busy fraction per kernel
 
 HBM traffic (the roofline's `traffic`) comes from two rocprofv3 --pmc runs of
 this script (FETCH_SIZE, then WRITE_SIZE) scaled by what the same counters read
@@ -103,6 +104,36 @@ def pmc_summary(fetch_csv: str, fetch_copy_csv: str, write_csv: str, write_copy_
     print("\n".join(lines))
 
 
+def mfma_busy_summary(path: str, n_xcd: int = 8, n_simd: int = 1024) -> None:
+    """Markdown of the MFMA-busy fraction per kernel from a rocprofv3 --pmc run of
+    SQ_VALU_MFMA_BUSY_CYCLES, SQ_INSTS_MFMA and GRBM_GUI_ACTIVE: GRBM_GUI_ACTIVE is summed over
+    the XCDs (cycles of the launch = value / n_xcd) and the busy count over all SIMDs, so
+    busy / (cycles x n_simd) is the fraction of SIMD cycles with an MFMA in flight."""
+    rows = list(csv.DictReader(open(path)))
+    per = {}
+    for r in rows:
+        name = r["Kernel_Name"]
+        key = name.replace("(anonymous namespace)::", "").split("(")[0].replace("void ", "")
+        if "attn_fwd_kernel" not in key and "linear_kernel" not in key:
+            continue
+        d = per.setdefault(key, {}).setdefault(r["Dispatch_Id"], {})
+        d[r["Counter_Name"]] = d.get(r["Counter_Name"], 0.0) + float(r["Counter_Value"])
+        d["ns"] = float(r["End_Timestamp"]) - float(r["Start_Timestamp"])
+    print("| kernel | launches | MFMA instr. per launch | cycles per launch (GRBM / XCDs) | clock MHz | "
+          "MFMA TFLOP/s (instr. x 32768 / time) | MFMA busy fraction |")
+    print("|---|---|---|---|---|---|---|")
+    for key, disp in sorted(per.items()):
+        ok = [v for v in disp.values() if all(c in v for c in ("SQ_VALU_MFMA_BUSY_CYCLES", "SQ_INSTS_MFMA", "GRBM_GUI_ACTIVE"))]
+        if not ok:
+            continue
+        busy = sum(v["SQ_VALU_MFMA_BUSY_CYCLES"] for v in ok) / len(ok)
+        inst = sum(v["SQ_INSTS_MFMA"] for v in ok) / len(ok)
+        cyc = sum(v["GRBM_GUI_ACTIVE"] for v in ok) / len(ok) / n_xcd
+        ns = sum(v["ns"] for v in ok) / len(ok)
+        print(f"| `{key}` | {len(ok)} | {inst:.4g} | {cyc:.4g} | {cyc / ns * 1e3:.0f} | "
+              f"{inst * 32768 / ns / 1e3:.0f} | {busy / (cyc * n_simd):.3f} |")
+
+
 def rocprof_summary(path: str) -> None:
     """Print a short markdown table of a rocprofv3 --stats kernel_stats.csv."""
     rows = list(csv.DictReader(open(path)))
@@ -140,6 +171,7 @@ def main() -> int:
     ap.add_argument("--no-sweep", action="store_true")
     ap.add_argument("--cpu-rows", type=int, default=3072, help="oracle sample: query rows per sample")
     ap.add_argument("--rocprof-summary", type=str, default=None)
+    ap.add_argument("--mfma-busy-summary", type=str, default=None)
     ap.add_argument("--copy-probe", action="store_true")
     ap.add_argument("--pmc-summary", nargs=4, metavar=("FETCH_CSV", "FETCH_COPY_CSV", "WRITE_CSV", "WRITE_COPY_CSV"),
                     default=None)
@@ -147,6 +179,9 @@ def main() -> int:
 
     if args.rocprof_summary:
         rocprof_summary(args.rocprof_summary)
+        return 0
+    if args.mfma_busy_summary:
+        mfma_busy_summary(args.mfma_busy_summary)
         return 0
     if args.pmc_summary:
         pmc_summary(*args.pmc_summary)
