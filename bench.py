@@ -364,6 +364,7 @@ def main() -> int:
                                        "bytes": ip_bytes}
         del kc2, vc2
         out["sw_cfg"] = sw_cfg_lines(sq, acc, wl, args.sigma, k)
+        out["hbm_measured"] = hbm_measured(out)
         out["midt"] = midt_lines(sq, q, kx, vx, mask, idx, stage_ms, tf)
         del mask
         torch.cuda.empty_cache()
@@ -414,6 +415,31 @@ def s_brackets(sq, q, k_glob, v_glob, wl, rho: int, dense_ms: float, tf) -> dict
         res[name] = {"k": k, "ms": round(ms, 4), "tflops": round(t, 2), "pct_peak": round(100 * t / PEAK_BF16_TFLOPS, 2),
                      "dense_ratio": round(dense_ms / ms, 3)}
     return res
+
+
+def hbm_measured(out: dict) -> dict:
+    """The box's streaming bandwidth as torch's device copy reaches it (1 GiB read + 1 GiB
+    written, three buffer pairs rotated so no pass hits in the 256 MB last-level cache), and
+    the HBM-bound kernels against it as well as against the 8 TB/s spec."""
+    import torch
+    n = 1 << 30
+    bufs = [(torch.empty(n, dtype=torch.uint8, device="cuda"), torch.empty(n, dtype=torch.uint8, device="cuda"))
+            for _ in range(3)]
+    for a, b in bufs:
+        a.fill_(1)
+    i = [0]
+
+    def one():
+        a, b = bufs[i[0] % 3]
+        b.copy_(a)
+        i[0] += 1
+    ms = _time_ms(one, 9)
+    gbs = 2 * n / (ms * 1e-3) / 1e9
+    del bufs
+    torch.cuda.empty_cache()
+    return {"copy_gbs": round(gbs, 1), "copy_pct_spec": round(100 * gbs / PEAK_HBM_GBS, 2),
+            "classify_pct_of_copy": round(100 * out["classify_gbs"] / gbs, 2),
+            "kv_assemble_pct_of_copy": round(100 * out["kv_assemble_gbs"] / gbs, 2)}
 
 
 def block_lines(sq, W, idx, tf) -> dict:
