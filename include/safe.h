@@ -242,8 +242,8 @@ int safe_kv_assemble(const safe_kv_args* a, void* stream);
  *               of 16 bytes (SAFE_ERR_ALIGN).  Not combinable with kv_len
  *               (SAFE_ERR_UNSUPPORTED).
  *               Rows whose token is outside [0, Nq) read a zero query row and mask
- *               row 0 of their (b, h).  mask_dtype and mask_stride are ignored when
- *               mask is NULL.
+ *               row 0 of their (b, h) (with Nq == 0 the mask has no rows and is not
+ *               read).  mask_dtype and mask_stride are ignored when mask is NULL.
  *
  * workspace     optional device scratch of workspace_bytes bytes (16-byte aligned),
  *               owned by the caller and not retained.  The rows are processed in
