@@ -50,7 +50,7 @@ COPY_PROBE_BYTES = 1 << 30  # bytes read and bytes written by one copy-probe lau
 ATTN_SOURCES = ("sparse_query_sdpa_amd/csrc/attn_kernel.h", "sparse_query_sdpa_amd/csrc/attn_fwd.hip",
                 "sparse_query_sdpa_amd/csrc/common.h")
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "attn_fwd_hbm_traffic_2560sq.md")
-KERNELS = {"dense": "attn_fwd_kernel<96, false, false, 0>", "srsu": "attn_fwd_kernel<96, true, false, 0>"}
+KERNELS = {"dense": "attn_fwd_kernel<96, false, false, 0, ", "srsu": "attn_fwd_kernel<96, true, false, 0, "}
 
 
 def attn_source_hash() -> str:
@@ -316,12 +316,12 @@ def main() -> int:
         "classify_pct_hbm": round(100 * mask_bytes / (stage_ms["classify"] * 1e-3) / 1e9 / PEAK_HBM_GBS, 2),
         "kv_assemble_gbs": round(kv_bytes / (stage_ms["kv_assemble"] * 1e-3) / 1e9, 1),
         "kv_assemble_pct_hbm": round(100 * kv_bytes / (stage_ms["kv_assemble"] * 1e-3) / 1e9 / PEAK_HBM_GBS, 2),
-        "roofline": {"bound": "mfma", "kernel": "attn_fwd_kernel<96,false,false,0> + attn_merge_kernel of the split tail tiles (dense anchor pass; the event time covers both)",
+        "roofline": {"bound": "mfma", "kernel": "attn_fwd_kernel<96,false,false,0,RB> + attn_merge_kernel of the split tail tiles (dense anchor pass, RB = row blocks per wave chosen per call; the event time covers both)",
                      "achieved": round(dense_tf, 2), "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s",
                      "frac": round(dense_tf / PEAK_BF16_TFLOPS, 4),
                      "traffic": traffic.get("dense", {}).get("bytes"),
                      "algorithmic_flops_per_launch": fl_dense, "avg_launch_ms": round(stage_ms["dense"], 4)},
-        "roofline_srsu": {"bound": "mfma", "kernel": "attn_fwd_kernel<96,true,false,0> + attn_merge_kernel of the split tail tiles (SRSU self-attention; the event time covers both)",
+        "roofline_srsu": {"bound": "mfma", "kernel": "attn_fwd_kernel<96,true,false,0,RB> + attn_merge_kernel of the split tail tiles (SRSU self-attention, RB chosen per call; the event time covers both)",
                           "achieved": round(srsu_tf, 2), "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s",
                           "frac": round(srsu_tf / PEAK_BF16_TFLOPS, 4),
                           "traffic": traffic.get("srsu", {}).get("bytes"),

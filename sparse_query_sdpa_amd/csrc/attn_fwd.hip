@@ -8,17 +8,30 @@ namespace {
 
 template <int D>
 hipError_t dispatch_flags(const AttnParams& p, bool gather, bool kvlen, hipStream_t s) {
-  if (gather) return kvlen ? launch<D, true, true, kMaskNone>(p, s) : launch<D, true, false, kMaskNone>(p, s);
-  return kvlen ? launch<D, false, true, kMaskNone>(p, s) : launch<D, false, false, kMaskNone>(p, s);
+  if (gather) return kvlen ? launch<D, true, true, kMaskNone, 1>(p, s) : launch<D, true, false, kMaskNone, 1>(p, s);
+  return kvlen ? launch<D, false, true, kMaskNone, 1>(p, s) : launch<D, false, false, kMaskNone, 1>(p, s);
+}
+template <int D>
+hipError_t dispatch_two_blocks(const AttnParams& p, bool gather, hipStream_t s) {
+  return gather ? launch<D, true, false, kMaskNone, 2>(p, s) : launch<D, false, false, kMaskNone, 2>(p, s);
 }
 
-int resident_for(int d, bool gather) {
+// Two row blocks per wave are compiled for the head dimensions of the workloads (96) and of
+// the paper's tax measurement (72), without key lengths (the text cross-attention keeps one).
+bool two_blocks_available(int d) { return d == 96 || d == 72; }
+
+template <int D, int RB>
+int resident_rb(bool gather) {
+  return gather ? resident_workgroups<D, true, false, kMaskNone, RB>() : resident_workgroups<D, false, false, kMaskNone, RB>();
+}
+
+int resident_for(int d, bool gather, int rb) {
   switch (d) {
-    case 32: return gather ? resident_workgroups<32, true, false, kMaskNone>() : resident_workgroups<32, false, false, kMaskNone>();
-    case 64: return gather ? resident_workgroups<64, true, false, kMaskNone>() : resident_workgroups<64, false, false, kMaskNone>();
-    case 72: return gather ? resident_workgroups<72, true, false, kMaskNone>() : resident_workgroups<72, false, false, kMaskNone>();
-    case 96: return gather ? resident_workgroups<96, true, false, kMaskNone>() : resident_workgroups<96, false, false, kMaskNone>();
-    case 128: return gather ? resident_workgroups<128, true, false, kMaskNone>() : resident_workgroups<128, false, false, kMaskNone>();
+    case 32: return resident_rb<32, 1>(gather);
+    case 64: return resident_rb<64, 1>(gather);
+    case 72: return rb == 2 ? resident_rb<72, 2>(gather) : resident_rb<72, 1>(gather);
+    case 96: return rb == 2 ? resident_rb<96, 2>(gather) : resident_rb<96, 1>(gather);
+    case 128: return resident_rb<128, 1>(gather);
     default: return 0;
   }
 }
@@ -45,14 +58,10 @@ struct SplitPlan {
 constexpr int kMinSplitTiles = 4;
 constexpr int kMaxSplit = 16;
 
-SplitPlan plan_split(const safe_attn_args* a, int64_t total_tiles) {
+SplitPlan plan_split(const safe_attn_args* a, int64_t total_tiles, int S, int rows) {
   SplitPlan pl;
   pl.n_full = (int)total_tiles;
-  if (a->kv_len != nullptr || total_tiles <= 0 || a->Nk <= 0) return pl;
-  const int mt = mask_kind(a);
-  const bool gather = a->q_rows != nullptr;
-  const int S = mt == kMaskNone ? resident_for(a->d, gather) : attn_masked_resident(a->d, gather, mt);
-  if (S <= 0) return pl;
+  if (a->kv_len != nullptr || total_tiles <= 0 || a->Nk <= 0 || S <= 0) return pl;
   const int64_t tail = total_tiles % S;
   if (tail == 0) return pl;
   const int nk_tiles = (a->Nk + BN - 1) / BN;
@@ -64,16 +73,57 @@ SplitPlan plan_split(const safe_attn_args* a, int64_t total_tiles) {
   if (pl.nsplit < 2) return SplitPlan{(int)total_tiles};
   pl.tail = (int)tail;
   pl.n_full = (int)(total_tiles - tail);
-  pl.bytes = (int64_t)pl.tail * pl.nsplit * BM * ((int64_t)a->d * 4 + 8);
+  pl.bytes = (int64_t)pl.tail * pl.nsplit * rows * ((int64_t)a->d * 4 + 8);
   return pl;
+}
+
+// Row blocks per wave and the split plan of a call.  Two row blocks do the same work 6%
+// faster per CU (measured at d = 96: half the LDS fragment reads and copies per MFMA) but
+// hold two workgroups per CU instead of three and make tiles twice as tall, which can leave
+// the last round emptier; the estimate below compares the two: rounds (the split tail
+// counting 1 / nsplit of a round) x resident workgroups x rows per tile / speed.
+constexpr double kTwoBlockSpeed = 1.06;
+struct Choice {
+  int rb = 1, rows = 0;
+  int64_t tiles = 0;
+  SplitPlan split;
+};
+Choice choose(const safe_attn_args* a, bool allow_split) {
+  const int mt = mask_kind(a);
+  const bool gather = a->q_rows != nullptr;
+  Choice best;
+  double best_cost = 0.0;
+  const int max_rb = (mt == kMaskNone && a->kv_len == nullptr && two_blocks_available(a->d)) ? 2 : 1;
+  for (int rb = 1; rb <= max_rb; ++rb) {
+    Choice c;
+    c.rb = rb;
+    c.rows = tile_rows(rb);
+    c.tiles = (int64_t)((a->n_rows + c.rows - 1) / c.rows) * a->H * a->B;
+    const int S = mt == kMaskNone ? resident_for(a->d, gather, rb) : attn_masked_resident(a->d, gather, mt);
+    if (rb > 1 && S <= 0) break;
+    c.split = SplitPlan{(int)std::min<int64_t>(c.tiles, 0x7fffffff)};
+    if (allow_split && c.tiles <= 0x7fffffff) c.split = plan_split(a, c.tiles, S, c.rows);
+    double cost = 0.0;
+    if (S > 0) {
+      const int64_t full = c.tiles / S, tail = c.tiles % S;
+      const double rounds = (double)full + (tail == 0 ? 0.0 : (c.split.tail > 0 ? 1.0 / c.split.nsplit : 1.0));
+      cost = rounds * S * c.rows / (rb > 1 ? kTwoBlockSpeed : 1.0);
+    }
+    if (rb == 1 || cost < best_cost) {
+      best = c;
+      best_cost = cost;
+    }
+  }
+  return best;
 }
 
 }  // namespace
 
 int64_t attn_workspace_bytes(const safe_attn_args* a) {
-  const int64_t total = (int64_t)((a->n_rows + BM - 1) / BM) * a->H * a->B;
-  if (a->n_rows == 0 || total == 0 || total > 0x7fffffff) return 0;
-  return plan_split(a, total).bytes;
+  if (a->n_rows == 0 || (int64_t)a->H * a->B == 0) return 0;
+  const Choice c = choose(a, true);
+  if (c.tiles > 0x7fffffff) return 0;
+  return c.split.tail > 0 ? c.split.bytes : 0;
 }
 
 // Enqueue the attention kernel (and the merge of split tiles).  Arguments were validated
@@ -94,21 +144,18 @@ int attn_fwd_launch(const safe_attn_args* a, float scale, hipStream_t stream) {
   p.kv_len = a->kv_len;
   p.lse = a->lse;
   p.B = a->B; p.H = a->H; p.Nq = a->Nq; p.Nk = a->Nk; p.n_rows = a->n_rows;
-  p.n_row_tiles = (a->n_rows + BM - 1) / BM;
+  const int mt = mask_kind(a);
+  Choice c = choose(a, a->workspace != nullptr && a->workspace_bytes > 0);
+  if (c.split.tail > 0 && a->workspace_bytes < c.split.bytes) c = choose(a, false);
+  p.n_row_tiles = (a->n_rows + c.rows - 1) / c.rows;
   const int64_t total = (int64_t)p.n_row_tiles * a->H * a->B;
   if (total > 0x7fffffff) return SAFE_ERR_SHAPE;
   p.scale_log2 = scale * 1.4426950408889634f;
   p.scatter = (a->flags & SAFE_ATTN_SCATTER_OUT) ? 1 : 0;
-  const int mt = mask_kind(a);
   p.mask = static_cast<const char*>(mt == kMaskNone ? nullptr : a->mask);
   p.ms0 = a->mask_stride[0]; p.ms1 = a->mask_stride[1]; p.ms2 = a->mask_stride[2];
   p.inv_scale = 1.0f / scale;
-  SplitPlan pl;
-  pl.n_full = (int)total;
-  if (a->workspace != nullptr && a->workspace_bytes > 0) {
-    pl = plan_split(a, total);
-    if (pl.tail == 0 || a->workspace_bytes < pl.bytes) pl = SplitPlan{(int)total};
-  }
+  const SplitPlan& pl = c.split;
   p.n_full = pl.n_full;
   p.nsplit = pl.nsplit;
   p.split_tiles = pl.split_tiles;
@@ -124,8 +171,8 @@ int attn_fwd_launch(const safe_attn_args* a, float scale, hipStream_t stream) {
     switch (a->d) {
       case 32: e = dispatch_flags<32>(p, gather, kvlen, stream); break;
       case 64: e = dispatch_flags<64>(p, gather, kvlen, stream); break;
-      case 72: e = dispatch_flags<72>(p, gather, kvlen, stream); break;
-      case 96: e = dispatch_flags<96>(p, gather, kvlen, stream); break;
+      case 72: e = c.rb == 2 ? dispatch_two_blocks<72>(p, gather, stream) : dispatch_flags<72>(p, gather, kvlen, stream); break;
+      case 96: e = c.rb == 2 ? dispatch_two_blocks<96>(p, gather, stream) : dispatch_flags<96>(p, gather, kvlen, stream); break;
       case 128: e = dispatch_flags<128>(p, gather, kvlen, stream); break;
       default: return SAFE_ERR_UNSUPPORTED;
     }

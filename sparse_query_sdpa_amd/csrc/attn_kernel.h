@@ -79,7 +79,8 @@ struct AttnParams {
   // Tail split: workgroups [0, n_full) take whole row tiles (logical tiles 0..n_full-1);
   // workgroup n_full + t takes key range t % nsplit (split_tiles key tiles each) of
   // logical tile n_full + t / nsplit and leaves unnormalised partials in `part`:
-  // O as fp32 [n_slots][BM][d], then (max, sum) as fp32 [n_slots][BM][2].
+  // O as fp32 [n_slots][rows][d], then (max, sum) as fp32 [n_slots][rows][2], rows = the
+  // instance's query rows per workgroup.
   int n_full, nsplit, split_tiles, n_slots;
   float* part;
   // dense mask (masked instances): element (b, h, query token i, key j) at
@@ -94,11 +95,13 @@ int attn_masked_resident(int d, bool gather, int mt);
 
 namespace {
 
-constexpr int BM = 128;       // query rows per workgroup
 constexpr int BN = 64;        // keys per tile
 constexpr int NTHREADS = 256;
 constexpr int NWAVES = NTHREADS / 64;
 constexpr float kRescaleThreshold = 8.0f;  // log2 units
+// Query row blocks (of 32) per wave, RB: each K and V^T fragment read from LDS feeds RB
+// MFMAs, and a K/V tile copied into LDS serves NWAVES * 32 * RB query rows.
+constexpr int tile_rows(int rb) { return NWAVES * 32 * rb; }
 constexpr float kSumLimit = 65536.0f;          // a lane's tile-sum share above this moves the reference
 
 // LDS tile geometry.  K rows are read 16 bytes per lane, 16 lanes on 16 rows at once:
@@ -184,9 +187,12 @@ __device__ __forceinline__ i16x4 lds_read_tr(const char* p) {
   return __builtin_amdgcn_ds_read_tr16_b64_v4i16((__attribute__((address_space(3))) i16x4*)p);
 }
 
-template <int D, bool GATHER, bool KVLEN, int MT>
-__global__ __launch_bounds__(NTHREADS, (D >= 128 || MT != kMaskNone) ? 2 : 3) void attn_fwd_kernel(AttnParams p) {
+template <int D, bool GATHER, bool KVLEN, int MT, int RB>
+__global__ __launch_bounds__(NTHREADS, (D >= 128 || MT != kMaskNone || RB > 1) ? 2 : 3)
+void attn_fwd_kernel(AttnParams p) {
   using T = Tile<D>;
+  constexpr int TBM = tile_rows(RB);   // query rows per workgroup
+  static_assert(RB == 1 || MT == kMaskNone, "masked instances use one row block per wave");
   using MR = MaskRun<MT>;
   typedef typename MR::type MRun;
   constexpr int KS = T::KS;   // k-steps of the Q K^T product
@@ -215,23 +221,25 @@ __global__ __launch_bounds__(NTHREADS, (D >= 128 || MT != kMaskNone) ? 2 : 3) vo
   int tile, h, b;
   split_logical(logical, p, tile, h, b);
 
-  // ---- this lane's query row --------------------------------------------------
-  const int rr = tile * BM + wave * 32 + col;  // output row (compact index)
-  const bool row_ok = rr < p.n_rows;
-  int qi = rr;
-  if (GATHER) qi = row_ok ? p.q_rows[(int64_t)b * p.qr_bs + rr] : -1;
-  const bool q_ok = row_ok && qi >= 0 && qi < p.Nq;
-
-  bf16x8 qf[KS];
-  {
-    const u16* qp = p.q + (int64_t)b * p.qs0 + (int64_t)(q_ok ? qi : 0) * p.qs1 + (int64_t)h * p.qs2 + half * 8;
+  // ---- this lane's query rows (one per row block) ------------------------------
+  int rr[RB], qi[RB];
+  bool row_ok[RB], q_ok[RB];
+  bf16x8 qf[RB][KS];
+#pragma unroll
+  for (int rb = 0; rb < RB; ++rb) {
+    rr[rb] = tile * TBM + (wave * RB + rb) * 32 + col;  // output row (compact index)
+    row_ok[rb] = rr[rb] < p.n_rows;
+    qi[rb] = rr[rb];
+    if (GATHER) qi[rb] = row_ok[rb] ? p.q_rows[(int64_t)b * p.qr_bs + rr[rb]] : -1;
+    q_ok[rb] = row_ok[rb] && qi[rb] >= 0 && qi[rb] < p.Nq;
+    const u16* qp = p.q + (int64_t)b * p.qs0 + (int64_t)(q_ok[rb] ? qi[rb] : 0) * p.qs1 + (int64_t)h * p.qs2 + half * 8;
 #pragma unroll
     for (int s = 0; s < KS; ++s) {
       u32x4 v = {0u, 0u, 0u, 0u};
       // columns past d (the upper half of the last k-step when d % 16 == 8) stay zero
       const bool in_row = s * 16 + 16 <= D || half == 0;
-      if (q_ok && in_row) v = ld16(qp + s * 16);
-      qf[s] = as_bf16x8(v);
+      if (q_ok[rb] && in_row) v = ld16(qp + s * 16);
+      qf[rb][s] = as_bf16x8(v);
     }
   }
 
@@ -322,7 +330,7 @@ __global__ __launch_bounds__(NTHREADS, (D >= 128 || MT != kMaskNone) ? 2 : 3) vo
   const char* mld[NMI];         // the rows this lane stages, its chunk offset included
   if constexpr (HAS_MASK) {
     const char* mbh = p.mask + ((int64_t)b * p.ms0 + (int64_t)h * p.ms1) * MR::esz;
-    const int qrow = q_ok ? qi : 0;
+    const int qrow = q_ok[0] ? qi[0] : 0;
     mrow = mbh + ((int64_t)qrow * p.ms2 + 4 * half) * MR::esz;
 #pragma unroll
     for (int i = 0; i < NMI; ++i) {
@@ -389,11 +397,15 @@ __global__ __launch_bounds__(NTHREADS, (D >= 128 || MT != kMaskNone) ? 2 : 3) vo
     }
   };
 
-  f32x16 oacc[DB];
+  f32x16 oacc[RB][DB];
+  float m_ref[RB], l_run[RB];   // reference max (log2 domain; -FLT_MAX: none yet), this lane's row-sum share
 #pragma unroll
-  for (int i = 0; i < DB; ++i) oacc[i] = f32x16{};
-  float m_ref = -FLT_MAX;   // reference max, log2 domain (-FLT_MAX: none yet)
-  float l_run = 0.f;        // this lane's share of the row sum
+  for (int rb = 0; rb < RB; ++rb) {
+#pragma unroll
+    for (int i = 0; i < DB; ++i) oacc[rb][i] = f32x16{};
+    m_ref[rb] = -FLT_MAX;
+    l_run[rb] = 0.f;
+  }
   const float sl2 = p.scale_log2;
 
   // LDS addresses of this lane's operand reads (byte offsets inside a tile)
@@ -404,14 +416,15 @@ __global__ __launch_bounds__(NTHREADS, (D >= 128 || MT != kMaskNone) ? 2 : 3) vo
   // Per-lane pieces of a tile.  A tile's two 32-key halves are independent once
   // scores exist: probabilities are taken against the current reference, so the
   // softmax of one half can run between the MFMAs of the other half.
-  auto s_half = [&](const char* Kt, int blk) -> f32x16 {   // S^T rows blk*32.. of the tile
-    f32x16 acc = f32x16{};
+  auto s_half = [&](const char* Kt, int blk, f32x16 (&acc)[RB]) {   // S^T rows blk*32.. of the tile
+#pragma unroll
+    for (int rb = 0; rb < RB; ++rb) acc[rb] = f32x16{};
 #pragma unroll
     for (int s = 0; s < KS; ++s) {
       const bf16x8 kf = as_bf16x8(ld16(Kt + k_lane + blk * 32 * T::K_ROWB + s * 32));
-      acc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kf, qf[s], acc, 0, 0, 0);
+#pragma unroll
+      for (int rb = 0; rb < RB; ++rb) acc[rb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kf, qf[rb][s], acc[rb], 0, 0, 0);
     }
-    return acc;
   };
   auto fold_half = [&](f32x16& sc, int blk, const MRun (&r)[8]) {
     if constexpr (HAS_MASK) {
@@ -420,15 +433,15 @@ __global__ __launch_bounds__(NTHREADS, (D >= 128 || MT != kMaskNone) ? 2 : 3) vo
     }
   };
   // bf16 P^T operands of one half and this lane's share of its sum
-  auto probs_half = [&](const f32x16& sc, bf16x8 (&pb)[2]) -> float {
+  auto probs_half = [&](const f32x16& sc, bf16x8 (&pb)[2], int rb) -> float {
     float ts = 0.f;
 #pragma unroll
     for (int t = 0; t < 2; ++t) {
       u32x4 packed;
 #pragma unroll
       for (int e = 0; e < 4; ++e) {
-        const float p0 = __builtin_amdgcn_exp2f(__builtin_fmaf(sc[8 * t + 2 * e], sl2, -m_ref));
-        const float p1 = __builtin_amdgcn_exp2f(__builtin_fmaf(sc[8 * t + 2 * e + 1], sl2, -m_ref));
+        const float p0 = __builtin_amdgcn_exp2f(__builtin_fmaf(sc[8 * t + 2 * e], sl2, -m_ref[rb]));
+        const float p1 = __builtin_amdgcn_exp2f(__builtin_fmaf(sc[8 * t + 2 * e + 1], sl2, -m_ref[rb]));
         packed[e] = pack_bf16x2(p0, p1);
         ts += p0 + p1;
       }
@@ -442,25 +455,25 @@ __global__ __launch_bounds__(NTHREADS, (D >= 128 || MT != kMaskNone) ? 2 : 3) vo
   // hold every earlier half) are rescaled and the half is recomputed.  A row whose
   // keys are all blocked so far (-inf scores) keeps the reference at -FLT_MAX, its
   // probabilities exp2(-inf) = 0 and O and l zero.
-  auto settle_half = [&](const f32x16& sc, bf16x8 (&pb)[2], float ts) -> float {
+  auto settle_half = [&](const f32x16& sc, bf16x8 (&pb)[2], float ts, int rb) -> float {
     if (__any(!(ts <= kSumLimit))) {
       float mt = sc[0];
 #pragma unroll
       for (int r = 1; r < 16; ++r) mt = fmaxf(mt, sc[r]);
       mt = fmaxf(mt, __shfl_xor(mt, 32));
       const float mt2 = mt * sl2;
-      const bool move = mt2 > m_ref + kRescaleThreshold;
-      const float m_new = move ? mt2 : m_ref;
-      const float alpha = __builtin_amdgcn_exp2f(m_ref - m_new);  // 0 on the first move
-      l_run *= alpha;
+      const bool move = mt2 > m_ref[rb] + kRescaleThreshold;
+      const float m_new = move ? mt2 : m_ref[rb];
+      const float alpha = __builtin_amdgcn_exp2f(m_ref[rb] - m_new);  // 0 on the first move
+      l_run[rb] *= alpha;
 #pragma unroll
-      for (int i = 0; i < DB; ++i) oacc[i] *= alpha;
-      m_ref = m_new;
-      ts = probs_half(sc, pb);
+      for (int i = 0; i < DB; ++i) oacc[rb][i] *= alpha;
+      m_ref[rb] = m_new;
+      ts = probs_half(sc, pb, rb);
     }
     return ts;
   };
-  auto pv_half = [&](const char* Vt, int blk, const bf16x8 (&pb)[2]) {   // O^T += V^T P^T, one half
+  auto pv_half = [&](const char* Vt, int blk, const bf16x8 (&pb)[RB][2]) {   // O^T += V^T P^T, one half
 #pragma unroll
     for (int db = 0; db < DB; ++db)
 #pragma unroll
@@ -469,7 +482,9 @@ __global__ __launch_bounds__(NTHREADS, (D >= 128 || MT != kMaskNone) ? 2 : 3) vo
         const i16x4 lo = lds_read_tr(vp);
         const i16x4 hi = lds_read_tr(vp + 8 * T::V_ROWB);
         const bf16x8 vf = __builtin_bit_cast(bf16x8, __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7));
-        oacc[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(vf, pb[t], oacc[db], 0, 0, 0);
+#pragma unroll
+        for (int rb = 0; rb < RB; ++rb)
+          oacc[rb][db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(vf, pb[rb][t], oacc[rb][db], 0, 0, 0);
       }
   };
   // keys past the valid length get -inf (the partial last tile only)
@@ -511,23 +526,38 @@ __global__ __launch_bounds__(NTHREADS, (D >= 128 || MT != kMaskNone) ? 2 : 3) vo
     const char* Kt = cur;
     const char* Vt = cur + T::K_BYTES;
 
-    f32x16 s0 = s_half(Kt, 0);
-    fold_half(s0, 0, mc);
-    if constexpr (MASKED) mask_half(s0, j0, 0);
-    bf16x8 pb0[2], pb1[2];
+    f32x16 s0[RB], s1[RB];
+    bf16x8 pb0[RB][2], pb1[RB][2];
+    float ts0[RB], ts1[RB];
+    s_half(Kt, 0, s0);
+#pragma unroll
+    for (int rb = 0; rb < RB; ++rb) {
+      fold_half(s0[rb], 0, mc);
+      if constexpr (MASKED) mask_half(s0[rb], j0, 0);
+    }
     __builtin_amdgcn_sched_barrier(0);
-    f32x16 s1 = s_half(Kt, 1);
-    fold_half(s1, 1, mc);
-    if constexpr (MASKED) mask_half(s1, j0, 1);
-    float ts0 = probs_half(s0, pb0);
+    s_half(Kt, 1, s1);
+#pragma unroll
+    for (int rb = 0; rb < RB; ++rb) {
+      fold_half(s1[rb], 1, mc);
+      if constexpr (MASKED) mask_half(s1[rb], j0, 1);
+      ts0[rb] = probs_half(s0[rb], pb0[rb], rb);
+    }
     __builtin_amdgcn_sched_barrier(0);
-    ts0 = settle_half(s0, pb0, ts0);
-    l_run += ts0;
+#pragma unroll
+    for (int rb = 0; rb < RB; ++rb) {
+      ts0[rb] = settle_half(s0[rb], pb0[rb], ts0[rb], rb);
+      l_run[rb] += ts0[rb];
+    }
     pv_half(Vt, 0, pb0);
-    float ts1 = probs_half(s1, pb1);
+#pragma unroll
+    for (int rb = 0; rb < RB; ++rb) ts1[rb] = probs_half(s1[rb], pb1[rb], rb);
     __builtin_amdgcn_sched_barrier(0);
-    ts1 = settle_half(s1, pb1, ts1);
-    l_run += ts1;
+#pragma unroll
+    for (int rb = 0; rb < RB; ++rb) {
+      ts1[rb] = settle_half(s1[rb], pb1[rb], ts1[rb], rb);
+      l_run[rb] += ts1[rb];
+    }
     pv_half(Vt, 1, pb1);
   };
 
@@ -555,44 +585,49 @@ __global__ __launch_bounds__(NTHREADS, (D >= 128 || MT != kMaskNone) ? 2 : 3) vo
   if (it < ntiles) tile_step(kMasked, it, (it & 1) ? stage1 : stage0, nullptr, mA, mB, sA, sB);
 
   // ---- epilogue: normalise, store O (bf16) and LSE ------------------------------
-  const float l_tot = l_run + __shfl_xor(l_run, 32);
-  if (!row_ok) return;
-  if (slot >= 0) {  // partial of a split tile: unnormalised O and this range's (max, sum)
-    const int rloc = wave * 32 + col;
-    float* po = p.part + ((int64_t)slot * BM + rloc) * D;
+  float l_tot[RB];
 #pragma unroll
-    for (int db = 0; db < DB; ++db)
+  for (int rb = 0; rb < RB; ++rb) l_tot[rb] = l_run[rb] + __shfl_xor(l_run[rb], 32);
 #pragma unroll
-      for (int g = 0; g < 4; ++g) {
-        if (db * 32 + 8 * g >= D) continue;   // padded O rows (d % 32 != 0)
-        const f32x4 w = {oacc[db][4 * g + 0], oacc[db][4 * g + 1], oacc[db][4 * g + 2], oacc[db][4 * g + 3]};
-        st16(po + db * 32 + 8 * g + 4 * half, __builtin_bit_cast(u32x4, w));
+  for (int rb = 0; rb < RB; ++rb) {
+    if (!row_ok[rb]) continue;
+    if (slot >= 0) {  // partial of a split tile: unnormalised O and this range's (max, sum)
+      const int rloc = (wave * RB + rb) * 32 + col;
+      float* po = p.part + ((int64_t)slot * TBM + rloc) * D;
+#pragma unroll
+      for (int db = 0; db < DB; ++db)
+#pragma unroll
+        for (int g = 0; g < 4; ++g) {
+          if (db * 32 + 8 * g >= D) continue;   // padded O rows (d % 32 != 0)
+          const f32x4 w = {oacc[rb][db][4 * g + 0], oacc[rb][db][4 * g + 1], oacc[rb][db][4 * g + 2], oacc[rb][db][4 * g + 3]};
+          st16(po + db * 32 + 8 * g + 4 * half, __builtin_bit_cast(u32x4, w));
+        }
+      if (half == 0) {
+        float* pm = p.part + (int64_t)p.n_slots * TBM * D + ((int64_t)slot * TBM + rloc) * 2;
+        pm[0] = m_ref[rb];
+        pm[1] = l_tot[rb];
       }
-    if (half == 0) {
-      float* pm = p.part + (int64_t)p.n_slots * BM * D + ((int64_t)slot * BM + rloc) * 2;
-      pm[0] = m_ref;
-      pm[1] = l_tot;
+      continue;
     }
-    return;
-  }
-  const float inv = l_tot > 0.f ? 1.0f / l_tot : 0.f;
-  const int orow = (GATHER && p.scatter) ? qi : rr;
-  if (!GATHER || !p.scatter || q_ok) {
-    u16* op = p.o + (int64_t)b * p.os0 + (int64_t)orow * p.os1 + (int64_t)h * p.os2;
+    const float inv = l_tot[rb] > 0.f ? 1.0f / l_tot[rb] : 0.f;
+    const int orow = (GATHER && p.scatter) ? qi[rb] : rr[rb];
+    if (!GATHER || !p.scatter || q_ok[rb]) {
+      u16* op = p.o + (int64_t)b * p.os0 + (int64_t)orow * p.os1 + (int64_t)h * p.os2;
 #pragma unroll
-    for (int db = 0; db < DB; ++db)
+      for (int db = 0; db < DB; ++db)
 #pragma unroll
-      for (int g = 0; g < 4; ++g) {
-        if (db * 32 + 8 * g >= D) continue;   // padded O rows (d % 32 != 0)
-        u32x2 w;
-        w[0] = pack_bf16x2(oacc[db][4 * g + 0] * inv, oacc[db][4 * g + 1] * inv);
-        w[1] = pack_bf16x2(oacc[db][4 * g + 2] * inv, oacc[db][4 * g + 3] * inv);
-        st8(op + db * 32 + 8 * g + 4 * half, w);
-      }
-  }
-  if (p.lse != nullptr && half == 0) {
-    const float lse = l_tot > 0.f ? (m_ref + __builtin_log2f(l_tot)) * 0.69314718055994530942f : -INFINITY;
-    p.lse[((int64_t)b * p.H + h) * p.n_rows + rr] = lse;
+        for (int g = 0; g < 4; ++g) {
+          if (db * 32 + 8 * g >= D) continue;   // padded O rows (d % 32 != 0)
+          u32x2 w;
+          w[0] = pack_bf16x2(oacc[rb][db][4 * g + 0] * inv, oacc[rb][db][4 * g + 1] * inv);
+          w[1] = pack_bf16x2(oacc[rb][db][4 * g + 2] * inv, oacc[rb][db][4 * g + 3] * inv);
+          st8(op + db * 32 + 8 * g + 4 * half, w);
+        }
+    }
+    if (p.lse != nullptr && half == 0) {
+      const float lse = l_tot[rb] > 0.f ? (m_ref[rb] + __builtin_log2f(l_tot[rb])) * 0.69314718055994530942f : -INFINITY;
+      p.lse[((int64_t)b * p.H + h) * p.n_rows + rr[rb]] = lse;
+    }
   }
 }
 
@@ -607,7 +642,7 @@ struct MergeShape {
   static constexpr int DT = D / TPR;                // columns per thread: 4, 8, 12 or 16
   static_assert(D % (4 * TPR) == 0, "whole 4-column groups per thread");
 };
-template <int D, bool GATHER>
+template <int D, bool GATHER, int TBM>
 __global__ __launch_bounds__(MERGE_ROWS * 8) void attn_merge_kernel(AttnParams p) {
   constexpr int TPR = MergeShape<D>::TPR;
   constexpr int DT = MergeShape<D>::DT;
@@ -617,21 +652,21 @@ __global__ __launch_bounds__(MERGE_ROWS * 8) void attn_merge_kernel(AttnParams p
   split_logical(logical, p, tile, h, b);
   const int rloc = blockIdx.y * MERGE_ROWS + threadIdx.x / TPR;
   const int part = threadIdx.x % TPR;
-  const int rr = tile * BM + rloc;
+  const int rr = tile * TBM + rloc;
   if (rr >= p.n_rows) return;
   int qi = rr;
   if (GATHER) qi = p.q_rows[(int64_t)b * p.qr_bs + rr];
   const bool q_ok = qi >= 0 && qi < p.Nq;
 
-  const float* pml = p.part + (int64_t)p.n_slots * BM * D;
+  const float* pml = p.part + (int64_t)p.n_slots * TBM * D;
   float M = -INFINITY;
-  for (int s = 0; s < p.nsplit; ++s) M = fmaxf(M, pml[((int64_t)(ti * p.nsplit + s) * BM + rloc) * 2]);
+  for (int s = 0; s < p.nsplit; ++s) M = fmaxf(M, pml[((int64_t)(ti * p.nsplit + s) * TBM + rloc) * 2]);
   float acc[DT];
 #pragma unroll
   for (int i = 0; i < DT; ++i) acc[i] = 0.f;
   float L = 0.f;
   for (int s = 0; s < p.nsplit; ++s) {
-    const int64_t sl = (int64_t)(ti * p.nsplit + s) * BM + rloc;
+    const int64_t sl = (int64_t)(ti * p.nsplit + s) * TBM + rloc;
     const float w = M == -INFINITY ? 0.f : __builtin_amdgcn_exp2f(pml[sl * 2] - M);
     L += w * pml[sl * 2 + 1];
     const float* po = p.part + sl * D + part * DT;
@@ -659,19 +694,19 @@ __global__ __launch_bounds__(MERGE_ROWS * 8) void attn_merge_kernel(AttnParams p
   }
 }
 
-template <int D, bool G, bool KV, int MT>
+template <int D, bool G, bool KV, int MT, int RB>
 hipError_t launch(const AttnParams& p, hipStream_t s) {
-  hipLaunchKernelGGL((attn_fwd_kernel<D, G, KV, MT>), dim3(p.total_wg), dim3(NTHREADS), 0, s, p);
+  hipLaunchKernelGGL((attn_fwd_kernel<D, G, KV, MT, RB>), dim3(p.total_wg), dim3(NTHREADS), 0, s, p);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess || p.n_slots == 0) return e;
-  hipLaunchKernelGGL((attn_merge_kernel<D, G>), dim3(p.n_slots / p.nsplit, BM / MERGE_ROWS),
+  hipLaunchKernelGGL((attn_merge_kernel<D, G, tile_rows(RB)>), dim3(p.n_slots / p.nsplit, tile_rows(RB) / MERGE_ROWS),
                      dim3(MERGE_ROWS * MergeShape<D>::TPR), 0, s, p);
   return hipGetLastError();
 }
 
 // Workgroups of one kernel instance resident on the whole device (0 if unknown).
 // Cached per device and instance; racing first calls store the same value.
-template <int D, bool G, bool KV, int MT>
+template <int D, bool G, bool KV, int MT, int RB>
 int resident_workgroups() {
   constexpr int kMaxDev = 64;
   static std::atomic<int> cache[kMaxDev];
@@ -680,7 +715,7 @@ int resident_workgroups() {
   int v = cache[dev].load(std::memory_order_relaxed);
   if (v > 0) return v;
   int per_cu = 0, cus = 0;
-  if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, attn_fwd_kernel<D, G, KV, MT>, NTHREADS, 0) != hipSuccess ||
+  if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, attn_fwd_kernel<D, G, KV, MT, RB>, NTHREADS, 0) != hipSuccess ||
       hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess)
     return 0;
   v = per_cu * cus;

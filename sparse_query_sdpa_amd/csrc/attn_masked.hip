@@ -10,7 +10,7 @@ namespace {
 
 template <int D, int MT>
 hipError_t dispatch_gather(const AttnParams& p, bool gather, hipStream_t s) {
-  return gather ? launch<D, true, false, MT>(p, s) : launch<D, false, false, MT>(p, s);
+  return gather ? launch<D, true, false, MT, 1>(p, s) : launch<D, false, false, MT, 1>(p, s);
 }
 
 template <int D>
@@ -26,7 +26,7 @@ hipError_t dispatch_mt(const AttnParams& p, bool gather, int mt, hipStream_t s) 
 
 template <int D, int MT>
 int resident_gather(bool gather) {
-  return gather ? resident_workgroups<D, true, false, MT>() : resident_workgroups<D, false, false, MT>();
+  return gather ? resident_workgroups<D, true, false, MT, 1>() : resident_workgroups<D, false, false, MT, 1>();
 }
 
 template <int D>
