@@ -47,10 +47,20 @@ int mask_kind(const safe_attn_args* a) {
   }
 }
 
+// Time model of a launch (seconds), for the split and row-block choices below: the
+// one-row-block kernel runs ~1.1e15 FLOP/s on the whole chip, two row blocks 6% faster
+// (both measured at d = 96), and the merge of split partials moves their bytes at ~2.5e12
+// B/s (read, plus the rows written).  Rounds of S resident workgroups take equal time.
+constexpr double kRate = 1.1e15;
+constexpr double kTwoBlockSpeed = 1.06;
+constexpr double kMergeBw = 2.5e12;
+
 // Tail split plan.  With S workgroups resident, T whole tiles run in rounds of S; the
-// last round holds tail = T mod S tiles (all of them when T < S).  Splitting each of
-// those along the keys into up to S / tail ranges (at least kMinSplitTiles key tiles
-// each, at most kMaxSplit ranges) fills that round with short workgroups instead.
+// last round holds tail = T mod S tiles (all of them when T < S).  Those tiles are split
+// along the keys into nsplit ranges (at least kMinSplitTiles key tiles each, at most
+// kMaxSplit ranges); the dispatcher hands the range workgroups to slots as they free up,
+// so tail * nsplit may exceed S: the tail then takes ceil(tail * nsplit / S) / nsplit of a
+// round.  nsplit minimises that time plus the merge of the partials.
 struct SplitPlan {
   int n_full = 0, nsplit = 1, split_tiles = 0, tail = 0;
   int64_t bytes = 0;
@@ -58,17 +68,25 @@ struct SplitPlan {
 constexpr int kMinSplitTiles = 4;
 constexpr int kMaxSplit = 16;
 
-SplitPlan plan_split(const safe_attn_args* a, int64_t total_tiles, int S, int rows) {
+SplitPlan plan_split(const safe_attn_args* a, int64_t total_tiles, int S, int rows, double round_s) {
   SplitPlan pl;
   pl.n_full = (int)total_tiles;
   if (a->kv_len != nullptr || total_tiles <= 0 || a->Nk <= 0 || S <= 0) return pl;
   const int64_t tail = total_tiles % S;
   if (tail == 0) return pl;
   const int nk_tiles = (a->Nk + BN - 1) / BN;
-  int nsplit = (int)std::min<int64_t>(S / tail, kMaxSplit);
-  nsplit = std::min(nsplit, nk_tiles / kMinSplitTiles);
-  if (nsplit < 2) return pl;
-  pl.split_tiles = (nk_tiles + nsplit - 1) / nsplit;
+  const double piece_bytes = (double)tail * rows * ((double)a->d * 4 + 8);
+  int best = 1;
+  double best_t = round_s;   // unsplit: the tail takes a whole round
+  for (int n = 2; n <= kMaxSplit && nk_tiles / n >= kMinSplitTiles; ++n) {
+    const double t = (double)((tail * n + S - 1) / S) / n * round_s + n * piece_bytes / kMergeBw;
+    if (t < best_t) {
+      best_t = t;
+      best = n;
+    }
+  }
+  if (best < 2) return pl;
+  pl.split_tiles = (nk_tiles + best - 1) / best;
   pl.nsplit = (nk_tiles + pl.split_tiles - 1) / pl.split_tiles;   // every range non-empty
   if (pl.nsplit < 2) return SplitPlan{(int)total_tiles};
   pl.tail = (int)tail;
@@ -78,11 +96,9 @@ SplitPlan plan_split(const safe_attn_args* a, int64_t total_tiles, int S, int ro
 }
 
 // Row blocks per wave and the split plan of a call.  Two row blocks do the same work 6%
-// faster per CU (measured at d = 96: half the LDS fragment reads and copies per MFMA) but
-// hold two workgroups per CU instead of three and make tiles twice as tall, which can leave
-// the last round emptier; the estimate below compares the two: rounds (the split tail
-// counting 1 / nsplit of a round) x resident workgroups x rows per tile / speed.
-constexpr double kTwoBlockSpeed = 1.06;
+// faster (half the LDS fragment reads and copies per MFMA, and the chip clocks higher for
+// it) but hold two workgroups per CU instead of three and make tiles twice as tall; the
+// time model picks the faster of the two.
 struct Choice {
   int rb = 1, rows = 0;
   int64_t tiles = 0;
@@ -91,8 +107,9 @@ struct Choice {
 Choice choose(const safe_attn_args* a, bool allow_split) {
   const int mt = mask_kind(a);
   const bool gather = a->q_rows != nullptr;
+  const double row_flops = 4.0 * a->Nk * a->d;
   Choice best;
-  double best_cost = 0.0;
+  double best_t = 0.0;
   const int max_rb = (mt == kMaskNone && a->kv_len == nullptr && two_blocks_available(a->d)) ? 2 : 1;
   for (int rb = 1; rb <= max_rb; ++rb) {
     Choice c;
@@ -101,17 +118,20 @@ Choice choose(const safe_attn_args* a, bool allow_split) {
     c.tiles = (int64_t)((a->n_rows + c.rows - 1) / c.rows) * a->H * a->B;
     const int S = mt == kMaskNone ? resident_for(a->d, gather, rb) : attn_masked_resident(a->d, gather, mt);
     if (rb > 1 && S <= 0) break;
+    const double round_s = S > 0 ? (double)S * c.rows * row_flops / (kRate * (rb > 1 ? kTwoBlockSpeed : 1.0)) : 0.0;
     c.split = SplitPlan{(int)std::min<int64_t>(c.tiles, 0x7fffffff)};
-    if (allow_split && c.tiles <= 0x7fffffff) c.split = plan_split(a, c.tiles, S, c.rows);
-    double cost = 0.0;
+    if (allow_split && c.tiles <= 0x7fffffff) c.split = plan_split(a, c.tiles, S, c.rows, round_s);
+    double t = 0.0;
     if (S > 0) {
       const int64_t full = c.tiles / S, tail = c.tiles % S;
-      const double rounds = (double)full + (tail == 0 ? 0.0 : (c.split.tail > 0 ? 1.0 / c.split.nsplit : 1.0));
-      cost = rounds * S * c.rows / (rb > 1 ? kTwoBlockSpeed : 1.0);
+      const SplitPlan& pl = c.split;
+      double rounds = (double)full;
+      if (tail > 0) rounds += pl.tail > 0 ? (double)((pl.tail * pl.nsplit + S - 1) / S) / pl.nsplit : 1.0;
+      t = rounds * round_s + (pl.tail > 0 ? (double)pl.bytes / kMergeBw : 0.0);
     }
-    if (rb == 1 || cost < best_cost) {
+    if (rb == 1 || t < best_t) {
       best = c;
-      best_cost = cost;
+      best_t = t;
     }
   }
   return best;
