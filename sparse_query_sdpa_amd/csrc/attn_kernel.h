@@ -443,7 +443,7 @@ void attn_fwd_kernel(AttnParams p) {
         const float p0 = __builtin_amdgcn_exp2f(__builtin_fmaf(sc[8 * t + 2 * e], sl2, -m_ref[rb]));
         const float p1 = __builtin_amdgcn_exp2f(__builtin_fmaf(sc[8 * t + 2 * e + 1], sl2, -m_ref[rb]));
         packed[e] = pack_bf16x2(p0, p1);
-        ts += p0 + p1;
+        ts = (t == 0 && e == 0) ? p0 + p1 : ts + (p0 + p1);   // 0 + x is not folded (signed zeros)
       }
       pb[t] = as_bf16x8(packed);
     }
@@ -536,6 +536,10 @@ void attn_fwd_kernel(AttnParams p) {
       if constexpr (MASKED) mask_half(s0[rb], j0, 0);
     }
     __builtin_amdgcn_sched_barrier(0);
+    // The two middle brackets carry the softmax: their VALU work is this wave's critical
+    // path, so the wave issues ahead of its SIMD partner (whose own S^T half 0 or P V
+    // half 1 is MFMA work only) until P V half 1 (+2-3%).
+    __builtin_amdgcn_s_setprio(1);
     s_half(Kt, 1, s1);
 #pragma unroll
     for (int rb = 0; rb < RB; ++rb) {
@@ -558,6 +562,7 @@ void attn_fwd_kernel(AttnParams p) {
       ts1[rb] = settle_half(s1[rb], pb1[rb], ts1[rb], rb);
       l_run[rb] += ts1[rb];
     }
+    __builtin_amdgcn_s_setprio(0);
     pv_half(Vt, 1, pb1);
   };
 

@@ -172,8 +172,10 @@ def test_logits_growing_along_keys_and_a_late_spike(d):
 
 
 def _sample_rows(rng, n, per=24):
-    """Sampled output rows: the first, the last, rows around the 128-row tile edges and random ones."""
-    pick = {0, n - 1, min(n - 1, 127), min(n - 1, 128), max(0, n - 129)}
+    """Sampled output rows: the first, the last, rows around the 128- and 256-row tile edges
+    (one and two row blocks per wave) and random ones."""
+    pick = {0, n - 1, max(0, n - 129), max(0, n - 257)}
+    pick.update(min(n - 1, r) for r in (127, 128, 255, 256, 383, 384))
     pick.update(rng.choice(n, size=min(n, per), replace=False).tolist())
     return np.array(sorted(pick))
 
