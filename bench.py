@@ -337,16 +337,7 @@ def main() -> int:
             kk = wl.k_for(rho)
             ids = sq.pcsp_select(acc, wl.grid_h, wl.grid_w, args.sigma, kk)
             o = torch.empty((B, kk, H, d), dtype=torch.bfloat16, device=dev)
-            for _ in range(2):
-                sq.attn_fwd(q, k_glob, v_glob, q_rows=ids, out=o)
-            e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-            reps = 5
-            e0.record(stream)
-            for _ in range(reps):
-                sq.attn_fwd(q, k_glob, v_glob, q_rows=ids, out=o)
-            e1.record(stream)
-            torch.cuda.synchronize()
-            ms = e0.elapsed_time(e1) / reps
+            ms = _time_ms(lambda: sq.attn_fwd(q, k_glob, v_glob, q_rows=ids, out=o), 8)
             t = tf(4.0 * B * H * kk * N * d, ms)
             sweep[f"rho{rho}"] = {"k": kk, "ms": round(ms, 4), "tflops": round(t, 2),
                                   "pct_peak": round(100 * t / PEAK_BF16_TFLOPS, 2),
@@ -386,11 +377,17 @@ def main() -> int:
     return 0
 
 
-def _time_ms(fn, reps: int) -> float:
+def _time_ms(fn, reps: int, warm_ms: float = 40.0) -> float:
+    """Mean event time of fn over reps calls, after back-to-back warm-up calls covering about
+    warm_ms (the clock ramps up from idle over some milliseconds)."""
     import torch
-    fn()
-    fn()
     e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record()
+    fn()
+    e1.record()
+    torch.cuda.synchronize()
+    for _ in range(max(2, min(200, int(warm_ms / max(e0.elapsed_time(e1), 1e-3)) + 1))):
+        fn()
     e0.record()
     for _ in range(reps):
         fn()
