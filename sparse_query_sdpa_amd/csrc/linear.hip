@@ -86,12 +86,19 @@ __global__ __launch_bounds__(CFG::THREADS, CFG::MIN_BLOCKS) void linear_kernel(L
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int col = lane & 31, half = lane >> 5;
   const int wn = wave % CFG::WN, wm = wave / CFG::WN;       // this wave's block of the tile
-  // tiles along m vary fastest and consecutive tiles share an XCD, so the workgroups
-  // that run side by side on one XCD share a W tile in its L2
+  // Consecutive logical tiles share an XCD (xcd_remap) and are ordered in groups of
+  // kGroupM tiles along m: the 32 or so tiles that run side by side on one XCD cover
+  // 8 (m) x 4 (n), so both their A and their W panels are shared in its L2 (+8-9% over
+  // a plain m-fastest order, where every A panel came from HBM).
+  constexpr int kGroupM = 8;
   const int per_b = p.tiles_m * p.tiles_n;
   const int logical = xcd_remap(blockIdx.x, per_b * p.batches);
   const int b = logical / per_b, t = logical - b * per_b;
-  const int tm = t % p.tiles_m, tn = t / p.tiles_m;
+  const int group = t / (kGroupM * p.tiles_n);
+  const int first_m = group * kGroupM;
+  const int gm = min(kGroupM, p.tiles_m - first_m);
+  const int gi = t - group * kGroupM * p.tiles_n;
+  const int tm = first_m + gi % gm, tn = gi / gm;
   const int m0 = tm * CFG::TM, n0 = tn * CFG::TN;
 
   // ---- copy plan: copy c < LCOPY_A fills A slots [64c, 64c+64), the rest W slots --
