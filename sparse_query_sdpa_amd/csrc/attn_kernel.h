@@ -511,6 +511,9 @@ void attn_fwd_kernel(AttnParams p) {
     __syncthreads();                     // ... everyone's, and tile it-1 is no longer read
     if constexpr (!MASKED) {
       if constexpr (STAGED) stage_runs(sc_, mc);
+      // the next tile's copies go out first at the top priority: the sooner they are in
+      // flight, the more of the tile hides their latency (+1-2%)
+      __builtin_amdgcn_s_setprio(2);
       if (it + 1 < ntiles) {
         issue_tile(j0 + BN, nxt);
         if constexpr (HAS_MASK) {
@@ -525,6 +528,7 @@ void attn_fwd_kernel(AttnParams p) {
     }
     const char* Kt = cur;
     const char* Vt = cur + T::K_BYTES;
+    __builtin_amdgcn_s_setprio(0);
 
     f32x16 s0[RB], s1[RB];
     bf16x8 pb0[RB][2], pb1[RB][2];
