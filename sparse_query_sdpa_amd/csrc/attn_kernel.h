@@ -8,16 +8,20 @@
 // call that the rewrite removes, kept for masks outside R.
 //
 // Work decomposition
-//   workgroup = 4 waves = 128 query rows of one (b, h); each wave owns 32 rows;
-//   three workgroups per CU (<= 168 registers per lane; two for d = 128 and for the
-//   masked instances) so the waves on a SIMD overlap one another's MFMA and softmax
-//   work.  Keys stream in tiles of 64 through LDS, double buffered (two separate LDS
-//   objects, loop unrolled by two), one barrier per tile.
+//   workgroup = 4 waves of one (b, h); each wave owns RB row blocks of 32 query rows
+//   (RB = 1: 128 rows per workgroup, three workgroups per CU, <= 168 registers per
+//   lane; two for d = 128 and for the masked instances.  RB = 2, compiled for d = 96
+//   and 72 without mask or key lengths: 256 rows, two workgroups per CU, and every K
+//   and V fragment read from LDS feeds two MFMAs).  The waves on a SIMD overlap one
+//   another's MFMA and softmax work; wave priorities (s_setprio) let the wave whose
+//   softmax is on its critical path issue first.  Keys stream in tiles of 64 through
+//   LDS, double buffered (two separate LDS objects, loop unrolled by two), one barrier
+//   per tile.
 //   K and V tiles are copied global -> LDS by the direct-to-LDS loads
 //   (global_load_lds_dwordx4): no staging registers, no LDS store instructions.
 //   Both tiles keep the natural [key][d] layout; row strides are chosen for
 //   conflict-free LDS reads (see Tile).
-//   Per wave and tile:
+//   Per wave, row block and tile:
 //     S^T[64 keys x 32 queries] = K_tile . Q^T     (v_mfma_f32_32x32x16_bf16)
 //       A = K rows from LDS (ds_read_b128, d contiguous); B = the wave's Q^T,
 //       held in registers for the whole loop.  In the 32x32 accumulator layout
