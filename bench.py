@@ -54,9 +54,14 @@ KERNELS = {"dense": "attn_fwd_kernel<96, false, false, 0, ", "srsu": "attn_fwd_k
 
 
 def attn_source_hash() -> str:
+    """Hash of the attention kernel's code with comments and blank lines removed (a comment
+    edit leaves the recorded counters valid; any code change invalidates them)."""
     h = hashlib.sha256()
     for rel in ATTN_SOURCES:
-        h.update(open(os.path.join(ROOT, rel), "rb").read())
+        text = open(os.path.join(ROOT, rel), encoding="utf-8").read()
+        text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+        lines = (re.sub(r"//.*$", "", ln).rstrip() for ln in text.splitlines())
+        h.update("\n".join(ln for ln in lines if ln).encode())
     return h.hexdigest()[:16]
 
 
