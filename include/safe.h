@@ -41,7 +41,7 @@
 extern "C" {
 #endif
 
-#define SAFE_ABI_VERSION 5
+#define SAFE_ABI_VERSION 6
 
 /* ---- status codes (negative = error) ----------------------------------- */
 enum {
@@ -247,8 +247,9 @@ int safe_kv_assemble(const safe_kv_args* a, void* stream);
  *
  * workspace     optional device scratch of workspace_bytes bytes (16-byte aligned),
  *               owned by the caller and not retained.  The rows are processed in
- *               128-row tiles, one workgroup each; when the tile count leaves the last
- *               round of workgroups on the GPU partly empty, the tiles of that round
+ *               tiles of 128 or 256 rows of one (b, h), one workgroup each (the size
+ *               is chosen per call, see safe_attn_plan); when the tile count leaves
+ *               the last round of workgroups on the GPU partly empty, the tiles of that round
  *               are split along the keys into partial results (unnormalised fp32 O,
  *               running max and sum per row) kept in the workspace and merged by a
  *               second kernel on the same stream.  The result is the same attention,
@@ -279,6 +280,26 @@ int safe_attn_fwd(const safe_attn_args* a, void* stream);
  * only whether mask and q_rows are NULL is read.  Negative: the SAFE_ERR_* status
  * safe_attn_fwd would return for the sizes. */
 int64_t safe_attn_workspace_bytes(const safe_attn_args* a);
+
+/* The schedule safe_attn_fwd runs for these arguments on the current device: rows per
+ * tile (128 or 256), the tile count (tiles per (b, h) x H x B), how many tiles of the
+ * last round are split along the keys and into how many ranges of how many keys, and
+ * the workspace bytes those partials take.  Reads the sizes, flags, workspace_bytes and
+ * whether workspace, q_rows, kv_len and mask are NULL, like the call; dereferences no
+ * pointer of a.  out is a host pointer, filled on SAFE_OK (all zero when there is no
+ * row to compute).  Errors: SAFE_ERR_NULL (a or out NULL) and the size errors of
+ * safe_attn_fwd.  The plan depends only on these values and on the device (its
+ * compute units and the kernels' occupancy), so repeated calls give the same plan. */
+typedef struct {
+  int32_t rows_per_tile;
+  int32_t row_tiles;
+  int32_t split_tiles;      /* 0: nothing is split */
+  int32_t key_ranges;       /* ranges per split tile (1 when nothing is split) */
+  int32_t keys_per_range;   /* keys per range (the last range may hold fewer) */
+  int64_t workspace_bytes;  /* partials of the split tiles */
+} safe_attn_plan_info;
+
+int safe_attn_plan(const safe_attn_args* a, safe_attn_plan_info* out);
 
 /* Human-readable name of a status code (static storage). */
 const char* safe_status_str(int status);

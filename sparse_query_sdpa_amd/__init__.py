@@ -31,7 +31,7 @@ CLASSIFY_ASYNC = 1 << 2
 PCSP_ACCUM = 1 << 3
 PCSP_SELECT = 1 << 4
 
-ABI_VERSION = 5   # struct layouts below match include/safe.h of this version
+ABI_VERSION = 6   # struct layouts below match include/safe.h of this version
 DT_BOOL, DT_BF16, DT_F16, DT_F32 = 0, 1, 2, 3
 MASK_CLASS_NAMES = ("ALL_VALID", "ZERO", "ROW_CONST", "KEY_PADDING", "NONCONST", "BLOCKED", "NONFINITE")
 
@@ -78,6 +78,12 @@ class AttnArgs(ctypes.Structure):
                 ("mask", ctypes.c_void_p), ("mask_dtype", ctypes.c_int32), ("mask_stride", _i64x3)]
 
 
+class AttnPlanInfo(ctypes.Structure):
+    _fields_ = [("rows_per_tile", ctypes.c_int32), ("row_tiles", ctypes.c_int32),
+                ("split_tiles", ctypes.c_int32), ("key_ranges", ctypes.c_int32),
+                ("keys_per_range", ctypes.c_int32), ("workspace_bytes", ctypes.c_int64)]
+
+
 class CfgArgs(ctypes.Structure):
     _fields_ = [("B", ctypes.c_int32), ("N", ctypes.c_int32), ("C", ctypes.c_int32), ("dtype", ctypes.c_int32),
                 ("f_c", ctypes.c_void_p), ("f_u", ctypes.c_void_p), ("out", ctypes.c_void_p),
@@ -118,6 +124,8 @@ def _load():
     lib.safe_sw_cfg.argtypes = [ctypes.POINTER(CfgArgs), ctypes.c_void_p]
     lib.safe_attn_workspace_bytes.restype = ctypes.c_int64
     lib.safe_attn_workspace_bytes.argtypes = [ctypes.POINTER(AttnArgs)]
+    lib.safe_attn_plan.restype = ctypes.c_int
+    lib.safe_attn_plan.argtypes = [ctypes.POINTER(AttnArgs), ctypes.POINTER(AttnPlanInfo)]
     lib.safe_kv_assemble.restype = ctypes.c_int
     lib.safe_kv_assemble.argtypes = [ctypes.POINTER(KvArgs), ctypes.c_void_p]
     lib.safe_pcsp_select.restype = ctypes.c_int
@@ -279,6 +287,31 @@ def attn_workspace_bytes(q: torch.Tensor, k: torch.Tensor, q_rows: Optional[torc
     if n < 0:
         _check("safe_attn_workspace_bytes", int(n))
     return int(n)
+
+
+def attn_plan(q: torch.Tensor, k: torch.Tensor, q_rows: Optional[torch.Tensor] = None,
+              kv_len: Optional[torch.Tensor] = None, mask: Optional[torch.Tensor] = None,
+              workspace_bytes: Optional[int] = None) -> dict:
+    """The schedule attn_fwd runs for these shapes on the current device (safe_attn_plan):
+    rows per tile, tile count, split tiles, key ranges, keys per range, workspace bytes.
+    workspace_bytes None: the workspace attn_fwd allocates by default; 0: no workspace."""
+    B, Nq, H, d = q.shape
+    a = AttnArgs()
+    a.B, a.H, a.Nq, a.Nk, a.d = B, H, Nq, k.shape[1], d
+    a.n_rows = Nq if q_rows is None else q_rows.shape[-1]
+    a.q_rows = None if q_rows is None else _ptr(q_rows)
+    a.q_rows_bstride = 0 if q_rows is None or q_rows.dim() == 1 else q_rows.stride(0)
+    a.kv_len = None if kv_len is None else _ptr(kv_len)
+    a.mask, a.mask_dtype, ms = _attn_mask(mask, B, a.H, Nq, a.Nk)
+    a.mask_stride[:] = ms
+    if workspace_bytes is None:
+        workspace_bytes = attn_workspace_bytes(q, k, q_rows=q_rows, kv_len=kv_len, mask=mask)
+    if workspace_bytes > 0:
+        a.workspace = 16          # only its being non-NULL is read
+        a.workspace_bytes = int(workspace_bytes)
+    info = AttnPlanInfo()
+    _check("safe_attn_plan", lib.safe_attn_plan(ctypes.byref(a), ctypes.byref(info)))
+    return {f: int(getattr(info, f)) for f, _ in AttnPlanInfo._fields_}
 
 
 def kv_assemble(k_fresh: torch.Tensor, v_fresh: torch.Tensor, idx: torch.Tensor, k_cache: torch.Tensor,

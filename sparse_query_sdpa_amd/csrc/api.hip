@@ -9,6 +9,7 @@
 namespace safe {
 int attn_fwd_launch(const safe_attn_args* a, float scale, hipStream_t stream);
 int64_t attn_workspace_bytes(const safe_attn_args* a);
+int attn_plan(const safe_attn_args* a, safe_attn_plan_info* out);
 int sw_cfg_launch(const safe_cfg_args* a, hipStream_t stream);
 int linear_launch(const safe_linear_args* a, hipStream_t stream);
 int kv_assemble_launch(const safe_kv_args* a, bool in_place, hipStream_t stream);
@@ -127,6 +128,13 @@ int64_t safe_attn_workspace_bytes(const safe_attn_args* a) {
   const int st = check_attn_sizes(a);
   if (st != SAFE_OK) return st;
   return attn_workspace_bytes(a);
+}
+
+int safe_attn_plan(const safe_attn_args* a, safe_attn_plan_info* out) {
+  if (out == nullptr) return SAFE_ERR_NULL;
+  const int st = check_attn_sizes(a);
+  if (st != SAFE_OK) return st;
+  return attn_plan(a, out);
 }
 
 int safe_attn_fwd(const safe_attn_args* a, void* stream) {

@@ -139,6 +139,28 @@ Choice choose(const safe_attn_args* a, bool allow_split) {
 
 }  // namespace
 
+// The schedule of a call: the split needs a workspace of at least its bytes, else the
+// best unsplit schedule runs.
+static Choice call_plan(const safe_attn_args* a) {
+  Choice c = choose(a, a->workspace != nullptr && a->workspace_bytes > 0);
+  if (c.split.tail > 0 && a->workspace_bytes < c.split.bytes) c = choose(a, false);
+  return c;
+}
+
+int attn_plan(const safe_attn_args* a, safe_attn_plan_info* out) {
+  *out = safe_attn_plan_info{};
+  if (a->n_rows == 0 || (int64_t)a->H * a->B == 0) return SAFE_OK;
+  const Choice c = call_plan(a);
+  if (c.tiles > 0x7fffffff) return SAFE_ERR_SHAPE;
+  out->rows_per_tile = c.rows;
+  out->row_tiles = (int32_t)c.tiles;
+  out->split_tiles = c.split.tail;
+  out->key_ranges = c.split.tail > 0 ? c.split.nsplit : 1;
+  out->keys_per_range = c.split.tail > 0 ? c.split.split_tiles * BN : a->Nk;
+  out->workspace_bytes = c.split.tail > 0 ? c.split.bytes : 0;
+  return SAFE_OK;
+}
+
 int64_t attn_workspace_bytes(const safe_attn_args* a) {
   if (a->n_rows == 0 || (int64_t)a->H * a->B == 0) return 0;
   const Choice c = choose(a, true);
@@ -165,8 +187,7 @@ int attn_fwd_launch(const safe_attn_args* a, float scale, hipStream_t stream) {
   p.lse = a->lse;
   p.B = a->B; p.H = a->H; p.Nq = a->Nq; p.Nk = a->Nk; p.n_rows = a->n_rows;
   const int mt = mask_kind(a);
-  Choice c = choose(a, a->workspace != nullptr && a->workspace_bytes > 0);
-  if (c.split.tail > 0 && a->workspace_bytes < c.split.bytes) c = choose(a, false);
+  const Choice c = call_plan(a);
   p.n_row_tiles = (a->n_rows + c.rows - 1) / c.rows;
   const int64_t total = (int64_t)p.n_row_tiles * a->H * a->B;
   if (total > 0x7fffffff) return SAFE_ERR_SHAPE;

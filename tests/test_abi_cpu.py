@@ -21,7 +21,7 @@ def declared_functions():
 def test_header_declares_the_four_entry_points():
     names = declared_functions()
     for n in ("safe_mask_classify", "safe_pcsp_select", "safe_kv_assemble", "safe_attn_fwd", "safe_sw_cfg", "safe_linear",
-              "safe_attn_workspace_bytes", "safe_status_str", "safe_abi_version"):
+              "safe_attn_workspace_bytes", "safe_attn_plan", "safe_status_str", "safe_abi_version"):
         assert n in names
 
 
@@ -32,7 +32,7 @@ def test_every_declared_symbol_is_exported():
 
 
 def test_abi_version_and_status_strings():
-    assert sq.lib.safe_abi_version() == 5 == sq.ABI_VERSION
+    assert sq.lib.safe_abi_version() == 6 == sq.ABI_VERSION
     for code, name in sq.STATUS.items():
         assert sq.lib.safe_status_str(code).decode().startswith(name)
     assert sq.lib.safe_status_str(12345) == b"unknown status"
@@ -75,6 +75,19 @@ def test_attn_stride_checks():
         a = _attn_args()
         getattr(a, name)[1] = 1 << 25
         assert sq.lib.safe_attn_fwd(ctypes.byref(a), None) == -5
+
+
+def test_attn_plan_arguments_without_gpu():
+    info = sq.AttnPlanInfo()
+    assert sq.lib.safe_attn_plan(None, ctypes.byref(info)) == -1
+    assert sq.lib.safe_attn_plan(ctypes.byref(_attn_args()), None) == -1
+    for kw, status in ((dict(d=48), -5), (dict(B=-1), -2), (dict(n_rows=5), -2), (dict(flags=1 << 7), -4),
+                       (dict(workspace_bytes=-1), -6)):
+        assert sq.lib.safe_attn_plan(ctypes.byref(_attn_args(**kw)), ctypes.byref(info)) == status, kw
+    # no row to compute: an all-zero plan, no device needed
+    info.rows_per_tile = 7
+    assert sq.lib.safe_attn_plan(ctypes.byref(_attn_args(n_rows=0, Nq=0)), ctypes.byref(info)) == 0
+    assert (info.rows_per_tile, info.row_tiles, info.split_tiles, info.workspace_bytes) == (0, 0, 0, 0)
 
 
 def test_attn_workspace_arguments_without_gpu():

@@ -205,3 +205,42 @@ def test_full_size_workloads_sampled_rows(number):
     samp = _sample_rows(rng, w.N)
     ref, _ = oracle.sdpa(inp["q_x"].value, inp["k_x"].value, inp["v_x"].value, q_rows=samp)
     assert_attn_close(o[:, torch.from_numpy(samp).long()], ref, f"dense N={w.N}")
+
+
+@pytest.mark.parametrize("H,d,Nq,n_sel", [(24, 96, 3201, 2695), (32, 72, 4225, 2440)])
+def test_two_row_blocks_partial_key_tile_ragged_rows(H, d, Nq, n_sel):
+    """Shapes the planner runs with 256-row tiles (two row blocks per wave) and a split tail,
+    with a partial last key tile (Nk % 64 != 0) and row counts that are not a multiple of
+    256: dense, gathered per-sample rows and scattered output, oracle on sampled rows of
+    every (b, h)."""
+    B, Nk = 2, 8250
+    q, k, v = W.attention_inputs(B, Nq, Nk, H, d, seed=40 + d)
+    qd, kd, vd = to_dev_bf16(q), to_dev_bf16(k), to_dev_bf16(v)
+    rng = np.random.default_rng(41)
+    rows = np.stack([W.random_rows(rng, Nq, n_sel) for _ in range(B)])
+    rows_t = to_dev(rows)
+    for name, qr in (("dense", None), ("gathered", rows_t)):
+        plan = sq.attn_plan(qd, kd, q_rows=qr)
+        assert plan["rows_per_tile"] == 256 and plan["split_tiles"] > 0, (name, plan)
+        assert plan["keys_per_range"] % 64 == 0 and plan["key_ranges"] >= 2, (name, plan)
+        # the same plan twice; the unsplit plan when no workspace is given
+        assert sq.attn_plan(qd, kd, q_rows=qr) == plan
+        assert sq.attn_plan(qd, kd, q_rows=qr, workspace_bytes=0)["split_tiles"] == 0
+    o, lse = sq.attn_fwd(qd, kd, vd, return_lse=True)
+    samp = _sample_rows(rng, Nq)
+    ref, ref_lse = oracle.sdpa(q.value, k.value, v.value, q_rows=samp)
+    sel = torch.from_numpy(samp).long()
+    assert_attn_close(o[:, sel], ref, f"dense d={d}")
+    assert_lse_close(lse.cpu()[:, :, sel], ref_lse, f"dense lse d={d}")
+    out = torch.full((B, Nq, H, d), 5.0, dtype=torch.bfloat16, device=qd.device)
+    sq.attn_fwd(qd, kd, vd, q_rows=rows_t, out=out, scatter_out=True)
+    compact = sq.attn_fwd(qd, kd, vd, q_rows=rows_t)
+    samp = _sample_rows(rng, rows.shape[1])
+    for b in range(B):
+        ref, _ = oracle.sdpa(q.value[b:b + 1], k.value[b:b + 1], v.value[b:b + 1], q_rows=rows[b, samp])
+        assert_attn_close(compact[b:b + 1, torch.from_numpy(samp).long()], ref, f"gathered b={b} d={d}")
+        assert torch.equal(out[b, torch.from_numpy(rows[b]).long()], compact[b]), "scatter = compact rows"
+    untouched = np.ones((B, Nq), bool)
+    for b in range(B):
+        untouched[b, rows[b]] = False
+    assert bool((out.float().cpu().numpy()[untouched] == 5.0).all())
