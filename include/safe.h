@@ -103,7 +103,7 @@ typedef struct {
  * safe_mask_classify -- certify whether an attention mask is removable.
  *
  * Defined by the paper's Eq. 6 (the row-constant class R), the rule that
- * batched or head-specific masks are judged on every broadcast query row, the
+ * batched or head-specific masks are classified on every broadcast query row, the
  * statements after Eq. 7 (all-valid Boolean and all-zero additive masks are in
  * R; finite non-uniform biases and masks with blocked positions are kept) and
  * the Eq. 8 rewrite (drop the mask iff it is in R).  A mask whose rows are all
