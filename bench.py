@@ -377,6 +377,7 @@ def main() -> int:
 
     if not args.no_cpu_baseline:
         out["cpu_baseline"] = cpu_baseline(inp, args.cpu_rows)
+        out["cpu_baseline_small_case"] = oracle_small_case()
 
     print(json.dumps(out), flush=True)
     return 0
@@ -647,6 +648,48 @@ def cpu_baseline(inp, rows_per_bh: int):
     return {"value": round(flops / secs / 1e12, 6), "unit": "TFLOP/s", "cores": int(cores), "kind": "oracle",
             "sample": f"SRSU self-attention on {rows_per_bh} query rows per sample x {H} heads against all {N} keys "
                       f"(B={B}, d={d}): {flops / 1e9:.1f} GFLOP in fp64, {secs:.1f} s"}
+
+
+def oracle_small_case() -> dict:
+    """The whole fp64 oracle path on the 16x16-grid workload (B=1, H=2, d=32, N=256, M=16,
+    kv_len=11): the six classifier cases, PCSP accumulate + smooth + top-k, K/V assembly, SRSU
+    self- and cross-attention and the dense pass, timed on all host cores and on one."""
+    import numpy as np
+
+    import oracle
+    import workloads as W
+    from threadpoolctl import threadpool_info, threadpool_limits
+    inp = W.workload_inputs(1)
+    w = inp["workload"]
+    masks = W.c1_mask_cases()
+    wts = W.pcsp_content_weights(inp["kv_len"], w.M)
+    k = w.k_for(25)
+    q, kx, vx = inp["q_x"].value, inp["k_x"].value, inp["v_x"].value
+
+    def path():
+        for m in masks.values():
+            oracle.classify_mask(m, m.dtype == np.uint8)
+        _, _, _, idx = oracle.pcsp_scores(inp["q_c"].value, inp["k_txt"].value, inp["kv_len"], wts,
+                                          w.grid_h, w.grid_w, 1.0, k)
+        idx2 = np.broadcast_to(idx, (w.B, k))
+        kg = oracle.kv_assemble(np.stack([kx[b, idx2[b]] for b in range(w.B)]), idx2, kx)
+        vg = oracle.kv_assemble(np.stack([vx[b, idx2[b]] for b in range(w.B)]), idx2, vx)
+        oracle.sdpa(q, kg, vg, q_rows=idx2)
+        oracle.sdpa(inp["q_c"].value, inp["k_txt"].value, inp["v_txt"].value, q_rows=idx2, kv_len=inp["kv_len"])
+        oracle.sdpa(q, kx, vx)
+
+    def timed(reps=3):
+        path()
+        t0 = time.perf_counter()
+        for _ in range(reps):
+            path()
+        return (time.perf_counter() - t0) / reps * 1e3
+    cores = max([i.get("num_threads", 1) for i in threadpool_info()] or [1])
+    all_ms = timed()
+    with threadpool_limits(limits=1):
+        one_ms = timed()
+    return {"workload": "16x16 grid: B=1 H=2 d=32 N=256 M=16 kv_len=11, k=64 (rho 25%)", "kind": "oracle",
+            "all_cores_ms": round(all_ms, 3), "cores": int(cores), "one_core_ms": round(one_ms, 3)}
 
 
 if __name__ == "__main__":
