@@ -192,7 +192,7 @@ def main() -> int:
         pmc_summary(*args.pmc_summary)
         return 0
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) > 1:
-        print("bench.py measures one GPU only: this build has no multi-GPU path "
+        print("bench.py measures one GPU only: the library has no multi-GPU path "
               "(the work shards by (sample, head) with no exchange; see the design notes). "
               "Run with --gpus 1.", file=sys.stderr)
         return 2
