@@ -193,7 +193,7 @@ def main() -> int:
         return 0
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) > 1:
         print("bench.py measures one GPU only: the library has no multi-GPU path "
-              "(the work shards by (sample, head) with no exchange; see the design notes). "
+              "(attention shards by (sample, head) pairs with no exchange between GPUs). "
               "Run with --gpus 1.", file=sys.stderr)
         return 2
     if args.copy_probe:
