@@ -293,6 +293,7 @@ def main() -> int:
     kv_bytes = 4.0 * B * N * H * d * 2
     tf = lambda fl, ms: fl / (ms * 1e-3) / 1e12
     traffic = recorded_traffic()
+    plans = {"dense": sq.attn_plan(q, kx), "srsu_self": sq.attn_plan(q, k_glob, q_rows=idx0)}
     srsu_tf = tf(fl_srsu, stage_ms["srsu_self"])
     dense_tf = tf(fl_dense, stage_ms["dense"])
     out = {
@@ -331,6 +332,7 @@ def main() -> int:
                           "frac": round(srsu_tf / PEAK_BF16_TFLOPS, 4),
                           "traffic": traffic.get("srsu", {}).get("bytes"),
                           "algorithmic_flops_per_launch": fl_srsu, "avg_launch_ms": round(stage_ms["srsu_self"], 4)},
+        "attn_plans": plans,
         "peak_mem_gb": round(torch.cuda.max_memory_allocated() / 1e9, 2),
         "pages_context": "PyTorch SDPA stack on unstated hardware: masked SDPA 4.1-5.8x slower than mask-free; "
                          "end-to-end 2.69x at 1024^2 and 5.09x at 2560^2; peak memory 94.1 -> 27.9 GB",

@@ -244,3 +244,20 @@ def test_two_row_blocks_partial_key_tile_ragged_rows(H, d, Nq, n_sel):
     for b in range(B):
         untouched[b, rows[b]] = False
     assert bool((out.float().cpu().numpy()[untouched] == 5.0).all())
+
+
+def test_two_row_blocks_unsplit_ragged():
+    """256-row tiles with no split (the tile count fills whole rounds), a ragged last row
+    tile and a partial last key tile: oracle on sampled rows of every (b, h), LSE included."""
+    B, Nq, Nk, H, d = 2, 8100, 4133, 24, 96
+    q, k, v = W.attention_inputs(B, Nq, Nk, H, d, seed=44)
+    qd, kd, vd = to_dev_bf16(q), to_dev_bf16(k), to_dev_bf16(v)
+    plan = sq.attn_plan(qd, kd)
+    assert plan["rows_per_tile"] == 256 and plan["split_tiles"] == 0 and plan["workspace_bytes"] == 0, plan
+    o, lse = sq.attn_fwd(qd, kd, vd, return_lse=True)
+    rng = np.random.default_rng(45)
+    samp = np.unique(np.concatenate([_sample_rows(rng, Nq), [Nq - 1, Nq - 2, 31 * 256, 31 * 256 - 1]]))
+    ref, ref_lse = oracle.sdpa(q.value, k.value, v.value, q_rows=samp)
+    sel = torch.from_numpy(samp).long()
+    assert_attn_close(o[:, sel], ref, "unsplit 256-row tiles")
+    assert_lse_close(lse.cpu()[:, :, sel], ref_lse, "unsplit 256-row tiles lse")
