@@ -110,33 +110,32 @@ def pmc_summary(fetch_csv: str, fetch_copy_csv: str, write_csv: str, write_copy_
 
 
 def mfma_busy_summary(path: str, n_xcd: int = 8, n_simd: int = 1024) -> None:
-    """Markdown of the MFMA-busy fraction per kernel from a rocprofv3 --pmc run of
-    SQ_VALU_MFMA_BUSY_CYCLES, SQ_INSTS_MFMA and GRBM_GUI_ACTIVE: GRBM_GUI_ACTIVE is summed over
-    the XCDs (cycles of the launch = value / n_xcd) and the busy count over all SIMDs, so
-    busy / (cycles x n_simd) is the fraction of SIMD cycles with an MFMA in flight."""
-    rows = list(csv.DictReader(open(path)))
-    per = {}
-    for r in rows:
-        name = r["Kernel_Name"]
-        key = name.replace("(anonymous namespace)::", "").split("(")[0].replace("void ", "")
+    """Markdown of the MFMA-busy fraction per kernel and workload shape (launches grouped by
+    grid and MFMA instruction count) from a rocprofv3 --pmc run of SQ_VALU_MFMA_BUSY_CYCLES,
+    SQ_INSTS_MFMA and GRBM_GUI_ACTIVE: GRBM_GUI_ACTIVE is summed over the XCDs (cycles of the
+    launch = value / n_xcd) and the busy count over all SIMDs, so busy / (cycles x n_simd) is
+    the fraction of SIMD cycles with an MFMA in flight."""
+    disp = {}
+    for r in csv.DictReader(open(path)):
+        key = r["Kernel_Name"].replace("(anonymous namespace)::", "").split("(")[0].replace("void ", "")
         if "attn_fwd_kernel" not in key and "linear_kernel" not in key:
             continue
-        d = per.setdefault(key, {}).setdefault(r["Dispatch_Id"], {})
+        d = disp.setdefault(r["Dispatch_Id"], {"key": key, "grid": int(r["Grid_Size"])})
         d[r["Counter_Name"]] = d.get(r["Counter_Name"], 0.0) + float(r["Counter_Value"])
         d["ns"] = float(r["End_Timestamp"]) - float(r["Start_Timestamp"])
-    print("| kernel | launches | MFMA instr. per launch | cycles per launch (GRBM / XCDs) | clock MHz | "
-          "MFMA TFLOP/s (instr. x 32768 / time) | MFMA busy fraction |")
-    print("|---|---|---|---|---|---|---|")
-    for key, disp in sorted(per.items()):
-        ok = [v for v in disp.values() if all(c in v for c in ("SQ_VALU_MFMA_BUSY_CYCLES", "SQ_INSTS_MFMA", "GRBM_GUI_ACTIVE"))]
-        if not ok:
-            continue
+    groups = {}
+    for d in disp.values():
+        if all(c in d for c in ("SQ_VALU_MFMA_BUSY_CYCLES", "SQ_INSTS_MFMA", "GRBM_GUI_ACTIVE")):
+            groups.setdefault((d["key"], d["grid"], int(d["SQ_INSTS_MFMA"])), []).append(d)
+    print("| kernel | grid (threads) | launches | MFMA instr. per launch | TFLOP per launch | cycles per launch "
+          "(GRBM / XCDs) | clock MHz | MFMA TFLOP/s (instr. x 32768 / time) | MFMA busy fraction |")
+    print("|---|---|---|---|---|---|---|---|---|")
+    for (key, grid, inst), ok in sorted(groups.items()):
         busy = sum(v["SQ_VALU_MFMA_BUSY_CYCLES"] for v in ok) / len(ok)
-        inst = sum(v["SQ_INSTS_MFMA"] for v in ok) / len(ok)
         cyc = sum(v["GRBM_GUI_ACTIVE"] for v in ok) / len(ok) / n_xcd
         ns = sum(v["ns"] for v in ok) / len(ok)
-        print(f"| `{key}` | {len(ok)} | {inst:.4g} | {cyc:.4g} | {cyc / ns * 1e3:.0f} | "
-              f"{inst * 32768 / ns / 1e3:.0f} | {busy / (cyc * n_simd):.3f} |")
+        print(f"| `{key}` | {grid} | {len(ok)} | {inst:.4g} | {inst * 32768 / 1e12:.3f} | {cyc:.4g} | "
+              f"{cyc / ns * 1e3:.0f} | {inst * 32768 / ns / 1e3:.0f} | {busy / (cyc * n_simd):.3f} |")
 
 
 def rocprof_summary(path: str) -> None:
