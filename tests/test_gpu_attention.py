@@ -261,3 +261,33 @@ def test_two_row_blocks_unsplit_ragged():
     sel = torch.from_numpy(samp).long()
     assert_attn_close(o[:, sel], ref, "unsplit 256-row tiles")
     assert_lse_close(lse.cpu()[:, :, sel], ref_lse, "unsplit 256-row tiles lse")
+
+
+@pytest.mark.parametrize("d", [32, 64, 72, 96, 128])
+def test_plan_is_consistent_with_the_workspace_query(d):
+    """safe_attn_plan agrees with safe_attn_workspace_bytes, counts the tiles it says, covers
+    every key with its ranges, and keeps 128-row tiles with key lengths and at head dimensions
+    without a two-row-block instance."""
+    dev = torch.device("cuda:0")
+    for B, Nq, Nk, H, n_sel in ((2, 300, 3000, 3, None), (2, 5000, 4133, 8, 3001), (1, 20000, 700, 4, None),
+                                (2, 1000, 64, 24, 17)):
+        q = torch.zeros((B, Nq, H, d), dtype=torch.bfloat16, device=dev)
+        k = torch.zeros((B, Nk, H, d), dtype=torch.bfloat16, device=dev)
+        rows = None if n_sel is None else torch.arange(n_sel, dtype=torch.int32, device=dev)
+        n_rows = Nq if rows is None else n_sel
+        for kw in ({}, {"kv_len": torch.full((B,), Nk // 2, dtype=torch.int32, device=dev)}):
+            plan = sq.attn_plan(q, k, q_rows=rows, **kw)
+            assert plan["rows_per_tile"] in (128, 256), plan
+            if kw or d not in (72, 96):
+                assert plan["rows_per_tile"] == 128, plan
+            assert plan["row_tiles"] == -(-n_rows // plan["rows_per_tile"]) * H * B, plan
+            assert plan["workspace_bytes"] == sq.attn_workspace_bytes(q, k, q_rows=rows, **kw), plan
+            if plan["split_tiles"]:
+                assert not kw, "the key-length form is never split"
+                assert plan["split_tiles"] <= plan["row_tiles"], plan
+                assert plan["key_ranges"] >= 2 and plan["keys_per_range"] % 64 == 0
+                assert (plan["key_ranges"] - 1) * plan["keys_per_range"] < Nk <= plan["key_ranges"] * plan["keys_per_range"]
+                assert plan["workspace_bytes"] == plan["split_tiles"] * plan["key_ranges"] * plan["rows_per_tile"] * (4 * d + 8)
+            else:
+                assert plan["key_ranges"] == 1 and plan["workspace_bytes"] == 0
+            assert sq.attn_plan(q, k, q_rows=rows, workspace_bytes=0, **kw)["split_tiles"] == 0
