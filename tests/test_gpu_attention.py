@@ -291,3 +291,22 @@ def test_plan_is_consistent_with_the_workspace_query(d):
             else:
                 assert plan["key_ranges"] == 1 and plan["workspace_bytes"] == 0
             assert sq.attn_plan(q, k, q_rows=rows, workspace_bytes=0, **kw)["split_tiles"] == 0
+
+
+def test_side_stream_matches_default_stream():
+    """The same calls enqueued on a second stream (its own workspace in the binding) give
+    bitwise the same results as on the default stream, split tails included."""
+    B, N, H, d = 2, 3000, 4, 96
+    q, k, v = W.attention_inputs(B, N, N, H, d, seed=46)
+    qd, kd, vd = to_dev_bf16(q), to_dev_bf16(k), to_dev_bf16(v)
+    rows_t = to_dev(W.random_rows(np.random.default_rng(47), N, 1111))
+    assert sq.attn_plan(qd, kd)["split_tiles"] > 0, "the shape must take the split path"
+    ref_d, ref_lse = sq.attn_fwd(qd, kd, vd, return_lse=True)
+    ref_s = sq.attn_fwd(qd, kd, vd, q_rows=rows_t)
+    torch.cuda.synchronize()
+    side = torch.cuda.Stream()
+    with torch.cuda.stream(side):
+        od, lse = sq.attn_fwd(qd, kd, vd, return_lse=True)
+        os_ = sq.attn_fwd(qd, kd, vd, q_rows=rows_t)
+    side.synchronize()
+    assert torch.equal(od, ref_d) and torch.equal(lse, ref_lse) and torch.equal(os_, ref_s)
