@@ -5,7 +5,7 @@ import torch
 
 import oracle
 import workloads as W
-from gpu_util import to_dev, to_dev_bf16
+from gpu_util import assert_attn_close, to_dev, to_dev_bf16
 
 pytestmark = pytest.mark.gpu
 
@@ -70,7 +70,8 @@ def test_out_of_range_indices_are_skipped_or_rejected():
 
 
 def test_multistep_cache_workload():
-    """One anchor then three SRSU steps on the 64x64-grid workload (drift N(0, 0.05))."""
+    """One anchor then three SRSU steps on the 64x64-grid workload (drift N(0, 0.05)): the
+    assembly bit-exact, SRSU self- and cross-attention against the oracle at every step."""
     inp = W.workload_inputs(2)
     w = inp["workload"]
     rng = W.rng_for(2, stream=4)
@@ -88,3 +89,17 @@ def test_multistep_cache_workload():
         rk = oracle.kv_assemble(fk.bits, S, ref_k)
         rv = oracle.kv_assemble(fv.bits, S, ref_v)
         assert np.array_equal(_bits(ko), rk) and np.array_equal(_bits(vo), rv), step
+        # SRSU self-attention on the assembled K/V (Eq. 16) and the text cross-attention with
+        # per-sample lengths (Eq. 17), oracle on sampled rows of S in every (b, h)
+        qx = to_dev_bf16(inp["q_x"])
+        o_s = sq.attn_fwd(qx, ko, vo, q_rows=to_dev(S))
+        o_c = sq.attn_fwd(to_dev_bf16(inp["q_c"]), to_dev_bf16(inp["k_txt"]), to_dev_bf16(inp["v_txt"]),
+                          q_rows=to_dev(S), kv_len=to_dev(inp["kv_len"]))
+        samp = np.unique(np.concatenate([[0, len(S) - 1], rng.choice(len(S), 24, replace=False)]))
+        kg = oracle.kv_assemble(fk.value, S, inp["k_x"].value)   # the oracle's own global K/V
+        vg = oracle.kv_assemble(fv.value, S, inp["v_x"].value)
+        ref, _ = oracle.sdpa(inp["q_x"].value, kg, vg, q_rows=S[samp])
+        assert_attn_close(o_s[:, torch.from_numpy(samp).long()], ref, f"srsu step {step}")
+        ref, _ = oracle.sdpa(inp["q_c"].value, inp["k_txt"].value, inp["v_txt"].value, q_rows=S[samp],
+                             kv_len=inp["kv_len"])
+        assert_attn_close(o_c[:, torch.from_numpy(samp).long()], ref, f"cross step {step}")
