@@ -107,6 +107,18 @@ def pmc_summary(fetch_csv: str, fetch_copy_csv: str, write_csv: str, write_copy_
         lines.append(f"traffic {key} bytes={total} fetch={int(f * ff)} write={int(w * fw)} source={src}")
     print()
     print("\n".join(lines))
+    # the HBM-bound kernels of the step against their algorithmic bytes
+    N, BH, hd = 25600, 2 * 24, 96
+    hbm = (("mask_scan_kernel<", "classifier: [2,1,N,N] bf16 mask read once", 2 * N * N * 2),
+           ("kv_assemble_packed_kernel", "K/V assembly out of place: cache and fresh rows read, K/V written",
+            4 * 2 * N * 24 * hd * 2))
+    print("\n| HBM-bound kernel | launches | HBM bytes per launch (scaled) | algorithmic bytes | ratio |")
+    print("|---|---|---|---|---|")
+    for needle, what, alg in hbm:
+        f, nf = mean_of(fetch, lambda n: needle in n)
+        w, _ = mean_of(write, lambda n: needle in n)
+        total = f * ff + w * fw
+        print(f"| `{needle}` ({what}) | {nf} | {total / 1e6:.1f} MB | {alg / 1e6:.1f} MB | {total / alg:.3f} |")
 
 
 def mfma_busy_summary(path: str, n_xcd: int = 8, n_simd: int = 1024) -> None:
