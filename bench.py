@@ -372,6 +372,7 @@ def main() -> int:
                                        "pct_hbm": round(100 * ip_bytes / (ms_ip * 1e-3) / 1e9 / PEAK_HBM_GBS, 2),
                                        "bytes": ip_bytes}
         del kc2, vc2
+        out["fused_kv"] = fused_kv_lines(sq, q, kx, vx, k_fresh, v_fresh, idx, o_srsu, stage_ms, fl_srsu, tf)
         out["sw_cfg"] = sw_cfg_lines(sq, acc, wl, args.sigma, k)
         out["hbm_measured"] = hbm_measured(out)
         out["midt"] = midt_lines(sq, q, kx, vx, mask, idx, stage_ms, tf)
@@ -456,6 +457,21 @@ def hbm_measured(out: dict) -> dict:
     return {"copy_gbs": round(gbs, 1), "copy_pct_spec": round(100 * gbs / PEAK_HBM_GBS, 2),
             "classify_pct_of_copy": round(100 * out["classify_gbs"] / gbs, 2),
             "kv_assemble_pct_of_copy": round(100 * out["kv_assemble_gbs"] / gbs, 2)}
+
+
+def fused_kv_lines(sq, q, kx, vx, k_fresh, v_fresh, idx, o, stage_ms: dict, fl_srsu: float, tf) -> dict:
+    """SRSU self-attention reading the global K/V through the source map (the fresh rows of S
+    and the cache, no assembled copy) against the two passes kv_assemble + attention."""
+    B, N = kx.shape[0], kx.shape[1]
+    src = sq.kv_source_map(idx, N, batch=B)
+    ms_map = _time_ms(lambda: sq.kv_source_map(idx, N, batch=B, out=src), 20)
+    ms_f = _time_ms(lambda: sq.attn_fwd(q, kx, vx, q_rows=idx, out=o, kv_src=src, k_fresh=k_fresh,
+                                        v_fresh=v_fresh), 8)
+    two = stage_ms["kv_assemble"] + stage_ms["srsu_self"]
+    return {"map_ms": round(ms_map, 4), "fused_attn_ms": round(ms_f, 4),
+            "fused_attn_tflops": round(tf(fl_srsu, ms_f), 2),
+            "two_pass_ms": round(two, 4), "fused_over_two_pass": round((ms_f + ms_map) / two, 3),
+            "plan": sq.attn_plan(q, kx, q_rows=idx, kv_src=src)}
 
 
 def block_lines(sq, W, idx, tf) -> dict:

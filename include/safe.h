@@ -41,7 +41,7 @@
 extern "C" {
 #endif
 
-#define SAFE_ABI_VERSION 6
+#define SAFE_ABI_VERSION 7
 
 /* ---- status codes (negative = error) ----------------------------------- */
 enum {
@@ -205,6 +205,13 @@ typedef struct {
 
 int safe_kv_assemble(const safe_kv_args* a, void* stream);
 
+/* Source map of the fused global K/V read (see safe_attn_fwd.kv_src): writes kv_src,
+ * device int32 [B, N] row-major (sample stride N), with kv_src[b][j] = r when
+ * idx[b][r] == j and -1 for the other tokens.  Of a, only B, N, idx, nsel, idx_bstride
+ * and flags are read; idx must be ascending (SAFE_FLAG_CHECK verifies it and the range,
+ * SAFE_ERR_RANGE).  Entries outside [0, N) are skipped.  Enqueued on stream; one launch. */
+int safe_kv_source_map(const safe_kv_args* a, int32_t* kv_src, void* stream);
+
 /*
  * safe_attn_fwd -- scaled dot-product attention, normally without a mask tensor.
  *
@@ -256,6 +263,19 @@ int safe_kv_assemble(const safe_kv_args* a, void* stream);
  *               rounded differently for those rows.  With workspace NULL or smaller
  *               than safe_attn_workspace_bytes() reports, no tile is split.  Calls that
  *               share a workspace must be ordered on one stream.
+ *
+ * kv_src        optional fused global K/V (Eq. 14 and 16 read in place of a separate
+ *               safe_kv_assemble pass): device int32 [B, Nk] (sample stride
+ *               kv_src_bstride, 0 = one map for every sample).  Key j of sample b is
+ *               read from row kv_src[b][j] of k_fresh / v_fresh ([B, n_fresh, H, d] bf16,
+ *               element strides fresh_stride) when that value is in [0, n_fresh), and
+ *               from k / v (the cache) otherwise.  safe_kv_source_map builds the map
+ *               from the ascending index list of S.  The result is attention on the
+ *               assembled K/V (bit for bit where safe_attn_plan reports the same schedule
+ *               for both calls; the split of long key ranges may differ).  Not combinable with kv_len or a mask
+ *               (SAFE_ERR_UNSUPPORTED); n_fresh < 2^24, fresh_stride[1] < 2^23 and
+ *               n_fresh * fresh_stride[1] * 2 + 2 d <= 2^32 bytes, else SAFE_ERR_UNSUPPORTED.
+ *               NULL: k and v are read as given.
  */
 typedef struct {
   int32_t B, H, Nq, Nk, d;
@@ -270,6 +290,8 @@ typedef struct {
   uint32_t flags;                         /* SAFE_ATTN_SCATTER_OUT | SAFE_FLAG_CHECK */
   void* workspace; int64_t workspace_bytes;   /* optional, see above */
   const void* mask; int32_t mask_dtype; int64_t mask_stride[3];   /* optional, see above */
+  const int32_t* kv_src; int64_t kv_src_bstride;                   /* optional, see below */
+  const void* k_fresh; const void* v_fresh; int64_t fresh_stride[3]; int32_t n_fresh;
 } safe_attn_args;
 
 int safe_attn_fwd(const safe_attn_args* a, void* stream);

@@ -31,7 +31,7 @@ CLASSIFY_ASYNC = 1 << 2
 PCSP_ACCUM = 1 << 3
 PCSP_SELECT = 1 << 4
 
-ABI_VERSION = 6   # struct layouts below match include/safe.h of this version
+ABI_VERSION = 7   # struct layouts below match include/safe.h of this version
 DT_BOOL, DT_BF16, DT_F16, DT_F32 = 0, 1, 2, 3
 MASK_CLASS_NAMES = ("ALL_VALID", "ZERO", "ROW_CONST", "KEY_PADDING", "NONCONST", "BLOCKED", "NONFINITE")
 
@@ -75,7 +75,10 @@ class AttnArgs(ctypes.Structure):
                 ("q_rows", ctypes.c_void_p), ("n_rows", ctypes.c_int32), ("q_rows_bstride", ctypes.c_int64),
                 ("kv_len", ctypes.c_void_p), ("scale", ctypes.c_float), ("lse", ctypes.c_void_p),
                 ("flags", ctypes.c_uint32), ("workspace", ctypes.c_void_p), ("workspace_bytes", ctypes.c_int64),
-                ("mask", ctypes.c_void_p), ("mask_dtype", ctypes.c_int32), ("mask_stride", _i64x3)]
+                ("mask", ctypes.c_void_p), ("mask_dtype", ctypes.c_int32), ("mask_stride", _i64x3),
+                ("kv_src", ctypes.c_void_p), ("kv_src_bstride", ctypes.c_int64),
+                ("k_fresh", ctypes.c_void_p), ("v_fresh", ctypes.c_void_p), ("fresh_stride", _i64x3),
+                ("n_fresh", ctypes.c_int32)]
 
 
 class AttnPlanInfo(ctypes.Structure):
@@ -128,6 +131,8 @@ def _load():
     lib.safe_attn_plan.argtypes = [ctypes.POINTER(AttnArgs), ctypes.POINTER(AttnPlanInfo)]
     lib.safe_kv_assemble.restype = ctypes.c_int
     lib.safe_kv_assemble.argtypes = [ctypes.POINTER(KvArgs), ctypes.c_void_p]
+    lib.safe_kv_source_map.restype = ctypes.c_int
+    lib.safe_kv_source_map.argtypes = [ctypes.POINTER(KvArgs), ctypes.c_void_p, ctypes.c_void_p]
     lib.safe_pcsp_select.restype = ctypes.c_int
     lib.safe_pcsp_select.argtypes = [ctypes.POINTER(PcspArgs), ctypes.c_void_p, ctypes.POINTER(ctypes.c_size_t),
                                      ctypes.c_void_p]
@@ -223,9 +228,13 @@ def _attn_mask(mask: Optional[torch.Tensor], B: int, H: int, Nq: int, Nk: int):
 def attn_fwd(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, q_rows: Optional[torch.Tensor] = None,
              kv_len: Optional[torch.Tensor] = None, scale: Optional[float] = None, out: Optional[torch.Tensor] = None,
              return_lse: bool = False, scatter_out: bool = False, check: bool = False, stream=None,
-             workspace="auto", mask: Optional[torch.Tensor] = None):
+             workspace="auto", mask: Optional[torch.Tensor] = None, kv_src: Optional[torch.Tensor] = None,
+             k_fresh: Optional[torch.Tensor] = None, v_fresh: Optional[torch.Tensor] = None):
     """Attention on all rows (q_rows None) or on gathered rows q_rows [n] / [B, n]; see safe.h.
 
+    kv_src: optional source map [Nk] / [1|B, Nk] int32 (kv_source_map) for the fused global
+    K/V read: key j comes from row kv_src[.., j] of k_fresh / v_fresh [B, n_fresh, H, d]
+    when that is in [0, n_fresh), else from k / v (the cache).
     workspace: "auto" (a buffer cached per device and stream, sized by
     safe_attn_workspace_bytes), None (no tail split), or a uint8 device tensor.
     mask: optional dense mask [B|1, H|1, Nq|1, Nk] (size-1 dims broadcast), indexed by
@@ -258,6 +267,7 @@ def attn_fwd(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, q_rows: Optional
                  (ATTN_SCATTER_OUT if scatter_out else 0) | (FLAG_CHECK if check else 0), None, 0)
     a.mask, a.mask_dtype, ms = _attn_mask(mask, B, H, Nq, Nk)
     a.mask_stride[:] = ms
+    _attn_kv_src(a, kv_src, k_fresh, v_fresh, B, Nk, H, d)
     st = _stream(stream)
     if isinstance(workspace, str):
         if workspace != "auto":
@@ -269,8 +279,57 @@ def attn_fwd(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, q_rows: Optional
     return (out, lse) if return_lse else out
 
 
+def _attn_kv_src(a, kv_src, k_fresh, v_fresh, B, Nk, H, d):
+    """Fill the fused global K/V fields of AttnArgs (all three tensors or none)."""
+    if kv_src is None:
+        if k_fresh is not None or v_fresh is not None:
+            raise ValueError("k_fresh / v_fresh need kv_src")
+        return
+    kv_src = _i32(kv_src, "kv_src")
+    if kv_src.dim() not in (1, 2) or kv_src.shape[-1] != Nk or kv_src.stride(-1) != 1 \
+            or (kv_src.dim() == 2 and kv_src.shape[0] not in (1, B)):
+        raise ValueError("kv_src must be [Nk], [1, Nk] or [B, Nk] with contiguous rows")
+    if k_fresh is None or v_fresh is None:
+        raise ValueError("kv_src needs k_fresh and v_fresh")
+    _bits16(k_fresh, "k_fresh")
+    _bits16(v_fresh, "v_fresh")
+    if k_fresh.dim() != 4 or k_fresh.shape[0] != B or k_fresh.shape[2:] != (H, d) or v_fresh.shape != k_fresh.shape:
+        raise ValueError("k_fresh and v_fresh must be [B, n_fresh, H, d]")
+    fs = _bnhd(k_fresh, "k_fresh")
+    if _bnhd(v_fresh, "v_fresh")[:] != fs[:]:
+        raise ValueError("k_fresh and v_fresh must share strides")
+    shared = kv_src.dim() == 1 or kv_src.shape[0] == 1
+    a.kv_src, a.kv_src_bstride = _ptr(kv_src), (0 if shared else kv_src.stride(0))
+    a.k_fresh, a.v_fresh, a.n_fresh = _ptr(k_fresh), _ptr(v_fresh), k_fresh.shape[1]
+    a.fresh_stride[:] = fs[:]
+
+
+def kv_source_map(idx: torch.Tensor, n_tokens: int, batch: Optional[int] = None, out: Optional[torch.Tensor] = None,
+                  check: bool = False, stream=None) -> torch.Tensor:
+    """Source map [B, N] int32 of the fused global K/V read: r where idx[b, r] == j, else -1.
+
+    idx: ascending int32 token list [nsel] (shared by the batch, B = batch) or [B, nsel]."""
+    idx = _i32(idx, "idx")
+    if idx.dim() == 1:
+        B, nsel, ibs = (1 if batch is None else int(batch)), idx.shape[0], 0
+    else:
+        B, nsel, ibs = idx.shape[0], idx.shape[1], idx.stride(0)
+        if idx.stride(1) != 1:
+            raise ValueError("idx rows must be contiguous")
+    if out is None:
+        out = torch.empty((B, n_tokens), dtype=torch.int32, device=idx.device)
+    if out.dtype != torch.int32 or out.shape != (B, n_tokens) or not out.is_contiguous():
+        raise ValueError("out must be contiguous int32 [B, N]")
+    a = KvArgs()
+    a.B, a.N, a.nsel, a.idx, a.idx_bstride = B, n_tokens, nsel, _ptr(idx), ibs
+    a.flags = FLAG_CHECK if check else 0
+    _check("safe_kv_source_map", lib.safe_kv_source_map(ctypes.byref(a), _ptr(out), _stream(stream)))
+    return out
+
+
 def attn_workspace_bytes(q: torch.Tensor, k: torch.Tensor, q_rows: Optional[torch.Tensor] = None,
-                         kv_len: Optional[torch.Tensor] = None, mask: Optional[torch.Tensor] = None) -> int:
+                         kv_len: Optional[torch.Tensor] = None, mask: Optional[torch.Tensor] = None,
+                         kv_src: Optional[torch.Tensor] = None) -> int:
     """Workspace bytes attn_fwd would use on the current device for these shapes (0: no split)."""
     B, Nq, H, d = q.shape
     if q_rows is None:
@@ -283,6 +342,7 @@ def attn_workspace_bytes(q: torch.Tensor, k: torch.Tensor, q_rows: Optional[torc
     a.kv_len = None if kv_len is None else _ptr(kv_len)
     a.mask, a.mask_dtype, ms = _attn_mask(mask, B, a.H, Nq, a.Nk)
     a.mask_stride[:] = ms
+    a.kv_src = None if kv_src is None else 16   # only its being non-NULL is read
     n = lib.safe_attn_workspace_bytes(ctypes.byref(a))
     if n < 0:
         _check("safe_attn_workspace_bytes", int(n))
@@ -291,7 +351,7 @@ def attn_workspace_bytes(q: torch.Tensor, k: torch.Tensor, q_rows: Optional[torc
 
 def attn_plan(q: torch.Tensor, k: torch.Tensor, q_rows: Optional[torch.Tensor] = None,
               kv_len: Optional[torch.Tensor] = None, mask: Optional[torch.Tensor] = None,
-              workspace_bytes: Optional[int] = None) -> dict:
+              workspace_bytes: Optional[int] = None, kv_src: Optional[torch.Tensor] = None) -> dict:
     """The schedule attn_fwd runs for these shapes on the current device (safe_attn_plan):
     rows per tile, tile count, split tiles, key ranges, keys per range, workspace bytes.
     workspace_bytes None: the workspace attn_fwd allocates by default; 0: no workspace."""
@@ -304,8 +364,9 @@ def attn_plan(q: torch.Tensor, k: torch.Tensor, q_rows: Optional[torch.Tensor] =
     a.kv_len = None if kv_len is None else _ptr(kv_len)
     a.mask, a.mask_dtype, ms = _attn_mask(mask, B, a.H, Nq, a.Nk)
     a.mask_stride[:] = ms
+    a.kv_src = None if kv_src is None else 16   # only its being non-NULL is read
     if workspace_bytes is None:
-        workspace_bytes = attn_workspace_bytes(q, k, q_rows=q_rows, kv_len=kv_len, mask=mask)
+        workspace_bytes = attn_workspace_bytes(q, k, q_rows=q_rows, kv_len=kv_len, mask=mask, kv_src=kv_src)
     if workspace_bytes > 0:
         a.workspace = 16          # only its being non-NULL is read
         a.workspace_bytes = int(workspace_bytes)

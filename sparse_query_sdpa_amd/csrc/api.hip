@@ -13,6 +13,7 @@ int attn_plan(const safe_attn_args* a, safe_attn_plan_info* out);
 int sw_cfg_launch(const safe_cfg_args* a, hipStream_t stream);
 int linear_launch(const safe_linear_args* a, hipStream_t stream);
 int kv_assemble_launch(const safe_kv_args* a, bool in_place, hipStream_t stream);
+int kv_source_map_launch(const safe_kv_args* a, int32_t* src, hipStream_t stream);
 int mask_classify_launch(const void* mask, int32_t dtype, const int64_t size[4], const int64_t stride[4],
                          uint32_t flags, safe_mask_info* info, uint8_t* row_class, int32_t* kv_len_out,
                          void* workspace, hipStream_t stream);
@@ -111,6 +112,11 @@ static int check_attn_sizes(const safe_attn_args* a) {
   if (a->q_rows != nullptr && a->q_rows_bstride != 0 && a->q_rows_bstride < a->n_rows) return SAFE_ERR_SHAPE;
   if (a->flags & ~(SAFE_ATTN_SCATTER_OUT | SAFE_FLAG_CHECK)) return SAFE_ERR_RANGE;
   if (a->workspace_bytes < 0) return SAFE_ERR_WORKSPACE;
+  if (a->kv_src != nullptr) {   // fused global K/V: no key lengths, no mask
+    if (a->kv_len != nullptr || a->mask != nullptr) return SAFE_ERR_UNSUPPORTED;
+    if (a->n_fresh < 0 || a->kv_src_bstride < 0 || (a->kv_src_bstride != 0 && a->kv_src_bstride < a->Nk))
+      return SAFE_ERR_SHAPE;
+  }
   if (a->mask != nullptr) {
     if (a->mask_dtype < SAFE_DT_BOOL || a->mask_dtype > SAFE_DT_F32) return SAFE_ERR_DTYPE;
     if (a->kv_len != nullptr) return SAFE_ERR_UNSUPPORTED;
@@ -147,6 +153,15 @@ int safe_attn_fwd(const safe_attn_args* a, void* stream) {
   if ((st = check_bnhd(a->k, a->k_stride, work && a->Nk > 0)) != SAFE_OK) return st;
   if ((st = check_bnhd(a->v, a->v_stride, work && a->Nk > 0)) != SAFE_OK) return st;
   if ((st = check_bnhd(a->o, a->o_stride, work)) != SAFE_OK) return st;
+  if (a->kv_src != nullptr) {
+    const bool fresh = work && a->Nk > 0 && a->n_fresh > 0;
+    if ((st = check_bnhd(a->k_fresh, a->fresh_stride, fresh)) != SAFE_OK) return st;
+    if ((st = check_bnhd(a->v_fresh, a->fresh_stride, fresh)) != SAFE_OK) return st;
+    // a fresh row is addressed with a 32-bit byte offset from a 24-bit product (row x row bytes)
+    if (a->n_fresh >= (1 << 24) || a->fresh_stride[1] >= (1 << 23) ||
+        (int64_t)a->n_fresh * a->fresh_stride[1] * 2 + 2 * (int64_t)a->d > ((int64_t)1 << 32))
+      return SAFE_ERR_UNSUPPORTED;
+  }
   if (!work) return SAFE_OK;
   // key/value token strides: the kernel addresses a 64-key tile with 32-bit byte offsets
   // (63 rows of 2 * stride bytes plus a row), so strides stay below 2^25 elements
@@ -188,6 +203,21 @@ int safe_kv_assemble(const safe_kv_args* a, void* stream) {
       (st = check_rows(a->idx, a->B, a->nsel, a->idx_bstride, a->N, true, s)) != SAFE_OK)
     return st;
   return kv_assemble_launch(a, k_same, s);
+}
+
+int safe_kv_source_map(const safe_kv_args* a, int32_t* kv_src, void* stream) {
+  if (a == nullptr) return SAFE_ERR_NULL;
+  if (a->B < 0 || a->N < 0 || a->nsel < 0 || a->nsel > a->N) return SAFE_ERR_SHAPE;
+  if (a->idx_bstride < 0 || (a->idx_bstride != 0 && a->idx_bstride < a->nsel)) return SAFE_ERR_SHAPE;
+  if (a->flags & ~SAFE_FLAG_CHECK) return SAFE_ERR_RANGE;
+  if ((int64_t)a->B * a->N == 0) return SAFE_OK;
+  if (kv_src == nullptr || (a->nsel > 0 && a->idx == nullptr)) return SAFE_ERR_NULL;
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  int st;
+  if ((a->flags & SAFE_FLAG_CHECK) && a->nsel > 0 &&
+      (st = check_rows(a->idx, a->B, a->nsel, a->idx_bstride, a->N, true, s)) != SAFE_OK)
+    return st;
+  return kv_source_map_launch(a, kv_src, s);
 }
 
 int safe_mask_classify(const void* mask, int32_t dtype, const int64_t size[4], const int64_t stride[4],

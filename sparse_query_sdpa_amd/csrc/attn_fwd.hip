@@ -16,6 +16,28 @@ hipError_t dispatch_two_blocks(const AttnParams& p, bool gather, hipStream_t s) 
   return gather ? launch<D, true, false, kMaskNone, 2>(p, s) : launch<D, false, false, kMaskNone, 2>(p, s);
 }
 
+// Fused global K/V (a per-token source map, Eq. 14/16 without the assembly pass): one row
+// block per wave, no key lengths, no mask.
+template <int D>
+hipError_t dispatch_map(const AttnParams& p, bool gather, hipStream_t s) {
+  return gather ? launch<D, true, false, kMaskNone, 1, true>(p, s) : launch<D, false, false, kMaskNone, 1, true>(p, s);
+}
+template <int D>
+int resident_map_d(bool gather) {
+  return gather ? resident_workgroups<D, true, false, kMaskNone, 1, true>()
+                : resident_workgroups<D, false, false, kMaskNone, 1, true>();
+}
+int resident_map(int d, bool gather) {
+  switch (d) {
+    case 32: return resident_map_d<32>(gather);
+    case 64: return resident_map_d<64>(gather);
+    case 72: return resident_map_d<72>(gather);
+    case 96: return resident_map_d<96>(gather);
+    case 128: return resident_map_d<128>(gather);
+    default: return 0;
+  }
+}
+
 // Two row blocks per wave are compiled for the head dimensions of the workloads (96) and of
 // the paper's tax measurement (72), without key lengths (the text cross-attention keeps one).
 bool two_blocks_available(int d) { return d == 96 || d == 72; }
@@ -110,13 +132,15 @@ Choice choose(const safe_attn_args* a, bool allow_split) {
   const double row_flops = 4.0 * a->Nk * a->d;
   Choice best;
   double best_t = 0.0;
-  const int max_rb = (mt == kMaskNone && a->kv_len == nullptr && two_blocks_available(a->d)) ? 2 : 1;
+  const bool map = a->kv_src != nullptr;
+  const int max_rb = (mt == kMaskNone && a->kv_len == nullptr && !map && two_blocks_available(a->d)) ? 2 : 1;
   for (int rb = 1; rb <= max_rb; ++rb) {
     Choice c;
     c.rb = rb;
     c.rows = tile_rows(rb);
     c.tiles = (int64_t)((a->n_rows + c.rows - 1) / c.rows) * a->H * a->B;
-    const int S = mt == kMaskNone ? resident_for(a->d, gather, rb) : attn_masked_resident(a->d, gather, mt);
+    const int S = map ? resident_map(a->d, gather)
+                      : (mt == kMaskNone ? resident_for(a->d, gather, rb) : attn_masked_resident(a->d, gather, mt));
     if (rb > 1 && S <= 0) break;
     const double round_s = S > 0 ? (double)S * c.rows * row_flops / (kRate * (rb > 1 ? kTwoBlockSpeed : 1.0)) : 0.0;
     c.split = SplitPlan{(int)std::min<int64_t>(c.tiles, 0x7fffffff)};
@@ -196,6 +220,12 @@ int attn_fwd_launch(const safe_attn_args* a, float scale, hipStream_t stream) {
   p.mask = static_cast<const char*>(mt == kMaskNone ? nullptr : a->mask);
   p.ms0 = a->mask_stride[0]; p.ms1 = a->mask_stride[1]; p.ms2 = a->mask_stride[2];
   p.inv_scale = 1.0f / scale;
+  p.kv_src = a->kv_src;
+  p.src_bs = a->kv_src_bstride;
+  p.nsel = a->n_fresh;
+  p.kf = static_cast<const u16*>(a->k_fresh);
+  p.vf = static_cast<const u16*>(a->v_fresh);
+  p.fs0 = a->fresh_stride[0]; p.fs1 = a->fresh_stride[1]; p.fs2 = a->fresh_stride[2];
   const SplitPlan& pl = c.split;
   p.n_full = pl.n_full;
   p.nsplit = pl.nsplit;
@@ -206,7 +236,16 @@ int attn_fwd_launch(const safe_attn_args* a, float scale, hipStream_t stream) {
   const bool gather = a->q_rows != nullptr;
   const bool kvlen = a->kv_len != nullptr;
   hipError_t e;
-  if (mt != kMaskNone) {
+  if (p.kv_src != nullptr) {
+    switch (a->d) {
+      case 32: e = dispatch_map<32>(p, gather, stream); break;
+      case 64: e = dispatch_map<64>(p, gather, stream); break;
+      case 72: e = dispatch_map<72>(p, gather, stream); break;
+      case 96: e = dispatch_map<96>(p, gather, stream); break;
+      case 128: e = dispatch_map<128>(p, gather, stream); break;
+      default: return SAFE_ERR_UNSUPPORTED;
+    }
+  } else if (mt != kMaskNone) {
     e = attn_masked_dispatch(p, a->d, gather, mt, stream);
   } else {
     switch (a->d) {

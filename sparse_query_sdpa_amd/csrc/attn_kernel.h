@@ -92,6 +92,14 @@ struct AttnParams {
   const char* mask;
   int64_t ms0, ms1, ms2;
   float inv_scale;
+  // fused global K/V (source-map instances): key j of sample b comes from fresh row
+  // kv_src[b * src_bs + j] when that is >= 0, else from k / v (the cache)
+  const int32_t* kv_src;
+  int64_t src_bs;
+  int nsel;                 // fresh rows per sample; map entries outside [0, nsel) read the cache
+  const u16* kf;
+  const u16* vf;
+  int64_t fs0, fs1, fs2;
 };
 
 hipError_t attn_masked_dispatch(const AttnParams& p, int d, bool gather, int mt, hipStream_t s);
@@ -191,7 +199,7 @@ __device__ __forceinline__ i16x4 lds_read_tr(const char* p) {
   return __builtin_amdgcn_ds_read_tr16_b64_v4i16((__attribute__((address_space(3))) i16x4*)p);
 }
 
-template <int D, bool GATHER, bool KVLEN, int MT, int RB>
+template <int D, bool GATHER, bool KVLEN, int MT, int RB, bool KVMAP = false>
 __global__ __launch_bounds__(NTHREADS, (D >= 128 || MT != kMaskNone || RB > 1) ? 2 : 3)
 void attn_fwd_kernel(AttnParams p) {
   using T = Tile<D>;
@@ -268,7 +276,15 @@ void attn_fwd_kernel(AttnParams p) {
   const char* kbase = reinterpret_cast<const char*>(p.k + (int64_t)b * p.ks0 + (int64_t)h * p.ks2);
   const char* vbase = reinterpret_cast<const char*>(p.v + (int64_t)b * p.vs0 + (int64_t)h * p.vs2);
   const int64_t krow_b = p.ks1 * 2, vrow_b = p.vs1 * 2;   // bytes between consecutive keys
+  const char* kfresh = nullptr;                             // fused global K/V: fresh rows of (b, h)
+  const char* vfresh = nullptr;
+  if constexpr (KVMAP) {
+    kfresh = reinterpret_cast<const char*>(p.kf + (int64_t)b * p.fs0 + (int64_t)h * p.fs2);
+    vfresh = reinterpret_cast<const char*>(p.vf + (int64_t)b * p.fs0 + (int64_t)h * p.fs2);
+  }
   uint32_t coff[T::PER_WAVE];                               // byte offset of this lane's chunk in a tile
+  uint32_t msel[KVMAP ? T::PER_WAVE : 1];                   // map byte offset of its row << 16 | chunk bytes
+  const uint32_t frow_b = KVMAP ? (uint32_t)p.fs1 * 2u : 0u;   // fresh row stride in bytes (< 2^24)
 #pragma unroll
   for (int m = 0; m < T::PER_WAVE; ++m) {
     const int c = wave + NWAVES * m;
@@ -279,11 +295,79 @@ void attn_fwd_kernel(AttnParams p) {
     int chunk = sigma % slots;
     if (chunk >= T::CH) chunk = 0;
     coff[m] = (uint32_t)(row * (isk ? krow_b : vrow_b) + chunk * 16);
+    if constexpr (KVMAP) msel[m] = ((uint32_t)row * 4u << 16) | (uint32_t)(chunk * 16);
   }
+  // Fused global K/V: each copy reads its key's row from the fresh rows or the cache, as
+  // the source map says.  A tile's 64 map entries reach LDS one tile ahead (one dword copy
+  // by wave 0, issued with the copies of the tile before), so the wait for a tile's copies
+  // covers them and no map value is held in registers across a tile.  Slot s of mapbuf
+  // holds the map of the tiles staged in stage s.  Rows past the valid keys use row 0.
+  __shared__ __attribute__((aligned(256))) int mapbuf[KVMAP ? 2 * BN : 1];
+  const int32_t* smap = KVMAP ? p.kv_src + (int64_t)b * p.src_bs : nullptr;
+  auto load_map = [&](int j0, int slot) {
+    if (wave == 0) {
+      const int r = lane < nkeys - j0 ? lane : 0;
+      __builtin_amdgcn_global_load_lds(reinterpret_cast<const char*>(smap + j0 + r),
+                                       (lds_void*)(mapbuf + slot * BN), 4, 0, 0);
+    }
+  };
   auto issue_tile = [&](int j0, char* stage) {
     const char* kb = kbase + (int64_t)j0 * krow_b;
     const char* vb = vbase + (int64_t)j0 * vrow_b;
     const int nrow_valid = nkeys - j0;
+    if constexpr (KVMAP) {
+      const int slot = stage == stage0 ? 0 : 1;
+      if (nrow_valid >= BN) {
+        // full tile: the cache copy keeps the scalar-base form with this lane's 32-bit
+        // offset; lanes whose key is fresh copy instead from the fresh rows' base, offset
+        // src * row bytes (24-bit product) + chunk
+        int wlds = __builtin_amdgcn_readfirstlane(wave * 1024);
+        asm volatile("" : "+s"(wlds));
+        const char* mslot = reinterpret_cast<const char*>(mapbuf) + slot * BN * 4;
+#pragma unroll
+        for (int m = 0; m < T::PER_WAVE; ++m) {
+          const int c = wave + NWAVES * m;
+          const bool all_k = NWAVES * m + NWAVES - 1 < T::K_SLOTS;
+          const bool all_v = NWAVES * m >= T::K_SLOTS;
+          const bool ck = all_k || (!all_v && c < T::K_SLOTS);
+          asm volatile("" : "+v"(coff[m]), "+v"(msel[m]));
+          if (m < FULL || c < T::NCOPY) {
+            const int src = *reinterpret_cast<const int*>(mslot + (msel[m] >> 16));
+            char* dst = stage + wlds + m * NWAVES * 1024;
+            if ((unsigned)src < (unsigned)p.nsel)
+              copy16_to_lds((ck ? kfresh : vfresh) + (__umul24((unsigned)src, frow_b) + (msel[m] & 0xffffu)), dst);
+            else
+              copy16_to_lds((ck ? kb : vb) + coff[m], dst);
+          }
+        }
+        if (j0 + BN < kend) load_map(j0 + BN, slot ^ 1);
+        return;
+      }
+      const int* mrow = mapbuf + slot * BN;
+      // laundered so that no per-copy offset is hoisted into registers live across the loop
+      int ln = lane, wv = wave;
+      asm volatile("" : "+v"(ln), "+v"(wv));
+#pragma unroll
+      for (int m = 0; m < T::PER_WAVE; ++m) {
+        const int c = wv + NWAVES * m;
+        if (m < FULL || c < T::NCOPY) {
+          const bool isk = c < T::K_SLOTS;
+          const int slots = isk ? T::K_SLOTS : T::V_SLOTS;
+          const int sigma = (isk ? c : c - T::K_SLOTS) * 64 + ln;
+          int row = sigma / slots;
+          int chunk = sigma - row * slots;
+          if (chunk >= T::CH) chunk = 0;
+          if (row >= nrow_valid) row = 0;
+          const int src = mrow[row];
+          const char* from = (unsigned)src < (unsigned)p.nsel
+              ? (isk ? kfresh : vfresh) + (int64_t)src * p.fs1 * 2
+              : (isk ? kb : vb) + (int64_t)row * (isk ? krow_b : vrow_b);
+          copy16_to_lds(from + chunk * 16, stage + c * 1024);
+        }
+      }
+      if (j0 + BN < kend) load_map(j0 + BN, slot ^ 1);
+      return;
+    }
     if (nrow_valid >= BN) {
       // The empty asm statements redefine the offsets in place each tile: the 32-bit
       // lane offsets are then not widened and hoisted out of the loop (the copy keeps
@@ -579,6 +663,13 @@ void attn_fwd_kernel(AttnParams p) {
   MRun mA[8], mB[8];        // mask runs of the even / odd tiles (unused without a mask)
   MStage sA, sB;            // staged mask loads of the even / odd tiles (unused unless STAGED)
   const int nfull = (kend - kb0) / BN;   // tiles whose 64 keys are all valid
+  if constexpr (KVMAP) {
+    if (ntiles > 0) {
+      load_map(kb0, 0);
+      __builtin_amdgcn_s_waitcnt(0x0F70);  // vmcnt(0): the first tile's map landed
+      __syncthreads();
+    }
+  }
   if (ntiles > 0) issue_tile(kb0, stage0);
   if constexpr (HAS_MASK) {
     if (nfull > 0) {
@@ -707,9 +798,9 @@ __global__ __launch_bounds__(MERGE_ROWS * 8) void attn_merge_kernel(AttnParams p
   }
 }
 
-template <int D, bool G, bool KV, int MT, int RB>
+template <int D, bool G, bool KV, int MT, int RB, bool KVMAP = false>
 hipError_t launch(const AttnParams& p, hipStream_t s) {
-  hipLaunchKernelGGL((attn_fwd_kernel<D, G, KV, MT, RB>), dim3(p.total_wg), dim3(NTHREADS), 0, s, p);
+  hipLaunchKernelGGL((attn_fwd_kernel<D, G, KV, MT, RB, KVMAP>), dim3(p.total_wg), dim3(NTHREADS), 0, s, p);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess || p.n_slots == 0) return e;
   hipLaunchKernelGGL((attn_merge_kernel<D, G, tile_rows(RB)>), dim3(p.n_slots / p.nsplit, tile_rows(RB) / MERGE_ROWS),
@@ -719,7 +810,7 @@ hipError_t launch(const AttnParams& p, hipStream_t s) {
 
 // Workgroups of one kernel instance resident on the whole device (0 if unknown).
 // Cached per device and instance; racing first calls store the same value.
-template <int D, bool G, bool KV, int MT, int RB>
+template <int D, bool G, bool KV, int MT, int RB, bool KVMAP = false>
 int resident_workgroups() {
   constexpr int kMaxDev = 64;
   static std::atomic<int> cache[kMaxDev];
@@ -728,7 +819,7 @@ int resident_workgroups() {
   int v = cache[dev].load(std::memory_order_relaxed);
   if (v > 0) return v;
   int per_cu = 0, cus = 0;
-  if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, attn_fwd_kernel<D, G, KV, MT, RB>, NTHREADS, 0) != hipSuccess ||
+  if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, attn_fwd_kernel<D, G, KV, MT, RB, KVMAP>, NTHREADS, 0) != hipSuccess ||
       hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess)
     return 0;
   v = per_cu * cus;

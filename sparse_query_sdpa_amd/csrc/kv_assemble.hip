@@ -188,7 +188,52 @@ __global__ __launch_bounds__(NT) void kv_scatter_kernel(KvParams p) {
   }
 }
 
+// Source map of the fused global K/V read: src[b, j] = r when idx[b, r] == j, else -1.
+// A workgroup owns NT consecutive tokens of one sample: one binary search (lower bound
+// of its first token in the ascending list) finds the entries that land in its range,
+// which are then consecutive in the list (at most NT of them).
+__global__ __launch_bounds__(NT) void kv_srcmap_kernel(KvParams p, int32_t* src) {
+  __shared__ int map[NT];
+  __shared__ int lo_s;
+  const int tid = threadIdx.x;
+  const int b = blockIdx.x / p.blocks_per_b;
+  const int t0 = (blockIdx.x % p.blocks_per_b) * NT;
+  const int32_t* idx = p.idx + (int64_t)b * p.ibs;
+  map[tid] = -1;
+  if (tid == 0) {
+    int lo = 0, hi = p.nsel;
+    while (lo < hi) {
+      const int mid = (lo + hi) >> 1;
+      if (idx[mid] < t0) lo = mid + 1;
+      else hi = mid;
+    }
+    lo_s = lo;
+  }
+  __syncthreads();
+  const int r = lo_s + tid;
+  if (r < p.nsel) {
+    const int j = idx[r];
+    if (j >= t0 && j < t0 + NT && j < p.N) map[j - t0] = r;
+  }
+  __syncthreads();
+  const int j = t0 + tid;
+  if (j < p.N) src[(int64_t)b * p.N + j] = map[tid];
+}
+
 }  // namespace
+
+int kv_source_map_launch(const safe_kv_args* a, int32_t* src, hipStream_t s) {
+  KvParams p = {};
+  p.idx = a->idx;
+  p.ibs = a->idx_bstride;
+  p.B = a->B; p.N = a->N; p.nsel = a->nsel;
+  p.blocks_per_b = (a->N + NT - 1) / NT;
+  const int64_t grid = (int64_t)p.blocks_per_b * a->B;
+  if (grid == 0) return SAFE_OK;
+  if (grid > 0x7fffffff) return SAFE_ERR_SHAPE;
+  hipLaunchKernelGGL(kv_srcmap_kernel, dim3((unsigned)grid), dim3(NT), 0, s, p, src);
+  return hipGetLastError() == hipSuccess ? SAFE_OK : SAFE_ERR_HIP;
+}
 
 int kv_assemble_launch(const safe_kv_args* a, bool in_place, hipStream_t s) {
   KvParams p;

@@ -21,7 +21,8 @@ def declared_functions():
 def test_header_declares_the_four_entry_points():
     names = declared_functions()
     for n in ("safe_mask_classify", "safe_pcsp_select", "safe_kv_assemble", "safe_attn_fwd", "safe_sw_cfg", "safe_linear",
-              "safe_attn_workspace_bytes", "safe_attn_plan", "safe_status_str", "safe_abi_version"):
+              "safe_attn_workspace_bytes", "safe_attn_plan", "safe_kv_source_map", "safe_status_str",
+              "safe_abi_version"):
         assert n in names
 
 
@@ -32,7 +33,7 @@ def test_every_declared_symbol_is_exported():
 
 
 def test_abi_version_and_status_strings():
-    assert sq.lib.safe_abi_version() == 6 == sq.ABI_VERSION
+    assert sq.lib.safe_abi_version() == 7 == sq.ABI_VERSION
     for code, name in sq.STATUS.items():
         assert sq.lib.safe_status_str(code).decode().startswith(name)
     assert sq.lib.safe_status_str(12345) == b"unknown status"
@@ -124,6 +125,37 @@ def test_attn_mask_arguments_without_gpu():
     assert sq.lib.safe_attn_workspace_bytes(ctypes.byref(_attn_args(mask_dtype=9))) >= 0
     # d = 72 is a supported head dimension (the size query runs without a device)
     assert sq.lib.safe_attn_workspace_bytes(ctypes.byref(_attn_args(d=72))) >= 0
+
+
+def test_attn_fused_kv_arguments_without_gpu():
+    src, fresh = 0x70000, 0x80000
+    ok = dict(kv_src=src, n_fresh=4, k_fresh=fresh, v_fresh=fresh)
+    # no key lengths or mask with the fused read
+    assert sq.lib.safe_attn_fwd(ctypes.byref(_attn_args(kv_len=0x30000, **ok)), None) == -5
+    assert sq.lib.safe_attn_fwd(ctypes.byref(_attn_args(mask=0x60000, mask_dtype=1, **ok)), None) == -5
+    for kw, status in ((dict(n_fresh=-1), -2), (dict(kv_src_bstride=5), -2), (dict(kv_src_bstride=-128), -2),
+                       (dict(k_fresh=None), -1), (dict(v_fresh=0x80004), -8)):
+        assert sq.lib.safe_attn_fwd(ctypes.byref(_attn_args(**{**ok, **kw})), None) == status, kw
+    a = _attn_args(**ok)
+    a.fresh_stride[:] = [4 * 96, 100, 96]   # not a multiple of 8 elements
+    assert sq.lib.safe_attn_fwd(ctypes.byref(a), None) == -8
+    # the size query and the plan validate the same fields
+    assert sq.lib.safe_attn_workspace_bytes(ctypes.byref(_attn_args(kv_len=0x30000, **ok))) == -5
+    assert sq.lib.safe_attn_workspace_bytes(ctypes.byref(_attn_args(**ok))) >= 0
+    # empty work returns before any pointer is read
+    assert sq.lib.safe_attn_fwd(ctypes.byref(_attn_args(B=0, **ok)), None) == 0
+
+
+def test_kv_source_map_arguments_without_gpu():
+    a = _kv_args()
+    assert sq.lib.safe_kv_source_map(None, 0x90000, None) == -1
+    assert sq.lib.safe_kv_source_map(ctypes.byref(a), None, None) == -1
+    for kw, status in ((dict(nsel=65), -2), (dict(N=-1), -2), (dict(idx_bstride=3), -2), (dict(flags=4), -4),
+                       (dict(idx=None), -1)):
+        assert sq.lib.safe_kv_source_map(ctypes.byref(_kv_args(**kw)), 0x90000, None) == status, kw
+    # nothing to write: no pointer is read
+    assert sq.lib.safe_kv_source_map(ctypes.byref(_kv_args(B=0, idx=None)), None, None) == 0
+    assert sq.lib.safe_kv_source_map(ctypes.byref(_kv_args(N=0, nsel=0, idx=None)), None, None) == 0
 
 
 def test_attn_empty_work_is_ok_without_gpu():
