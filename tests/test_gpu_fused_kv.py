@@ -169,3 +169,40 @@ def test_full_size_srsu_step_sampled_rows(number):
     vg = oracle.kv_assemble(fv.value, S, inp["v_x"].value)
     ref, _ = oracle.sdpa(inp["q_x"].value, kg, vg, q_rows=S[samp])
     assert_attn_close(o_f[:, torch.from_numpy(samp).long()], ref, "fused full size")
+
+
+def test_fused_step_in_a_hip_graph():
+    """Source map + fused SRSU attention captured in a HIP graph: every replay, with eager
+    work in between and the map buffer cleared, gives the eager result bitwise."""
+    B, N, H, d, n_sel = 2, 3000, 4, 96, 777
+    q, k, v = W.attention_inputs(B, N, N, H, d, seed=86)
+    qd, kc, vc = to_dev_bf16(q), to_dev_bf16(k), to_dev_bf16(v)
+    rows = to_dev(np.stack([W.random_rows(np.random.default_rng(87 + b), N, n_sel) for b in range(B)]))
+    g = torch.Generator(device="cuda").manual_seed(88)
+    kf = torch.randn((B, n_sel, H, d), generator=g, device="cuda").to(torch.bfloat16)
+    vf = torch.randn((B, n_sel, H, d), generator=g, device="cuda").to(torch.bfloat16)
+    src = torch.empty((B, N), dtype=torch.int32, device="cuda")
+    o = torch.empty((B, n_sel, H, d), dtype=torch.bfloat16, device="cuda")
+
+    def step():
+        sq.kv_source_map(rows, N, out=src)
+        sq.attn_fwd(qd, kc, vc, q_rows=rows, out=o, kv_src=src, k_fresh=kf, v_fresh=vf)
+
+    side = torch.cuda.Stream()
+    side.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(side):      # warm-up on the capture stream (its workspace)
+        step()
+    torch.cuda.current_stream().wait_stream(side)
+    torch.cuda.synchronize()
+    ref = o.clone()
+    graph = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(graph, stream=side):
+        step()
+    for rep in range(3):
+        o.zero_()
+        src.fill_(-1)
+        eager = sq.attn_fwd(qd, kc, vc, q_rows=rows)      # unrelated eager work between replays
+        graph.replay()
+        torch.cuda.synchronize()
+        assert torch.equal(o, ref), f"replay {rep}"
+        assert eager.shape == o.shape
