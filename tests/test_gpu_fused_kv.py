@@ -206,3 +206,26 @@ def test_fused_step_in_a_hip_graph():
         torch.cuda.synchronize()
         assert torch.equal(o, ref), f"replay {rep}"
         assert eager.shape == o.shape
+
+
+@pytest.mark.parametrize("d", [64, 128])
+def test_fused_strided_fresh_and_cache(d):
+    """Fresh rows and the cache as views with padded rows (token stride > H·d, head stride > d),
+    three samples with their own S and a ragged key count: the oracle on sampled rows."""
+    B, N, H, nsel = 3, 777, 2, 200
+    rng, q, ck, cv, fk, fv, S = _case(B, N, H, d, nsel, seed=90 + d)
+    qd = to_dev_bf16(q)
+
+    def padded(t, rows):
+        big = torch.zeros((B, rows, H, d + 32), dtype=torch.bfloat16, device="cuda")
+        big[..., :d] = to_dev_bf16(t)
+        return big[..., :d]
+
+    ckd, cvd, fkd, fvd = padded(ck, N), padded(cv, N), padded(fk, nsel), padded(fv, nsel)
+    assert fkd.stride(1) == H * (d + 32) and not fkd.is_contiguous()
+    src = sq.kv_source_map(to_dev(S), N, check=True)
+    o = sq.attn_fwd(qd, ckd, cvd, q_rows=to_dev(S), kv_src=src, k_fresh=fkd, v_fresh=fvd)
+    kg, vg = _oracle_global(fk, fv, S, ck, cv)
+    samp = np.unique(np.concatenate([[0, nsel - 1], rng.choice(nsel, 16, replace=False)]))
+    ref, _ = oracle.sdpa(q.value, kg, vg, q_rows=S[:, samp])
+    assert_attn_close(o[:, torch.from_numpy(samp).long()], ref, f"strided d={d}")
