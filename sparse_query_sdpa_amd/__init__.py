@@ -318,8 +318,8 @@ def kv_source_map(idx: torch.Tensor, n_tokens: int, batch: Optional[int] = None,
             raise ValueError("idx rows must be contiguous")
     if out is None:
         out = torch.empty((B, n_tokens), dtype=torch.int32, device=idx.device)
-    if out.dtype != torch.int32 or out.shape != (B, n_tokens) or not out.is_contiguous():
-        raise ValueError("out must be contiguous int32 [B, N]")
+    if out.dtype != torch.int32 or out.shape != (B, n_tokens) or not out.is_contiguous() or not out.is_cuda:
+        raise ValueError("out must be a contiguous int32 device tensor [B, N]")
     a = KvArgs()
     a.B, a.N, a.nsel, a.idx, a.idx_bstride = B, n_tokens, nsel, _ptr(idx), ibs
     a.flags = FLAG_CHECK if check else 0

@@ -5,6 +5,7 @@ import os
 import re
 
 import pytest
+import torch
 
 ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
 HEADER = os.path.join(ROOT, "include", "safe.h")
@@ -323,3 +324,9 @@ def test_linear_rejects_bad_arguments_without_gpu(kw, status):
 def test_linear_empty_work_is_ok_without_gpu():
     for kw in (dict(M=0), dict(batches=0), dict(N=0, a=None, w=None, out=None)):
         assert sq.lib.safe_linear(ctypes.byref(_lin_args(**kw)), None) == 0, kw
+
+
+def test_kv_source_map_binding_rejects_host_tensors():
+    idx = torch.arange(4, dtype=torch.int32)
+    with pytest.raises(TypeError):
+        sq.kv_source_map(idx, 16)          # the index list must be a device tensor
