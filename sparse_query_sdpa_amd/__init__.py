@@ -166,7 +166,12 @@ def _stream(stream=None) -> int:
 
 
 def _ptr(t: Optional[torch.Tensor]) -> Optional[int]:
-    return None if t is None else t.data_ptr()
+    """Device address of a tensor passed to the library (every tensor argument is device memory)."""
+    if t is None:
+        return None
+    if not t.is_cuda:
+        raise ValueError("tensor arguments must be device tensors")
+    return t.data_ptr()
 
 
 def _bnhd(t: torch.Tensor, name: str):

@@ -330,3 +330,10 @@ def test_kv_source_map_binding_rejects_host_tensors():
     idx = torch.arange(4, dtype=torch.int32)
     with pytest.raises(TypeError):
         sq.kv_source_map(idx, 16)          # the index list must be a device tensor
+
+
+def test_binding_rejects_host_output_tensors():
+    # no tensor of host memory reaches a kernel, outputs included
+    with pytest.raises(ValueError):
+        sq._ptr(torch.empty(4, dtype=torch.int32))
+    assert sq._ptr(None) is None
