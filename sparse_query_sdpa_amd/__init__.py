@@ -174,6 +174,12 @@ def _ptr(t: Optional[torch.Tensor]) -> Optional[int]:
     return t.data_ptr()
 
 
+def _need(t: torch.Tensor, shape, name: str):
+    """A caller-provided tensor must have exactly the shape the call reads or writes."""
+    if tuple(t.shape) != tuple(shape):
+        raise ValueError(f"{name} must have shape {list(shape)}, got {list(t.shape)}")
+
+
 def _bnhd(t: torch.Tensor, name: str):
     if t.dim() != 4:
         raise ValueError(f"{name} must be 4-D [B, N, H, d]")
@@ -263,6 +269,8 @@ def attn_fwd(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, q_rows: Optional
         n_rows, bstride = Nq, 0
     if out is None:
         out = torch.empty((B, Nq if scatter_out else n_rows, H, d), dtype=q.dtype, device=q.device)
+    _bits16(out, "out")
+    _need(out, (B, Nq if scatter_out else n_rows, H, d), "out")
     lse = torch.empty((B, H, n_rows), dtype=torch.float32, device=q.device) if return_lse else None
     if q_rows is not None and n_rows == 0:   # an empty row list has no storage pointer: nothing to compute
         return (out, lse) if return_lse else out
@@ -401,6 +409,9 @@ def kv_assemble(k_fresh: torch.Tensor, v_fresh: torch.Tensor, idx: torch.Tensor,
             k_out = torch.empty_like(k_cache)
         if v_out is None:
             v_out = torch.empty_like(v_cache)
+        for t, n in ((k_out, "k_out"), (v_out, "v_out")):
+            _bits16(t, n)
+            _need(t, k_cache.shape, n)
     a = KvArgs(B, N, H, d, nsel, _ptr(k_fresh), _ptr(v_fresh), _bnhd(k_fresh, "k_fresh"), _ptr(idx), ibs,
                _ptr(k_cache), _ptr(v_cache), _bnhd(k_cache, "k_cache"), _ptr(k_out), _ptr(v_out),
                _bnhd(k_out, "k_out"), FLAG_CHECK if check else 0)
@@ -552,7 +563,8 @@ def sw_cfg(f_c: torch.Tensor, f_u: torch.Tensor, g_ctx: float, g_sens: Optional[
     return out
 
 
-__all__ = ["attn_fwd", "kv_assemble", "mask_classify", "pcsp_accumulate", "pcsp_select", "sw_cfg", "lib", "SafeError",
+__all__ = ["attn_fwd", "attn_plan", "attn_workspace_bytes", "kv_assemble", "kv_source_map", "mask_classify",
+           "pcsp_accumulate", "pcsp_select", "sw_cfg", "linear", "block_dense", "block_srsu", "lib", "SafeError",
            "LIB_PATH", "MASK_CLASS_NAMES"]
 
 
@@ -602,6 +614,16 @@ def linear(a: torch.Tensor, w: torch.Tensor, bias: Optional[torch.Tensor] = None
         if out_rows is not None:
             raise ValueError("out_rows needs an output tensor holding the other rows")
         out = torch.empty((B, M, N), dtype=a.dtype, device=a.device)
+    # without a row list, row r of a tensor is its row r: it needs at least M rows
+    # (with one, every listed tensor has the same row count, checked above)
+    for t, x, n, shared in ((out, out_rows, "out", False), (res, res_rows, "res", True)):
+        if t is None:
+            continue
+        if t.dim() != 3 or t.shape[2] != N or t.shape[0] not in ((1, B) if shared else (B,)) \
+                or (x is None and t.shape[1] < M):
+            raise ValueError(f"{n} must be [B{'|1' if shared else ''}, rows >= {M}, {N}], got {list(t.shape)}")
+    if a_rows is None and Ta < M:
+        raise ValueError(f"a without a row list needs at least {M} rows")
     if bias is not None and (bias.dtype != torch.float32 or bias.shape != (N,) or not bias.is_contiguous()):
         raise ValueError("bias must be contiguous float32 [N]")
     args = LinearArgs()
