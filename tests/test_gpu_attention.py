@@ -350,3 +350,26 @@ def test_hip_graph_replays_match_eager():
         torch.cuda.synchronize()
         assert torch.equal(o_s, ref_s) and torch.equal(o_d, ref_d), f"replay {rep}"
         assert torch.equal(eager, ref_d)
+
+
+def test_caller_outputs_of_the_wrong_shape_or_memory_are_refused():
+    """Outputs that the call would write past, of another dtype, or in host memory raise
+    before any launch."""
+    B, N, H, d = 1, 256, 2, 64
+    q, k, v = W.attention_inputs(B, N, N, H, d, seed=60)
+    qd, kd, vd = to_dev_bf16(q), to_dev_bf16(k), to_dev_bf16(v)
+    rows = to_dev(np.arange(0, 256, 4, dtype=np.int32))
+    for bad in (torch.empty((B, 63, H, d), dtype=torch.bfloat16, device="cuda"),     # one row short
+                torch.empty((B, 64, H, d), dtype=torch.float32, device="cuda"),
+                torch.empty((B, 64, H, d), dtype=torch.bfloat16)):                   # host memory
+        with pytest.raises((ValueError, TypeError)):
+            sq.attn_fwd(qd, kd, vd, q_rows=rows, out=bad)
+    with pytest.raises(ValueError):                                                  # scatter needs all rows
+        sq.attn_fwd(qd, kd, vd, q_rows=rows, out=torch.empty((B, 64, H, d), dtype=torch.bfloat16,
+                                                                device="cuda"), scatter_out=True)
+    f = qd[:, :64].contiguous()
+    with pytest.raises(ValueError):
+        sq.kv_assemble(f, f, rows, kd, vd, k_out=torch.empty((B, N - 1, H, d), dtype=torch.bfloat16, device="cuda"))
+    o = sq.attn_fwd(qd, kd, vd, q_rows=rows, out=torch.empty((B, 64, H, d), dtype=torch.bfloat16, device="cuda"))
+    ref, _ = oracle.sdpa(q.value, k.value, v.value, q_rows=np.arange(0, 256, 4)[[0, 63]])
+    assert_attn_close(o[:, [0, 63]], ref, "valid caller output")
