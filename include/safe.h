@@ -10,6 +10,9 @@
  *   safe_attn_fwd       Eq. 2,16-18 attention on all rows (dense anchor pass) or on the
  *                       gathered rows of S, with optional per-sample valid key lengths
  *                       (or, for masks the rewrite cannot drop, a dense mask)
+ *   safe_sdpa           Eq. 8     the rewrite as one call: certify the mask, then run
+ *                                 safe_attn_fwd without it, with per-sample key lengths
+ *                                 (text padding) or with it, and report which
  *   safe_sw_cfg         Eq. 20-21 sensitivity-weighted classifier-free guidance
  *   safe_linear         Eq. 15    the row-wise linear maps of the block around attention
  *                                 (projections, residual updates, MLP) on gathered rows
@@ -41,7 +44,7 @@
 extern "C" {
 #endif
 
-#define SAFE_ABI_VERSION 7
+#define SAFE_ABI_VERSION 8
 
 /* ---- status codes (negative = error) ----------------------------------- */
 enum {
@@ -322,6 +325,49 @@ typedef struct {
 } safe_attn_plan_info;
 
 int safe_attn_plan(const safe_attn_args* a, safe_attn_plan_info* out);
+
+/*
+ * safe_sdpa -- the Eq. 8 rewrite as one call.  The paper's SAFE-SDPA replaces an SDPA
+ * call whose mask lies in the row-constant class R (Eq. 6; every stored row one real
+ * constant, all-valid Boolean and all-zero additive masks included) by the mask-free
+ * call, which Eq. 7 makes exact, and keeps every other mask; the text padding of the
+ * cross-attention (Eq. 4/17) is kept as well.  This call certifies a->mask with the
+ * classifier of safe_mask_classify and then runs safe_attn_fwd on a copy of a:
+ *   SAFE_ROUTE_NO_MASK  mask NULL, or every stored row in R      -> mask dropped
+ *   SAFE_ROUTE_KV_LEN   every row KEY_PADDING with one valid length L per sample
+ *                       (rows in R counting as L = Nk)          -> mask dropped,
+ *                       kv_len[b] = L of the mask row that serves sample b
+ *   SAFE_ROUTE_MASK     anything else (finite non-constant biases, other blocked
+ *                       patterns, NaN / +inf entries)           -> the mask is kept
+ * Correctness never depends on the rewrite firing: every route computes the attention
+ * of Eq. 2 with the given mask (up to the rounding of the kernels).
+ *
+ * a             as for safe_attn_fwd (its workspace serves the attention as there);
+ *               the mask is described by mask, mask_dtype and mask_stride as there:
+ *               a zero stride marks a broadcast dimension, stored with size 1, so the
+ *               classifier scans the [B|1, H|1, Nq|1, Nk] rows as stored.  kv_len must
+ *               be NULL when a mask is given (SAFE_ERR_UNSUPPORTED).  The classifier
+ *               accepts any alignment; the masked route needs the 16-byte mask rows
+ *               safe_attn_fwd requires (else SAFE_ERR_ALIGN, returned after the scan).
+ * classify_ws   device scratch for the classifier and the per-sample lengths, of
+ *               *classify_ws_bytes bytes (16-byte aligned); classify_ws == NULL writes
+ *               the required size to *classify_ws_bytes and returns SAFE_OK.  Not
+ *               needed (may be NULL) when mask is NULL.
+ * info          host, optional: the route taken, the mask's overall class and its
+ *               first row outside R (-1 if none; route NO_MASK without a mask: class
+ *               -1, row -1).
+ * Blocking when a mask is given (the verdict is a host decision: the stream is
+ * synchronised once); the attention itself is enqueued on stream and not waited for.
+ */
+enum { SAFE_ROUTE_NO_MASK = 0, SAFE_ROUTE_KV_LEN = 1, SAFE_ROUTE_MASK = 2 };
+typedef struct {
+  int32_t route;          /* SAFE_ROUTE_*                                     */
+  int32_t mask_class;     /* overall class of the mask (SAFE_MASK_*), or -1  */
+  int64_t first_bad_row;  /* lowest stored row outside R, or -1              */
+} safe_sdpa_info;
+
+int safe_sdpa(const safe_attn_args* a, void* classify_ws, size_t* classify_ws_bytes, safe_sdpa_info* info,
+              void* stream);
 
 /* Human-readable name of a status code (static storage). */
 const char* safe_status_str(int status);

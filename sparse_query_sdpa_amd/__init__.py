@@ -4,11 +4,18 @@ Argument marshalling only: every step runs in the HIP kernels of libsafe.so;
 PyTorch supplies device memory and the current HIP stream.  There is no CPU
 fallback: importing the package fails loudly when the library is missing.
 
-Entry points (same names as the C ABI in include/safe.h):
-  mask_classify  -- Eq. 6-8 row-constant certification of an attention mask
-  pcsp_select    -- Eq. 9-12 sensitivity accumulation / smoothing / top-k
-  kv_assemble    -- Eq. 14, 16 global K/V from fresh rows over cached rows
-  attn_fwd       -- Eq. 2, 16-18 attention, dense or on gathered rows, with kv_len
+Entry points (the C ABI in include/safe.h, same names without the safe_ prefix):
+  mask_classify   -- Eq. 6-8 row-constant certification of an attention mask
+  pcsp_accumulate -- Eq. 9-10 image->text sensitivity scores (safe_pcsp_select, ACCUM)
+  pcsp_select     -- Eq. 11-12 smoothing, Norm and the ascending top-k set S (SELECT)
+  kv_assemble     -- Eq. 14, 16 global K/V from fresh rows over cached rows
+  kv_source_map   -- the per-token map of the fused global K/V read (Eq. 14, 16 in one pass)
+  attn_fwd        -- Eq. 2, 16-18 attention, dense or on gathered rows, with kv_len or a mask
+  sdpa            -- Eq. 8 the rewrite as one call: certify the mask, run the exact cheapest form
+  attn_plan, attn_workspace_bytes -- the schedule and split workspace of an attn_fwd call
+  sw_cfg          -- Eq. 20-21 sensitivity-weighted classifier-free guidance
+  linear          -- Eq. 15 row-wise linear maps on gathered rows (the block around attention)
+  block_dense, block_srsu -- that block as a sequence of the calls above
 """
 from __future__ import annotations
 
@@ -31,7 +38,7 @@ CLASSIFY_ASYNC = 1 << 2
 PCSP_ACCUM = 1 << 3
 PCSP_SELECT = 1 << 4
 
-ABI_VERSION = 7   # struct layouts below match include/safe.h of this version
+ABI_VERSION = 8   # struct layouts below match include/safe.h of this version
 DT_BOOL, DT_BF16, DT_F16, DT_F32 = 0, 1, 2, 3
 MASK_CLASS_NAMES = ("ALL_VALID", "ZERO", "ROW_CONST", "KEY_PADDING", "NONCONST", "BLOCKED", "NONFINITE")
 
@@ -81,6 +88,13 @@ class AttnArgs(ctypes.Structure):
                 ("n_fresh", ctypes.c_int32)]
 
 
+class SdpaInfo(ctypes.Structure):
+    _fields_ = [("route", ctypes.c_int32), ("mask_class", ctypes.c_int32), ("first_bad_row", ctypes.c_int64)]
+
+
+ROUTE_NAMES = ("no_mask", "kv_len", "mask")
+
+
 class AttnPlanInfo(ctypes.Structure):
     _fields_ = [("rows_per_tile", ctypes.c_int32), ("row_tiles", ctypes.c_int32),
                 ("split_tiles", ctypes.c_int32), ("key_ranges", ctypes.c_int32),
@@ -123,6 +137,9 @@ def _load():
     lib.safe_status_str.argtypes = [ctypes.c_int]
     lib.safe_attn_fwd.restype = ctypes.c_int
     lib.safe_attn_fwd.argtypes = [ctypes.POINTER(AttnArgs), ctypes.c_void_p]
+    lib.safe_sdpa.restype = ctypes.c_int
+    lib.safe_sdpa.argtypes = [ctypes.POINTER(AttnArgs), ctypes.c_void_p, ctypes.POINTER(ctypes.c_size_t),
+                              ctypes.POINTER(SdpaInfo), ctypes.c_void_p]
     lib.safe_sw_cfg.restype = ctypes.c_int
     lib.safe_sw_cfg.argtypes = [ctypes.POINTER(CfgArgs), ctypes.c_void_p]
     lib.safe_attn_workspace_bytes.restype = ctypes.c_int64
@@ -189,8 +206,10 @@ def _bnhd(t: torch.Tensor, name: str):
 
 
 def _bits16(t: torch.Tensor, name: str):
-    if t.dtype not in (torch.bfloat16, torch.float16, torch.int16, torch.uint16):
-        raise TypeError(f"{name} must be a 16-bit tensor (bf16 storage)")
+    """Every attention, assembly and linear operand is read and written as bfloat16 (the
+    C ABI has no dtype field for them): any other dtype is refused, fp16 included."""
+    if t.dtype != torch.bfloat16:
+        raise TypeError(f"{name} must be a torch.bfloat16 tensor, got {t.dtype}")
     if not t.is_cuda:
         raise ValueError(f"{name} must be a device tensor")
 
@@ -203,8 +222,49 @@ def _i32(t: Optional[torch.Tensor], name: str):
     return t
 
 
+def _lengths(t: Optional[torch.Tensor], B: int, name: str = "kv_len"):
+    """Per-sample lengths: an int32 device tensor of exactly B entries (one per sample)."""
+    t = _i32(t, name)
+    if t is not None and (t.dim() != 1 or t.shape[0] != B or (B > 1 and t.stride(0) != 1)):
+        raise ValueError(f"{name} must be a contiguous int32 tensor of shape [{B}], got {list(t.shape)}")
+    return t
+
+
+def _row_lists(t: Optional[torch.Tensor], B: int, name: str):
+    """(rows per sample, sample stride) of an index list [n] / [1, n] (shared by every
+    sample: stride 0) or [B, n] (one list per sample); rows contiguous."""
+    if t is None:
+        return None, 0
+    if t.dim() == 1:
+        if t.shape[0] > 1 and t.stride(0) != 1:
+            raise ValueError(f"{name} must be contiguous")
+        return t.shape[0], 0
+    if t.dim() != 2 or t.shape[0] not in (1, B) or (t.shape[1] > 1 and t.stride(1) != 1):
+        raise ValueError(f"{name} must be [n], [1, n] or [{B}, n] with contiguous rows, got {list(t.shape)}")
+    return t.shape[1], (0 if t.shape[0] == 1 else t.stride(0))
+
+
 # ---------------------------------------------------------------------------------
-_ATTN_WS = {}  # (device index, stream handle) -> uint8 workspace tensor, grown on demand
+_ATTN_WS = {}      # (device index, stream handle) -> uint8 workspace tensor, grown on demand
+_RETIRED_WS = []   # superseded workspaces: never freed, a captured graph may still write them
+
+
+def _cached_workspace(cache: dict, key, need: int, device: torch.device, what: str) -> torch.Tensor:
+    """The workspace cached for (device, stream), grown when a call needs more.  A buffer
+    that a HIP graph may have captured must outlive the graph, so a superseded buffer is
+    kept alive rather than returned to the allocator; during capture nothing is allocated
+    (run the call once eagerly on the capture stream first, or pass a workspace tensor)."""
+    ws = cache.get(key)
+    if ws is None or ws.numel() < need:
+        if torch.cuda.is_current_stream_capturing():
+            raise RuntimeError(f"{what}: the cached workspace of this stream is smaller than the captured call "
+                               f"needs ({need} bytes); run the call once before capturing it, or pass an explicit "
+                               "workspace tensor")
+        if ws is not None:
+            _RETIRED_WS.append(ws)
+        ws = torch.empty(int(need), dtype=torch.uint8, device=device)
+        cache[key] = ws
+    return ws
 
 
 def _attn_workspace(a: AttnArgs, device: torch.device, stream_handle) -> Optional[torch.Tensor]:
@@ -213,12 +273,7 @@ def _attn_workspace(a: AttnArgs, device: torch.device, stream_handle) -> Optiona
         _check("safe_attn_workspace_bytes", int(need))
     if need <= 0:
         return None
-    key = (device.index, stream_handle)
-    ws = _ATTN_WS.get(key)
-    if ws is None or ws.numel() < need:
-        ws = torch.empty(int(need), dtype=torch.uint8, device=device)
-        _ATTN_WS[key] = ws
-    return ws
+    return _cached_workspace(_ATTN_WS, (device.index, stream_handle), int(need), device, "attn_fwd")
 
 
 def _attn_mask(mask: Optional[torch.Tensor], B: int, H: int, Nq: int, Nk: int):
@@ -236,35 +291,22 @@ def _attn_mask(mask: Optional[torch.Tensor], B: int, H: int, Nq: int, Nk: int):
     return _ptr(mask), _MASK_DT[mask.dtype], st
 
 
-def attn_fwd(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, q_rows: Optional[torch.Tensor] = None,
-             kv_len: Optional[torch.Tensor] = None, scale: Optional[float] = None, out: Optional[torch.Tensor] = None,
-             return_lse: bool = False, scatter_out: bool = False, check: bool = False, stream=None,
-             workspace="auto", mask: Optional[torch.Tensor] = None, kv_src: Optional[torch.Tensor] = None,
-             k_fresh: Optional[torch.Tensor] = None, v_fresh: Optional[torch.Tensor] = None):
-    """Attention on all rows (q_rows None) or on gathered rows q_rows [n] / [B, n]; see safe.h.
-
-    kv_src: optional source map [Nk] / [1|B, Nk] int32 (kv_source_map) for the fused global
-    K/V read: key j comes from row kv_src[.., j] of k_fresh / v_fresh [B, n_fresh, H, d]
-    when that is in [0, n_fresh), else from k / v (the cache).
-    workspace: "auto" (a buffer cached per device and stream, sized by
-    safe_attn_workspace_bytes), None (no tail split), or a uint8 device tensor.
-    mask: optional dense mask [B|1, H|1, Nq|1, Nk] (size-1 dims broadcast), indexed by
-    query token; bool/uint8 attend-where-nonzero or an additive bf16/f16/f32 bias."""
+def _attn_call(q, k, v, q_rows, kv_len, scale, out, return_lse, scatter_out, check, mask, kv_src, k_fresh,
+               v_fresh):
+    """Checked AttnArgs of a call plus its output tensors: (args or None when there is nothing
+    to compute, out, lse)."""
     for t, n in ((q, "q"), (k, "k"), (v, "v")):
         _bits16(t, n)
+    if q.dim() != 4 or k.dim() != 4:
+        raise ValueError("q, k and v must be 4-D [B, N, H, d]")
     B, Nq, H, d = q.shape
     Nk = k.shape[1]
     if k.shape != (B, Nk, H, d) or v.shape != k.shape:
         raise ValueError("k and v must be [B, Nk, H, d] matching q")
     q_rows = _i32(q_rows, "q_rows")
-    kv_len = _i32(kv_len, "kv_len")
+    kv_len = _lengths(kv_len, B)
     if q_rows is not None:
-        if q_rows.dim() == 1:
-            n_rows, bstride = q_rows.shape[0], 0
-        else:
-            if q_rows.shape[0] != B or q_rows.stride(1) != 1:
-                raise ValueError("q_rows must be [n] or [B, n] with contiguous rows")
-            n_rows, bstride = q_rows.shape[1], q_rows.stride(0)
+        n_rows, bstride = _row_lists(q_rows, B, "q_rows")
     else:
         n_rows, bstride = Nq, 0
     if out is None:
@@ -273,7 +315,7 @@ def attn_fwd(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, q_rows: Optional
     _need(out, (B, Nq if scatter_out else n_rows, H, d), "out")
     lse = torch.empty((B, H, n_rows), dtype=torch.float32, device=q.device) if return_lse else None
     if q_rows is not None and n_rows == 0:   # an empty row list has no storage pointer: nothing to compute
-        return (out, lse) if return_lse else out
+        return None, out, lse
     a = AttnArgs(B, H, Nq, Nk, d, _ptr(q), _bnhd(q, "q"), _ptr(k), _bnhd(k, "k"), _ptr(v), _bnhd(v, "v"),
                  _ptr(out), _bnhd(out, "out"), _ptr(q_rows), n_rows, bstride, _ptr(kv_len),
                  0.0 if scale is None else float(scale), _ptr(lse),
@@ -281,15 +323,81 @@ def attn_fwd(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, q_rows: Optional
     a.mask, a.mask_dtype, ms = _attn_mask(mask, B, H, Nq, Nk)
     a.mask_stride[:] = ms
     _attn_kv_src(a, kv_src, k_fresh, v_fresh, B, Nk, H, d)
-    st = _stream(stream)
+    return a, out, lse
+
+
+def _attn_set_workspace(a: AttnArgs, workspace, device: torch.device, st: int):
+    """Point a at the split workspace: "auto" (cached per device and stream), None, or a tensor."""
     if isinstance(workspace, str):
         if workspace != "auto":
             raise ValueError("workspace must be 'auto', None or a device tensor")
-        workspace = _attn_workspace(a, q.device, st)
+        workspace = _attn_workspace(a, device, st)
     if workspace is not None:
-        a.workspace, a.workspace_bytes = _ptr(workspace), workspace.numel() * workspace.element_size()
-    _check("safe_attn_fwd", lib.safe_attn_fwd(ctypes.byref(a), st))
+        if workspace.dtype != torch.uint8 or not workspace.is_contiguous():
+            raise ValueError("workspace must be a contiguous uint8 device tensor")
+        a.workspace, a.workspace_bytes = _ptr(workspace), workspace.numel()
+
+
+def attn_fwd(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, q_rows: Optional[torch.Tensor] = None,
+             kv_len: Optional[torch.Tensor] = None, scale: Optional[float] = None, out: Optional[torch.Tensor] = None,
+             return_lse: bool = False, scatter_out: bool = False, check: bool = False, stream=None,
+             workspace="auto", mask: Optional[torch.Tensor] = None, kv_src: Optional[torch.Tensor] = None,
+             k_fresh: Optional[torch.Tensor] = None, v_fresh: Optional[torch.Tensor] = None):
+    """Attention on all rows (q_rows None) or on gathered rows q_rows [n] / [1|B, n]; see safe.h.
+
+    kv_len: int32 [B] valid key counts.  kv_src: optional source map [Nk] / [1|B, Nk] int32
+    (kv_source_map) for the fused global K/V read: key j comes from row kv_src[.., j] of
+    k_fresh / v_fresh [B, n_fresh, H, d] when that is in [0, n_fresh), else from k / v (the
+    cache).  workspace: "auto" (a buffer cached per device and stream, sized by
+    safe_attn_workspace_bytes; under HIP graph capture it must already be large enough),
+    None (no tail split), or a uint8 device tensor.  mask: optional dense mask
+    [B|1, H|1, Nq|1, Nk] (size-1 dims broadcast), indexed by query token; bool/uint8
+    attend-where-nonzero or an additive bf16/f16/f32 bias."""
+    a, out, lse = _attn_call(q, k, v, q_rows, kv_len, scale, out, return_lse, scatter_out, check, mask, kv_src,
+                             k_fresh, v_fresh)
+    if a is not None:
+        st = _stream(stream)
+        _attn_set_workspace(a, workspace, q.device, st)
+        _check("safe_attn_fwd", lib.safe_attn_fwd(ctypes.byref(a), st))
     return (out, lse) if return_lse else out
+
+
+_SDPA_WS = {}   # (device index, stream handle) -> classifier scratch of sdpa
+
+
+def sdpa(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, mask: Optional[torch.Tensor] = None,
+         q_rows: Optional[torch.Tensor] = None, scale: Optional[float] = None, out: Optional[torch.Tensor] = None,
+         return_lse: bool = False, scatter_out: bool = False, stream=None, workspace="auto"):
+    """The Eq. 8 rewrite as one call (safe_sdpa): certify `mask` on the GPU, then run the
+    attention without it (every stored row in R), with per-sample key lengths (a text-padding
+    mask with one valid length per sample) or with it (anything else).  mask as for attn_fwd
+    ([B|1, H|1, Nq|1, Nk], size-1 dims broadcast).  Returns (out[, lse], info) with info a
+    dict: route ("no_mask", "kv_len" or "mask"), mask_class (name, or None without a mask)
+    and first_bad_row.  Blocks on the classifier's verdict when a mask is given."""
+    a, out, lse = _attn_call(q, k, v, q_rows, None, scale, out, return_lse, scatter_out, False, mask, None,
+                             None, None)
+    if a is None:
+        res = {"route": None, "mask_class": None, "first_bad_row": -1}
+        return (out, lse, res) if return_lse else (out, res)
+    st = _stream(stream)
+    # the split workspace is sized for the mask-free form; a route whose plan needs more runs unsplit
+    free = AttnArgs.from_buffer_copy(a)
+    free.mask = None
+    _attn_set_workspace(free, workspace, q.device, st)
+    a.workspace, a.workspace_bytes = free.workspace, free.workspace_bytes
+    need = ctypes.c_size_t(0)
+    _check("safe_sdpa", lib.safe_sdpa(ctypes.byref(a), None, ctypes.byref(need), None, st))
+    cws = None
+    if need.value > 0:
+        cws = _cached_workspace(_SDPA_WS, (q.device.index, st), int(need.value), q.device, "sdpa")
+    info = SdpaInfo()
+    size = ctypes.c_size_t(0 if cws is None else cws.numel())
+    _check("safe_sdpa", lib.safe_sdpa(ctypes.byref(a), _ptr(cws), ctypes.byref(size) if cws is not None else None,
+                                      ctypes.byref(info), st))
+    res = {"route": ROUTE_NAMES[info.route],
+           "mask_class": MASK_CLASS_NAMES[info.mask_class] if info.mask_class >= 0 else None,
+           "first_bad_row": int(info.first_bad_row)}
+    return (out, lse, res) if return_lse else (out, res)
 
 
 def _attn_kv_src(a, kv_src, k_fresh, v_fresh, B, Nk, H, d):
@@ -324,11 +432,12 @@ def kv_source_map(idx: torch.Tensor, n_tokens: int, batch: Optional[int] = None,
     idx: ascending int32 token list [nsel] (shared by the batch, B = batch) or [B, nsel]."""
     idx = _i32(idx, "idx")
     if idx.dim() == 1:
-        B, nsel, ibs = (1 if batch is None else int(batch)), idx.shape[0], 0
+        B = 1 if batch is None else int(batch)
+    elif idx.dim() == 2:
+        B = idx.shape[0] if batch is None or idx.shape[0] != 1 else int(batch)
     else:
-        B, nsel, ibs = idx.shape[0], idx.shape[1], idx.stride(0)
-        if idx.stride(1) != 1:
-            raise ValueError("idx rows must be contiguous")
+        raise ValueError("idx must be [nsel] or [B, nsel]")
+    nsel, ibs = _row_lists(idx, B, "idx")
     if out is None:
         out = torch.empty((B, n_tokens), dtype=torch.int32, device=idx.device)
     if out.dtype != torch.int32 or out.shape != (B, n_tokens) or not out.is_contiguous() or not out.is_cuda:
@@ -373,7 +482,7 @@ def attn_plan(q: torch.Tensor, k: torch.Tensor, q_rows: Optional[torch.Tensor] =
     a.B, a.H, a.Nq, a.Nk, a.d = B, H, Nq, k.shape[1], d
     a.n_rows = Nq if q_rows is None else q_rows.shape[-1]
     a.q_rows = None if q_rows is None else _ptr(q_rows)
-    a.q_rows_bstride = 0 if q_rows is None or q_rows.dim() == 1 else q_rows.stride(0)
+    a.q_rows_bstride = _row_lists(q_rows, B, "q_rows")[1]
     a.kv_len = None if kv_len is None else _ptr(kv_len)
     a.mask, a.mask_dtype, ms = _attn_mask(mask, B, a.H, Nq, a.Nk)
     a.mask_stride[:] = ms
@@ -394,12 +503,11 @@ def kv_assemble(k_fresh: torch.Tensor, v_fresh: torch.Tensor, idx: torch.Tensor,
     """Global K/V = fresh rows (token idx) over cached rows; see safe.h.  Returns (k_out, v_out)."""
     for t, n in ((k_fresh, "k_fresh"), (v_fresh, "v_fresh"), (k_cache, "k_cache"), (v_cache, "v_cache")):
         _bits16(t, n)
+    if k_cache.dim() != 4:
+        raise ValueError("k_cache must be 4-D [B, N, H, d]")
     B, N, H, d = k_cache.shape
     idx = _i32(idx, "idx")
-    if idx.dim() == 1:
-        nsel, ibs = idx.shape[0], 0
-    else:
-        nsel, ibs = idx.shape[1], idx.stride(0)
+    nsel, ibs = _row_lists(idx, B, "idx")
     if k_fresh.shape != (B, nsel, H, d) or v_fresh.shape != k_fresh.shape or v_cache.shape != k_cache.shape:
         raise ValueError("shape mismatch: fresh [B, nsel, H, d], cache [B, N, H, d]")
     if in_place:
@@ -476,7 +584,7 @@ def pcsp_accumulate(q_c: torch.Tensor, k_txt: torch.Tensor, w: torch.Tensor, acc
         raise ValueError("w must be contiguous float32 [B, M]")
     if acc.dtype != torch.float32 or acc.shape != (B, N) or not acc.is_contiguous():
         raise ValueError("acc must be contiguous float32 [B, N]")
-    kv_len = _i32(kv_len, "kv_len")
+    kv_len = _lengths(kv_len, B)
     a = PcspArgs()
     a.flags = PCSP_ACCUM
     a.B, a.N, a.M, a.H, a.d = B, N, M, H, d
@@ -493,11 +601,8 @@ def pcsp_accumulate(q_c: torch.Tensor, k_txt: torch.Tensor, w: torch.Tensor, acc
         _check("safe_pcsp_select", lib.safe_pcsp_select(ctypes.byref(a), None, ctypes.byref(need), st))
         workspace = None
         if need.value > 0:
-            key = (acc.device.index, st)
-            workspace = _PCSP_WS.get(key)
-            if workspace is None or workspace.numel() < need.value:
-                workspace = torch.empty(need.value, dtype=torch.uint8, device=acc.device)
-                _PCSP_WS[key] = workspace
+            workspace = _cached_workspace(_PCSP_WS, (acc.device.index, st), int(need.value), acc.device,
+                                          "pcsp_accumulate")
     if workspace is None:
         _check("safe_pcsp_select", lib.safe_pcsp_select(ctypes.byref(a), None, None, st))
     else:
@@ -550,13 +655,17 @@ def sw_cfg(f_c: torch.Tensor, f_u: torch.Tensor, g_ctx: float, g_sens: Optional[
     a.dtype = DT_BF16 if f_c.dtype == torch.bfloat16 else DT_F32
     a.f_c, a.f_u, a.out = _ptr(f_c), _ptr(f_u), _ptr(out)
     a.stride[:] = [f_c.stride(0), f_c.stride(1)]
+    if s is not None and idx is not None:
+        raise ValueError("give at most one of s and idx")
     if s is not None:
-        if s.dtype != torch.float32 or s.shape[-1] != N or s.stride(-1) != 1:
-            raise ValueError("s must be float32 [B, N] or [N] with contiguous rows")
-        a.s, a.s_bstride = _ptr(s), (s.stride(0) if s.dim() == 2 else 0)
+        if s.dtype != torch.float32 or s.dim() not in (1, 2) or s.shape[-1] != N:
+            raise ValueError("s must be float32 [N], [1, N] or [B, N]")
+        _, sbs = _row_lists(s, B, "s")
+        a.s, a.s_bstride = _ptr(s), sbs
     idx = _i32(idx, "idx")
     if idx is not None:
-        a.idx, a.k, a.idx_bstride = _ptr(idx), idx.shape[-1], (idx.stride(0) if idx.dim() == 2 else 0)
+        kk, ibs = _row_lists(idx, B, "idx")
+        a.idx, a.k, a.idx_bstride = _ptr(idx), kk, ibs
     a.g_ctx = float(g_ctx)
     a.g_sens = float(g_ctx if g_sens is None else g_sens)
     _check("safe_sw_cfg", lib.safe_sw_cfg(ctypes.byref(a), _stream(stream)))
@@ -564,8 +673,8 @@ def sw_cfg(f_c: torch.Tensor, f_u: torch.Tensor, g_ctx: float, g_sens: Optional[
 
 
 __all__ = ["attn_fwd", "attn_plan", "attn_workspace_bytes", "kv_assemble", "kv_source_map", "mask_classify",
-           "pcsp_accumulate", "pcsp_select", "sw_cfg", "linear", "block_dense", "block_srsu", "lib", "SafeError",
-           "LIB_PATH", "MASK_CLASS_NAMES"]
+           "pcsp_accumulate", "pcsp_select", "sdpa", "sw_cfg", "linear", "block_dense", "block_srsu", "lib",
+           "SafeError", "LIB_PATH", "MASK_CLASS_NAMES", "ROUTE_NAMES"]
 
 
 def _rows3(t: torch.Tensor, name: str):

@@ -143,7 +143,8 @@ int safe_attn_plan(const safe_attn_args* a, safe_attn_plan_info* out) {
   return attn_plan(a, out);
 }
 
-int safe_attn_fwd(const safe_attn_args* a, void* stream) {
+// Every host-side check of an attention call (sizes, flags, pointers, alignment).
+static int check_attn_call(const safe_attn_args* a) {
   int st = check_attn_sizes(a);
   if (st != SAFE_OK) return st;
   if (a->workspace != nullptr && !aligned16(a->workspace)) return SAFE_ERR_ALIGN;
@@ -166,6 +167,13 @@ int safe_attn_fwd(const safe_attn_args* a, void* stream) {
   // key/value token strides: the kernel addresses a 64-key tile with 32-bit byte offsets
   // (63 rows of 2 * stride bytes plus a row), so strides stay below 2^25 elements
   if (a->k_stride[1] >= (int64_t(1) << 25) || a->v_stride[1] >= (int64_t(1) << 25)) return SAFE_ERR_UNSUPPORTED;
+  return SAFE_OK;
+}
+
+int safe_attn_fwd(const safe_attn_args* a, void* stream) {
+  int st = check_attn_call(a);
+  if (st != SAFE_OK) return st;
+  if ((int64_t)a->B * a->H * a->n_rows == 0) return SAFE_OK;
   hipStream_t s = static_cast<hipStream_t>(stream);
   if (a->flags & SAFE_FLAG_CHECK) {
     if (a->q_rows != nullptr &&
@@ -174,6 +182,89 @@ int safe_attn_fwd(const safe_attn_args* a, void* stream) {
     if (a->kv_len != nullptr && (st = check_lengths(a->kv_len, a->B, a->Nk, s)) != SAFE_OK) return st;
   }
   return attn_fwd_launch(a, resolve_scale(a->scale, a->d), s);
+}
+
+// ---- safe_sdpa: the Eq. 8 rewrite as one call ------------------------------------------
+
+// Stored sizes and element strides of the mask of an attention call: a zero stride marks
+// a broadcast dimension, which is stored with size 1; keys are contiguous.
+static void mask_geometry(const safe_attn_args* a, int64_t size[4], int64_t stride[4]) {
+  const int64_t full[3] = {a->B, a->H, a->Nq};
+  for (int i = 0; i < 3; ++i) {
+    size[i] = a->mask_stride[i] == 0 ? 1 : full[i];
+    stride[i] = a->mask_stride[i];
+  }
+  size[3] = a->Nk;
+  stride[3] = 1;
+}
+
+// Layout of safe_sdpa's scratch: the classifier's workspace, its per-stored-sample key
+// lengths, and (for a mask shared by the batch) those lengths repeated for every sample.
+static size_t align256(size_t x) { return (x + 255) / 256 * 256; }
+static size_t sdpa_scratch(const safe_attn_args* a, const int64_t size[4], size_t* off_len, size_t* off_rep) {
+  *off_len = align256(mask_classify_workspace(size));
+  *off_rep = *off_len + align256((size_t)size[0] * sizeof(int32_t));
+  return *off_rep + align256((size_t)a->B * sizeof(int32_t));
+}
+
+static __global__ void kv_len_repeat_kernel(const int32_t* __restrict__ src, int32_t* __restrict__ dst, int n) {
+  const int i = blockIdx.x * blockDim.x + threadIdx.x;
+  if (i < n) dst[i] = src[0];
+}
+
+int safe_sdpa(const safe_attn_args* a, void* classify_ws, size_t* classify_ws_bytes, safe_sdpa_info* info,
+              void* stream) {
+  if (a == nullptr) return SAFE_ERR_NULL;
+  if (info != nullptr) *info = safe_sdpa_info{SAFE_ROUTE_NO_MASK, -1, -1};
+  // the mask-free call must be valid whatever the route: check it before any scan
+  safe_attn_args c = *a;
+  c.mask = nullptr;
+  int st = check_attn_call(&c);
+  if (st != SAFE_OK) return st;
+  int64_t size[4] = {0, 0, 0, 0}, stride[4] = {0, 0, 0, 1};
+  size_t off_len = 0, off_rep = 0, need = 0;
+  if (a->mask != nullptr) {
+    if (a->kv_len != nullptr || a->kv_src != nullptr) return SAFE_ERR_UNSUPPORTED;
+    if (a->mask_dtype < SAFE_DT_BOOL || a->mask_dtype > SAFE_DT_F32) return SAFE_ERR_DTYPE;
+    for (int i = 0; i < 3; ++i)
+      if (a->mask_stride[i] < 0) return SAFE_ERR_SHAPE;
+    mask_geometry(a, size, stride);
+    need = sdpa_scratch(a, size, &off_len, &off_rep);
+  }
+  if (classify_ws == nullptr && classify_ws_bytes != nullptr) {   // size query: nothing runs
+    *classify_ws_bytes = need;
+    return SAFE_OK;
+  }
+  if (a->mask == nullptr) return safe_attn_fwd(a, stream);
+  if (classify_ws == nullptr) return SAFE_ERR_WORKSPACE;
+  if (classify_ws_bytes != nullptr && *classify_ws_bytes < need) return SAFE_ERR_WORKSPACE;
+  if (!aligned16(classify_ws)) return SAFE_ERR_ALIGN;
+
+  char* ws = static_cast<char*>(classify_ws);
+  int32_t* len = reinterpret_cast<int32_t*>(ws + off_len);
+  int32_t* rep = reinterpret_cast<int32_t*>(ws + off_rep);
+  size_t cls_bytes = mask_classify_workspace(size);
+  safe_mask_info mi;
+  st = safe_mask_classify(a->mask, a->mask_dtype, size, stride, 0, &mi, nullptr, len, ws, &cls_bytes, stream);
+  if (st != SAFE_OK) return st;
+  int route = SAFE_ROUTE_MASK;
+  c = *a;
+  if (mi.verdict) {
+    route = SAFE_ROUTE_NO_MASK;
+    c.mask = nullptr;
+  } else if (mi.mask_class == SAFE_MASK_KEY_PADDING) {
+    route = SAFE_ROUTE_KV_LEN;
+    c.mask = nullptr;
+    c.kv_len = len;
+    if (size[0] != a->B && a->B > 0) {   // one mask batch row serves every sample
+      hipLaunchKernelGGL(kv_len_repeat_kernel, dim3((a->B + 255) / 256), dim3(256), 0,
+                         static_cast<hipStream_t>(stream), len, rep, a->B);
+      if (hipGetLastError() != hipSuccess) return SAFE_ERR_HIP;
+      c.kv_len = rep;
+    }
+  }
+  if (info != nullptr) *info = safe_sdpa_info{route, mi.mask_class, mi.first_bad_row};
+  return safe_attn_fwd(&c, stream);
 }
 
 int safe_kv_assemble(const safe_kv_args* a, void* stream) {

@@ -22,7 +22,7 @@ def declared_functions():
 def test_header_declares_the_four_entry_points():
     names = declared_functions()
     for n in ("safe_mask_classify", "safe_pcsp_select", "safe_kv_assemble", "safe_attn_fwd", "safe_sw_cfg", "safe_linear",
-              "safe_attn_workspace_bytes", "safe_attn_plan", "safe_kv_source_map", "safe_status_str",
+              "safe_attn_workspace_bytes", "safe_attn_plan", "safe_kv_source_map", "safe_sdpa", "safe_status_str",
               "safe_abi_version"):
         assert n in names
 
@@ -34,7 +34,7 @@ def test_every_declared_symbol_is_exported():
 
 
 def test_abi_version_and_status_strings():
-    assert sq.lib.safe_abi_version() == 7 == sq.ABI_VERSION
+    assert sq.lib.safe_abi_version() == 8 == sq.ABI_VERSION
     for code, name in sq.STATUS.items():
         assert sq.lib.safe_status_str(code).decode().startswith(name)
     assert sq.lib.safe_status_str(12345) == b"unknown status"
@@ -61,6 +61,34 @@ def _attn_args(**kw):
 def test_attn_rejects_bad_arguments_without_gpu(kw, status):
     a = _attn_args(**kw)
     assert sq.lib.safe_attn_fwd(ctypes.byref(a), None) == status
+
+
+def test_sdpa_validates_and_sizes_its_scratch_without_gpu():
+    """safe_sdpa (the Eq. 8 rewrite as one call) checks the attention call and the mask on the
+    host, answers the scratch-size query, and refuses a missing or misaligned scratch before
+    any HIP call."""
+    need = ctypes.c_size_t(123)
+    a = _attn_args()
+    assert sq.lib.safe_sdpa(ctypes.byref(a), None, ctypes.byref(need), None, None) == 0
+    assert need.value == 0, "no mask: no scratch"
+    a = _attn_args(mask=0x30000, mask_dtype=1)
+    a.mask_stride[:] = [0, 0, 128]                       # one [Nq, Nk] mask for every (b, h)
+    assert sq.lib.safe_sdpa(ctypes.byref(a), None, ctypes.byref(need), None, None) == 0
+    assert need.value > 0 and need.value % 256 == 0
+    assert sq.lib.safe_sdpa(ctypes.byref(a), None, None, None, None) == -6           # scratch missing
+    small = ctypes.c_size_t(need.value - 1)
+    assert sq.lib.safe_sdpa(ctypes.byref(a), 0x40000, ctypes.byref(small), None, None) == -6
+    assert sq.lib.safe_sdpa(ctypes.byref(a), 0x40008, ctypes.byref(need), None, None) == -8
+    for kw, status in ((dict(mask_dtype=9), -3), (dict(kv_len=0x50000), -5), (dict(d=48), -5),
+                       (dict(kv_src=0x50000), -5), (dict(q=None), -1)):
+        b = _attn_args(**{"mask": 0x30000, "mask_dtype": 1, **kw})
+        assert sq.lib.safe_sdpa(ctypes.byref(b), None, ctypes.byref(need), None, None) == status, kw
+    b = _attn_args(mask=0x30000, mask_dtype=1)
+    b.mask_stride[:] = [0, -1, 128]
+    assert sq.lib.safe_sdpa(ctypes.byref(b), None, ctypes.byref(need), None, None) == -2
+    # an unaligned mask row stride is accepted by the classifier (the masked route checks it later)
+    b.mask_stride[:] = [0, 0, 127]
+    assert sq.lib.safe_sdpa(ctypes.byref(b), None, ctypes.byref(need), None, None) == 0
 
 
 def test_attn_stride_checks():

@@ -373,3 +373,82 @@ def test_caller_outputs_of_the_wrong_shape_or_memory_are_refused():
     o = sq.attn_fwd(qd, kd, vd, q_rows=rows, out=torch.empty((B, 64, H, d), dtype=torch.bfloat16, device="cuda"))
     ref, _ = oracle.sdpa(q.value, k.value, v.value, q_rows=np.arange(0, 256, 4)[[0, 63]])
     assert_attn_close(o[:, [0, 63]], ref, "valid caller output")
+
+
+def test_graph_replay_after_the_cached_workspace_grew():
+    """A call captured with the binding's cached workspace keeps writing that buffer on replay;
+    a larger eager call on the same stream afterwards grows the cache, and the superseded
+    buffer must stay allocated so the replay cannot land in memory that other tensors took."""
+    B, N, H, d = 2, 2000, 4, 96
+    q, k, v = W.attention_inputs(B, N, N, H, d, seed=52)
+    qd, kd, vd = to_dev_bf16(q), to_dev_bf16(k), to_dev_bf16(v)
+    big_q = torch.randn((B, 6000, H, d), device="cuda").to(torch.bfloat16)
+    big_k = torch.randn((B, 9000, H, d), device="cuda").to(torch.bfloat16)
+    small_need = sq.attn_workspace_bytes(qd, kd)
+    big_need = sq.attn_workspace_bytes(big_q, big_k)
+    assert 0 < small_need < big_need, (small_need, big_need)
+    side = torch.cuda.Stream()
+    side.wait_stream(torch.cuda.current_stream())
+    o = torch.empty_like(qd)
+    with torch.cuda.stream(side):
+        sq.attn_fwd(qd, kd, vd, out=o)          # sizes this stream's cached workspace
+    side.synchronize()
+    ref = o.clone()
+    graph = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(graph, stream=side):
+        sq.attn_fwd(qd, kd, vd, out=o)
+    with torch.cuda.stream(side):
+        big = sq.attn_fwd(big_q, big_k, big_k)   # grows the cached workspace of this stream
+    side.synchronize()
+    fillers = [torch.full((small_need // 4 + 1,), 7.0, device="cuda") for _ in range(4)]
+    for rep in range(3):
+        o.zero_()
+        graph.replay()
+        torch.cuda.synchronize()
+        assert torch.equal(o, ref), f"replay {rep}"
+        assert all(bool((f == 7.0).all()) for f in fillers), "a replay wrote into another tensor"
+    assert torch.isfinite(big.float()).all()
+
+
+def test_operands_of_the_wrong_dtype_or_batch_are_refused_before_launch():
+    """Every attention, assembly and linear operand is bf16 (fp16 bits would be read as bf16);
+    key lengths have one entry per sample; index lists are [n], [1, n] or [B, n]."""
+    B, N, H, d = 2, 256, 2, 64
+    q, k, v = W.attention_inputs(B, N, N, H, d, seed=61)
+    qd, kd, vd = to_dev_bf16(q), to_dev_bf16(k), to_dev_bf16(v)
+    for bad in ((qd.half(), kd, vd), (qd, kd.view(torch.int16), vd), (qd, kd, vd.float())):
+        with pytest.raises(TypeError):
+            sq.attn_fwd(*bad)
+    with pytest.raises(TypeError):
+        sq.attn_fwd(qd, kd, vd, out=torch.empty_like(qd).half())
+    for kv in (torch.tensor([5], dtype=torch.int32, device="cuda"),
+               torch.tensor([5, 6, 7], dtype=torch.int32, device="cuda"),
+               torch.tensor([[5, 6]], dtype=torch.int32, device="cuda")):
+        with pytest.raises(ValueError):
+            sq.attn_fwd(qd, kd, vd, kv_len=kv)
+        with pytest.raises(ValueError):
+            sq.pcsp_accumulate(qd, kd, torch.ones((B, N), device="cuda"), torch.zeros((B, N), device="cuda"),
+                               kv_len=kv)
+    rows3 = torch.zeros((3, 10), dtype=torch.int32, device="cuda")
+    with pytest.raises(ValueError):
+        sq.attn_fwd(qd, kd, vd, q_rows=rows3)
+    with pytest.raises(ValueError):
+        sq.attn_fwd(qd, kd, vd, q_rows=torch.zeros((B, 20), dtype=torch.int32, device="cuda")[:, ::2])
+    idx = torch.arange(0, N, 4, dtype=torch.int32, device="cuda")
+    f = qd[:, :idx.shape[0]].contiguous()
+    for bad_idx in (rows3, idx.view(1, 1, -1), torch.stack([idx, idx], 1)):
+        with pytest.raises(ValueError):
+            sq.kv_assemble(f, f, bad_idx, kd, vd)
+    with pytest.raises(TypeError):
+        sq.kv_assemble(f.half(), f.half(), idx, kd, vd)
+    # a [1, n] list is shared by every sample (sample stride 0), like a [n] list
+    ko1, _ = sq.kv_assemble(f, f, idx.view(1, -1), kd, vd)
+    ko2, _ = sq.kv_assemble(f, f, idx, kd, vd)
+    assert torch.equal(ko1, ko2)
+    o1 = sq.attn_fwd(qd, kd, vd, q_rows=idx.view(1, -1))
+    assert torch.equal(o1, sq.attn_fwd(qd, kd, vd, q_rows=idx))
+    fc = torch.zeros((B, N, 16), dtype=torch.float32, device="cuda")
+    with pytest.raises(ValueError):
+        sq.sw_cfg(fc, fc, 3.0, 5.0, s=torch.zeros((3, N), device="cuda"))
+    with pytest.raises(ValueError):
+        sq.sw_cfg(fc, fc, 3.0, 5.0, idx=rows3)

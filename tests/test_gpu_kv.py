@@ -103,3 +103,24 @@ def test_multistep_cache_workload():
         ref, _ = oracle.sdpa(inp["q_c"].value, inp["k_txt"].value, inp["v_txt"].value, q_rows=S[samp],
                              kv_len=inp["kv_len"])
         assert_attn_close(o_c[:, torch.from_numpy(samp).long()], ref, f"cross step {step}")
+
+
+def test_assemble_full_size_bit_exact():
+    """Eq. 14/16 at the 160x160 workload in the bench's form: the drifted fresh rows of the
+    PCSP-sized set (k = 6400 per sample, per-sample lists) over the cached K/V, out of place
+    and in place, compared with the definition bit for bit over every element."""
+    inp = W.workload_inputs(4)
+    w = inp["workload"]
+    k = w.k_for(25)
+    rng = W.rng_for(4, stream=9)
+    idx = np.stack([W.random_rows(rng, w.N, k) for _ in range(w.B)])
+    fk = W.bf16_from_f32(inp["k_x"].value[np.arange(w.B)[:, None], idx] + W.drift((1004, 20), (w.B, k, w.H, w.d)))
+    fv = W.bf16_from_f32(inp["v_x"].value[np.arange(w.B)[:, None], idx] + W.drift((1004, 21), (w.B, k, w.H, w.d)))
+    kc, vc = to_dev_bf16(inp["k_x"]), to_dev_bf16(inp["v_x"])
+    ko, vo = sq.kv_assemble(to_dev_bf16(fk), to_dev_bf16(fv), to_dev(idx), kc, vc)
+    ref_k = oracle.kv_assemble(fk.bits, idx, inp["k_x"].bits)
+    assert np.array_equal(_bits(ko), ref_k)
+    ref_v = oracle.kv_assemble(fv.bits, idx, inp["v_x"].bits)
+    assert np.array_equal(_bits(vo), ref_v)
+    sq.kv_assemble(to_dev_bf16(fk), to_dev_bf16(fv), to_dev(idx), kc, vc, in_place=True)
+    assert np.array_equal(_bits(kc), ref_k) and np.array_equal(_bits(vc), ref_v)

@@ -136,3 +136,54 @@ def test_pipeline_tiny_workload():
     kth = np.sort(sbar[0])[::-1][w.k_for(25) - 1]
     for t in got ^ exp:
         assert abs(sbar[0, t] - kth) <= 1e-4 * np.abs(sbar).max()
+
+
+def _sampled_tokens(rng, N, per=400):
+    """The first two and last two tokens plus `per` random ones."""
+    return np.unique(np.concatenate([[0, 1, N - 2, N - 1], rng.choice(N, size=per, replace=False)]))
+
+
+@pytest.mark.parametrize("number", [3, 4, 5])
+def test_accumulate_full_size_sampled_tokens(number):
+    """Eq. 9-10 at the 128x128, 160x160 and 192x192 grids in the bench's launch configuration
+    (head-group split with the binding's workspace): the oracle on sampled image tokens of
+    both samples (a token's score depends only on its own query rows)."""
+    inp = W.workload_inputs(number)
+    w = inp["workload"]
+    wts = W.pcsp_content_weights(inp["kv_len"], w.M)
+    acc = torch.zeros((w.B, w.N), dtype=torch.float32, device=dev())
+    sq.pcsp_accumulate(to_dev_bf16(inp["q_c"]), to_dev_bf16(inp["k_txt"]), to_dev(wts), acc,
+                       kv_len=to_dev(inp["kv_len"]))
+    samp = _sampled_tokens(W.rng_for(number, stream=8), w.N)
+    ref = oracle.pcsp_accumulate(inp["q_c"].value[:, samp], inp["k_txt"].value, inp["kv_len"], wts)
+    np.testing.assert_allclose(acc.cpu().numpy()[:, samp], ref, rtol=ACC_RTOL, atol=1e-7)
+
+
+def test_select_on_the_full_size_field():
+    """Eq. 11-12 on the 160x160 workload's own accumulated field (k = 3840 / 6400 / 10240):
+    with sigma = 0 both sides rank the identical fp32 array, so the index sets are equal bit
+    for bit; with sigma = 1 (the bench's setting) the oracle smooths the same fp32 field in
+    fp64, and the sets may differ only at tokens whose oracle score lies within 1e-5 max|s|
+    of the k-th score."""
+    inp = W.workload_inputs(4)
+    w = inp["workload"]
+    wts = W.pcsp_content_weights(inp["kv_len"], w.M)
+    acc = torch.zeros((w.B, w.N), dtype=torch.float32, device=dev())
+    sq.pcsp_accumulate(to_dev_bf16(inp["q_c"]), to_dev_bf16(inp["k_txt"]), to_dev(wts), acc,
+                       kv_len=to_dev(inp["kv_len"]))
+    field = acc.cpu().numpy().astype(np.float64)
+    sbar = oracle.gaussian_smooth(field, w.grid_h, w.grid_w, 1.0)
+    for rho in w.rho_percent:
+        k = w.k_for(rho)
+        idx0 = sq.pcsp_select(acc, w.grid_h, w.grid_w, 0.0, k)
+        assert np.array_equal(idx0.cpu().numpy(), oracle.topk_select(field, k)), ("sigma 0", k)
+        idx1, so = sq.pcsp_select(acc, w.grid_h, w.grid_w, 1.0, k, score_out=True)
+        np.testing.assert_allclose(so.cpu().numpy(), oracle.minmax_normalize(sbar), atol=2e-5)
+        ref = oracle.topk_select(sbar, k)
+        for b in range(w.B):
+            got = idx1[b].cpu().numpy()
+            assert got.shape == (k,) and np.all(np.diff(got) > 0)
+            kth = np.sort(sbar[b])[::-1][k - 1]
+            band = 1e-5 * np.abs(sbar[b]).max()
+            diff = set(got.tolist()) ^ set(ref[b].tolist())
+            assert all(abs(sbar[b, t] - kth) <= band for t in diff), ("sigma 1", k, b, len(diff))
