@@ -185,6 +185,7 @@ def main() -> int:
     ap.add_argument("--sigma", type=float, default=1.0)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-sweep", action="store_true")
+    ap.add_argument("--no-parity", action="store_true", help="skip the oracle checks of the timed outputs")
     ap.add_argument("--cpu-rows", type=int, default=3072, help="oracle sample: query rows per sample")
     ap.add_argument("--rocprof-summary", type=str, default=None)
     ap.add_argument("--mfma-busy-summary", type=str, default=None)
@@ -349,7 +350,15 @@ def main() -> int:
                          "end-to-end 2.69x at 1024^2 and 5.09x at 2560^2; peak memory 94.1 -> 27.9 GB",
     }
 
+    if not args.no_parity:
+        out["parity"] = parity_lines(sq, W, inp, wl, idx, k_fresh, v_fresh, k_glob, v_glob, o_srsu, o_cross,
+                                     o_dense, acc, args.sigma, k, mask, verdict)
+        if not out["parity"]["pass"]:
+            print("bench.py: the timed outputs do NOT match the oracle: " + json.dumps(out["parity"]),
+                  file=sys.stderr, flush=True)
+
     if not args.no_sweep:
+        out["anchor_and_three_srsu_steps_64x64"] = c2_steps(sq, W, tf, args.sigma)
         sweep = {}
         for rho in wl.rho_percent:
             kk = wl.k_for(rho)
@@ -392,9 +401,202 @@ def main() -> int:
     if not args.no_cpu_baseline:
         out["cpu_baseline"] = cpu_baseline(inp, args.cpu_rows)
         out["cpu_baseline_small_case"] = oracle_small_case()
+        out["cpu_baseline_workloads"] = cpu_baseline_workloads(W, inp)
 
     print(json.dumps(out), flush=True)
     return 0
+
+
+ATOL_MAX, ATOL_MEAN, REL_L2 = 1e-2, 1e-3, 1e-2   # attention against the fp64 oracle (bf16 inputs)
+
+
+def attn_errors(got, ref) -> dict:
+    """max-abs, mean-abs and relative L2 error of sampled attention rows against the oracle."""
+    import numpy as np
+    g = got.float().cpu().numpy().astype(np.float64)
+    err = np.abs(g - ref)
+    nref = float(np.sqrt(np.sum(ref * ref)))
+    res = {"rows": int(np.prod(ref.shape[:2])), "max_abs": float(err.max()), "mean_abs": float(err.mean()),
+           "rel_l2": float(np.sqrt(np.sum(err * err)) / nref) if nref > 0 else float(np.sqrt(np.sum(err * err))),
+           "finite": bool(np.isfinite(g).all())}
+    res["ok"] = bool(res["finite"] and res["max_abs"] <= ATOL_MAX and res["mean_abs"] <= ATOL_MEAN
+                     and res["rel_l2"] <= REL_L2)
+    return {kk: (round(v, 8) if isinstance(v, float) else v) for kk, v in res.items()}
+
+
+def _bits_np(t):
+    import numpy as np
+    return t.contiguous().view(__import__("torch").int16).cpu().numpy().view(np.uint16)
+
+
+def parity_lines(sq, W, inp, wl, idx, k_fresh, v_fresh, k_glob, v_glob, o_srsu, o_cross, o_dense, acc,
+                 sigma: float, k: int, mask, verdict) -> dict:
+    """The outputs of the last timed step checked against the fp64 oracle on the same inputs:
+    attention on sampled rows (SRSU self- and cross-attention on rows of the PCSP set, the dense
+    pass on sampled tokens; max-abs, mean-abs, relative L2), the assembled global K/V bit for
+    bit, the top-k set on the step's own accumulated field (sigma 0: bit for bit on the same
+    fp32 array; the bench's sigma: the oracle smooths that array in fp64, sets may differ only
+    within 1e-5 max|s| of the k-th score), and the classifier's verdict against the oracle's full
+    scan of the same mask (copied back in 256 MB chunks)."""
+    import numpy as np
+    import oracle
+    B, N, H, d = wl.B, wl.N, wl.H, wl.d
+    res = {"tolerance": {"attn_max_abs": ATOL_MAX, "attn_mean_abs": ATOL_MEAN, "attn_rel_l2": REL_L2}}
+    idx_np = idx.cpu().numpy().astype(np.int64)
+    # global K/V: bit for bit against the definition
+    kg_bits = oracle.kv_assemble(_bits_np(k_fresh), idx_np, inp["k_x"].bits)
+    vg_bits = oracle.kv_assemble(_bits_np(v_fresh), idx_np, inp["v_x"].bits)
+    res["kv_assemble_bitwise"] = bool(np.array_equal(_bits_np(k_glob), kg_bits)
+                                      and np.array_equal(_bits_np(v_glob), vg_bits))
+    kg, vg = W.bf16_bits_to_f32(kg_bits), W.bf16_bits_to_f32(vg_bits)
+    del kg_bits, vg_bits
+    rng = W.rng_for(wl.number, stream=11)
+    pos = np.unique(np.concatenate([[0, 127, 128, 255, 256, k - 1], rng.choice(k, 26, replace=False)]))
+    rows = idx_np[:, pos]
+    ref, _ = oracle.sdpa(inp["q_x"].value, kg, vg, q_rows=rows)
+    res["srsu_self"] = attn_errors(o_srsu[:, pos.tolist()], ref)
+    del kg, vg
+    ref, _ = oracle.sdpa(inp["q_c"].value, inp["k_txt"].value, inp["v_txt"].value, q_rows=rows,
+                         kv_len=inp["kv_len"])
+    res["srsu_cross"] = attn_errors(o_cross[:, pos.tolist()], ref)
+    tok = np.unique(np.concatenate([[0, 255, 256, N - 257, N - 1], rng.choice(N, 27, replace=False)]))
+    ref, _ = oracle.sdpa(inp["q_x"].value, inp["k_x"].value, inp["v_x"].value, q_rows=tok)
+    res["dense"] = attn_errors(o_dense[:, tok.tolist()], ref)
+    # top-k on the step's own field
+    field = acc.cpu().numpy().astype(np.float64)
+    idx_s0 = sq.pcsp_select(acc, wl.grid_h, wl.grid_w, 0.0, k).cpu().numpy()
+    res["topk_sigma0_bitwise"] = bool(np.array_equal(idx_s0, oracle.topk_select(field, k)))
+    sbar = oracle.gaussian_smooth(field, wl.grid_h, wl.grid_w, sigma)
+    ref_idx = oracle.topk_select(sbar, k)
+    n_diff, in_band = 0, True
+    for b in range(B):
+        diff = set(idx_np[b].tolist()) ^ set(ref_idx[b].tolist())
+        kth = np.sort(sbar[b])[::-1][k - 1]
+        band = 1e-5 * np.abs(sbar[b]).max()
+        n_diff += len(diff)
+        in_band &= all(abs(sbar[b, t] - kth) <= band for t in diff)
+    res["topk_sigma_bench"] = {"sigma": sigma, "equal": n_diff == 0, "tokens_differing": n_diff,
+                               "differences_within_band": bool(in_band)}
+    # the classifier's verdict against the oracle's full scan of the same mask
+    host = np.empty(tuple(mask.shape), dtype=np.float32)
+    flat, hflat = mask.view(-1), host.reshape(-1)
+    chunk = (256 << 20) // 2
+    t0 = time.perf_counter()
+    for s0 in range(0, flat.numel(), chunk):
+        hflat[s0:s0 + chunk] = flat[s0:s0 + chunk].float().cpu().numpy()
+    t_copy = time.perf_counter() - t0
+    t0 = time.perf_counter()
+    ov = oracle.classify_mask(host, False)
+    t_scan = time.perf_counter() - t0
+    del host
+    res["classify"] = {"gpu_verdict": verdict[0], "gpu_class": verdict[1], "oracle_verdict": ov.verdict,
+                       "oracle_class": ov.mask_class, "equal": [verdict[0], verdict[1]] == [ov.verdict, ov.mask_class],
+                       "oracle_full_scan_s": round(t_scan, 3), "d2h_copy_s": round(t_copy, 3),
+                       "oracle_gbs": round(mask.numel() * 2 / t_scan / 1e9, 3)}
+    res["pass"] = bool(res["kv_assemble_bitwise"] and res["srsu_self"]["ok"] and res["srsu_cross"]["ok"]
+                       and res["dense"]["ok"] and res["topk_sigma0_bitwise"] and in_band and res["classify"]["equal"])
+    return res
+
+
+def c2_steps(sq, W, tf, sigma: float) -> dict:
+    """The 64x64-grid workload (B=2, H=24, d=96, N=4096, M=256, rho 30%: k=1229) as the pages'
+    schedule runs it: a dense anchor pass on (K0, V0) whose K/V become the cache (Eq. 18-19),
+    then three SRSU steps t = 1..3 with K_t = K_(t-1) + N(0, 0.05) drift (same for V): the fresh
+    rows of S assembled over the cache, SRSU self-attention and the text cross-attention with
+    per-sample lengths.  Each call is timed per step; the oracle checks sampled rows of S at
+    every step."""
+    import numpy as np
+    import torch
+    import oracle
+    inp = W.workload_inputs(2)
+    wl = inp["workload"]
+    B, N, H, d, M = wl.B, wl.N, wl.H, wl.d, wl.M
+    k = wl.k_for(wl.rho_percent[0])
+    dv = lambda t: torch.from_numpy(np.ascontiguousarray(t.bits).view(np.int16)).cuda().view(torch.bfloat16)
+    q, k0, v0, qc, kt, vt = (dv(inp[n]) for n in ("q_x", "k_x", "v_x", "q_c", "k_txt", "v_txt"))
+    kv_len = torch.from_numpy(inp["kv_len"]).cuda()
+    wts = torch.from_numpy(W.pcsp_content_weights(inp["kv_len"], M)).cuda()
+    acc = torch.zeros((B, N), dtype=torch.float32, device="cuda")
+    sq.pcsp_accumulate(qc, kt, wts, acc, kv_len=kv_len)
+    S = sq.pcsp_select(acc, wl.grid_h, wl.grid_w, sigma, k)
+    S_np = S.cpu().numpy().astype(np.int64)
+    o_d = torch.empty_like(q)
+    dense_ms = _time_ms(lambda: sq.attn_fwd(q, k0, v0, out=o_d), 20)
+    fl_dense, fl_srsu = 4.0 * B * H * N * N * d, 4.0 * B * H * k * N * d
+    fl_cross = 4.0 * H * d * k * int(inp["kv_len"].sum())
+    res = {"workload": "64x64 grid: B=2 H=24 d=96 N=4096 M=256 kv_len=%s, k=%d (rho 30%%), sigma %g"
+                       % (inp["kv_len"].tolist(), k, sigma),
+           "anchor_dense_ms": round(dense_ms, 4), "anchor_dense_tflops": round(tf(fl_dense, dense_ms), 2), "steps": []}
+    k_glob, v_glob = torch.empty_like(k0), torch.empty_like(v0)
+    o_s = torch.empty((B, k, H, d), dtype=torch.bfloat16, device="cuda")
+    o_c = torch.empty_like(o_s)
+    k_t, v_t = inp["k_x"].value.copy(), inp["v_x"].value.copy()
+    rng = W.rng_for(2, stream=12)
+    ok = True
+    bidx = np.arange(B)[:, None]
+    for step in range(1, 4):
+        k_t = k_t + W.drift((1002, 10, step), k_t.shape)
+        v_t = v_t + W.drift((1002, 11, step), v_t.shape)
+        fk, fv = W.bf16_from_f32(k_t[bidx, S_np]), W.bf16_from_f32(v_t[bidx, S_np])
+        kf, vf = dv(fk), dv(fv)
+        ms_kv = _time_ms(lambda: sq.kv_assemble(kf, vf, S, k0, v0, k_out=k_glob, v_out=v_glob), 50)
+        ms_s = _time_ms(lambda: sq.attn_fwd(q, k_glob, v_glob, q_rows=S, out=o_s), 50)
+        ms_c = _time_ms(lambda: sq.attn_fwd(qc, kt, vt, q_rows=S, kv_len=kv_len, out=o_c), 50)
+        pos = np.unique(np.concatenate([[0, k - 1], rng.choice(k, 14, replace=False)]))
+        kg = oracle.kv_assemble(fk.value, S_np, inp["k_x"].value)
+        vg = oracle.kv_assemble(fv.value, S_np, inp["v_x"].value)
+        ref, _ = oracle.sdpa(inp["q_x"].value, kg, vg, q_rows=S_np[:, pos])
+        e_s = attn_errors(o_s[:, pos.tolist()], ref)
+        ref, _ = oracle.sdpa(inp["q_c"].value, inp["k_txt"].value, inp["v_txt"].value, q_rows=S_np[:, pos],
+                             kv_len=inp["kv_len"])
+        e_c = attn_errors(o_c[:, pos.tolist()], ref)
+        asm_bitwise = bool(np.array_equal(_bits_np(k_glob), oracle.kv_assemble(fk.bits, S_np, inp["k_x"].bits)))
+        ok &= e_s["ok"] and e_c["ok"] and asm_bitwise
+        res["steps"].append({"t": step, "kv_assemble_ms": round(ms_kv, 4), "srsu_self_ms": round(ms_s, 4),
+                             "srsu_self_tflops": round(tf(fl_srsu, ms_s), 2), "srsu_cross_ms": round(ms_c, 4),
+                             "srsu_cross_tflops": round(tf(fl_cross, ms_c), 2),
+                             "dense_over_step": round(dense_ms / (ms_kv + ms_s + ms_c), 3),
+                             "kv_assemble_bitwise": asm_bitwise, "srsu_self_err": e_s, "srsu_cross_err": e_c})
+    res["ideal_dense_over_srsu"] = round(N / k, 3)
+    res["parity_ok"] = bool(ok)
+    return res
+
+
+def cpu_baseline_workloads(W, inp4) -> dict:
+    """The fp64 oracle's attention on sampled rows of every full-size workload, timed on this
+    host and extrapolated linearly to all rows (labelled as such): SRSU self-attention on k rows
+    and the dense pass on N rows per sample; the 160x160 inputs are the bench's own, the others
+    are N(0, 1) draws of the workload's shape (the oracle's time depends only on the shapes)."""
+    import numpy as np
+    import oracle
+    try:
+        from threadpoolctl import threadpool_info
+        cores = max([i.get("num_threads", 1) for i in threadpool_info()] or [1])
+    except Exception:  # pragma: no cover
+        cores = len(os.sched_getaffinity(0))
+    res = {"kind": "oracle", "cores": int(cores), "note": "sampled rows, time extrapolated linearly to all rows"}
+    for num in (2, 3, 4, 5):
+        wl = W.WORKLOADS[num]
+        B, N, H, d = wl.B, wl.N, wl.H, wl.d
+        k = wl.k_for(wl.rho_percent[0])
+        if num == 4:
+            q, kk, vv = inp4["q_x"].value, inp4["k_x"].value, inp4["v_x"].value
+        else:
+            g = np.random.default_rng(9000 + num)
+            q = g.standard_normal((B, 64, H, d), dtype=np.float32)
+            kk = g.standard_normal((B, N, H, d), dtype=np.float32)
+            vv = g.standard_normal((B, N, H, d), dtype=np.float32)
+        n = 64
+        rows = np.tile(np.arange(n), (B, 1))
+        t0 = time.perf_counter()
+        oracle.sdpa(q, kk, vv, q_rows=rows)
+        secs = time.perf_counter() - t0
+        per_row = secs / (B * n)
+        res[wl.name] = {"sampled_rows": B * n, "sample_s": round(secs, 3),
+                        "srsu_extrapolated_s": round(per_row * B * k, 2),
+                        "dense_extrapolated_s": round(per_row * B * N, 2),
+                        "tflops": round(4.0 * B * H * n * N * d / secs / 1e12, 6)}
+    return res
 
 
 def _time_ms(fn, reps: int, warm_ms: float = 40.0) -> float:

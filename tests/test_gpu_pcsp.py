@@ -138,6 +138,18 @@ def test_pipeline_tiny_workload():
         assert abs(sbar[0, t] - kth) <= 1e-4 * np.abs(sbar).max()
 
 
+def _norm_tol(sbar: np.ndarray) -> float:
+    """Bound on |Norm_gpu - Norm_oracle| for one sample row.  The GPU smooths in fp32: each pass of
+    at most 2*ceil(3 sigma) + 1 taps (renormalised weights) rounds at most ~16 times, so s_bar is
+    off by <= 16 * 2^-24 * max|s_bar| per pass, two passes; min-max then subtracts the minimum
+    and divides by (max - min), which turns that absolute error into a relative one scaled by
+    max|s_bar| / (max - min), plus a rounding of the quotient.  A field whose spread is small
+    against its magnitude (sums over 24 heads of softmax-weighted scores) therefore carries a
+    larger Norm error than a unit-range field."""
+    span = float(sbar.max() - sbar.min())
+    return float(2 * 2 * 16 * 2.0 ** -24 * np.abs(sbar).max() / span + 2.0 ** -22)
+
+
 def _sampled_tokens(rng, N, per=400):
     """The first two and last two tokens plus `per` random ones."""
     return np.unique(np.concatenate([[0, 1, N - 2, N - 1], rng.choice(N, size=per, replace=False)]))
@@ -178,7 +190,9 @@ def test_select_on_the_full_size_field():
         idx0 = sq.pcsp_select(acc, w.grid_h, w.grid_w, 0.0, k)
         assert np.array_equal(idx0.cpu().numpy(), oracle.topk_select(field, k)), ("sigma 0", k)
         idx1, so = sq.pcsp_select(acc, w.grid_h, w.grid_w, 1.0, k, score_out=True)
-        np.testing.assert_allclose(so.cpu().numpy(), oracle.minmax_normalize(sbar), atol=2e-5)
+        got_norm, ref_norm = so.cpu().numpy(), oracle.minmax_normalize(sbar)
+        for b in range(w.B):
+            np.testing.assert_allclose(got_norm[b], ref_norm[b], atol=_norm_tol(sbar[b]))
         ref = oracle.topk_select(sbar, k)
         for b in range(w.B):
             got = idx1[b].cpu().numpy()

@@ -10,10 +10,13 @@ Execution for High-Resolution Diffusion Transformers", Eq. 1-4): image tokens
 N on a grid_h x grid_w latent raster, M text tokens, H heads of size d.
 Tensors are token-major [B, N, H, d] with d contiguous.
 
-Recipe (stated once, used everywhere): numpy PCG64 seeded with
-1000 + workload number; activations N(0, 1) drawn in float32 and rounded to
-bfloat16 with round-to-nearest-even; per-sample valid text lengths uniform
-integers; the drift between steps N(0, 0.05) (0.05 is a standard deviation).
+Recipe (stated once, used everywhere): activations N(0, 1) drawn in float32
+with torch's CPU generator (Mersenne Twister, thread-count independent) seeded
+from numpy's SeedSequence of (1000 + workload number, tensor id), then rounded
+to bfloat16 with round-to-nearest-even; per-sample valid text lengths, sensitive
+row sets and masks from numpy PCG64 seeded with 1000 + workload number (plus a
+per-purpose stream offset); the drift between steps N(0, 0.05) drawn like the
+activations (0.05 is a standard deviation).
 """
 from __future__ import annotations
 
