@@ -44,7 +44,7 @@
 extern "C" {
 #endif
 
-#define SAFE_ABI_VERSION 8
+#define SAFE_ABI_VERSION 9
 
 /* ---- status codes (negative = error) ----------------------------------- */
 enum {
@@ -298,6 +298,28 @@ typedef struct {
 } safe_attn_args;
 
 int safe_attn_fwd(const safe_attn_args* a, void* stream);
+
+/*
+ * safe_attn_fwd_noalloc -- safe_attn_fwd for callers that cannot allocate device memory:
+ * code under HIP graph capture, tight serving loops, harnesses that forbid allocation.
+ * The partials of the split tail tiles go to a library-owned static device array of
+ * SAFE_NOALLOC_SCRATCH_BYTES bytes (one per GPU, held until the process ends) instead of a
+ * caller workspace: the call runs the schedule safe_attn_fwd runs with a workspace of that
+ * size (bit for bit the same result), so a shape whose split needs more runs unsplit and no
+ * call can exceed the array.  No allocation, no free, no host synchronisation.
+ *
+ * a             as for safe_attn_fwd, except: workspace must be NULL and workspace_bytes 0
+ *               (SAFE_ERR_WORKSPACE otherwise: the scratch is the library's), and
+ *               SAFE_FLAG_CHECK is refused (SAFE_ERR_UNSUPPORTED: it copies device values
+ *               to host memory).
+ * The first call on a device resolves the array's address there (hipGetSymbolAddress;
+ * SAFE_ERR_HIP if that fails).  Every call on a GPU shares that GPU's array and leaves
+ * its partials in it; no call reads a byte of it that the same call has not written first,
+ * so nothing needs clearing, but calls that overlap on one GPU (other streams, other host
+ * threads) race on the array: order them on one stream.
+ */
+#define SAFE_NOALLOC_SCRATCH_BYTES (64ull << 20)
+int safe_attn_fwd_noalloc(const safe_attn_args* a, void* stream);
 
 /* Workspace bytes that let safe_attn_fwd split the last round of tiles for these
  * arguments on the current device (0: this shape gains nothing from a split, the

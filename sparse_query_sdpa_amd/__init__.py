@@ -38,7 +38,7 @@ CLASSIFY_ASYNC = 1 << 2
 PCSP_ACCUM = 1 << 3
 PCSP_SELECT = 1 << 4
 
-ABI_VERSION = 8   # struct layouts below match include/safe.h of this version
+ABI_VERSION = 9   # struct layouts below match include/safe.h of this version
 DT_BOOL, DT_BF16, DT_F16, DT_F32 = 0, 1, 2, 3
 MASK_CLASS_NAMES = ("ALL_VALID", "ZERO", "ROW_CONST", "KEY_PADDING", "NONCONST", "BLOCKED", "NONFINITE")
 
@@ -137,6 +137,8 @@ def _load():
     lib.safe_status_str.argtypes = [ctypes.c_int]
     lib.safe_attn_fwd.restype = ctypes.c_int
     lib.safe_attn_fwd.argtypes = [ctypes.POINTER(AttnArgs), ctypes.c_void_p]
+    lib.safe_attn_fwd_noalloc.restype = ctypes.c_int
+    lib.safe_attn_fwd_noalloc.argtypes = [ctypes.POINTER(AttnArgs), ctypes.c_void_p]
     lib.safe_sdpa.restype = ctypes.c_int
     lib.safe_sdpa.argtypes = [ctypes.POINTER(AttnArgs), ctypes.c_void_p, ctypes.POINTER(ctypes.c_size_t),
                               ctypes.POINTER(SdpaInfo), ctypes.c_void_p]

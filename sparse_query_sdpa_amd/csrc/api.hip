@@ -2,6 +2,7 @@
 #include <math.h>
 #include <string.h>
 
+#include <atomic>
 #include <vector>
 
 #include "common.h"
@@ -182,6 +183,48 @@ int safe_attn_fwd(const safe_attn_args* a, void* stream) {
     if (a->kv_len != nullptr && (st = check_lengths(a->kv_len, a->B, a->Nk, s)) != SAFE_OK) return st;
   }
   return attn_fwd_launch(a, resolve_scale(a->scale, a->d), s);
+}
+
+// ---- safe_attn_fwd_noalloc: the split partials in a static device array ----------------
+
+// The scratch of the allocation-free attention entry point.  In host code `scratch` names a
+// host-side stand-in, not device memory: its device address is resolved once per device
+// with hipGetSymbolAddress and only that address is ever handed to a kernel.
+static __device__ __align__(256) unsigned char scratch[SAFE_NOALLOC_SCRATCH_BYTES];
+
+static constexpr int kMaxScratchDevices = 64;
+static std::atomic<void*> g_scratch_ptr[kMaxScratchDevices];
+
+// Device address of this device's copy of `scratch` (resolved on the first call on the
+// device, with the device current; racing first calls store the same address).
+static int current_scratch(void** out) {
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess) return SAFE_ERR_HIP;
+  if (dev < 0 || dev >= kMaxScratchDevices) return SAFE_ERR_UNSUPPORTED;
+  void* p = g_scratch_ptr[dev].load(std::memory_order_acquire);
+  if (p == nullptr) {
+    if (hipGetSymbolAddress(&p, HIP_SYMBOL(scratch)) != hipSuccess || p == nullptr) return SAFE_ERR_HIP;
+    g_scratch_ptr[dev].store(p, std::memory_order_release);
+  }
+  *out = p;
+  return SAFE_OK;
+}
+
+int safe_attn_fwd_noalloc(const safe_attn_args* a, void* stream) {
+  if (a == nullptr) return SAFE_ERR_NULL;
+  if (a->workspace != nullptr || a->workspace_bytes != 0) return SAFE_ERR_WORKSPACE;
+  if (a->flags & SAFE_FLAG_CHECK) return SAFE_ERR_UNSUPPORTED;
+  int st = check_attn_call(a);
+  if (st != SAFE_OK) return st;
+  if ((int64_t)a->B * a->H * a->n_rows == 0) return SAFE_OK;
+  safe_attn_args c = *a;
+  if ((st = current_scratch(&c.workspace)) != SAFE_OK) return st;
+  c.workspace_bytes = (int64_t)SAFE_NOALLOC_SCRATCH_BYTES;
+  // the plan takes a split only when its partials fit the array; checked, not assumed
+  safe_attn_plan_info plan;
+  if ((st = attn_plan(&c, &plan)) != SAFE_OK) return st;
+  if (plan.workspace_bytes > (int64_t)SAFE_NOALLOC_SCRATCH_BYTES) return SAFE_ERR_WORKSPACE;
+  return attn_fwd_launch(&c, resolve_scale(c.scale, c.d), static_cast<hipStream_t>(stream));
 }
 
 // ---- safe_sdpa: the Eq. 8 rewrite as one call ------------------------------------------

@@ -34,7 +34,7 @@ def test_every_declared_symbol_is_exported():
 
 
 def test_abi_version_and_status_strings():
-    assert sq.lib.safe_abi_version() == 8 == sq.ABI_VERSION
+    assert sq.lib.safe_abi_version() == 9 == sq.ABI_VERSION
     for code, name in sq.STATUS.items():
         assert sq.lib.safe_status_str(code).decode().startswith(name)
     assert sq.lib.safe_status_str(12345) == b"unknown status"
