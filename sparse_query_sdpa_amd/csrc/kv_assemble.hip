@@ -8,8 +8,8 @@
 // (lower bound of the first token) plus a 32-entry map in LDS, then streams each
 // token's K and V rows from their single source to the output in 16-byte chunks.
 // Every output byte is read once and written once.
-// In place (output == cache): a workgroup copies 32 fresh rows to their tokens;
-// context rows are not touched.
+// In place (output == cache): a workgroup copies one (packed rows) or 32 fresh rows to
+// their tokens; context rows are not touched.
 // Index entries outside [0, N) are skipped, so no index value can address
 // memory outside the tensors.
 #include "common.h"
@@ -95,6 +95,13 @@ __global__ __launch_bounds__(NT) void kv_assemble_kernel(KvParams p) {
 // per workgroup move 6.0 TB/s, 8 tokens 5.4, 16 tokens 4.9.)
 constexpr int PTOK = 4;
 constexpr int PU = 4;   // chunks per thread per step
+// The packed in-place scatter moves 4 k H d bytes (236 MB at the 160x160 grid, rho 25%):
+// one fresh row (2 x 288 chunks) per workgroup of 256 threads, two chunks per thread, reached
+// 69% of 8 TB/s (42.8 us); 2, 4, 8 and 16 rows per workgroup 67, 63, 58 and 56%, 64- to
+// 192-thread workgroups 63-69%.  At this size the launch and drain take a tenth of the time.
+constexpr int SROWS = 1;     // fresh rows per workgroup
+constexpr int SPU = 2;       // chunks per thread per step
+constexpr int SNT = 256;     // threads per workgroup
 __global__ __launch_bounds__(NT) void kv_assemble_packed_kernel(KvParams p) {
   __shared__ int src_row[PTOK];
   const int tid = threadIdx.x;
@@ -188,6 +195,55 @@ __global__ __launch_bounds__(NT) void kv_scatter_kernel(KvParams p) {
   }
 }
 
+// In place with packed rows: a workgroup owns SROWS fresh rows of one sample and copies
+// their K rows, then their V rows, to the tokens the index list names, as one flat run of
+// 16-byte chunks (SPU per thread per step, non-temporal on both sides), so at the 160x160
+// grid 12800 workgroups stream instead of 400.  Rows whose token is outside [0, N) are
+// skipped.
+__global__ __launch_bounds__(SNT) void kv_scatter_packed_kernel(KvParams p) {
+  __shared__ int dst_tok[SROWS];
+  const int tid = threadIdx.x;
+  const int b = blockIdx.x / p.blocks_per_b;
+  const int r0 = (blockIdx.x % p.blocks_per_b) * SROWS;
+  const int nr = min(SROWS, p.nsel - r0);
+  if (tid < SROWS) {
+    const int j = tid < nr ? p.idx[(int64_t)b * p.ibs + r0 + tid] : -1;
+    dst_tok[tid] = (j >= 0 && j < p.N) ? j : -1;
+  }
+  __syncthreads();
+  const int R = p.H * p.d8;          // 16-byte chunks per row
+  const int per = nr * R;            // chunks of one tensor in this workgroup
+  const int total = 2 * per;
+  const float inv_r = 1.0f / (float)R;
+  const int64_t fb = (int64_t)b * p.fs0, ob = (int64_t)b * p.os0;
+  for (int base = 0; base < total; base += SPU * SNT) {
+    u32x4 v[SPU];
+    u32x4* dst[SPU];
+#pragma unroll
+    for (int u = 0; u < SPU; ++u) {
+      const int c = base + u * SNT + tid;
+      dst[u] = nullptr;
+      if (c < total) {
+        const bool isv = c >= per;
+        const int cc = isv ? c - per : c;
+        int t = (int)((float)cc * inv_r);          // row of the chunk, t < SROWS: one correction
+        if (t * R > cc) --t;
+        else if ((t + 1) * R <= cc) ++t;
+        const int ch = cc - t * R;
+        const int j = dst_tok[t];
+        if (j >= 0) {
+          const u16* src = (isv ? p.vf : p.kf) + fb + (int64_t)(r0 + t) * p.fs1;
+          v[u] = __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(src) + ch);
+          dst[u] = reinterpret_cast<u32x4*>((isv ? p.vo : p.ko) + ob + (int64_t)j * p.os1) + ch;
+        }
+      }
+    }
+#pragma unroll
+    for (int u = 0; u < SPU; ++u)
+      if (dst[u] != nullptr) __builtin_nontemporal_store(v[u], dst[u]);
+  }
+}
+
 // Source map of the fused global K/V read: src[b, j] = r when idx[b, r] == j, else -1.
 // A workgroup owns NT consecutive tokens of one sample: one binary search (lower bound
 // of its first token in the ascending list) finds the entries that land in its range,
@@ -251,10 +307,14 @@ int kv_assemble_launch(const safe_kv_args* a, bool in_place, hipStream_t s) {
   p.B = a->B; p.N = a->N; p.H = a->H; p.d8 = a->d / 8; p.nsel = a->nsel;
   if (in_place) {
     if (a->nsel == 0) return SAFE_OK;
-    p.blocks_per_b = (a->nsel + TOK - 1) / TOK;
+    const bool packed = a->fresh_stride[2] == a->d && a->out_stride[2] == a->d &&
+                        (int64_t)a->H * (a->d / 8) * SROWS * 2 < 0x7fffffff;
+    const int rows = packed ? SROWS : TOK;
+    p.blocks_per_b = (a->nsel + rows - 1) / rows;
     const int64_t grid = (int64_t)p.blocks_per_b * a->B;
     if (grid > 0x7fffffff) return SAFE_ERR_SHAPE;
-    hipLaunchKernelGGL(kv_scatter_kernel, dim3((unsigned)grid), dim3(NT), 0, s, p);
+    if (packed) hipLaunchKernelGGL(kv_scatter_packed_kernel, dim3((unsigned)grid), dim3(SNT), 0, s, p);
+    else hipLaunchKernelGGL(kv_scatter_kernel, dim3((unsigned)grid), dim3(NT), 0, s, p);
   } else {
     const bool packed = a->fresh_stride[2] == a->d && a->cache_stride[2] == a->d && a->out_stride[2] == a->d &&
                         (int64_t)a->H * (a->d / 8) * PTOK * 2 < 0x7fffffff;
