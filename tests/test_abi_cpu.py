@@ -91,6 +91,23 @@ def test_sdpa_validates_and_sizes_its_scratch_without_gpu():
     assert sq.lib.safe_sdpa(ctypes.byref(b), None, ctypes.byref(need), None, None) == 0
 
 
+def test_noalloc_validates_on_the_host_without_gpu():
+    """safe_attn_fwd_noalloc owns its scratch: a caller workspace or the host-side check flag
+    is refused, and the size checks of safe_attn_fwd apply, all before any HIP call."""
+    f = sq.lib.safe_attn_fwd_noalloc
+    assert f(None, None) == -1
+    a = _attn_args(workspace=0x60000, workspace_bytes=1 << 20)
+    assert f(ctypes.byref(a), None) == -6
+    a = _attn_args(workspace_bytes=16)
+    assert f(ctypes.byref(a), None) == -6
+    a = _attn_args(flags=1)
+    assert f(ctypes.byref(a), None) == -5
+    for kw, status in ((dict(d=48), -5), (dict(B=-1), -2), (dict(q=None), -1), (dict(n_rows=5), -2)):
+        assert f(ctypes.byref(_attn_args(**kw)), None) == status, kw
+    a = _attn_args(n_rows=0, q_rows=0x20000)    # nothing to compute: no HIP call, OK
+    assert f(ctypes.byref(a), None) == 0
+
+
 def test_attn_stride_checks():
     a = _attn_args()
     a.k_stride[1] = 100  # not a multiple of 8 elements

@@ -74,3 +74,38 @@ def test_row_selective_equals_dense_on_its_own_anchor():
     z_s = sq.block_srsu(xd, to_dev(idx), z.clone(), qkv.clone(), wd, H)
     diff = (z_s.float() - z.float()).abs()
     assert diff.max().item() <= 2.0 ** -6 * (1 + z.float().abs().max().item())
+
+
+def test_dense_block_stage_by_stage():
+    """The same block, one intermediate at a time: each stage is compared with the oracle
+    applied to the GPU's own input to that stage, so every stage carries its own derived
+    bound instead of the compounded one -- the row-wise maps the linear bound (one bf16
+    rounding of the result plus the fp32 accumulation bound, the GELU slope, the residual
+    add), the attention the attention bound (max-abs, mean-abs, relative L2) -- and the
+    stages reproduce block_dense bit for bit."""
+    from gpu_util import assert_attn_close
+    from test_gpu_linear import bound, check
+    B, N, H, d, F = 2, 1000, 4, 96, 1536
+    C = H * d
+    x, w64, wd = _setup(B, N, H, d, F, 80)
+    xd = to_dev_bf16(x)
+    f64 = lambda t: t.float().cpu().numpy().astype(np.float64)
+    qkv = sq.linear(xd, wd["w_qkv"])
+    ref = oracle.linear(x.value, w64["w_qkv"])
+    check(qkv, ref, bound(x.value, w64["w_qkv"], ref, C), "qkv projection")
+    q, k, v = (qkv[..., i * C:(i + 1) * C].unflatten(-1, (H, d)) for i in range(3))
+    a = sq.attn_fwd(q, k, v)
+    ref_a, _ = oracle.sdpa(f64(q), f64(k), f64(v))
+    assert_attn_close(a, ref_a, "attention on the projected q, k, v")
+    a2 = a.view(B, N, C)
+    y = sq.linear(a2, wd["w_o"], res=xd)
+    ref = oracle.linear(f64(a2), w64["w_o"]) + x.value
+    check(y, ref, bound(f64(a2), w64["w_o"], ref, C, res=x.value), "output projection + residual")
+    u = sq.linear(y, wd["w1"], bias=wd["b1"], gelu=True)
+    ref = oracle.gelu_tanh(oracle.linear(f64(y), w64["w1"], w64["b1"]))
+    check(u, ref, bound(f64(y), w64["w1"], ref, C, gelu=True), "MLP up + GELU")
+    z = sq.linear(u, wd["w2"], bias=wd["b2"], res=y)
+    ref = oracle.linear(f64(u), w64["w2"], w64["b2"]) + f64(y)
+    check(z, ref, bound(f64(u), w64["w2"], ref, F, res=f64(y)), "MLP down + residual")
+    z_blk, qkv_blk = sq.block_dense(xd, wd, H)
+    assert torch.equal(z_blk, z) and torch.equal(qkv_blk, qkv), "the block is this sequence of calls"
