@@ -835,6 +835,10 @@ def clock_under_load(launch, seconds: float = 1.5):
     tool = shutil.which("amd-smi")
     if tool is None:
         return None
+    # Under rocprofv3 the tool's preloaded library would start with the child process and open
+    # the GPU before amd-smi's launcher replaces itself; no sample is taken in profiled runs.
+    if "rocprof" in os.environ.get("LD_PRELOAD", "") or any(k.startswith("ROCPROF") for k in os.environ):
+        return None
     result = {}
 
     def sample():
