@@ -26,7 +26,8 @@ from typing import Optional
 import torch
 
 _HERE = os.path.dirname(os.path.abspath(__file__))
-LIB_PATH = os.path.join(_HERE, "libsafe.so")
+# SAFE_LIB_PATH selects another build of the same library (e.g. the host-sanitized one)
+LIB_PATH = os.environ.get("SAFE_LIB_PATH") or os.path.join(_HERE, "libsafe.so")
 
 SAFE_OK = 0
 STATUS = {0: "SAFE_OK", -1: "SAFE_ERR_NULL", -2: "SAFE_ERR_SHAPE", -3: "SAFE_ERR_DTYPE", -4: "SAFE_ERR_RANGE",

@@ -2,6 +2,8 @@
 
 Usage: python sparse_query_sdpa_amd/build.py [-v]   (run by path: importing the package
 loads the library, which may be missing or older than the sources)
+       python sparse_query_sdpa_amd/build.py --host-sanitize   (ASan + UBSan on the host code,
+       into _build/hostsan/; load it with SAFE_LIB_PATH and the runtime in LD_PRELOAD)
 """
 from __future__ import annotations
 
@@ -65,5 +67,44 @@ def build(verbose: bool = False, jobs: int = 0) -> str:
     return LIB
 
 
+# Host-sanitized build: AddressSanitizer and UndefinedBehaviorSanitizer on the host code only
+# (argument checks, planners, the C ABI); the device code is the ordinary gfx950 build.  The
+# library links the shared sanitizer runtime, which the loading process must preload.
+SANITIZE_FLAGS = ["-Xarch_host", "-fsanitize=address", "-Xarch_host", "-fsanitize=undefined",
+                  "-Xarch_host", "-fno-omit-frame-pointer", "-g"]
+
+
+def sanitizer_runtime() -> str:
+    """Path of the shared AddressSanitizer runtime of the HIP toolchain's clang."""
+    clang = os.path.join(os.path.dirname(os.path.realpath(hipcc())), "..", "lib", "llvm", "bin", "clang")
+    for cand in (clang, "/opt/rocm/llvm/bin/clang", shutil.which("clang")):
+        if cand and os.path.exists(cand):
+            r = subprocess.run([cand, "-print-file-name=libclang_rt.asan-x86_64.so"], stdout=subprocess.PIPE,
+                               text=True)
+            path = r.stdout.strip()
+            if r.returncode == 0 and os.path.isabs(path) and os.path.exists(path):
+                return path
+    raise RuntimeError("the clang AddressSanitizer runtime was not found")
+
+
+def build_host_sanitized(out_dir: str, verbose: bool = False, jobs: int = 0) -> str:
+    """Compile the library with the host sanitizers into out_dir; return the library's path."""
+    cc = hipcc()
+    os.makedirs(out_dir, exist_ok=True)
+    jobs = jobs or min(8, len(SOURCES))
+    flags = [f for f in HIPCC_FLAGS if f != "-O3"] + ["-O1"] + SANITIZE_FLAGS
+    objs = [os.path.join(out_dir, src.replace(".hip", ".o")) for src in SOURCES]
+    cmds = [[cc, *flags, "-c", os.path.join(CSRC, src), "-o", obj] for src, obj in zip(SOURCES, objs)]
+    with concurrent.futures.ThreadPoolExecutor(max_workers=jobs) as ex:
+        list(ex.map(lambda c: _run(c, verbose), cmds))
+    lib = os.path.join(out_dir, "libsafe_hostsan.so")
+    _run([cc, "--offload-arch=gfx950", "-shared", "-fPIC", *SANITIZE_FLAGS[:4], "-shared-libsan", *objs, "-o", lib],
+         verbose)
+    return lib
+
+
 if __name__ == "__main__":
-    print(build(verbose="-v" in sys.argv))
+    if "--host-sanitize" in sys.argv:
+        print(build_host_sanitized(os.path.join(OBJ, "hostsan"), verbose="-v" in sys.argv))
+    else:
+        print(build(verbose="-v" in sys.argv))
