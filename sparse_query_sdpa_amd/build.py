@@ -63,8 +63,19 @@ def build(verbose: bool = False, jobs: int = 0) -> str:
         list(ex.map(lambda c: _run(c, verbose), cmds))
     tmp = LIB + ".tmp"
     _run([cc, "--offload-arch=gfx950", "-shared", "-fPIC", *objs, "-o", tmp], verbose)
+    _check_loads(tmp)
     os.replace(tmp, LIB)
     return LIB
+
+
+def _check_loads(path: str) -> None:
+    """Resolve every symbol of the linked library now: a kernel whose host-side launch stub
+    was not emitted links fine but leaves an undefined symbol that only loading reveals."""
+    import ctypes
+    try:
+        ctypes.CDLL(os.path.abspath(path), mode=os.RTLD_NOW | os.RTLD_LOCAL)
+    except OSError as e:
+        raise RuntimeError(f"the linked library does not load: {e}") from e
 
 
 # Host-sanitized build: AddressSanitizer and UndefinedBehaviorSanitizer on the host code only

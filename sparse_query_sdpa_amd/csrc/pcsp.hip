@@ -6,12 +6,16 @@
 //   thousand workgroups, each group's per-token sum goes to its own slice of the
 //   workspace, and pcsp_reduce_kernel adds the slices to acc in group order (the
 //   result does not depend on scheduling); without one, one group holds every head
-//   and the sum is added to acc directly.  For each head
-//   the text keys stream through LDS in tiles of 64; S^T = K_txt Q^T runs on
-//   v_mfma_f32_32x32x16_bf16 exactly as in the attention kernel (each lane owns one
-//   image token), and instead of a P V product each lane keeps an online softmax
-//   numerator sum_j w_j p_j and denominator sum_j p_j.  The probabilities are never
-//   stored: only the N-vector acc is kept, as the paper's instrumentation does.
+//   and the sum is added to acc directly.  The workgroup walks its (head, key tile)
+//   steps as one software pipeline: a tile's 64 text keys and weights are copied
+//   straight into LDS (two stages) one step ahead, and the next head's 128 query rows
+//   are copied into an LDS buffer during the last step of the head before (and read
+//   into registers at the head's first step), so each step waits only for copies
+//   issued one step earlier.  S^T = K_txt Q^T
+//   runs on v_mfma_f32_32x32x16_bf16 exactly as in the attention kernel (each lane
+//   owns one image token), and instead of a P V product each lane keeps an online
+//   softmax numerator sum_j w_j p_j and denominator sum_j p_j.  The probabilities are
+//   never stored: only the N-vector acc is kept, as the paper's instrumentation does.
 // SELECT (Eq. 11-12): the separable Gaussian (rows, then columns, one thread per
 //   token, in-grid taps renormalised) runs as two grid-wide kernels; then one
 //   workgroup per sample (1024 threads, the sample's keys held in LDS when they fit)
@@ -29,9 +33,42 @@ namespace safe {
 namespace {
 
 // ============================== ACCUM ========================================
-constexpr int ABM = 128;
-constexpr int ABN = 64;
+constexpr int ABM = 128;   // image tokens per workgroup
+constexpr int ABN = 32;    // text keys per tile (one 32 x 32 score block per wave)
 constexpr int ANT = 256;
+constexpr int AWAVES = ANT / 64;
+constexpr float kAccSumLimit = 65536.f;   // a 32-key block's per-lane sum of probabilities kept below this
+constexpr float kAccMoveMargin = 8.f;     // the reference moves to a max more than 2^8 above it
+
+typedef __attribute__((address_space(3))) void lds_void;
+
+// One direct-to-LDS copy per lane of 16 (4) bytes from src; lds_dst is the wave's LDS base,
+// the lane's bytes land at lds_dst + 16 (4) * lane.
+__device__ __forceinline__ void lds_copy16(const void* src, void* lds_dst) {
+  __builtin_amdgcn_global_load_lds(src, (lds_void*)lds_dst, 16, 0, 0);
+}
+__device__ __forceinline__ void lds_copy4(const void* src, void* lds_dst) {
+  __builtin_amdgcn_global_load_lds(src, (lds_void*)lds_dst, 4, 0, 0);
+}
+
+// LDS layout of a key tile: ABN rows of SLOTS 16-byte chunks (an odd count, so the 16
+// lanes of a fragment read hit distinct banks); the copies fill it in order, one
+// wave-wide 1 KB copy per 64 chunks (lanes past the tile's last chunk idle), and pad
+// chunks fetch chunk 0 of their row.
+template <int D>
+struct AccTile {
+  static constexpr int CH = D / 8;        // 16-byte chunks of a key row
+  static constexpr int KS = D / 16;       // k-steps of the S^T product
+  static constexpr int SLOTS = CH | 1;
+  static constexpr int ROWB = SLOTS * 16;
+  static constexpr int BYTES = ABN * ROWB;
+  static constexpr int NCHUNK = ABN * SLOTS;              // 16-byte chunks of a tile
+  static constexpr int NCOPY = (NCHUNK + 63) / 64;          // wave-wide copies (the last may be partial)
+  static constexpr int PER_WAVE = (NCOPY + AWAVES - 1) / AWAVES;
+  static constexpr int QBYTES = ABM * D * 2;            // the workgroup's query rows, packed
+  static constexpr int QPER_WAVE = ABM * CH / 64 / AWAVES;
+  static_assert(D % 16 == 0 && ABM * CH % (64 * AWAVES) == 0, "whole k-steps and query copies");
+};
 
 struct AccParams {
   const u16* q; int64_t qs0, qs1, qs2;
@@ -46,14 +83,18 @@ struct AccParams {
 };
 
 template <int D>
-__global__ __launch_bounds__(ANT) void pcsp_accum_kernel(AccParams p) {
-  constexpr int KS = D / 16;
-  constexpr int PARTS = D / 8;
-  constexpr int KCH = ABN * PARTS;
-  __shared__ __attribute__((aligned(16))) u16 Ks[ABN][D + 8];
-  __shared__ float Ws[ABN];
+__global__ __launch_bounds__(ANT, D >= 128 ? 3 : 4) void pcsp_accum_kernel(AccParams p) {
+  using T = AccTile<D>;
+  constexpr int KS = T::KS;
+  // two stages as separate objects, so a read of one is not held for a copy into the other
+  __shared__ __attribute__((aligned(1024))) char kst0[T::BYTES];
+  __shared__ __attribute__((aligned(1024))) char kst1[T::BYTES];
+  __shared__ __attribute__((aligned(256))) float wst0[ABN];
+  __shared__ __attribute__((aligned(256))) float wst1[ABN];
+  __shared__ __attribute__((aligned(1024))) char qst[T::QBYTES];
 
-  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int col = lane & 31, half = lane >> 5;
   const int b = blockIdx.x / p.tiles_per_b;
   const int tile = blockIdx.x % p.tiles_per_b;
@@ -64,72 +105,187 @@ __global__ __launch_bounds__(ANT) void pcsp_accum_kernel(AccParams p) {
   L = L < 0 ? 0 : (L > p.M ? p.M : L);
   const int ntiles = (L + ABN - 1) / ABN;
   const float sl2 = p.scale_log2;
-
   const int g = blockIdx.y;
-  const int h_end = min(p.H, (g + 1) * p.heads_per_group);
-  float total = 0.f;
-  for (int h = g * p.heads_per_group; h < h_end; ++h) {
-    if (p.head_mask != 0 && !((p.head_mask >> h) & 1ull)) continue;
-    bf16x8 qf[KS];
-    const u16* qp = p.q + (int64_t)b * p.qs0 + (int64_t)(ok ? i : 0) * p.qs1 + (int64_t)h * p.qs2 + half * 8;
+  const int h_first = g * p.heads_per_group;
+  const int h_end = min(p.H, h_first + p.heads_per_group);
+  auto next_head = [&](int h) {   // the next head of the set in this group, or h_end
+    for (++h; h < h_end; ++h)
+      if (p.head_mask == 0 || ((p.head_mask >> h) & 1ull)) break;
+    return h;
+  };
+
+  // Copy plans, fixed per lane: query copy m moves chunk `chunk` of row `row` of the
+  // workgroup's token tile (a token past N copies the tile's first token: finite scores,
+  // never written out); key copy m moves chunk `chunk` (pad chunks: chunk 0) of key row
+  // `row` of a tile.  The byte offsets stay in registers for the whole loop.
+  const char* qbase = reinterpret_cast<const char*>(p.q + (int64_t)b * p.qs0 + (int64_t)tile * ABM * p.qs1);
+  const char* kbase = reinterpret_cast<const char*>(p.kt + (int64_t)b * p.ks0);
+  const int64_t krow_b = p.ks1 * 2;
+  const float* wrow = p.w + (int64_t)b * p.M;
+  int64_t qoff[T::QPER_WAVE], koff[T::PER_WAVE];
 #pragma unroll
-    for (int s = 0; s < KS; ++s) {
-      u32x4 v = {0u, 0u, 0u, 0u};
-      if (ok) v = ld16(qp + s * 16);
-      qf[s] = as_bf16x8(v);
+  for (int m = 0; m < T::QPER_WAVE; ++m) {
+    const int sigma = (wave + AWAVES * m) * 64 + lane;
+    const int row = sigma / T::CH;
+    const int chunk = sigma - row * T::CH;
+    qoff[m] = (int64_t)(tile * ABM + row < p.N ? row : 0) * p.qs1 * 2 + chunk * 16;
+  }
+#pragma unroll
+  for (int m = 0; m < T::PER_WAVE; ++m) {
+    const int sigma = (wave + AWAVES * m) * 64 + lane;
+    const int row = sigma / T::SLOTS;
+    int chunk = sigma - row * T::SLOTS;
+    if (chunk >= T::CH) chunk = 0;
+    koff[m] = (int64_t)row * krow_b + chunk * 16;
+  }
+  auto issue_q = [&](int h) {   // head h's query rows -> qst (row r = token tile * 128 + r)
+    const char* qb = qbase + (int64_t)h * p.qs2 * 2;
+#pragma unroll
+    for (int m = 0; m < T::QPER_WAVE; ++m) {
+      lds_copy16(qb + qoff[m], qst + (wave + AWAVES * m) * 1024);
     }
-    float m = -INFINITY, num = 0.f, den = 0.f;
-    const u16* kb = p.kt + (int64_t)b * p.ks0 + (int64_t)h * p.ks2;
-    for (int it = 0; it < ntiles; ++it) {
-      const int j0 = it * ABN;
-      __syncthreads();  // previous tile consumed
-      for (int c = tid; c < KCH; c += ANT) {
-        const int key = c / PARTS, part = c % PARTS;
-        u32x4 v = {0u, 0u, 0u, 0u};
-        if (j0 + key < L) v = ld16(kb + (int64_t)(j0 + key) * p.ks1 + part * 8);
-        st16(&Ks[key][part * 8], v);
-      }
-      if (tid < ABN) Ws[tid] = (j0 + tid < L) ? p.w[(int64_t)b * p.M + j0 + tid] : 0.f;
-      __syncthreads();
-      f32x16 sacc[2];
+  };
+  // keys and weights of step (h, j0); on a partial tile, key rows past L fetch the tile's
+  // row 0 and weights past L weight 0 of the tile (their scores are masked); the weights
+  // are dwords (w rows need not be aligned), copied by the last wave
+  auto issue = [&](int h, int j0, char* kst, float* wst) {
+    const char* kb = kbase + (int64_t)h * p.ks2 * 2 + (int64_t)j0 * krow_b;
+    const int nvalid = L - j0;
+    if (nvalid >= ABN) {
 #pragma unroll
-      for (int blk = 0; blk < 2; ++blk) {
-        f32x16 a = f32x16{};
+      for (int m = 0; m < T::PER_WAVE; ++m) {
+        const int c = wave + AWAVES * m;
+        if (c < T::NCOPY && (T::NCHUNK % 64 == 0 || c * 64 + lane < T::NCHUNK))   // c: wave-uniform
+          lds_copy16(kb + koff[m], kst + c * 1024);
+      }
+    } else {
+      int ln = lane;
+      asm volatile("" : "+v"(ln));
+#pragma unroll
+      for (int m = 0; m < T::PER_WAVE; ++m) {
+        const int c = wave + AWAVES * m;
+        if (c < T::NCOPY && (T::NCHUNK % 64 == 0 || c * 64 + ln < T::NCHUNK)) {
+          const int sigma = c * 64 + ln;
+          const int row = sigma / T::SLOTS;
+          int chunk = sigma - row * T::SLOTS;
+          if (chunk >= T::CH) chunk = 0;
+          lds_copy16(kb + (int64_t)(row < nvalid ? row : 0) * krow_b + chunk * 16, kst + c * 1024);
+        }
+      }
+    }
+    if (wave == AWAVES - 1 && lane < ABN) {
+      const int r = lane < nvalid ? lane : 0;
+      lds_copy4(wrow + j0 + r, wst);
+    }
+  };
+
+  float total = 0.f;
+  int h = next_head(h_first - 1);
+  if (ntiles > 0 && h < h_end) {
+    bf16x8 qc[KS];   // this lane's query row of the current head
+    issue_q(h);
+    issue(h, 0, kst0, wst0);
+    int hn = next_head(h), t = 0;
+    // online softmax of the current head against a lazy reference m (log2 domain; -inf:
+    // none yet): probabilities are taken as exp2(s - m) and the reference moves only when
+    // a 32-key block's sum leaves [0, kAccSumLimit] (the first block of every head, or scores
+    // more than kAccMoveMargin above m); num and den are rescaled with it
+    float m = -INFINITY, num = 0.f, den = 0.f;
+    const int k_lane = col * T::ROWB + half * 16;
+    const char* q_lane = qst + (wave * 32 + col) * (D * 2) + half * 16;
+
+    // One step: wait for what the step before issued (this step's keys and weights,
+    // and at a head's first step its query rows), start the next step's copies into the
+    // other stage (and, at a head's last step, the next head's query rows), then scores,
+    // online softmax and the weighted sums.
+    auto step = [&](const char* kcur, const float* wcur, char* knext, float* wnext) -> bool {
+      __builtin_amdgcn_s_waitcnt(0x0F70);   // vmcnt(0): this wave's copies landed
+      __syncthreads();                      // ... everyone's, and the other stage is free
+      const int j0 = t * ABN;
+      const bool last = t + 1 == ntiles;
+      if (t == 0) {
+#pragma unroll
+        for (int s = 0; s < KS; ++s) qc[s] = as_bf16x8(ld16(q_lane + s * 32));
+        // a one-tile head refills qst in this same step: every wave has read it first
+        if (last && hn < h_end) __syncthreads();
+      }
+      const bool more = !last || hn < h_end;
+      if (!last) {
+        issue(h, j0 + ABN, knext, wnext);
+      } else if (hn < h_end) {
+        issue(hn, 0, knext, wnext);
+        issue_q(hn);
+      }
+
+      // the tile's 32-key blocks in turn; a block wholly past L is skipped (the first
+      // always holds key j0 < L)
+#pragma unroll
+      for (int blk = 0; blk < ABN / 32; ++blk) {
+        const int kh = j0 + blk * 32;   // first key of the block
+        if (blk > 0 && kh >= L) break;
+        f32x16 sc = f32x16{};
 #pragma unroll
         for (int s = 0; s < KS; ++s) {
-          const bf16x8 kf = as_bf16x8(ld16(&Ks[blk * 32 + col][s * 16 + half * 8]));
-          a = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kf, qf[s], a, 0, 0, 0);
+          const bf16x8 kf = as_bf16x8(ld16(kcur + k_lane + blk * 32 * T::ROWB + s * 32));
+          sc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kf, qc[s], sc, 0, 0, 0);
         }
-        sacc[blk] = a;
+        if (kh + 32 > L) {   // keys past L get -inf
+          const int lim = L - kh - 4 * half;   // valid: 8 (r / 4) + r % 4 < lim
+#pragma unroll
+          for (int r = 0; r < 16; ++r)
+            if (8 * (r >> 2) + (r & 3) >= lim) sc[r] = -INFINITY;
+        }
+        float ts, tn;   // this lane's share of the block's sum of p and of w p
+        auto probs = [&]() {
+          ts = 0.f;
+          tn = 0.f;
+#pragma unroll
+          for (int r4 = 0; r4 < 4; ++r4) {
+            const f32x4 wv = *reinterpret_cast<const f32x4*>(wcur + blk * 32 + 8 * r4 + 4 * half);
+#pragma unroll
+            for (int e = 0; e < 4; ++e) {
+              const float pr = __builtin_amdgcn_exp2f(__builtin_fmaf(sc[4 * r4 + e], sl2, -m));
+              ts += pr;
+              tn = __builtin_fmaf(pr, wv[e], tn);
+            }
+          }
+        };
+        probs();
+        if (__any(!(ts <= kAccSumLimit))) {   // wave-uniform, rare after a head's first block
+          // the token's max over both lanes holding it: finite, since key kh < L is valid
+          float mt = sc[0];
+#pragma unroll
+          for (int r = 1; r < 16; ++r) mt = fmaxf(mt, sc[r]);
+          mt = fmaxf(mt, __shfl_xor(mt, 32)) * sl2;
+          const float m_new = mt > m + kAccMoveMargin ? mt : m;
+          const float alpha = __builtin_amdgcn_exp2f(m - m_new);   // 0 on the first move
+          num *= alpha;
+          den *= alpha;
+          m = m_new;
+          probs();
+        }
+        den += ts;
+        num += tn;
       }
-      float mt = -INFINITY;
-#pragma unroll
-      for (int blk = 0; blk < 2; ++blk)
-#pragma unroll
-        for (int r = 0; r < 16; ++r) {
-          const int kk = blk * 32 + 8 * (r >> 2) + 4 * half + (r & 3);
-          if (j0 + kk >= L) sacc[blk][r] = -INFINITY;
-          mt = fmaxf(mt, sacc[blk][r]);
-        }
-      mt = fmaxf(mt, __shfl_xor(mt, 32)) * sl2;
-      const float m_new = fmaxf(m, mt);
-      const float alpha = __builtin_amdgcn_exp2f(m - m_new);
-      num *= alpha;
-      den *= alpha;
-      m = m_new;
-#pragma unroll
-      for (int blk = 0; blk < 2; ++blk)
-#pragma unroll
-        for (int r = 0; r < 16; ++r) {
-          const int kk = blk * 32 + 8 * (r >> 2) + 4 * half + (r & 3);
-          const float pr = __builtin_amdgcn_exp2f(__builtin_fmaf(sacc[blk][r], sl2, -m));
-          den += pr;
-          num = __builtin_fmaf(pr, Ws[kk], num);
-        }
+      if (last) {   // the head's last tile: its share of the sum over heads
+        const float num_t = num + __shfl_xor(num, 32);
+        const float den_t = den + __shfl_xor(den, 32);
+        if (den_t > 0.f) total += num_t / den_t;
+        m = -INFINITY;
+        num = 0.f;
+        den = 0.f;
+        h = hn;
+        hn = next_head(hn);
+        t = 0;
+      } else {
+        ++t;
+      }
+      return more;
+    };
+    for (;;) {
+      if (!step(kst0, wst0, kst1, wst1)) break;
+      if (!step(kst1, wst1, kst0, wst0)) break;
     }
-    const float num_t = num + __shfl_xor(num, 32);
-    const float den_t = den + __shfl_xor(den, 32);
-    if (den_t > 0.f) total += num_t / den_t;
   }
   if (p.part != nullptr) {
     if (ok && half == 0) p.part[((int64_t)g * p.B + b) * p.N + i] = total;

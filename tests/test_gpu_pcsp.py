@@ -74,6 +74,45 @@ def test_accumulate_ragged_lengths():
     assert torch.all(acc[2] == 0)
 
 
+@pytest.mark.parametrize("d", [32, 64, 96, 128])
+def test_accumulate_head_dims_and_text_lengths(d):
+    """Every head dim, text lengths on and around the 64-key tile edges (0, 1, 63, 64, 65,
+    the full M = 300 with a partial last tile), N not a multiple of the 128-token tile, a
+    head subset, and with and without the head-group split: the oracle on all tokens."""
+    B, N, M, H = 6, 333, 300, 5
+    q, k, _ = W.attention_inputs(B, N, M, H, d, seed=40 + d)
+    kv = np.array([0, 1, 63, 64, 65, 300], np.int32)
+    wts = np.random.default_rng(d).random((B, M)).astype(np.float32)
+    ref = oracle.pcsp_accumulate(q.value, k.value, kv, wts)
+    for ws in ("auto", None):
+        acc = torch.zeros((B, N), dtype=torch.float32, device=dev())
+        kw = {} if ws == "auto" else {"workspace": None}
+        sq.pcsp_accumulate(to_dev_bf16(q), to_dev_bf16(k), to_dev(wts), acc, kv_len=to_dev(kv), **kw)
+        np.testing.assert_allclose(acc.cpu().numpy(), ref, rtol=ACC_RTOL, atol=1e-7)
+        assert torch.all(acc[0] == 0)
+    heads = [1, 4]
+    acc = torch.zeros((B, N), dtype=torch.float32, device=dev())
+    sq.pcsp_accumulate(to_dev_bf16(q), to_dev_bf16(k), to_dev(wts), acc, kv_len=to_dev(kv), head_mask=(1 << 1) | (1 << 4))
+    ref_h = oracle.pcsp_accumulate(q.value, k.value, kv, wts, heads=heads)
+    np.testing.assert_allclose(acc.cpu().numpy(), ref_h, rtol=ACC_RTOL, atol=1e-7)
+
+
+def test_accumulate_strided_views_and_long_text():
+    """Query and key views inside wider buffers (token and head strides not the packed
+    ones) and the largest text length (M = 1024, every key valid)."""
+    B, N, M, H, d = 2, 260, 1024, 3, 64
+    q, k, _ = W.attention_inputs(B, N, M, H, d, seed=77)
+    wts = np.random.default_rng(5).random((B, M)).astype(np.float32)
+    qd = torch.zeros((B, N, H + 1, d + 16), dtype=torch.bfloat16, device=dev())
+    kd = torch.zeros((B, M, H + 2, d + 8), dtype=torch.bfloat16, device=dev())
+    qd[:, :, :H, :d] = to_dev_bf16(q)
+    kd[:, :, 1:H + 1, 8:] = to_dev_bf16(k)
+    acc = torch.zeros((B, N), dtype=torch.float32, device=dev())
+    sq.pcsp_accumulate(qd[:, :, :H, :d], kd[:, :, 1:H + 1, 8:], to_dev(wts), acc)
+    ref = oracle.pcsp_accumulate(q.value, k.value, np.full(B, M, np.int32), wts)
+    np.testing.assert_allclose(acc.cpu().numpy(), ref, rtol=ACC_RTOL, atol=1e-7)
+
+
 def _select(s: np.ndarray, k: int, gh: int, gw: int, sigma: float = 0.0):
     acc = to_dev(s.astype(np.float32))
     return sq.pcsp_select(acc, gh, gw, sigma, k, score_out=True)
