@@ -330,6 +330,8 @@ def main() -> int:
         "stage_ms_median": {kk: round(float(np.median(v)), 4) for kk, v in per_step.items()},
         "stage_ms_min": {kk: round(float(np.min(v)), 4) for kk, v in per_step.items()},
         "cross_tflops": round(tf(fl_cross, stage_ms["srsu_cross"]), 2),
+        "stage_rooflines": stage_rooflines(stage_ms, B, N, H, d, M, k, mask_bytes, kv_bytes, fl_srsu, fl_cross,
+                                           fl_dense),
         "classify_gbs": round(mask_bytes / (stage_ms["classify"] * 1e-3) / 1e9, 1),
         "classify_pct_hbm": round(100 * mask_bytes / (stage_ms["classify"] * 1e-3) / 1e9 / PEAK_HBM_GBS, 2),
         "kv_assemble_gbs": round(kv_bytes / (stage_ms["kv_assemble"] * 1e-3) / 1e9, 1),
@@ -823,6 +825,35 @@ def other_configs(sq, W, tf) -> dict:
         del q, kx, vx, o_s, o_d
         torch.cuda.empty_cache()
     return res
+
+
+def stage_rooflines(stage_ms, B, N, H, d, M, k, mask_bytes, kv_bytes, fl_srsu, fl_cross, fl_dense) -> dict:
+    """Each stage of the step against the roofline that bounds it, from its event time and its
+    algorithmic bytes (HBM-bound stages: every input read once, every output written once) or
+    FLOPs (MFMA-bound stages).  pcsp_select moves under 1 MB and is bound by its launches and
+    the per-sample radix passes, so only its time is given."""
+    e = 2   # bf16 bytes
+    hbm = {
+        "classify": (mask_bytes, "[B,1,N,N] bf16 mask read once"),
+        "pcsp_accum": (B * N * H * d * e + B * M * H * d * e + B * M * 4 + 2 * B * N * 4,
+                       "image-query rows of every head read once, text keys and weights, acc read and written"),
+        "kv_assemble": (kv_bytes, "cache and fresh K/V rows read, global K/V written"),
+        "srsu_cross": (2 * B * k * H * d * e + 2 * B * M * H * d * e,
+                       "gathered query rows read and output rows written; text K/V"),
+    }
+    mfma = {"srsu_self": fl_srsu, "dense": fl_dense}
+    out = {}
+    for st, (nbytes, what) in hbm.items():
+        gbs = nbytes / (stage_ms[st] * 1e-3) / 1e9
+        out[st] = {"bound": "hbm", "bytes": int(nbytes), "what": what, "achieved": round(gbs, 1), "unit": "GB/s",
+                   "peak": PEAK_HBM_GBS, "frac": round(gbs / PEAK_HBM_GBS, 4), "ms": round(stage_ms[st], 4)}
+    for st, fl in mfma.items():
+        t = fl / (stage_ms[st] * 1e-3) / 1e12
+        out[st] = {"bound": "mfma", "flops": fl, "achieved": round(t, 2), "unit": "TFLOP/s",
+                   "peak": PEAK_BF16_TFLOPS, "frac": round(t / PEAK_BF16_TFLOPS, 4), "ms": round(stage_ms[st], 4)}
+    out["srsu_cross"]["mfma_tflops"] = round(fl_cross / (stage_ms["srsu_cross"] * 1e-3) / 1e12, 2)
+    out["pcsp_select"] = {"bound": "latency", "ms": round(stage_ms["pcsp_select"], 4)}
+    return out
 
 
 def clock_under_load(launch, seconds: float = 1.5):

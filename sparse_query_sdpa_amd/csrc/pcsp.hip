@@ -322,6 +322,7 @@ AccPlan plan_accum(const safe_pcsp_args* a) {
 
 // ============================== SELECT =======================================
 constexpr int SNT = 1024;
+constexpr int SUNR = 8;    // field elements per thread loaded together
 constexpr int MAX_TAPS = 2 * 96 + 1;  // sigma <= 32 -> radius <= 96
 
 struct SelParams {
@@ -397,12 +398,12 @@ __global__ __launch_bounds__(256) void pcsp_smooth_kernel(const float* in, float
 }
 
 // ---- Norm and Eq. 12: one workgroup per sample --------------------------------
-// KEYS_IN_LDS: the N order keys are loaded into LDS once (N <= kKeyCap) and every
-// radix pass and the compaction read them there; otherwise they are recomputed from
-// the field in global memory.  Histograms aggregate equal bins within a wave first
+// KEYS_IN_LDS: the N order keys are loaded into LDS once (N <= kKeyCap: grids up to
+// 192 x 192, 144 KB of the workgroup's LDS) and every radix pass and the compaction read
+// them there; otherwise they are recomputed from the field in global memory.  Histograms aggregate equal bins within a wave first
 // (the leading passes see few distinct bins), and the bin holding the k-th key is
 // found by a suffix scan over the 256 counts on the first wave.
-constexpr int kKeyCap = 32768;
+constexpr int kKeyCap = 36864;
 
 __device__ __forceinline__ void hist_add(int* hist, u32 bin, bool act) {
   const int lane = threadIdx.x & 63;
@@ -439,16 +440,29 @@ __global__ __launch_bounds__(SNT) void pcsp_select_kernel(SelParams p) {
     else return order_key(src[pos]);
   };
 
+  // the field is read SUNR elements per thread at a time, all loads issued before the
+  // first is used (a load per iteration would pay the full memory latency N / SNT times)
   float lo = INFINITY, hi = -INFINITY;
   u32 kmin = 0xFFFFFFFFu, kmax = 0u;
-  for (int pos = t; pos < N; pos += SNT) {
-    const float v = src[pos];
-    const u32 key = order_key(v);
-    if constexpr (KEYS_IN_LDS) kbuf[pos] = key;
-    lo = fminf(lo, v);
-    hi = fmaxf(hi, v);
-    kmin = min(kmin, key);
-    kmax = max(kmax, key);
+  for (int base = t; base < N; base += SNT * SUNR) {
+    float v[SUNR];
+#pragma unroll
+    for (int u = 0; u < SUNR; ++u) {
+      const int pos = base + u * SNT;
+      v[u] = pos < N ? src[pos] : 0.f;
+    }
+#pragma unroll
+    for (int u = 0; u < SUNR; ++u) {
+      const int pos = base + u * SNT;
+      if (pos < N) {
+        const u32 key = order_key(v[u]);
+        if constexpr (KEYS_IN_LDS) kbuf[pos] = key;
+        lo = fminf(lo, v[u]);
+        hi = fmaxf(hi, v[u]);
+        kmin = min(kmin, key);
+        kmax = max(kmax, key);
+      }
+    }
   }
 #pragma unroll
   for (int off = 32; off > 0; off >>= 1) {
@@ -469,7 +483,19 @@ __global__ __launch_bounds__(SNT) void pcsp_select_kernel(SelParams p) {
     for (int w = 1; w < SNT / 64; ++w) { lo = fminf(lo, red_min[w]); hi = fmaxf(hi, red_max[w]); }
     const float span = hi - lo;
     float* so = p.score_out + (int64_t)b * N;
-    for (int pos = t; pos < N; pos += SNT) so[pos] = span > 0.f ? (src[pos] - lo) / span : 0.f;
+    for (int base = t; base < N; base += SNT * SUNR) {
+      float v[SUNR];
+#pragma unroll
+      for (int u = 0; u < SUNR; ++u) {
+        const int pos = base + u * SNT;
+        v[u] = pos < N ? src[pos] : 0.f;
+      }
+#pragma unroll
+      for (int u = 0; u < SUNR; ++u) {
+        const int pos = base + u * SNT;
+        if (pos < N) so[pos] = span > 0.f ? (v[u] - lo) / span : 0.f;
+      }
+    }
   }
 
   // ---- Eq. 12: exact top-k ------------------------------------------------------

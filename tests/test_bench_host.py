@@ -87,3 +87,22 @@ def test_recorded_traffic_ignores_comment_edits(tmp_path, monkeypatch):
     assert bench.attn_source_hash() == h0
     src.write_text("int f() {\n  return 2;\n}\n")
     assert bench.attn_source_hash() != h0
+
+
+def test_stage_rooflines_bytes_and_fractions():
+    """Per-stage roofline entries: algorithmic bytes of the HBM-bound stages from the shapes,
+    achieved rates from the stage times, fractions of the MI355X peaks."""
+    B, N, H, d, M, k = 2, 1000, 4, 64, 100, 250
+    mask_bytes, kv_bytes = B * N * N * 2, 4 * B * N * H * d * 2
+    fl_s, fl_c, fl_d = 4.0 * B * H * k * N * d, 4.0 * H * d * k * 150, 4.0 * B * H * N * N * d
+    ms = {"classify": 0.5, "pcsp_accum": 0.1, "pcsp_select": 0.05, "kv_assemble": 0.2, "srsu_self": 1.0,
+          "srsu_cross": 0.02, "dense": 4.0}
+    r = bench.stage_rooflines(ms, B, N, H, d, M, k, mask_bytes, kv_bytes, fl_s, fl_c, fl_d)
+    assert r["classify"]["bytes"] == mask_bytes and r["classify"]["bound"] == "hbm"
+    assert r["pcsp_accum"]["bytes"] == B * N * H * d * 2 + B * M * H * d * 2 + B * M * 4 + 2 * B * N * 4
+    assert r["srsu_cross"]["bytes"] == 2 * B * k * H * d * 2 + 2 * B * M * H * d * 2
+    gbs = kv_bytes / 0.2e-3 / 1e9
+    assert abs(r["kv_assemble"]["achieved"] - gbs) < 0.1 and abs(r["kv_assemble"]["frac"] - gbs / 8000.0) < 1e-4
+    t = fl_d / 4.0e-3 / 1e12
+    assert r["dense"]["bound"] == "mfma" and abs(r["dense"]["frac"] - t / 2500.0) < 1e-4
+    assert r["pcsp_select"] == {"bound": "latency", "ms": 0.05}

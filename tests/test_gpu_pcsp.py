@@ -127,9 +127,11 @@ def test_topk_golden_cases():
 
 
 @pytest.mark.parametrize("levels", [None, 8, 1])
-@pytest.mark.parametrize("N,grid", [(256, (16, 16)), (4096, (64, 64)), (36864, (192, 192))])
+@pytest.mark.parametrize("N,grid", [(256, (16, 16)), (4096, (64, 64)), (36864, (192, 192)), (40000, (200, 200))])
 def test_topk_bit_exact_on_identical_scores(N, grid, levels):
-    """Same fp32 score array on both sides (sigma = 0): identical index sets, lower index wins ties."""
+    """Same fp32 score array on both sides (sigma = 0): identical index sets, lower index wins ties.
+    N = 36864 is the largest field held in LDS; N = 40000 takes the path that reads the field
+    from global memory in every pass."""
     rng = np.random.default_rng(N + (levels or 0))
     s = W.score_field(rng, 2, N, levels=levels)
     s[0, :5] = [-0.0, 0.0, np.nan, -np.inf, np.inf]
