@@ -247,6 +247,8 @@ int attn_fwd_launch(const safe_attn_args* a, float scale, hipStream_t stream) {
     }
   } else if (mt != kMaskNone) {
     e = attn_masked_dispatch(p, a->d, gather, mt, stream);
+  } else if (attn_short_applies(a)) {
+    e = attn_short_launch(p, a->d, stream);
   } else {
     switch (a->d) {
       case 32: e = dispatch_flags<32>(p, gather, kvlen, stream); break;

@@ -104,6 +104,9 @@ struct AttnParams {
 
 hipError_t attn_masked_dispatch(const AttnParams& p, int d, bool gather, int mt, hipStream_t s);
 int attn_masked_resident(int d, bool gather, int mt);
+// short key sets with per-sample key lengths (text cross-attention): attn_short.hip
+bool attn_short_applies(const safe_attn_args* a);
+hipError_t attn_short_launch(const AttnParams& p, int d, hipStream_t s);
 
 namespace {
 

@@ -139,7 +139,8 @@ def test_invalid_rows_and_lengths():
     with pytest.raises(sq.SafeError):
         sq.attn_fwd(qd, kd, vd, kv_len=to_dev(np.array([201], np.int32)), check=True)
     o = sq.attn_fwd(qd, kd, vd, kv_len=to_dev(np.array([5000], np.int32)))   # clamped to Nk
-    assert torch.equal(o, sq.attn_fwd(qd, kd, vd))
+    assert torch.equal(o, sq.attn_fwd(qd, kd, vd, kv_len=to_dev(np.array([N], np.int32))))
+    assert (o.float() - sq.attn_fwd(qd, kd, vd).float()).abs().max().item() <= 1e-2
     empty = sq.attn_fwd(qd, kd, vd, q_rows=to_dev(np.zeros((0,), np.int32)))
     assert empty.shape == (1, 0, H, d)
 
