@@ -14,8 +14,9 @@
 //   * S^T = K Q^T and O^T += V^T P^T run on v_mfma_f32_32x32x16_bf16 in the layouts of
 //     attn_fwd_kernel (each lane owns one query row; V^T read with the LDS transpose
 //     load; P^T packed to bf16 in registers), one 32-key block per step;
-//   * the softmax keeps a lazy reference as there: probabilities against the current
-//     reference, the max taken only when a block's per-lane sum leaves [0, 2^16];
+//   * the softmax keeps a lazy reference as there: the max of a head's first block, then
+//     probabilities against it, the max taken again only when a block's per-lane sum
+//     leaves [0, 2^16];
 //   * at a head's last step the rows are normalised and stored (and the LSE).
 // Rows outside the selection (index past Nq or negative) read a zero query row, as in
 // the general kernel; blocks wholly past the key length are skipped.
@@ -264,15 +265,21 @@ __global__ __launch_bounds__(SWAVES * 64, D >= 128 ? 2 : 3) void attn_short_kern
         pb[tt] = as_bf16x8(packed);
       }
     };
-    probs();
-    if (__any(!(ts <= kShortSumLimit))) {   // wave-uniform: a head's first block, or a rise
-      // the row's max over both lanes holding it: finite, since key j0 < nkeys is valid
+    // the row's max over both lanes holding it: finite, since key j0 < nkeys is valid
+    auto block_max = [&]() {
       float mt = sc[0];
 #pragma unroll
       for (int r = 1; r < 16; ++r) mt = fmaxf(mt, sc[r]);
-      mt = fmaxf(mt, __shfl_xor(mt, 32)) * sl2;
+      return fmaxf(mt, __shfl_xor(mt, 32)) * sl2;
+    };
+    // a head's first block (wave-uniform; O and l are 0): the reference is its max, so the
+    // trial pass against the empty reference is skipped
+    if (t == 0) m_ref = block_max();
+    probs();
+    if (__any(!(ts <= kShortSumLimit))) {   // wave-uniform and rare: scores rose past the reference
+      const float mt = block_max();
       const float m_new = mt > m_ref + kShortMoveMargin ? mt : m_ref;
-      const float alpha = __builtin_amdgcn_exp2f(m_ref - m_new);   // 0 on the first move
+      const float alpha = __builtin_amdgcn_exp2f(m_ref - m_new);
       l_run *= alpha;
 #pragma unroll
       for (int db = 0; db < DB; ++db) oacc[db] *= alpha;

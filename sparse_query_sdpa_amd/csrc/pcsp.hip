@@ -186,10 +186,10 @@ __global__ __launch_bounds__(ANT, D >= 128 ? 3 : 4) void pcsp_accum_kernel(AccPa
     issue_q(h);
     issue(h, 0, kst0, wst0);
     int hn = next_head(h), t = 0;
-    // online softmax of the current head against a lazy reference m (log2 domain; -inf:
-    // none yet): probabilities are taken as exp2(s - m) and the reference moves only when
-    // a 32-key block's sum leaves [0, kAccSumLimit] (the first block of every head, or scores
-    // more than kAccMoveMargin above m); num and den are rescaled with it
+    // online softmax of the current head against a lazy reference m (log2 domain): the
+    // max of the head's first block, then probabilities are taken as exp2(s - m) and the
+    // reference moves only when a 32-key block's sum leaves [0, kAccSumLimit] (scores more
+    // than kAccMoveMargin above m); num and den are rescaled with it
     float m = -INFINITY, num = 0.f, den = 0.f;
     const int k_lane = col * T::ROWB + half * 16;
     const char* q_lane = qst + (wave * 32 + col) * (D * 2) + half * 16;
@@ -250,15 +250,21 @@ __global__ __launch_bounds__(ANT, D >= 128 ? 3 : 4) void pcsp_accum_kernel(AccPa
             }
           }
         };
-        probs();
-        if (__any(!(ts <= kAccSumLimit))) {   // wave-uniform, rare after a head's first block
-          // the token's max over both lanes holding it: finite, since key kh < L is valid
+        // the token's max over both lanes holding it: finite, since key kh < L is valid
+        auto block_max = [&]() {
           float mt = sc[0];
 #pragma unroll
           for (int r = 1; r < 16; ++r) mt = fmaxf(mt, sc[r]);
-          mt = fmaxf(mt, __shfl_xor(mt, 32)) * sl2;
+          return fmaxf(mt, __shfl_xor(mt, 32)) * sl2;
+        };
+        // a head's first block (wave-uniform; num and den are 0): the reference is its max,
+        // so the trial pass against the empty reference is skipped
+        if (t == 0 && blk == 0) m = block_max();
+        probs();
+        if (__any(!(ts <= kAccSumLimit))) {   // wave-uniform and rare: scores rose past the reference
+          const float mt = block_max();
           const float m_new = mt > m + kAccMoveMargin ? mt : m;
-          const float alpha = __builtin_amdgcn_exp2f(m - m_new);   // 0 on the first move
+          const float alpha = __builtin_amdgcn_exp2f(m - m_new);
           num *= alpha;
           den *= alpha;
           m = m_new;
