@@ -780,16 +780,17 @@ def block_dense(x: torch.Tensor, w: dict, H: int, stream=None):
 def block_srsu(x: torch.Tensor, idx: torch.Tensor, z: torch.Tensor, qkv_cache: torch.Tensor, w: dict, H: int,
                stream=None):
     """The row-selective block (Eq. 15-16) for ascending token lists idx [B, k]: the rows of S
-    are projected from the current state x, their keys and values are written over the cached
-    ones in qkv_cache (in place: global K/V in token order, Eq. 16), their attention, residual
-    and MLP outputs are computed, and their outputs are written over the cached outputs in z
-    (in place: the context rows of z stay the cached ones, Eq. 15).  Returns z."""
+    are projected from the current state x and their query, key and value rows are written
+    straight over the cached ones in qkv_cache at their tokens (the projection's row scatter:
+    the cache then holds the global K/V of Eq. 16 in token order, with no assembly pass),
+    their attention (queries gathered from the same buffer), residual and MLP outputs are
+    computed, and their outputs are written over the cached outputs in z (in place: the
+    context rows of z stay the cached ones, Eq. 15).  Returns z."""
     B, N, C = x.shape
     k = idx.shape[-1]
-    qkv_s = linear(x, w["w_qkv"], a_rows=idx, stream=stream)
-    kc, vc = _heads(qkv_cache, 1, C, H), _heads(qkv_cache, 2, C, H)
-    kv_assemble(_heads(qkv_s, 1, C, H), _heads(qkv_s, 2, C, H), idx, kc, vc, in_place=True, stream=stream)
-    a_s = attn_fwd(_heads(qkv_s, 0, C, H), kc, vc, stream=stream)
+    linear(x, w["w_qkv"], a_rows=idx, out=qkv_cache, out_rows=idx, stream=stream)
+    a_s = attn_fwd(_heads(qkv_cache, 0, C, H), _heads(qkv_cache, 1, C, H), _heads(qkv_cache, 2, C, H),
+                   q_rows=idx, stream=stream)
     y_s = linear(a_s.view(B, k, C), w["w_o"], res=x, res_rows=idx, stream=stream)
     u_s = linear(y_s, w["w1"], bias=w["b1"], gelu=True, stream=stream)
     linear(u_s, w["w2"], bias=w["b2"], res=y_s, out=z, out_rows=idx, stream=stream)
