@@ -381,7 +381,8 @@ def main() -> int:
         ip_bytes = 4.0 * B * k * H * d * 2
         out["kv_assemble_in_place"] = {"ms": round(ms_ip, 4), "gbs": round(ip_bytes / (ms_ip * 1e-3) / 1e9, 1),
                                        "pct_hbm": round(100 * ip_bytes / (ms_ip * 1e-3) / 1e9 / PEAK_HBM_GBS, 2),
-                                       "bytes": ip_bytes}
+                                       "bytes": ip_bytes,
+                                       "dense_srsu_step_ratio": round(stage_ms["dense"] / (stage_ms["srsu_self"] + ms_ip), 3)}
         del kc2, vc2
         out["fused_kv"] = fused_kv_lines(sq, q, kx, vx, k_fresh, v_fresh, idx, o_srsu, stage_ms, fl_srsu, tf)
         out["sw_cfg"] = sw_cfg_lines(sq, acc, wl, args.sigma, k)
