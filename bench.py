@@ -562,7 +562,32 @@ def c2_steps(sq, W, tf, sigma: float) -> dict:
                              "kv_assemble_bitwise": asm_bitwise, "srsu_self_err": e_s, "srsu_cross_err": e_c})
     res["ideal_dense_over_srsu"] = round(N / k, 3)
     res["parity_ok"] = bool(ok)
+    res["graph"] = graph_step_lines(sq, lambda: (sq.kv_assemble(kf, vf, S, k0, v0, k_out=k_glob, v_out=v_glob),
+                                                 sq.attn_fwd(q, k_glob, v_glob, q_rows=S, out=o_s),
+                                                 sq.attn_fwd(qc, kt, vt, q_rows=S, kv_len=kv_len, out=o_c)))
     return res
+
+
+def graph_step_lines(sq, step) -> dict:
+    """A non-anchor step (assembly, SRSU self- and cross-attention) as eager calls and as one
+    captured HIP graph, each timed over back-to-back repetitions.  Eager launches run ahead of
+    the GPU whenever the step's GPU time exceeds the binding's host time per call, so the two
+    differ only where the host is the bound."""
+    import torch
+    side = torch.cuda.Stream()
+    side.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(side):      # the capture stream's cached workspaces
+        step()
+    torch.cuda.current_stream().wait_stream(side)
+    torch.cuda.synchronize()
+    graph = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(graph, stream=side):
+        step()
+    torch.cuda.synchronize()
+    eager_ms = _time_ms(step, 50)
+    graph_ms = _time_ms(graph.replay, 50)
+    return {"eager_step_ms": round(eager_ms, 4), "graph_step_ms": round(graph_ms, 4),
+            "eager_over_graph": round(eager_ms / graph_ms, 3)}
 
 
 def cpu_baseline_workloads(W, inp4) -> dict:
