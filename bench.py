@@ -392,8 +392,10 @@ def main() -> int:
         torch.cuda.empty_cache()
         out["block"] = block_lines(sq, W, idx, tf)
         out["configs"] = other_configs(sq, W, tf)
-        clk = clock_under_load(lambda: sq.attn_fwd(q, kx, vx, out=o_dense))
+        pw = {}
+        clk = clock_under_load(lambda: sq.attn_fwd(q, kx, vx, out=o_dense), power=pw)
         out["gfx_clock_mhz_under_dense_load"] = clk
+        out["power_under_dense_load"] = pw
         if clk is not None:
             peak_clk = PEAK_BF16_TFLOPS * clk / 2400.0
             out["roofline"]["peak_at_measured_clock"] = round(peak_clk, 1)
@@ -882,9 +884,10 @@ def stage_rooflines(stage_ms, B, N, H, d, M, k, mask_bytes, kv_bytes, fl_srsu, f
     return out
 
 
-def clock_under_load(launch, seconds: float = 1.5):
+def clock_under_load(launch, seconds: float = 1.5, power: dict = None):
     """Mean graphics clock (MHz, over the XCDs) read with amd-smi while `launch` runs in a
-    loop; None when the tool is not available."""
+    loop; None when the tool is not available.  When `power` is a dict it receives the socket
+    power read in the same sample (W) and the board's power cap from hwmon (W), where readable."""
     import shutil
     import subprocess
     import threading
@@ -901,7 +904,7 @@ def clock_under_load(launch, seconds: float = 1.5):
     def sample():
         try:
             time.sleep(seconds / 2)
-            txt = subprocess.run([tool, "metric", "-c"], capture_output=True, text=True, timeout=20).stdout
+            txt = subprocess.run([tool, "metric", "-p", "-c"], capture_output=True, text=True, timeout=20).stdout
             result["txt"] = txt
         except Exception:
             pass
@@ -916,6 +919,17 @@ def clock_under_load(launch, seconds: float = 1.5):
             break
     th.join()
     clks = [int(m) for m in re.findall(r"GFX_\d+:\s*\n\s*CLK:\s*(\d+)\s*MHz", result.get("txt", ""))]
+    if power is not None:
+        m = re.search(r"SOCKET_POWER:\s*(\d+)\s*W", result.get("txt", ""))
+        power["socket_power_w"] = int(m.group(1)) if m else None
+        caps = []
+        import glob
+        for f in glob.glob("/sys/class/drm/card*/device/hwmon/hwmon*/power1_cap"):
+            try:
+                caps.append(int(open(f).read().strip()) / 1e6)
+            except (OSError, ValueError):
+                pass
+        power["power_cap_w"] = round(max(caps), 1) if caps else None
     return round(sum(clks) / len(clks), 1) if clks else None
 
 
