@@ -86,3 +86,21 @@ def test_short_keys_strided_views_and_many_heads():
     ref, _ = oracle.sdpa(q.value, k.value, v.value, kv_len=kv)
     assert_attn_close(ow[..., :d], ref, "strided short")
     assert torch.all(ow[..., d:] == 0), "nothing written past the output view"
+
+
+@pytest.mark.parametrize("H", [7, 24])
+def test_short_keys_several_heads_per_workgroup(H):
+    """Enough rows that each workgroup walks several heads (the next head's query rows
+    prefetched during the current one), with a head count the groups do not divide evenly
+    (H = 7: groups of 4 and 3): the oracle on sampled rows of every sample and head."""
+    B, Nq, Nk, d = 4, 16384, 300, 64
+    q, k, v = W.attention_inputs(B, Nq, Nk, H, d, seed=123 + H)
+    kv = np.array([300, 1, 64, 211], dtype=np.int32)
+    qd, kd, vd = to_dev_bf16(q), to_dev_bf16(k), to_dev_bf16(v)
+    o, lse = sq.attn_fwd(qd, kd, vd, kv_len=to_dev(kv), return_lse=True)
+    rng = np.random.default_rng(H)
+    samp = np.unique(np.concatenate([[0, 127, 128, Nq - 1], rng.choice(Nq, 60, replace=False)]))
+    rows = np.broadcast_to(samp, (B, len(samp))).copy()
+    ref, ref_lse = oracle.sdpa(q.value, k.value, v.value, q_rows=rows, kv_len=kv)
+    assert_attn_close(o[:, torch.from_numpy(samp).long()], ref, f"H={H} sampled rows")
+    assert_lse_close(lse[:, :, torch.from_numpy(samp).long()], ref_lse, f"H={H} sampled LSE")
