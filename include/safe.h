@@ -441,7 +441,8 @@ int safe_sw_cfg(const safe_cfg_args* a, void* stream);
  * a, res, out   bf16 rows (K values for a, N for res and out); element strides
  *               stride[0] = batch, stride[1] = row; 16-byte aligned rows.
  * w             bf16 [N, K]: row n holds output feature n's weights (K contiguous),
- *               row stride w_stride elements (< 2^24).
+ *               row stride w_stride elements (< 2^23: a tile's 256 rows are addressed
+ *               with 32-bit byte offsets).
  * bias          fp32 [N] (16-byte aligned) or NULL.
  * a_rows, res_rows, out_rows  device int32 [batches, M] (batch stride rows_bstride; 0 =
  *               one list for all) or NULL; entries index rows [0, Ntok).  Out of range:

@@ -471,7 +471,7 @@ int safe_linear(const safe_linear_args* a, void* stream) {
   if ((st = check_rows2(a->res, a->res_stride, false)) != SAFE_OK) return st;
   if (work && a->K > 0) {
     if (a->w == nullptr) return SAFE_ERR_NULL;
-    if (a->w_stride < a->K || a->w_stride >= (int64_t(1) << 24)) return SAFE_ERR_SHAPE;
+    if (a->w_stride < a->K || a->w_stride >= (int64_t(1) << 23)) return SAFE_ERR_SHAPE;
     if (a->w_stride % 8 != 0 || !aligned16(a->w)) return SAFE_ERR_ALIGN;
   }
   if (a->bias != nullptr && !aligned16(a->bias)) return SAFE_ERR_ALIGN;

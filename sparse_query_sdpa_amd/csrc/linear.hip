@@ -13,17 +13,25 @@
 //   CU: 6 LDS fragment reads feed 8 MFMAs) when the problem fills the GPU at least once,
 //   else 128 x 128 (4 waves of 64 x 64, two workgroups per CU).  k advances 64 per
 //   stage; A and W tiles are copied global -> LDS with global_load_lds_dwordx4 (no
-//   staging registers), double buffered, one barrier per stage.  LDS rows are 9 chunks
-//   of 16 bytes (8 used): an odd chunk count keeps the 16-lane row reads conflict-free.
+//   staging registers), double buffered, one barrier per stage.  An LDS row holds the
+//   stage's 8 chunks of 16 bytes in an order rotated by the row (chunk c of row r sits
+//   at position c ^ ((r >> 1) & 7)): the 16 rows one fragment read touches then cover
+//   all 64 banks, and no copy bytes are spent on padding.  The copies fetch the chunks
+//   already in that order, so the LDS side stays lane-linear.
 //   Gathered A rows use per-lane 64-bit source pointers, fixed for the whole k loop; W
 //   rows use a scalar base and 32-bit offsets.
+//   The epilogue goes through LDS: the accumulators (fp32) are written into the freed
+//   stage buffers, then read back a token row at a time, so bias, GELU, residual and
+//   the bf16 store run along the row and every store instruction writes whole 256-byte
+//   runs of two rows (written straight from the accumulator layout, a store touched 32
+//   rows with 16 bytes each, and the tile's drain was a fifth of the kernel).
 #include "common.h"
 
 namespace safe {
 namespace {
 
 constexpr int LK = 64;           // k per stage
-constexpr int LSLOTS = 9;        // 16-byte chunks per LDS row (8 used)
+constexpr int LSLOTS = 8;        // 16-byte chunks per LDS row, stored rotated (see above)
 constexpr int LROWB = LSLOTS * 16;
 
 // Tile shapes: WN x WM waves, each owning BNB x BMB 32 x 32 MFMA blocks (features x tokens).
@@ -41,6 +49,9 @@ struct LinCfg {
   static constexpr int A_BYTES = TM * LROWB;
   static constexpr int STAGE = (TM + TN) * LROWB;          // A tile then W tile
   static constexpr int MIN_BLOCKS = 4 * STAGE <= 160 * 1024 ? 2 : 1;
+  // epilogue: the two stage buffers hold ER fp32 token rows of TN features
+  static constexpr int EROWB = TN * 4;
+  static constexpr int ER = 2 * STAGE / EROWB;
   static_assert(TM * LSLOTS % 64 == 0 && TN * LSLOTS % 64 == 0 && NCOPY % WAVES == 0, "copy plan");
 };
 // 128 x 128 tiles, 4 waves of 64 x 64 (two workgroups per CU), and 256 x 256 tiles, 8 waves
@@ -63,11 +74,13 @@ __device__ __forceinline__ void lcopy16(const void* src, char* lds_dst) {
 }
 
 // tanh-form GELU: x/2 (1 + tanh(u)), u = sqrt(2/pi) (x + 0.044715 x^3), with
-// tanh(u) = 1 - 2 / (1 + e^{2u}) (saturates to +-1 without overflow trouble).
+// tanh(u) = 1 - 2 / (1 + e^{2u}) (saturates to +-1 without overflow trouble).  The
+// reciprocal is the hardware's (1 ulp): its error in tanh is ~2^-23, far below the bf16
+// rounding of the result, and it replaces the ten-instruction IEEE division.
 __device__ __forceinline__ float gelu_tanh(float x) {
   const float u = 0.7978845608028654f * __builtin_fmaf(0.044715f * x, x * x, x);
   const float e = __builtin_amdgcn_exp2f(2.8853900817779268f * u);   // e^{2u}
-  const float t = 1.0f - 2.0f / (1.0f + e);
+  const float t = 1.0f - 2.0f * __builtin_amdgcn_rcpf(1.0f + e);
   return 0.5f * x * (1.0f + t);
 }
 
@@ -76,34 +89,171 @@ __device__ __forceinline__ int bounded_row(const int32_t* rows, int64_t bs, int 
   return (v >= 0 && v < limit) ? v : -1;
 }
 
-template <typename CFG>
-__global__ __launch_bounds__(CFG::THREADS, CFG::MIN_BLOCKS) void linear_kernel(LinParams p) {
-  constexpr int LWAVES = CFG::WAVES, LPER_WAVE = CFG::PER_WAVE, LCOPY_A = CFG::COPY_A;
-  constexpr int BNB = CFG::BNB, BMB = CFG::BMB;
-  __shared__ __attribute__((aligned(1024))) char st0[CFG::STAGE];
-  __shared__ __attribute__((aligned(1024))) char st1[CFG::STAGE];
-  const int tid = threadIdx.x, lane = tid & 63;
-  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
-  const int col = lane & 31, half = lane >> 5;
-  const int wn = wave % CFG::WN, wm = wave / CFG::WN;       // this wave's block of the tile
-  // Consecutive logical tiles share an XCD (xcd_remap) and are ordered in groups of
-  // kGroupM tiles along m: the 32 or so tiles that run side by side on one XCD cover
-  // 8 (m) x 4 (n), so both their A and their W panels are shared in its L2 (+8-9% over
-  // a plain m-fastest order, where every A panel came from HBM).
+// Logical tile -> (batch, first token, first feature).  Tiles are ordered in groups of
+// kGroupM along m: with consecutive logical tiles on one XCD (xcd_remap, or the persistent
+// walk below), the ~32 tiles that run side by side there cover 8 (m) x 4 (n), so both
+// their A and their W panels are shared in its L2 (+8-9% over a plain m-fastest order,
+// where every A panel came from HBM).
+__device__ __forceinline__ void lin_tile(const LinParams& p, int logical, int TM, int TN, int& b, int& m0, int& n0) {
   constexpr int kGroupM = 8;
   const int per_b = p.tiles_m * p.tiles_n;
-  const int logical = xcd_remap(blockIdx.x, per_b * p.batches);
-  const int b = logical / per_b, t = logical - b * per_b;
+  b = logical / per_b;
+  const int t = logical - b * per_b;
   const int group = t / (kGroupM * p.tiles_n);
   const int first_m = group * kGroupM;
   const int gm = min(kGroupM, p.tiles_m - first_m);
   const int gi = t - group * kGroupM * p.tiles_n;
-  const int tm = first_m + gi % gm, tn = gi / gm;
-  const int m0 = tm * CFG::TM, n0 = tn * CFG::TN;
+  m0 = (first_m + gi % gm) * TM;
+  n0 = (gi / gm) * TN;
+}
+
+// Workgroup barrier for LDS hand-offs only: waits for this wave's LDS operations, not for
+// its vector-memory ones (copies into other buffers stay in flight across it).
+__device__ __forceinline__ void lds_barrier() { asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory"); }
+
+// Staged epilogue of one tile, ER token rows a round.  Write: lane (col, half) of block
+// (i, j) holds token wm*BMB*32 + 32j + col and, for each g, features wn*BNB*32 + 32i + 8g +
+// 4half + [0, 4): a 16-byte chunk c = feature / 4 of the token's fp32 row, stored at position
+// c ^ (token & 15) (the 16 rows of one write then cover all banks).  Read: 32 lanes per
+// row, lane u holding chunks u, u + 32, ...; then bias, GELU, residual, bf16 and an
+// 8-byte store per chunk, 256 contiguous bytes per 32 lanes.  A lane finishes IT rows a
+// round; their index-list entries and residual runs are loaded before the round's LDS work,
+// so each round waits for memory once instead of once per row.  rowp(tt) is the LDS row
+// of staged token tt (rows of one 32-token block are contiguous).  The caller has made the
+// staging rows free (barrier); the function ends with them free again.
+template <typename CFG, int ER, typename RowPtr>
+__device__ __forceinline__ void lin_epilogue(const LinParams& p, const f32x16 (&acc)[CFG::BNB][CFG::BMB],
+                                             int b, int m0, int n0, int wave, int lane, RowPtr rowp) {
+  constexpr int BNB = CFG::BNB, BMB = CFG::BMB, LWAVES = CFG::WAVES;
+  constexpr int CPR = CFG::TN / 4;          // 16-byte fp32 chunks per staged row
+  constexpr int CPL = CPR / 32;             // of which each reading lane holds CPL
+  constexpr int ROUNDS = CFG::TM / ER;
+  constexpr int IT = ER / (2 * LWAVES);     // rows a lane finishes per round
+  static_assert(ER % 32 == 0 && CFG::TM % ER == 0 && CPR % 32 == 0 && ER % (2 * LWAVES) == 0, "epilogue plan");
+  const int col = lane & 31, half = lane >> 5;
+  const int wn = wave % CFG::WN, wm = wave / CFG::WN;
+  f32x4 bias[CPL];
+#pragma unroll
+  for (int u = 0; u < CPL; ++u) {
+    const int n = n0 + 4 * (col + 32 * u);
+    bias[u] = (p.bias != nullptr && n < p.N) ? __builtin_bit_cast(f32x4, ld16(p.bias + n)) : f32x4{};
+  }
+#pragma unroll
+  for (int rnd = 0; rnd < ROUNDS; ++rnd) {
+    // this lane's rows: output row (-1: skipped) and residual row (-1: none)
+    int ro[IT], rres[IT];
+#pragma unroll
+    for (int it = 0; it < IT; ++it) {
+      const int rr = m0 + rnd * ER + (wave * IT + it) * 2 + half;
+      ro[it] = -1; rres[it] = -1;
+      if (rr < p.M) {
+        ro[it] = p.out_rows != nullptr ? bounded_row(p.out_rows, p.rows_bs, b, rr, p.Ntok) : rr;
+        if (p.res != nullptr) rres[it] = p.res_rows != nullptr ? bounded_row(p.res_rows, p.rows_bs, b, rr, p.Ntok) : rr;
+      }
+    }
+    u32x2 rv[IT][CPL];
+#pragma unroll
+    for (int it = 0; it < IT; ++it)
+#pragma unroll
+      for (int u = 0; u < CPL; ++u) {
+        const int n = n0 + 4 * (col + 32 * u);
+        rv[it][u] = u32x2{0u, 0u};
+        if (ro[it] >= 0 && rres[it] >= 0 && n < p.N)
+          rv[it][u] = *reinterpret_cast<const u32x2*>(p.res + (int64_t)b * p.res_bs + (int64_t)rres[it] * p.res_s + n * 2);
+      }
+#pragma unroll
+    for (int j = 0; j < BMB; ++j) {
+      if ((wm * BMB * 32 + j * 32) / ER != rnd) continue;   // wave-uniform
+      const int tt = wm * BMB * 32 + j * 32 - rnd * ER + col;
+      char* row = rowp(tt);
+#pragma unroll
+      for (int i = 0; i < BNB; ++i)
+#pragma unroll
+        for (int g = 0; g < 4; ++g) {
+          const int c = (wn * BNB * 32 + i * 32 + 8 * g + 4 * half) >> 2;
+          const f32x4 v = {acc[i][j][4 * g], acc[i][j][4 * g + 1], acc[i][j][4 * g + 2], acc[i][j][4 * g + 3]};
+          *reinterpret_cast<f32x4*>(row + ((c ^ (tt & 15)) << 4)) = v;
+        }
+    }
+    lds_barrier();
+#pragma unroll
+    for (int it = 0; it < IT; ++it) {
+      const int tt = (wave * IT + it) * 2 + half;
+      const char* row = rowp(tt);
+      f32x4 y[CPL];
+#pragma unroll
+      for (int u = 0; u < CPL; ++u)
+        y[u] = *reinterpret_cast<const f32x4*>(row + (((col + 32 * u) ^ (tt & 15)) << 4));
+      if (ro[it] < 0) continue;   // past M, or an invalid scatter index: skipped
+      char* op = p.out + (int64_t)b * p.out_bs + (int64_t)ro[it] * p.out_s;
+#pragma unroll
+      for (int u = 0; u < CPL; ++u) {
+        const int n = n0 + 4 * (col + 32 * u);
+        if (n >= p.N) continue;
+        float e[4] = {y[u][0], y[u][1], y[u][2], y[u][3]};
+        if (p.bias != nullptr) {
+#pragma unroll
+          for (int q = 0; q < 4; ++q) e[q] += bias[u][q];
+        }
+        if (p.act == SAFE_ACT_GELU_TANH) {
+#pragma unroll
+          for (int q = 0; q < 4; ++q) e[q] = gelu_tanh(e[q]);
+        }
+        if (rres[it] >= 0) {
+          const f32x2 lo = __builtin_bit_cast(f32x2, rv[it][u] << 16);
+          const f32x2 hi = __builtin_bit_cast(f32x2, rv[it][u] & 0xFFFF0000u);
+          e[0] += lo[0]; e[1] += hi[0]; e[2] += lo[1]; e[3] += hi[1];
+        }
+        u32x2 w;
+        w[0] = pack_bf16x2(e[0], e[1]);
+        w[1] = pack_bf16x2(e[2], e[3]);
+        st8(op + n * 2, w);
+      }
+    }
+    lds_barrier();   // the rows are free for the next round (or the caller)
+  }
+}
+
+// One k stage of MFMAs: At / Wt are the stage's A and W tiles (LROWB-byte rotated rows).
+// Fragment rows are col + multiples of 32, so their rotation is (col >> 1) & 7; k-step s
+// reads chunk 2s + half, at position (2s + half) ^ rot = (half ^ rot) ^ 2s = hrot ^ 2s.
+template <typename CFG>
+__device__ __forceinline__ void lin_stage(f32x16 (&acc)[CFG::BNB][CFG::BMB], const char* At, const char* Wt,
+                                          int a_lane, int w_lane, int hrot) {
+  constexpr int BNB = CFG::BNB, BMB = CFG::BMB;
+#pragma unroll
+  for (int s = 0; s < LK / 16; ++s) {
+    const int co = (hrot ^ (2 * s)) << 4;
+    bf16x8 af[BMB], wf[BNB];
+#pragma unroll
+    for (int j = 0; j < BMB; ++j) af[j] = as_bf16x8(ld16(At + a_lane + j * 32 * LROWB + co));
+#pragma unroll
+    for (int i = 0; i < BNB; ++i) wf[i] = as_bf16x8(ld16(Wt + w_lane + i * 32 * LROWB + co));
+#pragma unroll
+    for (int i = 0; i < BNB; ++i)
+#pragma unroll
+      for (int j = 0; j < BMB; ++j)
+        acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(wf[i], af[j], acc[i][j], 0, 0, 0);
+  }
+}
+
+template <typename CFG>
+__global__ __launch_bounds__(CFG::THREADS, CFG::MIN_BLOCKS) void linear_kernel(LinParams p) {
+  constexpr int LWAVES = CFG::WAVES, LPER_WAVE = CFG::PER_WAVE, LCOPY_A = CFG::COPY_A;
+  constexpr int BNB = CFG::BNB, BMB = CFG::BMB;
+  __shared__ __attribute__((aligned(1024))) char lds[2 * CFG::STAGE];
+  char* const st0 = lds;
+  char* const st1 = lds + CFG::STAGE;
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int col = lane & 31, half = lane >> 5;
+  const int wn = wave % CFG::WN, wm = wave / CFG::WN;       // this wave's block of the tile
+  int b, m0, n0;
+  lin_tile(p, xcd_remap(blockIdx.x, p.tiles_m * p.tiles_n * p.batches), CFG::TM, CFG::TN, b, m0, n0);
 
   // ---- copy plan: copy c < LCOPY_A fills A slots [64c, 64c+64), the rest W slots --
-  // slot sigma: row sigma / 9, chunk sigma % 9 (chunk 8 is padding: it fetches chunk 0
-  // of its row, never read back).  Rows past M (tokens) or N (features) fetch row 0.
+  // slot sigma: row sigma / 8, position sigma % 8, which holds chunk position ^ ((row >> 1)
+  // & 7) of the row.  Rows past M (tokens) or N (features) fetch row 0.
   const char* aptr[LPER_WAVE];    // A copies: per-lane 64-bit source (k = 0)
   uint32_t woff[LPER_WAVE];       // W copies: byte offset from the tile's first row
   const char* wbase = p.w + (int64_t)n0 * p.w_s;
@@ -113,8 +263,7 @@ __global__ __launch_bounds__(CFG::THREADS, CFG::MIN_BLOCKS) void linear_kernel(L
     const bool isa = c < LCOPY_A;
     const int sigma = (isa ? c : c - LCOPY_A) * 64 + lane;
     const int row = sigma / LSLOTS;
-    int chunk = sigma % LSLOTS;
-    if (chunk >= 8) chunk = 0;
+    const int chunk = (sigma % LSLOTS) ^ ((row >> 1) & 7);
     if (isa) {
       const int r = m0 + row;
       int src = 0;
@@ -157,26 +306,10 @@ __global__ __launch_bounds__(CFG::THREADS, CFG::MIN_BLOCKS) void linear_kernel(L
   for (int i = 0; i < BNB; ++i)
 #pragma unroll
     for (int j = 0; j < BMB; ++j) acc[i][j] = f32x16{};
-  const int a_lane = (wm * BMB * 32 + col) * LROWB + half * 16;   // B operand: token rows
-  const int w_lane = (wn * BNB * 32 + col) * LROWB + half * 16;   // A operand: feature rows
-
-  auto compute = [&](const char* stage) {
-    const char* At = stage;
-    const char* Wt = stage + CFG::A_BYTES;
-#pragma unroll
-    for (int s = 0; s < LK / 16; ++s) {
-      bf16x8 af[BMB], wf[BNB];
-#pragma unroll
-      for (int j = 0; j < BMB; ++j) af[j] = as_bf16x8(ld16(At + a_lane + j * 32 * LROWB + s * 32));
-#pragma unroll
-      for (int i = 0; i < BNB; ++i) wf[i] = as_bf16x8(ld16(Wt + w_lane + i * 32 * LROWB + s * 32));
-#pragma unroll
-      for (int i = 0; i < BNB; ++i)
-#pragma unroll
-        for (int j = 0; j < BMB; ++j)
-          acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(wf[i], af[j], acc[i][j], 0, 0, 0);
-    }
-  };
+  const int a_lane = (wm * BMB * 32 + col) * LROWB;   // B operand: token rows
+  const int w_lane = (wn * BNB * 32 + col) * LROWB;   // A operand: feature rows
+  const int hrot = half ^ ((col >> 1) & 7);
+  auto compute = [&](const char* stage) { lin_stage<CFG>(acc, stage, stage + CFG::A_BYTES, a_lane, w_lane, hrot); };
 
   const int nst = p.K / LK;
   if (nst > 0) issue(0, st0);
@@ -197,46 +330,102 @@ __global__ __launch_bounds__(CFG::THREADS, CFG::MIN_BLOCKS) void linear_kernel(L
     compute(st0);
   }
 
-  // ---- epilogue: lane owns token m and, per feature block i, four runs of 4 features --
-  const int r = m0 + wm * BMB * 32;   // + j * 32 + col
+  __syncthreads();   // every wave is done with the stage buffers
+  lin_epilogue<CFG, CFG::ER>(p, acc, b, m0, n0, wave, lane, [&](int tt) { return lds + tt * CFG::EROWB; });
+}
+
+// ---- 256 x 256 tiles through a ring of half-stage buffers ------------------------------
+// The copies run through five half-stage buffers (the A or the W tile of one k stage, 32 KB
+// each, 160 KB): while stage s is multiplied, stage s + 1 and the A tile of stage s + 2 are
+// in flight (96 KB per CU instead of the 64 KB of a double-buffered stage), and each step
+// waits only for the copies it needs (vmcnt of the younger half-stage), with a barrier that
+// does not drain the copy queue.  Each step then issues the next two half-stages into the
+// buffers the previous step freed.  (A persistent form that also ran the ring on into the
+// next tile, so its first copies overlapped this tile's epilogue, measured no faster.)
+constexpr int PHALF = LinLarge::STAGE / 2;   // bytes of one half-stage buffer
+constexpr int PRING = 5;                     // half-stage buffers in the ring
+
+__global__ __launch_bounds__(LinLarge::THREADS, 1) void linear_ring_kernel(LinParams p) {
+  typedef LinLarge CFG;
+  constexpr int LWAVES = CFG::WAVES, BNB = CFG::BNB, BMB = CFG::BMB;
+  static_assert(CFG::COPY_A == 4 * LWAVES && CFG::COPY_W == 4 * LWAVES && CFG::A_BYTES == PHALF, "ring copy plan");
+  static_assert(PRING * PHALF <= 160 * 1024 && 2 * CFG::STAGE <= PRING * PHALF, "LDS");
+  __shared__ __attribute__((aligned(1024))) char lds[PRING * PHALF];
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int col = lane & 31, half = lane >> 5;
+  const int wn = wave % CFG::WN, wm = wave / CFG::WN;
+  int b, m0, n0;
+  lin_tile(p, xcd_remap(blockIdx.x, p.tiles_m * p.tiles_n * p.batches), CFG::TM, CFG::TN, b, m0, n0);
+
+  // Copy plan: copy mm of the A (W) half-stage fills slots 64 (wave + 8 mm) + lane; slot
+  // sigma = row sigma / 8, position sigma % 8 holding chunk position ^ ((row >> 1) & 7).
+  // Rows past M (tokens) or N (features) fetch row 0.
+  const char* aptr[4];
+  uint32_t woff[4];
+  const char* wbase = p.w + (int64_t)n0 * p.w_s;
 #pragma unroll
-  for (int j = 0; j < BMB; ++j) {
-    const int rr = r + j * 32 + col;
-    if (rr >= p.M) continue;
-    int ro = rr, rres = rr;
-    if (p.out_rows != nullptr) ro = bounded_row(p.out_rows, p.rows_bs, b, rr, p.Ntok);
-    if (ro < 0) continue;   // an invalid scatter index is skipped
-    if (p.res != nullptr && p.res_rows != nullptr) rres = bounded_row(p.res_rows, p.rows_bs, b, rr, p.Ntok);
-    const char* resp = (p.res != nullptr && rres >= 0) ? p.res + (int64_t)b * p.res_bs + (int64_t)rres * p.res_s : nullptr;
-    char* op = p.out + (int64_t)b * p.out_bs + (int64_t)ro * p.out_s;
-#pragma unroll
-    for (int i = 0; i < BNB; ++i)
-#pragma unroll
-      for (int g = 0; g < 4; ++g) {
-        const int n = n0 + wn * BNB * 32 + i * 32 + 8 * g + 4 * half;
-        if (n >= p.N) continue;
-        float y[4] = {acc[i][j][4 * g], acc[i][j][4 * g + 1], acc[i][j][4 * g + 2], acc[i][j][4 * g + 3]};
-        if (p.bias != nullptr) {
-          const f32x4 bv = __builtin_bit_cast(f32x4, ld16(p.bias + n));
-#pragma unroll
-          for (int e = 0; e < 4; ++e) y[e] += bv[e];
-        }
-        if (p.act == SAFE_ACT_GELU_TANH) {
-#pragma unroll
-          for (int e = 0; e < 4; ++e) y[e] = gelu_tanh(y[e]);
-        }
-        if (resp != nullptr) {
-          const u32x2 rv = *reinterpret_cast<const u32x2*>(resp + n * 2);
-          const f32x2 lo = __builtin_bit_cast(f32x2, rv << 16);
-          const f32x2 hi = __builtin_bit_cast(f32x2, rv & 0xFFFF0000u);
-          y[0] += lo[0]; y[1] += hi[0]; y[2] += lo[1]; y[3] += hi[1];
-        }
-        u32x2 w;
-        w[0] = pack_bf16x2(y[0], y[1]);
-        w[1] = pack_bf16x2(y[2], y[3]);
-        st8(op + n * 2, w);
+  for (int mm = 0; mm < 4; ++mm) {
+    const int sigma = (wave + LWAVES * mm) * 64 + lane;
+    const int row = sigma / LSLOTS;
+    const int chunk = (sigma % LSLOTS) ^ ((row >> 1) & 7);
+    const int r = m0 + row;
+    int src = 0;
+    if (r < p.M) {
+      src = r;
+      if (p.a_rows != nullptr) {
+        src = bounded_row(p.a_rows, p.rows_bs, b, r, p.Ntok);
+        if (src < 0) src = 0;
       }
+    }
+    aptr[mm] = p.a + (int64_t)b * p.a_bs + (int64_t)src * p.a_s + chunk * 16;
+    const int n = n0 + row < p.N ? row : 0;
+    woff[mm] = (uint32_t)(n * p.w_s + chunk * 16);
   }
+  // half-stage h: the A tile of stage h / 2 if h is even, else its W tile; buffer h % PRING
+  auto issue_half = [&](int h) {
+    const int64_t k2 = (int64_t)(h >> 1) * (LK * 2);
+    int wl = (h % PRING) * PHALF + wave * 1024;
+    asm volatile("" : "+s"(wl));
+    char* dst = lds + wl;
+    if ((h & 1) == 0) {
+#pragma unroll
+      for (int mm = 0; mm < 4; ++mm) lcopy16(aptr[mm] + k2, dst + mm * LWAVES * 1024);
+    } else {
+#pragma unroll
+      for (int mm = 0; mm < 4; ++mm) {
+        uint32_t o = woff[mm];
+        asm volatile("" : "+v"(o));
+        lcopy16(wbase + k2 + o, dst + mm * LWAVES * 1024);
+      }
+    }
+  };
+
+  f32x16 acc[BNB][BMB];
+#pragma unroll
+  for (int i = 0; i < BNB; ++i)
+#pragma unroll
+    for (int j = 0; j < BMB; ++j) acc[i][j] = f32x16{};
+  const int a_lane = (wm * BMB * 32 + col) * LROWB;
+  const int w_lane = (wn * BNB * 32 + col) * LROWB;
+  const int hrot = half ^ ((col >> 1) & 7);
+  const int nst = p.K / LK, nh = 2 * nst;
+  int issued = 0;
+  for (; issued < nh && issued < 2; ++issued) issue_half(issued);   // stage 0 alone: it is needed first
+  for (int s = 0; s < nst; ++s) {
+    // this wave's copies of half-stages up to 2s + 1 have landed; younger ones (4 copies
+    // each) may stay in flight
+    const int out = issued - (2 * s + 2);
+    if (out >= 3) __builtin_amdgcn_s_waitcnt(0x0F7C);        // vmcnt(12)
+    else if (out == 2) __builtin_amdgcn_s_waitcnt(0x0F78);   // vmcnt(8)
+    else if (out == 1) __builtin_amdgcn_s_waitcnt(0x0F74);   // vmcnt(4)
+    else __builtin_amdgcn_s_waitcnt(0x0F70);                 // vmcnt(0)
+    lds_barrier();   // everyone's have; step s - 1's buffers are free
+    for (; issued < nh && issued <= 2 * s + PRING - 1; ++issued) issue_half(issued);
+    lin_stage<CFG>(acc, lds + ((2 * s) % PRING) * PHALF, lds + ((2 * s + 1) % PRING) * PHALF, a_lane, w_lane, hrot);
+  }
+  lds_barrier();   // every wave is done with the stage buffers (all copies have landed)
+  lin_epilogue<CFG, CFG::ER>(p, acc, b, m0, n0, wave, lane, [&](int tt) { return lds + tt * CFG::EROWB; });
 }
 
 }  // namespace
@@ -271,7 +460,7 @@ int linear_launch(const safe_linear_args* a, hipStream_t s) {
   p.tiles_n = (a->N + TN - 1) / TN;
   const int64_t grid = (int64_t)p.tiles_m * p.tiles_n * a->batches;
   if (grid > 0x7fffffff) return SAFE_ERR_SHAPE;
-  if (large) hipLaunchKernelGGL(linear_kernel<LinLarge>, dim3((unsigned)grid), dim3(LinLarge::THREADS), 0, s, p);
+  if (large) hipLaunchKernelGGL(linear_ring_kernel, dim3((unsigned)grid), dim3(LinLarge::THREADS), 0, s, p);
   else hipLaunchKernelGGL(linear_kernel<LinSmall>, dim3((unsigned)grid), dim3(LinSmall::THREADS), 0, s, p);
   return hipGetLastError() == hipSuccess ? SAFE_OK : SAFE_ERR_HIP;
 }

@@ -355,7 +355,7 @@ def _lin_args(**kw):
 @pytest.mark.parametrize("kw,status", [
     (dict(K=100), -5), (dict(N=12), -8), (dict(M=-1), -2), (dict(act=5), -4), (dict(flags=1 << 5), -4),
     (dict(a=None), -1), (dict(out=None), -1), (dict(w=None), -1), (dict(a=0x10008), -8),
-    (dict(w_stride=64), -2), (dict(w_stride=1 << 24), -2), (dict(w_stride=132), -8), (dict(bias=0x40004), -8),
+    (dict(w_stride=64), -2), (dict(w_stride=1 << 23), -2), (dict(w_stride=132), -8), (dict(bias=0x40004), -8),
     (dict(a_rows=0x50000, rows_bstride=50), -2), (dict(a_rows=0x50000, Ntok=0), -2),
     (dict(res=0x60000), -2),
 ])
