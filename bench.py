@@ -130,7 +130,7 @@ def mfma_busy_summary(path: str, n_xcd: int = 8, n_simd: int = 1024) -> None:
     disp = {}
     for r in csv.DictReader(open(path)):
         key = r["Kernel_Name"].replace("(anonymous namespace)::", "").split("(")[0].replace("void ", "")
-        if not any(n in key for n in ("attn_fwd_kernel", "attn_short_kernel", "pcsp_accum_kernel", "linear_kernel")):
+        if not any(n in key for n in ("attn_fwd_kernel", "attn_short_kernel", "pcsp_accum_kernel", "linear_kernel", "linear_ring_kernel")):
             continue
         d = disp.setdefault(r["Dispatch_Id"], {"key": key, "grid": int(r["Grid_Size"])})
         d[r["Counter_Name"]] = d.get(r["Counter_Name"], 0.0) + float(r["Counter_Value"])
