@@ -4,27 +4,29 @@
 // scattered output rows, bias, tanh-GELU and a (gathered) residual.
 //
 // gfx950 design
-//   The product runs transposed, D^T = W . A^T, with v_mfma_f32_32x32x16_bf16: the
-//   MFMA A operand is 32 rows of W (output features n), the B operand 32 rows of A
+//   The product runs transposed, D^T = W . A^T, with v_mfma_f32_16x16x32_bf16: the
+//   MFMA A operand is 16 rows of W (output features n), the B operand 16 rows of A
 //   (tokens m); both are read 16 bytes per lane from LDS rows of k, so neither needs a
-//   transpose, and in the accumulator lane l owns token m = l % 32 and runs of four
-//   consecutive features -- the epilogue stores 8 bytes per run.
+//   transpose, and in the accumulator lane l owns token m = l % 16 and a run of four
+//   consecutive features.  The 16x16x32 shape moves the same LDS bytes per FLOP as
+//   32x32x16 for a given wave tile (the fragment reuse is set by the tile), and on this
+//   power-limited chip it runs 10-18% faster on these maps: with random operands it draws
+//   less energy per FLOP, so the clock stays higher (the outputs are bit-identical).
 //   Two tile shapes: 256 x 256 (8 waves of 64 features x 128 tokens, one workgroup per
-//   CU: 6 LDS fragment reads feed 8 MFMAs) when the problem fills the GPU at least once,
-//   else 128 x 128 (4 waves of 64 x 64, two workgroups per CU).  k advances 64 per
-//   stage; A and W tiles are copied global -> LDS with global_load_lds_dwordx4 (no
-//   staging registers), double buffered, one barrier per stage.  An LDS row holds the
-//   stage's 8 chunks of 16 bytes in an order rotated by the row (chunk c of row r sits
-//   at position c ^ ((r >> 1) & 7)): the 16 rows one fragment read touches then cover
-//   all 64 banks, and no copy bytes are spent on padding.  The copies fetch the chunks
-//   already in that order, so the LDS side stays lane-linear.
-//   Gathered A rows use per-lane 64-bit source pointers, fixed for the whole k loop; W
-//   rows use a scalar base and 32-bit offsets.
+//   CU: 12 LDS fragment reads feed 32 MFMAs per 32 k) when the problem fills the GPU at
+//   least once, else 128 x 128 (4 waves of 64 x 64, two workgroups per CU).  k advances 64
+//   per stage; A and W tiles are copied global -> LDS with global_load_lds_dwordx4 (no
+//   staging registers).  An LDS row holds the stage's 8 chunks of 16 bytes in an order
+//   rotated by the row (chunk c of row r sits at position c ^ ((r >> 1) & 7)): the 16
+//   rows one fragment read touches then cover all 64 banks, and no copy bytes are spent
+//   on padding.  The copies fetch the chunks already in that order, so the LDS side stays
+//   lane-linear.  Gathered A rows use per-lane 64-bit source pointers, fixed for the whole
+//   k loop; W rows use a scalar base and 32-bit offsets.
 //   The epilogue goes through LDS: the accumulators (fp32) are written into the freed
 //   stage buffers, then read back a token row at a time, so bias, GELU, residual and
 //   the bf16 store run along the row and every store instruction writes whole 256-byte
-//   runs of two rows (written straight from the accumulator layout, a store touched 32
-//   rows with 16 bytes each, and the tile's drain was a fifth of the kernel).
+//   runs of two rows (written straight from the accumulator layout, a store touched 16
+//   rows, and the tile's drain was a fifth of the kernel).
 #include "common.h"
 
 namespace safe {
@@ -38,6 +40,8 @@ constexpr int LROWB = LSLOTS * 16;
 template <int WN_, int WM_, int BNB_, int BMB_>
 struct LinCfg {
   static constexpr int WN = WN_, WM = WM_, BNB = BNB_, BMB = BMB_;
+  // a wave's 32-row blocks are NI x NJ v_mfma_f32_16x16x32_bf16 blocks of 16 features x 16 tokens
+  static constexpr int NI = BNB * 2, NJ = BMB * 2;
   static constexpr int WAVES = WN * WM;
   static constexpr int THREADS = WAVES * 64;
   static constexpr int TN = WN * BNB * 32;                 // features per tile
@@ -55,7 +59,7 @@ struct LinCfg {
   static_assert(TM * LSLOTS % 64 == 0 && TN * LSLOTS % 64 == 0 && NCOPY % WAVES == 0, "copy plan");
 };
 // 128 x 128 tiles, 4 waves of 64 x 64 (two workgroups per CU), and 256 x 256 tiles, 8 waves
-// of 64 x 128 (one workgroup per CU): 6 LDS reads feed 8 MFMAs instead of 4 feeding 4.
+// of 64 x 128 (one workgroup per CU): 12 LDS reads feed 32 MFMAs instead of 8 feeding 16.
 typedef LinCfg<2, 2, 2, 2> LinSmall;
 typedef LinCfg<4, 2, 2, 4> LinLarge;
 
@@ -111,10 +115,10 @@ __device__ __forceinline__ void lin_tile(const LinParams& p, int logical, int TM
 // its vector-memory ones (copies into other buffers stay in flight across it).
 __device__ __forceinline__ void lds_barrier() { asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory"); }
 
-// Staged epilogue of one tile, ER token rows a round.  Write: lane (col, half) of block
-// (i, j) holds token wm*BMB*32 + 32j + col and, for each g, features wn*BNB*32 + 32i + 8g +
-// 4half + [0, 4): a 16-byte chunk c = feature / 4 of the token's fp32 row, stored at position
-// c ^ (token & 15) (the 16 rows of one write then cover all banks).  Read: 32 lanes per
+// Staged epilogue of one tile, ER token rows a round.  Write: lane l of 16 x 16 block (i, j)
+// holds token wm*BMB*32 + 16j + l % 16 and features wn*BNB*32 + 16i + 4(l / 16) + [0, 4): a
+// 16-byte chunk c = feature / 4 of the token's fp32 row, stored at position c ^ (token & 15)
+// (the 16 rows of one write then cover all banks).  Read: 32 lanes per
 // row, lane u holding chunks u, u + 32, ...; then bias, GELU, residual, bf16 and an
 // 8-byte store per chunk, 256 contiguous bytes per 32 lanes.  A lane finishes IT rows a
 // round; their index-list entries and residual runs are loaded before the round's LDS work,
@@ -122,7 +126,7 @@ __device__ __forceinline__ void lds_barrier() { asm volatile("s_waitcnt lgkmcnt(
 // of staged token tt (rows of one 32-token block are contiguous).  The caller has made the
 // staging rows free (barrier); the function ends with them free again.
 template <typename CFG, int ER, typename RowPtr>
-__device__ __forceinline__ void lin_epilogue(const LinParams& p, const f32x16 (&acc)[CFG::BNB][CFG::BMB],
+__device__ __forceinline__ void lin_epilogue(const LinParams& p, const f32x4 (&acc)[CFG::NI][CFG::NJ],
                                              int b, int m0, int n0, int wave, int lane, RowPtr rowp) {
   constexpr int BNB = CFG::BNB, BMB = CFG::BMB, LWAVES = CFG::WAVES;
   constexpr int CPR = CFG::TN / 4;          // 16-byte fp32 chunks per staged row
@@ -162,18 +166,15 @@ __device__ __forceinline__ void lin_epilogue(const LinParams& p, const f32x16 (&
           rv[it][u] = *reinterpret_cast<const u32x2*>(p.res + (int64_t)b * p.res_bs + (int64_t)rres[it] * p.res_s + n * 2);
       }
 #pragma unroll
-    for (int j = 0; j < BMB; ++j) {
-      if ((wm * BMB * 32 + j * 32) / ER != rnd) continue;   // wave-uniform
-      const int tt = wm * BMB * 32 + j * 32 - rnd * ER + col;
+    for (int j = 0; j < CFG::NJ; ++j) {
+      if ((wm * BMB * 32 + j * 16) / ER != rnd) continue;   // wave-uniform
+      const int tt = wm * BMB * 32 + j * 16 - rnd * ER + (lane & 15);
       char* row = rowp(tt);
 #pragma unroll
-      for (int i = 0; i < BNB; ++i)
-#pragma unroll
-        for (int g = 0; g < 4; ++g) {
-          const int c = (wn * BNB * 32 + i * 32 + 8 * g + 4 * half) >> 2;
-          const f32x4 v = {acc[i][j][4 * g], acc[i][j][4 * g + 1], acc[i][j][4 * g + 2], acc[i][j][4 * g + 3]};
-          *reinterpret_cast<f32x4*>(row + ((c ^ (tt & 15)) << 4)) = v;
-        }
+      for (int i = 0; i < CFG::NI; ++i) {
+        const int c = (wn * BNB * 32 + i * 16 + 4 * (lane >> 4)) >> 2;
+        *reinterpret_cast<f32x4*>(row + ((c ^ (tt & 15)) << 4)) = acc[i][j];
+      }
     }
     lds_barrier();
 #pragma unroll
@@ -214,39 +215,49 @@ __device__ __forceinline__ void lin_epilogue(const LinParams& p, const f32x16 (&
   }
 }
 
-// One k stage of MFMAs: At / Wt are the stage's A and W tiles (LROWB-byte rotated rows).
-// Fragment rows are col + multiples of 32, so their rotation is (col >> 1) & 7; k-step s
-// reads chunk 2s + half, at position (2s + half) ^ rot = (half ^ rot) ^ 2s = hrot ^ 2s.
+// Lane addressing of the fragment reads.  Lane l reads row l % 16 of a 16-row block (plus
+// multiples of 16, so the row's rotation (row >> 1) & 7 depends on the lane alone) and k-step
+// s (32 k) takes its chunk 4s + l / 16, at position (4s + l/16) ^ rot = rq ^ 4s.
 template <typename CFG>
-__device__ __forceinline__ void lin_stage(f32x16 (&acc)[CFG::BNB][CFG::BMB], const char* At, const char* Wt,
-                                          int a_lane, int w_lane, int hrot) {
-  constexpr int BNB = CFG::BNB, BMB = CFG::BMB;
+struct LinLanes {
+  int a, w, rq;
+  __device__ __forceinline__ LinLanes(int lane, int wn, int wm) {
+    const int r = lane & 15;
+    a = (wm * CFG::BMB * 32 + r) * LROWB;   // B operand: token rows
+    w = (wn * CFG::BNB * 32 + r) * LROWB;   // A operand: feature rows
+    rq = (lane >> 4) ^ ((r >> 1) & 7);
+  }
+};
+
+// One k stage (64 k) of MFMAs: At / Wt are the stage's A and W tiles (LROWB-byte rotated rows).
+template <typename CFG>
+__device__ __forceinline__ void lin_stage(f32x4 (&acc)[CFG::NI][CFG::NJ], const char* At, const char* Wt,
+                                          const LinLanes<CFG>& ln) {
+  constexpr int NI = CFG::NI, NJ = CFG::NJ;
 #pragma unroll
-  for (int s = 0; s < LK / 16; ++s) {
-    const int co = (hrot ^ (2 * s)) << 4;
-    bf16x8 af[BMB], wf[BNB];
+  for (int s = 0; s < LK / 32; ++s) {
+    const int co = (ln.rq ^ (4 * s)) << 4;
+    bf16x8 af[NJ], wf[NI];
 #pragma unroll
-    for (int j = 0; j < BMB; ++j) af[j] = as_bf16x8(ld16(At + a_lane + j * 32 * LROWB + co));
+    for (int j = 0; j < NJ; ++j) af[j] = as_bf16x8(ld16(At + ln.a + j * 16 * LROWB + co));
 #pragma unroll
-    for (int i = 0; i < BNB; ++i) wf[i] = as_bf16x8(ld16(Wt + w_lane + i * 32 * LROWB + co));
+    for (int i = 0; i < NI; ++i) wf[i] = as_bf16x8(ld16(Wt + ln.w + i * 16 * LROWB + co));
 #pragma unroll
-    for (int i = 0; i < BNB; ++i)
+    for (int i = 0; i < NI; ++i)
 #pragma unroll
-      for (int j = 0; j < BMB; ++j)
-        acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(wf[i], af[j], acc[i][j], 0, 0, 0);
+      for (int j = 0; j < NJ; ++j)
+        acc[i][j] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(wf[i], af[j], acc[i][j], 0, 0, 0);
   }
 }
 
 template <typename CFG>
 __global__ __launch_bounds__(CFG::THREADS, CFG::MIN_BLOCKS) void linear_kernel(LinParams p) {
   constexpr int LWAVES = CFG::WAVES, LPER_WAVE = CFG::PER_WAVE, LCOPY_A = CFG::COPY_A;
-  constexpr int BNB = CFG::BNB, BMB = CFG::BMB;
   __shared__ __attribute__((aligned(1024))) char lds[2 * CFG::STAGE];
   char* const st0 = lds;
   char* const st1 = lds + CFG::STAGE;
   const int tid = threadIdx.x, lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
-  const int col = lane & 31, half = lane >> 5;
   const int wn = wave % CFG::WN, wm = wave / CFG::WN;       // this wave's block of the tile
   int b, m0, n0;
   lin_tile(p, xcd_remap(blockIdx.x, p.tiles_m * p.tiles_n * p.batches), CFG::TM, CFG::TN, b, m0, n0);
@@ -301,15 +312,13 @@ __global__ __launch_bounds__(CFG::THREADS, CFG::MIN_BLOCKS) void linear_kernel(L
     }
   };
 
-  f32x16 acc[BNB][BMB];
+  f32x4 acc[CFG::NI][CFG::NJ];
 #pragma unroll
-  for (int i = 0; i < BNB; ++i)
+  for (int i = 0; i < CFG::NI; ++i)
 #pragma unroll
-    for (int j = 0; j < BMB; ++j) acc[i][j] = f32x16{};
-  const int a_lane = (wm * BMB * 32 + col) * LROWB;   // B operand: token rows
-  const int w_lane = (wn * BNB * 32 + col) * LROWB;   // A operand: feature rows
-  const int hrot = half ^ ((col >> 1) & 7);
-  auto compute = [&](const char* stage) { lin_stage<CFG>(acc, stage, stage + CFG::A_BYTES, a_lane, w_lane, hrot); };
+    for (int j = 0; j < CFG::NJ; ++j) acc[i][j] = f32x4{};
+  const LinLanes<CFG> ln(lane, wn, wm);
+  auto compute = [&](const char* stage) { lin_stage<CFG>(acc, stage, stage + CFG::A_BYTES, ln); };
 
   const int nst = p.K / LK;
   if (nst > 0) issue(0, st0);
@@ -345,15 +354,14 @@ __global__ __launch_bounds__(CFG::THREADS, CFG::MIN_BLOCKS) void linear_kernel(L
 constexpr int PHALF = LinLarge::STAGE / 2;   // bytes of one half-stage buffer
 constexpr int PRING = 5;                     // half-stage buffers in the ring
 
-__global__ __launch_bounds__(LinLarge::THREADS, 1) void linear_ring_kernel(LinParams p) {
-  typedef LinLarge CFG;
-  constexpr int LWAVES = CFG::WAVES, BNB = CFG::BNB, BMB = CFG::BMB;
+template <typename CFG>
+__global__ __launch_bounds__(CFG::THREADS, 1) void linear_ring_kernel(LinParams p) {
+  constexpr int LWAVES = CFG::WAVES;
   static_assert(CFG::COPY_A == 4 * LWAVES && CFG::COPY_W == 4 * LWAVES && CFG::A_BYTES == PHALF, "ring copy plan");
   static_assert(PRING * PHALF <= 160 * 1024 && 2 * CFG::STAGE <= PRING * PHALF, "LDS");
   __shared__ __attribute__((aligned(1024))) char lds[PRING * PHALF];
   const int tid = threadIdx.x, lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
-  const int col = lane & 31, half = lane >> 5;
   const int wn = wave % CFG::WN, wm = wave / CFG::WN;
   int b, m0, n0;
   lin_tile(p, xcd_remap(blockIdx.x, p.tiles_m * p.tiles_n * p.batches), CFG::TM, CFG::TN, b, m0, n0);
@@ -401,14 +409,12 @@ __global__ __launch_bounds__(LinLarge::THREADS, 1) void linear_ring_kernel(LinPa
     }
   };
 
-  f32x16 acc[BNB][BMB];
+  f32x4 acc[CFG::NI][CFG::NJ];
 #pragma unroll
-  for (int i = 0; i < BNB; ++i)
+  for (int i = 0; i < CFG::NI; ++i)
 #pragma unroll
-    for (int j = 0; j < BMB; ++j) acc[i][j] = f32x16{};
-  const int a_lane = (wm * BMB * 32 + col) * LROWB;
-  const int w_lane = (wn * BNB * 32 + col) * LROWB;
-  const int hrot = half ^ ((col >> 1) & 7);
+    for (int j = 0; j < CFG::NJ; ++j) acc[i][j] = f32x4{};
+  const LinLanes<CFG> ln(lane, wn, wm);
   const int nst = p.K / LK, nh = 2 * nst;
   int issued = 0;
   for (; issued < nh && issued < 2; ++issued) issue_half(issued);   // stage 0 alone: it is needed first
@@ -422,7 +428,7 @@ __global__ __launch_bounds__(LinLarge::THREADS, 1) void linear_ring_kernel(LinPa
     else __builtin_amdgcn_s_waitcnt(0x0F70);                 // vmcnt(0)
     lds_barrier();   // everyone's have; step s - 1's buffers are free
     for (; issued < nh && issued <= 2 * s + PRING - 1; ++issued) issue_half(issued);
-    lin_stage<CFG>(acc, lds + ((2 * s) % PRING) * PHALF, lds + ((2 * s + 1) % PRING) * PHALF, a_lane, w_lane, hrot);
+    lin_stage<CFG>(acc, lds + ((2 * s) % PRING) * PHALF, lds + ((2 * s + 1) % PRING) * PHALF, ln);
   }
   lds_barrier();   // every wave is done with the stage buffers (all copies have landed)
   lin_epilogue<CFG, CFG::ER>(p, acc, b, m0, n0, wave, lane, [&](int tt) { return lds + tt * CFG::EROWB; });
@@ -460,7 +466,7 @@ int linear_launch(const safe_linear_args* a, hipStream_t s) {
   p.tiles_n = (a->N + TN - 1) / TN;
   const int64_t grid = (int64_t)p.tiles_m * p.tiles_n * a->batches;
   if (grid > 0x7fffffff) return SAFE_ERR_SHAPE;
-  if (large) hipLaunchKernelGGL(linear_ring_kernel, dim3((unsigned)grid), dim3(LinLarge::THREADS), 0, s, p);
+  if (large) hipLaunchKernelGGL(linear_ring_kernel<LinLarge>, dim3((unsigned)grid), dim3(LinLarge::THREADS), 0, s, p);
   else hipLaunchKernelGGL(linear_kernel<LinSmall>, dim3((unsigned)grid), dim3(LinSmall::THREADS), 0, s, p);
   return hipGetLastError() == hipSuccess ? SAFE_OK : SAFE_ERR_HIP;
 }
