@@ -302,6 +302,7 @@ def main() -> int:
     fl_dense = 4.0 * B * H * N * N * d
     Lsum = int(inp["kv_len"].sum())
     fl_cross = 4.0 * H * d * k * Lsum
+    fl_pcsp = 2.0 * N * H * d * Lsum   # Eq. 9 logits over the valid text keys
     kv_bytes = 4.0 * B * N * H * d * 2
     tf = lambda fl, ms: fl / (ms * 1e-3) / 1e12
     traffic = recorded_traffic()
@@ -331,7 +332,7 @@ def main() -> int:
         "stage_ms_min": {kk: round(float(np.min(v)), 4) for kk, v in per_step.items()},
         "cross_tflops": round(tf(fl_cross, stage_ms["srsu_cross"]), 2),
         "stage_rooflines": stage_rooflines(stage_ms, B, N, H, d, M, k, mask_bytes, kv_bytes, fl_srsu, fl_cross,
-                                           fl_dense),
+                                           fl_dense, fl_pcsp),
         "classify_gbs": round(mask_bytes / (stage_ms["classify"] * 1e-3) / 1e9, 1),
         "classify_pct_hbm": round(100 * mask_bytes / (stage_ms["classify"] * 1e-3) / 1e9 / PEAK_HBM_GBS, 2),
         "kv_assemble_gbs": round(kv_bytes / (stage_ms["kv_assemble"] * 1e-3) / 1e9, 1),
@@ -855,11 +856,14 @@ def other_configs(sq, W, tf) -> dict:
     return res
 
 
-def stage_rooflines(stage_ms, B, N, H, d, M, k, mask_bytes, kv_bytes, fl_srsu, fl_cross, fl_dense) -> dict:
+def stage_rooflines(stage_ms, B, N, H, d, M, k, mask_bytes, kv_bytes, fl_srsu, fl_cross, fl_dense,
+                    fl_pcsp=None) -> dict:
     """Each stage of the step against the roofline that bounds it, from its event time and its
     algorithmic bytes (HBM-bound stages: every input read once, every output written once) or
-    FLOPs (MFMA-bound stages).  pcsp_select moves under 1 MB and is bound by its launches and
-    the per-sample radix passes, so only its time is given."""
+    FLOPs (MFMA-bound stages).  The two text-side products (PCSP accumulation, cross-attention)
+    also carry their MFMA rate: their FLOPs (over the valid text keys) take about as long at
+    the bf16 rate as their bytes at the HBM rate.  pcsp_select moves under 1 MB and is bound by
+    its launches and the per-sample radix passes, so only its time is given."""
     e = 2   # bf16 bytes
     hbm = {
         "classify": (mask_bytes, "[B,1,N,N] bf16 mask read once"),
@@ -880,6 +884,9 @@ def stage_rooflines(stage_ms, B, N, H, d, M, k, mask_bytes, kv_bytes, fl_srsu, f
         out[st] = {"bound": "mfma", "flops": fl, "achieved": round(t, 2), "unit": "TFLOP/s",
                    "peak": PEAK_BF16_TFLOPS, "frac": round(t / PEAK_BF16_TFLOPS, 4), "ms": round(stage_ms[st], 4)}
     out["srsu_cross"]["mfma_tflops"] = round(fl_cross / (stage_ms["srsu_cross"] * 1e-3) / 1e12, 2)
+    if fl_pcsp is not None:
+        out["pcsp_accum"]["flops"] = fl_pcsp
+        out["pcsp_accum"]["mfma_tflops"] = round(fl_pcsp / (stage_ms["pcsp_accum"] * 1e-3) / 1e12, 2)
     out["pcsp_select"] = {"bound": "latency", "ms": round(stage_ms["pcsp_select"], 4)}
     return out
 

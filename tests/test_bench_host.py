@@ -106,3 +106,7 @@ def test_stage_rooflines_bytes_and_fractions():
     t = fl_d / 4.0e-3 / 1e12
     assert r["dense"]["bound"] == "mfma" and abs(r["dense"]["frac"] - t / 2500.0) < 1e-4
     assert r["pcsp_select"] == {"bound": "latency", "ms": 0.05}
+    assert "mfma_tflops" not in r["pcsp_accum"]
+    fl_p = 2.0 * N * H * d * 150
+    r = bench.stage_rooflines(ms, B, N, H, d, M, k, mask_bytes, kv_bytes, fl_s, fl_c, fl_d, fl_p)
+    assert r["pcsp_accum"]["flops"] == fl_p and abs(r["pcsp_accum"]["mfma_tflops"] - fl_p / 0.1e-3 / 1e12) < 0.01
