@@ -140,14 +140,22 @@ def mfma_busy_summary(path: str, n_xcd: int = 8, n_simd: int = 1024) -> None:
         if all(c in d for c in ("SQ_VALU_MFMA_BUSY_CYCLES", "SQ_INSTS_MFMA", "GRBM_GUI_ACTIVE")):
             groups.setdefault((d["key"], d["grid"], int(d["SQ_INSTS_MFMA"])), []).append(d)
     print("| kernel | grid (threads) | launches | MFMA instr. per launch | TFLOP per launch | cycles per launch "
-          "(GRBM / XCDs) | clock MHz | MFMA TFLOP/s (instr. x 32768 / time) | MFMA busy fraction |")
+          "(GRBM / XCDs) | clock MHz | MFMA TFLOP/s (instr. x FLOP per instr. / time) | MFMA busy fraction |")
     print("|---|---|---|---|---|---|---|---|---|")
     for (key, grid, inst), ok in sorted(groups.items()):
         busy = sum(v["SQ_VALU_MFMA_BUSY_CYCLES"] for v in ok) / len(ok)
         cyc = sum(v["GRBM_GUI_ACTIVE"] for v in ok) / len(ok) / n_xcd
         ns = sum(v["ns"] for v in ok) / len(ok)
-        print(f"| `{key}` | {grid} | {len(ok)} | {inst:.4g} | {inst * 32768 / 1e12:.3f} | {cyc:.4g} | "
-              f"{cyc / ns * 1e3:.0f} | {inst * 32768 / ns / 1e3:.0f} | {busy / (cyc * n_simd):.3f} |")
+        fpi = mfma_flops_per_instruction(key)
+        print(f"| `{key}` | {grid} | {len(ok)} | {inst:.4g} | {inst * fpi / 1e12:.3f} | {cyc:.4g} | "
+              f"{cyc / ns * 1e3:.0f} | {inst * fpi / ns / 1e3:.0f} | {busy / (cyc * n_simd):.3f} |")
+
+
+def mfma_flops_per_instruction(kernel: str) -> int:
+    """FLOPs of one MFMA instruction of the kernel: the row-wise linear maps issue
+    v_mfma_f32_16x16x32_bf16 (16384), the attention and PCSP kernels v_mfma_f32_32x32x16_bf16
+    (32768)."""
+    return 16384 if "linear_" in kernel else 32768
 
 
 def rocprof_summary(path: str) -> None:

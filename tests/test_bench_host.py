@@ -65,7 +65,7 @@ def test_mfma_busy_summary_fraction_and_clock(tmp_path):
     rows = []
     for disp in (1, 2):
         rows += [(disp, name, 1024, "GRBM_GUI_ACTIVE", cycles * 8, ns),
-                 (disp, name, 1024, "SQ_INSTS_MFMA", 1000, ns),
+                 (disp, name, 1024, "SQ_INSTS_MFMA", 30_000_000, ns),
                  (disp, name, 1024, "SQ_VALU_MFMA_BUSY_CYCLES", 0.5 * cycles * 1024, ns)]
     write_csv(tmp_path / "m.csv", rows)
     out = run(bench.mfma_busy_summary, str(tmp_path / "m.csv"))
@@ -75,6 +75,14 @@ def test_mfma_busy_summary_fraction_and_clock(tmp_path):
     assert cells[1] == "1024" and cells[2] == "2"          # grid, launches
     assert cells[6] == "1800"                               # clock MHz
     assert cells[8] == "0.500"                              # busy fraction
+    assert cells[7] == "983"                                # 3e7 x 32768 FLOP / 1 ms, in TFLOP/s
+
+
+def test_mfma_flops_per_instruction_follows_the_kernel_shape():
+    assert bench.mfma_flops_per_instruction("safe::attn_fwd_kernel<96, true, false, 0, 2, false>") == 32768
+    assert bench.mfma_flops_per_instruction("safe::pcsp_accum_kernel<96>") == 32768
+    assert bench.mfma_flops_per_instruction("safe::linear_ring_kernel<safe::LinCfg<4, 2, 2, 4> >") == 16384
+    assert bench.mfma_flops_per_instruction("safe::linear_kernel<safe::LinCfg<2, 2, 2, 2> >") == 16384
 
 
 def test_recorded_traffic_ignores_comment_edits(tmp_path, monkeypatch):
