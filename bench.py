@@ -401,6 +401,12 @@ def main() -> int:
         torch.cuda.empty_cache()
         out["block"] = block_lines(sq, W, idx, tf)
         out["configs"] = other_configs(sq, W, tf)
+        out["mfma_ceiling"] = mfma_ceiling_lines(sq)
+        ceil32 = out["mfma_ceiling"]["32x32x16_bf16_tflops"]
+        out["roofline"]["mfma_only_tflops_same_instruction"] = ceil32
+        out["roofline"]["frac_of_mfma_only_rate"] = round(dense_tf / ceil32, 4)
+        out["roofline_srsu"]["mfma_only_tflops_same_instruction"] = ceil32
+        out["roofline_srsu"]["frac_of_mfma_only_rate"] = round(srsu_tf / ceil32, 4)
         pw = {}
         clk = clock_under_load(lambda: sq.attn_fwd(q, kx, vx, out=o_dense), power=pw)
         out["gfx_clock_mhz_under_dense_load"] = clk
@@ -635,6 +641,29 @@ def cpu_baseline_workloads(W, inp4) -> dict:
                         "srsu_extrapolated_s": round(per_row * B * k, 2),
                         "dense_extrapolated_s": round(per_row * B * N, 2),
                         "tflops": round(4.0 * B * H * n * N * d / secs / 1e12, 6)}
+    return res
+
+
+def mfma_ceiling_lines(sq) -> dict:
+    """The matrix-core rate on random bf16 register operands with nothing else running
+    (safe_mfma_probe; two 4-wave workgroups per CU, as the attention kernel runs), for the
+    attention kernels' instruction (32x32x16) and the linear kernels' (16x16x32), with the
+    clock and socket power sampled while the 32x32x16 probe runs back to back.  On this
+    power-capped chip it is the rate the attention kernel's products could reach with no
+    softmax, LDS traffic or copies at all."""
+    import torch
+    cus = torch.cuda.get_device_properties(0).multi_processor_count
+    blocks, iters = 2 * cus, 2000   # launches of about 1.2 ms: the clock settles under the power cap
+    buf = torch.empty(blocks * 256, dtype=torch.float32, device="cuda")
+    res = {"blocks": blocks, "iters": iters}
+    for shape, fpi, name in ((32, 32768, "32x32x16_bf16"), (16, 16384, "16x16x32_bf16")):
+        ms = _time_ms(lambda: sq.mfma_probe(shape, iters, blocks, out=buf), 5, warm_ms=500.0)
+        res[name + "_tflops"] = round(blocks * 4 * iters * 16 * fpi / (ms * 1e-3) / 1e12, 1)
+        res[name + "_ms"] = round(ms, 3)
+    assert bool(torch.isfinite(buf).all()), "probe checksums"
+    pw = {}
+    res["gfx_clock_mhz_32x32x16"] = clock_under_load(lambda: sq.mfma_probe(32, iters, blocks, out=buf), power=pw)
+    res["power_32x32x16"] = pw
     return res
 
 

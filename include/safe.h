@@ -470,6 +470,25 @@ typedef struct {
 
 int safe_linear(const safe_linear_args* a, void* stream);
 
+/*
+ * safe_mfma_probe -- a measurement aid beside the method (no equation of the pages): the
+ * matrix-core rate the GPU sustains on random bf16 operands with nothing else running, the
+ * ceiling the attention and linear kernels are read against on a power-capped chip.
+ * `blocks` workgroups of 256 threads (two per CU fill the chip as the attention kernel does)
+ * each run `iters` rounds; a round is 16 MFMAs per wave into four independent accumulators,
+ * every instruction on a different pair of the lane's eight A and eight B register fragments:
+ *   shape 32: v_mfma_f32_32x32x16_bf16 (32768 FLOP each), shape 16: v_mfma_f32_16x16x32_bf16
+ *   (16384 FLOP each); FLOP per launch = blocks * 4 waves * iters * 16 * FLOP per MFMA.
+ * Operands: lane g = 256 * block + thread holds, in fragment f (A: f = 0..7, B: f = 8..15),
+ * element e = bf16_rne((h / 2^24 - 0.5) * 4) with h = H(seed ^ H(64 g + 8 f + e)) >> 8 and H the
+ * 32-bit mixer x ^= x >> 16; x *= 0x7feb352d; x ^= x >> 15; x *= 0x846ca68b; x ^= x >> 16.
+ * Round q (0..15) multiplies A fragment q % 8 by B fragment (q + q / 8) % 8 into accumulator q % 4.
+ * out: device float[blocks * 256], lane g's sum of its accumulator elements (keeps the
+ * products live; the sum over a wave's lanes is the sum of every product it issued).
+ * Errors: SAFE_ERR_RANGE (shape not 16 or 32, iters or blocks outside [1, 2^24]), SAFE_ERR_NULL.
+ */
+int safe_mfma_probe(int32_t shape, int32_t iters, int32_t blocks, uint32_t seed, float* out, void* stream);
+
 /* SAFE_ABI_VERSION of the built library. */
 int safe_abi_version(void);
 

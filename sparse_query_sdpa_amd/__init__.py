@@ -158,6 +158,9 @@ def _load():
                                      ctypes.c_void_p]
     lib.safe_linear.restype = ctypes.c_int
     lib.safe_linear.argtypes = [ctypes.POINTER(LinearArgs), ctypes.c_void_p]
+    lib.safe_mfma_probe.restype = ctypes.c_int
+    lib.safe_mfma_probe.argtypes = [ctypes.c_int32, ctypes.c_int32, ctypes.c_int32, ctypes.c_uint32, ctypes.c_void_p,
+                                    ctypes.c_void_p]
     lib.safe_mask_classify.restype = ctypes.c_int
     lib.safe_mask_classify.argtypes = [ctypes.c_void_p, ctypes.c_int32, ctypes.POINTER(ctypes.c_int64),
                                        ctypes.POINTER(ctypes.c_int64), ctypes.c_uint32, ctypes.POINTER(MaskInfo),
@@ -795,3 +798,18 @@ def block_srsu(x: torch.Tensor, idx: torch.Tensor, z: torch.Tensor, qkv_cache: t
     u_s = linear(y_s, w["w1"], bias=w["b1"], gelu=True, stream=stream)
     linear(u_s, w["w2"], bias=w["b2"], res=y_s, out=z, out_rows=idx, stream=stream)
     return z
+
+
+def mfma_probe(shape: int, iters: int, blocks: int, seed: int = 1, out: Optional[torch.Tensor] = None,
+               stream=None) -> torch.Tensor:
+    """The matrix-core rate probe (safe_mfma_probe, a measurement aid): `blocks` workgroups of
+    4 waves issue iters x 16 MFMAs each on random bf16 register operands (shape 32:
+    v_mfma_f32_32x32x16_bf16, 32768 FLOP; 16: v_mfma_f32_16x16x32_bf16, 16384 FLOP).  Returns the
+    float32 per-lane checksums [blocks * 256]."""
+    if out is None:
+        out = torch.empty(blocks * 256, dtype=torch.float32, device="cuda")
+    if out.dtype != torch.float32 or not out.is_contiguous() or out.numel() < blocks * 256:
+        raise ValueError("out must be a contiguous float32 tensor of at least blocks * 256 elements")
+    _check("safe_mfma_probe", lib.safe_mfma_probe(int(shape), int(iters), int(blocks), int(seed) & 0xFFFFFFFF,
+                                                  _ptr(out), _stream(stream)))
+    return out

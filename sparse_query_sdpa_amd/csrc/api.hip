@@ -13,6 +13,7 @@ int64_t attn_workspace_bytes(const safe_attn_args* a);
 int attn_plan(const safe_attn_args* a, safe_attn_plan_info* out);
 int sw_cfg_launch(const safe_cfg_args* a, hipStream_t stream);
 int linear_launch(const safe_linear_args* a, hipStream_t stream);
+int mfma_probe_launch(int shape, int iters, int blocks, uint32_t seed, float* out, hipStream_t stream);
 int kv_assemble_launch(const safe_kv_args* a, bool in_place, hipStream_t stream);
 int kv_source_map_launch(const safe_kv_args* a, int32_t* src, hipStream_t stream);
 int mask_classify_launch(const void* mask, int32_t dtype, const int64_t size[4], const int64_t stride[4],
@@ -484,6 +485,13 @@ int safe_linear(const safe_linear_args* a, void* stream) {
         return st;
   }
   return linear_launch(a, s);
+}
+
+int safe_mfma_probe(int32_t shape, int32_t iters, int32_t blocks, uint32_t seed, float* out, void* stream) {
+  if (shape != 32 && shape != 16) return SAFE_ERR_RANGE;
+  if (iters < 1 || iters > (1 << 24) || blocks < 1 || blocks > (1 << 24)) return SAFE_ERR_RANGE;
+  if (out == nullptr) return SAFE_ERR_NULL;
+  return mfma_probe_launch(shape, iters, blocks, seed, out, static_cast<hipStream_t>(stream));
 }
 
 }  // extern "C"
