@@ -233,6 +233,11 @@ int attn_fwd_launch(const safe_attn_args* a, float scale, hipStream_t stream) {
   p.n_slots = pl.tail * pl.nsplit;
   p.part = pl.tail > 0 ? static_cast<float*>(a->workspace) : nullptr;
   p.total_wg = pl.n_full + p.n_slots;
+  // a per-query-row mask shared by the heads: tiles of four (two) heads of one row tile side
+  // by side (a key mask, broadcast over the rows too, is small and keeps the K/V order)
+  p.head_group = 1;
+  if (mt != kMaskNone && a->mask_stride[1] == 0 && a->mask_stride[2] != 0)
+    p.head_group = a->H % 4 == 0 ? 4 : (a->H % 2 == 0 ? 2 : 1);
   const bool gather = a->q_rows != nullptr;
   const bool kvlen = a->kv_len != nullptr;
   hipError_t e;

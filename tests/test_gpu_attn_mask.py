@@ -74,6 +74,27 @@ def test_masked_against_oracle(d, kind):
     assert_lse_close(lse, ref_lse, f"masked rows d={d} {kind}")
 
 
+@pytest.mark.parametrize("H", [4, 6, 8])
+def test_head_shared_row_mask_groups_heads(H):
+    """A per-row mask shared by the heads ([B, 1, Nq, Nk]) runs its tiles in groups of four
+    (H = 4, 8) or two (H = 6) heads of one row tile: every head's rows still get their own
+    outputs and LSE (oracle), on all rows and on gathered rows."""
+    B, Nq, Nk, d = 2, 1500, 700, 64
+    q, k, v = W.attention_inputs(B, Nq, Nk, H, d, seed=600 + H)
+    qd, kd, vd = to_dev_bf16(q), to_dev_bf16(k), to_dev_bf16(v)
+    rng = np.random.default_rng(600 + H)
+    vals = additive_values(rng, (B, 1, Nq, Nk), "bf16")
+    mask = padded_mask(vals, "bf16")
+    o, lse = sq.attn_fwd(qd, kd, vd, mask=mask, return_lse=True)
+    ref, ref_lse = oracle.sdpa(q.value, k.value, v.value, mask=vals)
+    assert_attn_close(o, ref, f"head-shared mask H={H}")
+    assert_lse_close(lse, ref_lse, f"head-shared mask H={H}")
+    rows = np.stack([W.random_rows(rng, Nq, 333) for _ in range(B)])
+    o2 = sq.attn_fwd(qd, kd, vd, q_rows=to_dev(rows), mask=mask)
+    ref2, _ = oracle.sdpa(q.value, k.value, v.value, q_rows=rows, mask=vals)
+    assert_attn_close(o2, ref2, f"head-shared mask rows H={H}")
+
+
 def test_removable_masks_are_exact_to_drop():
     """Eq. 7-8 on this kernel: an all-valid Boolean mask and a zero additive mask give
     bit-identical outputs to the mask-free call (same scores, same softmax order); a
