@@ -426,57 +426,52 @@ void attn_fwd_kernel(AttnParams p) {
 
   // ---- mask runs: run i of a tile covers keys 32 (i / 4) + 8 (i % 4) + 4 half + 0..3 ----
   // Whole tiles are loaded one tile ahead.  Staged (when the LDS leaves room for two
-  // workgroups per CU): each of the wave's 32 rows as CPR consecutive 16-byte chunks,
-  // NMI coalesced loads per lane into registers, then written to the wave's own LDS rows
-  // and read back as runs -- a load instruction then touches 8 or fewer cache lines
-  // instead of 32.  Otherwise the runs are loaded directly (8 loads per lane).
+  // workgroups per CU): the wave's 32 rows of the next tile are copied straight into the
+  // wave's own LDS rows (NMI direct-to-LDS copies per lane, issued with the K/V copies and
+  // covered by the same wait), then read back as runs -- a copy touches 8 or fewer cache
+  // lines instead of the 32 a run load would, and no registers or LDS writes stage them.
+  // Row r's 16-byte chunk c sits at position c ^ rot(r), rot(r) = (r / (16 / CPR)) % CPR, so
+  // the 16 rows one run read touches cover all banks.  Otherwise the runs are loaded
+  // directly (8 loads per lane).
   constexpr int CPR = 4 * MR::esz;                                  // 16-byte chunks per row of a tile
-  constexpr int NMI = HAS_MASK ? 32 * CPR / 64 : 1;                 // staging loads per lane
-  constexpr int MRS = 64 * MR::esz + (MT == kMaskF32 ? 16 : 8);     // LDS row stride: conflict-free run reads
+  constexpr int NMI = HAS_MASK ? 32 * CPR / 64 : 1;                 // staging copies per lane
+  constexpr int MRS = CPR * 16;                                     // LDS row stride (no padding)
+  constexpr int RPB = 16 / CPR;                                     // rows per 256 bytes of LDS
   constexpr bool STAGED = HAS_MASK && 2 * T::STAGE + NWAVES * 32 * MRS <= 80 * 1024;
-  __shared__ __attribute__((aligned(16))) char mstage[STAGED ? NWAVES * 32 * MRS : 16];
+  __shared__ __attribute__((aligned(1024))) char mstage[STAGED ? NWAVES * 32 * MRS : 16];
   char* const mw = mstage + (STAGED ? wave * 32 * MRS : 0);          // this wave's LDS rows
   const char* mrow = nullptr;   // this lane's own row (and half): direct and partial-tile loads
-  const char* mld[NMI];         // the rows this lane stages, its chunk offset included
+  const char* mld[NMI];         // the row chunk this lane copies, its rotation included
   if constexpr (HAS_MASK) {
     const char* mbh = p.mask + ((int64_t)b * p.ms0 + (int64_t)h * p.ms1) * MR::esz;
     const int qrow = q_ok[0] ? qi[0] : 0;
     mrow = mbh + ((int64_t)qrow * p.ms2 + 4 * half) * MR::esz;
 #pragma unroll
     for (int i = 0; i < NMI; ++i) {
-      const int q = i * 64 + lane;
-      const int src_row = __shfl(qrow, q / CPR);   // lane r < 32 holds row r's token
-      mld[i] = mbh + (int64_t)src_row * p.ms2 * MR::esz + (q % CPR) * 16;
+      const int q = i * 64 + lane;            // LDS slot: row q / CPR, position q % CPR
+      const int r = q / CPR;
+      const int src_row = __shfl(qrow, r);    // lane r < 32 holds row r's token
+      const int chunk = (q % CPR) ^ ((r / RPB) % CPR);
+      mld[i] = mbh + (int64_t)src_row * p.ms2 * MR::esz + chunk * 16;
     }
   }
-  typedef u32x4 MStage[STAGED ? NMI : 1];
-  auto stage_load = [&](int j0, MStage& st) {
+  typedef u32x4 MStage[1];   // (unused: the staged rows go straight to LDS)
+  auto stage_load = [&](int j0, MStage&) {
     if constexpr (STAGED) {
+      // this wave's run reads of the rows must be done before the copies overwrite them
+      __builtin_amdgcn_s_waitcnt(0xC07F);   // lgkmcnt(0)
 #pragma unroll
-      for (int i = 0; i < NMI; ++i) st[i] = ld16(mld[i] + (int64_t)j0 * MR::esz);
+      for (int i = 0; i < NMI; ++i) copy16_to_lds(mld[i] + (int64_t)j0 * MR::esz, mw + i * 1024);
     }
   };
-  auto stage_runs = [&](const MStage& st, MRun (&r)[8]) {   // registers -> wave LDS rows -> runs
+  auto stage_runs = [&](const MStage&, MRun (&r)[8]) {   // the wave's LDS rows -> runs
     if constexpr (STAGED) {
+      const int rot = (col / RPB) % CPR;
 #pragma unroll
-      for (int i = 0; i < NMI; ++i) {
-        const int q = i * 64 + lane;
-        char* dst = mw + (q / CPR) * MRS + (q % CPR) * 16;
-        if constexpr (MRS % 16 == 0) {
-          st16(dst, st[i]);
-        } else {
-          st8(dst, __builtin_shufflevector(st[i], st[i], 0, 1));
-          st8(dst + 8, __builtin_shufflevector(st[i], st[i], 2, 3));
-        }
+      for (int i = 0; i < 8; ++i) {
+        const int byte = (32 * (i >> 2) + 8 * (i & 3) + 4 * half) * MR::esz;
+        r[i] = *reinterpret_cast<const MRun*>(mw + col * MRS + (((byte >> 4) ^ rot) << 4) + (byte & 15));
       }
-      // the rows were written by other lanes of this wave (LDS executes a wave's
-      // operations in order; the fences keep the compiler from reordering them)
-      __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
-      __builtin_amdgcn_wave_barrier();
-      __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
-#pragma unroll
-      for (int i = 0; i < 8; ++i)
-        r[i] = *reinterpret_cast<const MRun*>(mw + col * MRS + (32 * (i >> 2) + 8 * (i & 3) + 4 * half) * MR::esz);
     }
   };
   auto load_runs = [&](int j0, MRun (&r)[8]) {        // direct: a whole tile, every key valid
