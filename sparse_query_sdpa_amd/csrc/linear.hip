@@ -69,6 +69,10 @@ struct LinParams {
   const int32_t* a_rows; const int32_t* res_rows; const int32_t* out_rows;
   int64_t rows_bs;
   int M, N, K, Ntok, act, tiles_m, tiles_n, batches;
+  // Launch split: the 256 x 256 kernel takes logical tiles [0, grid); the 128 x 128 kernel
+  // with tail_first >= 0 takes the last partial round, large tiles tail_first.., as four
+  // 128 x 128 sub-tiles each (tiles_m / tiles_n count 256 x 256 tiles then).
+  int tail_first;
 };
 
 typedef __attribute__((address_space(3))) void lds_void;
@@ -260,7 +264,14 @@ __global__ __launch_bounds__(CFG::THREADS, CFG::MIN_BLOCKS) void linear_kernel(L
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int wn = wave % CFG::WN, wm = wave / CFG::WN;       // this wave's block of the tile
   int b, m0, n0;
-  lin_tile(p, xcd_remap(blockIdx.x, p.tiles_m * p.tiles_n * p.batches), CFG::TM, CFG::TN, b, m0, n0);
+  if (p.tail_first >= 0) {   // sub-tile q % 4 of large tile tail_first + q / 4
+    const int q = xcd_remap(blockIdx.x, gridDim.x);
+    lin_tile(p, p.tail_first + q / 4, 2 * CFG::TM, 2 * CFG::TN, b, m0, n0);
+    m0 += (q & 1) * CFG::TM;
+    n0 += ((q >> 1) & 1) * CFG::TN;
+  } else {
+    lin_tile(p, xcd_remap(blockIdx.x, p.tiles_m * p.tiles_n * p.batches), CFG::TM, CFG::TN, b, m0, n0);
+  }
 
   // ---- copy plan: copy c < LCOPY_A fills A slots [64c, 64c+64), the rest W slots --
   // slot sigma: row sigma / 8, position sigma % 8, which holds chunk position ^ ((row >> 1)
@@ -364,7 +375,7 @@ __global__ __launch_bounds__(CFG::THREADS, 1) void linear_ring_kernel(LinParams 
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int wn = wave % CFG::WN, wm = wave / CFG::WN;
   int b, m0, n0;
-  lin_tile(p, xcd_remap(blockIdx.x, p.tiles_m * p.tiles_n * p.batches), CFG::TM, CFG::TN, b, m0, n0);
+  lin_tile(p, xcd_remap(blockIdx.x, gridDim.x), CFG::TM, CFG::TN, b, m0, n0);
 
   // Copy plan: copy mm of the A (W) half-stage fills slots 64 (wave + 8 mm) + lane; slot
   // sigma = row sigma / 8, position sigma % 8 holding chunk position ^ ((row >> 1) & 7).
@@ -464,10 +475,26 @@ int linear_launch(const safe_linear_args* a, hipStream_t s) {
   const int TM = large ? LinLarge::TM : LinSmall::TM, TN = large ? LinLarge::TN : LinSmall::TN;
   p.tiles_m = (a->M + TM - 1) / TM;
   p.tiles_n = (a->N + TN - 1) / TN;
+  p.tail_first = -1;
   const int64_t grid = (int64_t)p.tiles_m * p.tiles_n * a->batches;
   if (grid > 0x7fffffff) return SAFE_ERR_SHAPE;
-  if (large) hipLaunchKernelGGL(linear_ring_kernel<LinLarge>, dim3((unsigned)grid), dim3(LinLarge::THREADS), 0, s, p);
-  else hipLaunchKernelGGL(linear_kernel<LinSmall>, dim3((unsigned)grid), dim3(LinSmall::THREADS), 0, s, p);
+  if (!large) {
+    hipLaunchKernelGGL(linear_kernel<LinSmall>, dim3((unsigned)grid), dim3(LinSmall::THREADS), 0, s, p);
+    return hipGetLastError() == hipSuccess ? SAFE_OK : SAFE_ERR_HIP;
+  }
+  // The last round of large tiles, when it would leave more than half the CUs idle, runs as
+  // 128 x 128 sub-tiles instead (two workgroups per CU): the 4 x rem sub-tiles finish in a
+  // quarter to a half of a large tile's time.  A tile's sums are the same either way (same
+  // MFMA shape, same k order), so the split does not change the result.
+  const int64_t rem = grid % cus;
+  const bool tail = rem > 0 && 4 * rem <= 2 * (int64_t)cus;
+  const int64_t head = tail ? grid - rem : grid;
+  hipLaunchKernelGGL(linear_ring_kernel<LinLarge>, dim3((unsigned)head), dim3(LinLarge::THREADS), 0, s, p);
+  if (tail) {
+    if (hipGetLastError() != hipSuccess) return SAFE_ERR_HIP;
+    p.tail_first = (int)head;
+    hipLaunchKernelGGL(linear_kernel<LinSmall>, dim3((unsigned)(4 * rem)), dim3(LinSmall::THREADS), 0, s, p);
+  }
   return hipGetLastError() == hipSuccess ? SAFE_OK : SAFE_ERR_HIP;
 }
 
