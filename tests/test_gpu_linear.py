@@ -124,12 +124,14 @@ def test_block_shapes_sampled_rows():
         check(y[b, torch.from_numpy(samp).cuda()], ref, bound(a_s, w64, ref, C), f"block shape b={b}")
 
 
-@pytest.mark.parametrize("K", [64, 128, 192, 576])
-def test_large_tiles_ragged_edges(K):
+@pytest.mark.parametrize("K,N", [(64, 4104), (128, 4104), (192, 4104), (576, 4104), (128, 6400)])
+def test_large_tiles_ragged_edges(K, N):
     """Enough 256 x 256 tiles to take the large-tile kernel (its ring of half-stage buffers:
     one, two, three and nine k stages), with ragged token and feature edges, a gathered
-    list, GELU and a residual."""
-    B, T, N, M = 1, 4100, 4104, 4000
+    list, GELU and a residual.  With N = 4104 the 16 x 17 = 272 tiles leave a last round of
+    16 (on 256 CUs), which runs as 128 x 128 sub-tiles; with N = 6400 the last round holds
+    144 tiles and stays 256 x 256."""
+    B, T, M = 1, 4100, 4000
     a, w, bias, res = inputs(B, T, N, K, 40 + K)
     rows = np.sort(np.random.default_rng(40).choice(T, M, replace=False)).astype(np.int32)[None]
     y = sq.linear(to_dev_bf16(a), to_dev_bf16(w), bias=to_dev(bias), gelu=True, res=to_dev_bf16(res),
@@ -137,4 +139,4 @@ def test_large_tiles_ragged_edges(K):
     a_s = a.value[:, rows[0]]
     r_s = res.value[:, rows[0]]
     ref = oracle.gelu_tanh(oracle.linear(a_s, w.value, bias)) + r_s
-    check(y, ref, bound(a_s, w.value, ref, K, gelu=True, res=r_s), f"large tiles K={K}")
+    check(y, ref, bound(a_s, w.value, ref, K, gelu=True, res=r_s), f"large tiles K={K} N={N}")
