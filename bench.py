@@ -395,7 +395,7 @@ def main() -> int:
         del kc2, vc2
         out["fused_kv"] = fused_kv_lines(sq, q, kx, vx, k_fresh, v_fresh, idx, o_srsu, stage_ms, fl_srsu, tf)
         out["sw_cfg"] = sw_cfg_lines(sq, acc, wl, args.sigma, k)
-        out["hbm_measured"] = hbm_measured(out)
+        out["hbm_measured"] = hbm_measured(sq, out)
         out["midt"] = midt_lines(sq, q, kx, vx, mask, idx, stage_ms, tf)
         del mask
         torch.cuda.empty_cache()
@@ -704,10 +704,12 @@ def s_brackets(sq, q, k_glob, v_glob, wl, rho: int, dense_ms: float, tf) -> dict
     return res
 
 
-def hbm_measured(out: dict) -> dict:
-    """The box's streaming bandwidth as torch's device copy reaches it (1 GiB read + 1 GiB
-    written, three buffer pairs rotated so no pass hits in the 256 MB last-level cache), and
-    the HBM-bound kernels against it as well as against the 8 TB/s spec."""
+def hbm_measured(sq, out: dict) -> dict:
+    """The box's streaming bandwidth, three ways over 1 GiB buffers (three sets rotated so no
+    pass hits in the 256 MB last-level cache): the library's streaming probe reading only
+    (safe_hbm_probe mode 0, the reference of the read-once classifier) and copying (mode 1, the
+    reference of the read+write assembly), each the best of five grid sizes, and torch's device
+    copy; the HBM-bound kernels against them as well as against the 8 TB/s spec."""
     import torch
     n = 1 << 30
     bufs = [(torch.empty(n, dtype=torch.uint8, device="cuda"), torch.empty(n, dtype=torch.uint8, device="cuda"))
@@ -722,11 +724,33 @@ def hbm_measured(out: dict) -> dict:
         i[0] += 1
     ms = _time_ms(one, 9)
     gbs = 2 * n / (ms * 1e-3) / 1e9
-    del bufs
+    cus = torch.cuda.get_device_properties(0).multi_processor_count
+    read, copy = {}, {}
+    for per_cu in (1, 2, 4, 8, 16):
+        blocks = per_cu * cus
+        words = torch.empty(blocks * 256, dtype=torch.int32, device="cuda")
+
+        def rd():
+            sq.hbm_probe(bufs[i[0] % 3][0], blocks, out=words)
+            i[0] += 1
+
+        def cp():
+            a, b = bufs[i[0] % 3]
+            sq.hbm_probe(a, blocks, dst=b)
+            i[0] += 1
+        read[per_cu] = n / (_time_ms(rd, 9) * 1e-3) / 1e9
+        copy[per_cu] = 2 * n / (_time_ms(cp, 9) * 1e-3) / 1e9
+    del bufs, words
     torch.cuda.empty_cache()
-    return {"copy_gbs": round(gbs, 1), "copy_pct_spec": round(100 * gbs / PEAK_HBM_GBS, 2),
-            "classify_pct_of_copy": round(100 * out["classify_gbs"] / gbs, 2),
-            "kv_assemble_pct_of_copy": round(100 * out["kv_assemble_gbs"] / gbs, 2)}
+    rbest, cbest = max(read, key=read.get), max(copy, key=copy.get)
+    r_gbs, c_gbs = read[rbest], copy[cbest]
+    return {"read_probe_gbs": round(r_gbs, 1), "read_probe_pct_spec": round(100 * r_gbs / PEAK_HBM_GBS, 2),
+            "read_probe_blocks_per_cu": rbest,
+            "copy_probe_gbs": round(c_gbs, 1), "copy_probe_pct_spec": round(100 * c_gbs / PEAK_HBM_GBS, 2),
+            "copy_probe_blocks_per_cu": cbest,
+            "torch_copy_gbs": round(gbs, 1), "torch_copy_pct_spec": round(100 * gbs / PEAK_HBM_GBS, 2),
+            "classify_pct_of_read_probe": round(100 * out["classify_gbs"] / r_gbs, 2),
+            "kv_assemble_pct_of_copy_probe": round(100 * out["kv_assemble_gbs"] / c_gbs, 2)}
 
 
 def fused_kv_lines(sq, q, kx, vx, k_fresh, v_fresh, idx, o, stage_ms: dict, fl_srsu: float, tf) -> dict:

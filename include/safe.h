@@ -44,7 +44,7 @@
 extern "C" {
 #endif
 
-#define SAFE_ABI_VERSION 9
+#define SAFE_ABI_VERSION 10
 
 /* ---- status codes (negative = error) ----------------------------------- */
 enum {
@@ -488,6 +488,23 @@ int safe_linear(const safe_linear_args* a, void* stream);
  * Errors: SAFE_ERR_RANGE (shape not 16 or 32, iters or blocks outside [1, 2^24]), SAFE_ERR_NULL.
  */
 int safe_mfma_probe(int32_t shape, int32_t iters, int32_t blocks, uint32_t seed, float* out, void* stream);
+
+/*
+ * safe_hbm_probe -- a measurement aid beside the method (no equation of the pages): the
+ * streaming bandwidth of the device memory, against which the bandwidth-bound steps (the
+ * classifier reads its mask once, the K/V assembly reads and writes each row once) are read.
+ * `blocks` workgroups of 256 threads; chunk c (16 bytes) of src belongs to thread
+ * c mod (256 * blocks), which loads it non-temporally with three more of its chunks in flight.
+ *   mode 0 (read):  out[t] = xor of every 32-bit word of thread t's chunks (0 for a thread
+ *                   with none); out is device uint32[256 * blocks], dst is unused.
+ *   mode 1 (copy):  dst[0, bytes) = src[0, bytes), stored non-temporally; out is unused.
+ * src and dst are device pointers, 16-byte aligned, not overlapping; bytes a multiple of 16 in
+ * [16, 2^40].  Enqueued on stream; one launch.
+ * Errors: SAFE_ERR_RANGE (mode not 0 or 1, blocks outside [1, 2^20], overlapping copy),
+ * SAFE_ERR_SHAPE (bytes), SAFE_ERR_NULL, SAFE_ERR_ALIGN.
+ */
+int safe_hbm_probe(int32_t mode, const void* src, void* dst, int64_t bytes, int32_t blocks, uint32_t* out,
+                   void* stream);
 
 /* SAFE_ABI_VERSION of the built library. */
 int safe_abi_version(void);

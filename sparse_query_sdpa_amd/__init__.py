@@ -16,6 +16,7 @@ Entry points (the C ABI in include/safe.h, same names without the safe_ prefix):
   sw_cfg          -- Eq. 20-21 sensitivity-weighted classifier-free guidance
   linear          -- Eq. 15 row-wise linear maps on gathered rows (the block around attention)
   block_dense, block_srsu -- that block as a sequence of the calls above
+  mfma_probe, hbm_probe -- measurement aids: the matrix-core and streaming memory rates of the GPU
 """
 from __future__ import annotations
 
@@ -39,7 +40,7 @@ CLASSIFY_ASYNC = 1 << 2
 PCSP_ACCUM = 1 << 3
 PCSP_SELECT = 1 << 4
 
-ABI_VERSION = 9   # struct layouts below match include/safe.h of this version
+ABI_VERSION = 10  # struct layouts below match include/safe.h of this version
 DT_BOOL, DT_BF16, DT_F16, DT_F32 = 0, 1, 2, 3
 MASK_CLASS_NAMES = ("ALL_VALID", "ZERO", "ROW_CONST", "KEY_PADDING", "NONCONST", "BLOCKED", "NONFINITE")
 
@@ -161,6 +162,9 @@ def _load():
     lib.safe_mfma_probe.restype = ctypes.c_int
     lib.safe_mfma_probe.argtypes = [ctypes.c_int32, ctypes.c_int32, ctypes.c_int32, ctypes.c_uint32, ctypes.c_void_p,
                                     ctypes.c_void_p]
+    lib.safe_hbm_probe.restype = ctypes.c_int
+    lib.safe_hbm_probe.argtypes = [ctypes.c_int32, ctypes.c_void_p, ctypes.c_void_p, ctypes.c_int64, ctypes.c_int32,
+                                   ctypes.c_void_p, ctypes.c_void_p]
     lib.safe_mask_classify.restype = ctypes.c_int
     lib.safe_mask_classify.argtypes = [ctypes.c_void_p, ctypes.c_int32, ctypes.POINTER(ctypes.c_int64),
                                        ctypes.POINTER(ctypes.c_int64), ctypes.c_uint32, ctypes.POINTER(MaskInfo),
@@ -680,7 +684,7 @@ def sw_cfg(f_c: torch.Tensor, f_u: torch.Tensor, g_ctx: float, g_sens: Optional[
 
 __all__ = ["attn_fwd", "attn_plan", "attn_workspace_bytes", "kv_assemble", "kv_source_map", "mask_classify",
            "pcsp_accumulate", "pcsp_select", "sdpa", "sw_cfg", "linear", "block_dense", "block_srsu", "lib",
-           "SafeError", "LIB_PATH", "MASK_CLASS_NAMES", "ROUTE_NAMES"]
+           "mfma_probe", "hbm_probe", "SafeError", "LIB_PATH", "MASK_CLASS_NAMES", "ROUTE_NAMES"]
 
 
 def _rows3(t: torch.Tensor, name: str):
@@ -812,4 +816,27 @@ def mfma_probe(shape: int, iters: int, blocks: int, seed: int = 1, out: Optional
         raise ValueError("out must be a contiguous float32 tensor of at least blocks * 256 elements")
     _check("safe_mfma_probe", lib.safe_mfma_probe(int(shape), int(iters), int(blocks), int(seed) & 0xFFFFFFFF,
                                                   _ptr(out), _stream(stream)))
+    return out
+
+
+def hbm_probe(src: torch.Tensor, blocks: int, dst: Optional[torch.Tensor] = None, out: Optional[torch.Tensor] = None,
+              stream=None) -> Optional[torch.Tensor]:
+    """The streaming probe (safe_hbm_probe, a measurement aid) over the bytes of the contiguous
+    device tensor `src`: with `dst` (a contiguous tensor of the same byte size) a non-temporal
+    copy into it, returning None; without, a read that returns the per-thread xor words
+    (uint32 as int32, [blocks * 256]; thread t owns 16-byte chunks t, t + 256 * blocks, ...)."""
+    if not src.is_cuda or not src.is_contiguous():
+        raise ValueError("src must be a contiguous device tensor")
+    nbytes = src.numel() * src.element_size()
+    if dst is not None:
+        if not dst.is_cuda or not dst.is_contiguous() or dst.numel() * dst.element_size() != nbytes:
+            raise ValueError("dst must be a contiguous device tensor of the same byte size as src")
+        _check("safe_hbm_probe", lib.safe_hbm_probe(1, _ptr(src), _ptr(dst), nbytes, int(blocks), None,
+                                                    _stream(stream)))
+        return None
+    if out is None:
+        out = torch.empty(blocks * 256, dtype=torch.int32, device=src.device)
+    if out.dtype != torch.int32 or not out.is_contiguous() or out.numel() < blocks * 256:
+        raise ValueError("out must be a contiguous int32 tensor of at least blocks * 256 elements")
+    _check("safe_hbm_probe", lib.safe_hbm_probe(0, _ptr(src), None, nbytes, int(blocks), _ptr(out), _stream(stream)))
     return out

@@ -14,6 +14,7 @@ int attn_plan(const safe_attn_args* a, safe_attn_plan_info* out);
 int sw_cfg_launch(const safe_cfg_args* a, hipStream_t stream);
 int linear_launch(const safe_linear_args* a, hipStream_t stream);
 int mfma_probe_launch(int shape, int iters, int blocks, uint32_t seed, float* out, hipStream_t stream);
+int hbm_probe_launch(int mode, const void* src, void* dst, int64_t bytes, int blocks, uint32_t* out, hipStream_t stream);
 int kv_assemble_launch(const safe_kv_args* a, bool in_place, hipStream_t stream);
 int kv_source_map_launch(const safe_kv_args* a, int32_t* src, hipStream_t stream);
 int mask_classify_launch(const void* mask, int32_t dtype, const int64_t size[4], const int64_t stride[4],
@@ -492,6 +493,20 @@ int safe_mfma_probe(int32_t shape, int32_t iters, int32_t blocks, uint32_t seed,
   if (iters < 1 || iters > (1 << 24) || blocks < 1 || blocks > (1 << 24)) return SAFE_ERR_RANGE;
   if (out == nullptr) return SAFE_ERR_NULL;
   return mfma_probe_launch(shape, iters, blocks, seed, out, static_cast<hipStream_t>(stream));
+}
+
+int safe_hbm_probe(int32_t mode, const void* src, void* dst, int64_t bytes, int32_t blocks, uint32_t* out,
+                   void* stream) {
+  if (mode != 0 && mode != 1) return SAFE_ERR_RANGE;
+  if (bytes < 16 || bytes > ((int64_t)1 << 40) || bytes % 16 != 0) return SAFE_ERR_SHAPE;
+  if (blocks < 1 || blocks > (1 << 20)) return SAFE_ERR_RANGE;
+  if (src == nullptr || (mode == 1 && dst == nullptr) || (mode == 0 && out == nullptr)) return SAFE_ERR_NULL;
+  if (!aligned16(src) || (mode == 1 && !aligned16(dst))) return SAFE_ERR_ALIGN;
+  if (mode == 1) {
+    const uintptr_t a = reinterpret_cast<uintptr_t>(src), b = reinterpret_cast<uintptr_t>(dst);
+    if (a < b + (uint64_t)bytes && b < a + (uint64_t)bytes) return SAFE_ERR_RANGE;   // overlapping copy
+  }
+  return hbm_probe_launch(mode, src, dst, bytes, blocks, out, static_cast<hipStream_t>(stream));
 }
 
 }  // extern "C"

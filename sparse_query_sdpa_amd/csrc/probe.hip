@@ -1,7 +1,9 @@
-// Matrix-core rate probe: the MFMA throughput the chip sustains on random bf16 operands with
-// nothing else running.  It is a measurement aid beside the method's kernels: on MI355X the
-// attention and linear kernels are limited by the board's power cap rather than by issue, and
-// this rate (which also drops under the cap) is the ceiling they are read against.
+// Measurement aids beside the method's kernels: the rates the chip itself sustains, which the
+// method's kernels are read against.
+//
+// Matrix-core rate probe: the MFMA throughput on random bf16 operands with nothing else
+// running.  On MI355X the attention and linear kernels are limited by the board's power cap
+// rather than by issue, and this rate (which also drops under the cap) is their ceiling.
 //
 // Every lane draws eight A and eight B fragments (8 bf16 each, uniform in [-2, 2)) from a
 // counter-based hash of (seed, global lane, fragment), keeps them in registers, and each round
@@ -69,7 +71,50 @@ __global__ __launch_bounds__(256, 2) void mfma_probe_kernel(int iters, uint32_t 
   out[lane_g] = s;
 }
 
+// Streaming probe: every 16-byte chunk of the source read once with non-temporal loads, four
+// chunks in flight per thread (grid-stride: chunk c belongs to thread c mod the thread count),
+// and either xor-folded into one word per thread (read) or stored to the same offset of the
+// destination (copy).  The read form is the box's streaming-read bandwidth that the classifier
+// is read against; the copy form the read+write rate the K/V assembly is read against.
+template <bool COPY>
+__global__ __launch_bounds__(256) void hbm_probe_kernel(const u32x4* __restrict__ src, u32x4* __restrict__ dst,
+                                                        int64_t nchunks, uint32_t* __restrict__ out) {
+  constexpr int U = 4;
+  const int64_t T = (int64_t)gridDim.x * 256;
+  const int64_t g = (int64_t)blockIdx.x * 256 + threadIdx.x;
+  uint32_t x = 0u;
+  int64_t c = g;
+  for (; c + (U - 1) * T < nchunks; c += U * T) {
+    u32x4 v[U];
+#pragma unroll
+    for (int u = 0; u < U; ++u) v[u] = __builtin_nontemporal_load(src + c + u * T);
+#pragma unroll
+    for (int u = 0; u < U; ++u) {
+      if constexpr (COPY) __builtin_nontemporal_store(v[u], dst + c + u * T);
+      else x ^= v[u][0] ^ v[u][1] ^ v[u][2] ^ v[u][3];
+    }
+  }
+  for (; c < nchunks; c += T) {
+    const u32x4 v = __builtin_nontemporal_load(src + c);
+    if constexpr (COPY) __builtin_nontemporal_store(v, dst + c);
+    else x ^= v[0] ^ v[1] ^ v[2] ^ v[3];
+  }
+  if constexpr (!COPY) out[g] = x;
+}
+
 }  // namespace
+
+// Arguments were validated by the caller.
+int hbm_probe_launch(int mode, const void* src, void* dst, int64_t bytes, int blocks, uint32_t* out, hipStream_t s) {
+  const int64_t nchunks = bytes / 16;
+  const u32x4* in = reinterpret_cast<const u32x4*>(src);
+  if (mode == 1)
+    hipLaunchKernelGGL(hbm_probe_kernel<true>, dim3(blocks), dim3(256), 0, s, in, reinterpret_cast<u32x4*>(dst), nchunks,
+                       out);
+  else
+    hipLaunchKernelGGL(hbm_probe_kernel<false>, dim3(blocks), dim3(256), 0, s, in, nullptr, nchunks, out);
+  return hipGetLastError() == hipSuccess ? SAFE_OK : SAFE_ERR_HIP;
+}
 
 // Arguments were validated by the caller.
 int mfma_probe_launch(int shape, int iters, int blocks, uint32_t seed, float* out, hipStream_t s) {

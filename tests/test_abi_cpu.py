@@ -34,7 +34,7 @@ def test_every_declared_symbol_is_exported():
 
 
 def test_abi_version_and_status_strings():
-    assert sq.lib.safe_abi_version() == 9 == sq.ABI_VERSION
+    assert sq.lib.safe_abi_version() == 10 == sq.ABI_VERSION
     for code, name in sq.STATUS.items():
         assert sq.lib.safe_status_str(code).decode().startswith(name)
     assert sq.lib.safe_status_str(12345) == b"unknown status"
@@ -382,3 +382,19 @@ def test_binding_rejects_host_output_tensors():
     with pytest.raises(ValueError):
         sq._ptr(torch.empty(4, dtype=torch.int32))
     assert sq._ptr(None) is None
+
+
+def test_probe_arguments_without_gpu():
+    lib, fake, out = sq.lib, 0x10000, 0x20000     # never dereferenced: validation fails first
+    assert lib.safe_mfma_probe(8, 1, 1, 1, out, None) == -4
+    assert lib.safe_mfma_probe(32, 0, 1, 1, out, None) == -4
+    assert lib.safe_mfma_probe(16, 1, 1 << 25, 1, out, None) == -4
+    assert lib.safe_mfma_probe(32, 1, 1, 1, None, None) == -1
+    assert lib.safe_hbm_probe(3, fake, None, 4096, 1, out, None) == -4
+    assert lib.safe_hbm_probe(0, fake, None, 8, 1, out, None) == -2
+    assert lib.safe_hbm_probe(0, fake, None, (1 << 40) + 16, 1, out, None) == -2
+    assert lib.safe_hbm_probe(0, fake, None, 4096, 1 << 21, out, None) == -4
+    assert lib.safe_hbm_probe(0, None, None, 4096, 1, out, None) == -1
+    assert lib.safe_hbm_probe(1, fake, fake + 8, 4096, 1, None, None) == -8
+    assert lib.safe_hbm_probe(1, fake, fake + 4096, 8192, 1, None, None) == -4   # overlap
+    assert lib.safe_hbm_probe(1, fake + 4096, fake, 8192, 1, None, None) == -4
