@@ -287,6 +287,49 @@ def main() -> int:
         mark(7)
         return idx
 
+    # the same step with the fused global K/V read (Eq. 14/16 in one pass): the source map of S,
+    # then SRSU self-attention reading the cache and the fresh rows through it
+    stages_fused = ["classify", "pcsp_accum", "pcsp_select", "kv_source_map", "srsu_self_fused", "srsu_cross", "dense"]
+    kv_src = torch.empty((B, N), dtype=torch.int32, device=dev)
+    o_srsu_fused = torch.empty_like(o_srsu)
+
+    def step_fused(ev=None):
+        def mark(i):
+            if ev is not None:
+                ev[i].record(stream)
+        mark(0)
+        sq.mask_classify(mask, workspace=mws, asynchronous=True)
+        mark(1)
+        acc.zero_()
+        sq.pcsp_accumulate(qc, kt, wts, acc, kv_len=kv_len)
+        mark(2)
+        idx = sq.pcsp_select(acc, wl.grid_h, wl.grid_w, args.sigma, k)
+        mark(3)
+        sq.kv_source_map(idx, N, batch=B, out=kv_src)
+        mark(4)
+        sq.attn_fwd(q, kx, vx, q_rows=idx, out=o_srsu_fused, kv_src=kv_src, k_fresh=k_fresh, v_fresh=v_fresh)
+        mark(5)
+        sq.attn_fwd(qc, kt, vt, q_rows=idx, kv_len=kv_len, out=o_cross)
+        mark(6)
+        sq.attn_fwd(q, kx, vx, out=o_dense)
+        mark(7)
+        return idx
+
+    def time_steps(fn, names):
+        for _ in range(args.warmup):
+            fn()
+        torch.cuda.synchronize()
+        evs = [[torch.cuda.Event(enable_timing=True) for _ in range(len(names) + 1)] for _ in range(args.steps)]
+        torch.cuda.synchronize()
+        t = time.perf_counter()
+        for i in range(args.steps):
+            fn(evs[i])
+        torch.cuda.synchronize()
+        ms = (time.perf_counter() - t) * 1e3 / args.steps
+        per = {name: float(np.mean([evs[i][j].elapsed_time(evs[i][j + 1]) for i in range(args.steps)]))
+               for j, name in enumerate(names)}
+        return ms, per
+
     for _ in range(args.warmup):
         step()
     torch.cuda.synchronize()
@@ -394,6 +437,13 @@ def main() -> int:
                                        "dense_srsu_step_ratio": round(stage_ms["dense"] / (stage_ms["srsu_self"] + ms_ip), 3)}
         del kc2, vc2
         out["fused_kv"] = fused_kv_lines(sq, q, kx, vx, k_fresh, v_fresh, idx, o_srsu, stage_ms, fl_srsu, tf)
+        ms_fs, st_fs = time_steps(step_fused, stages_fused)
+        out["fused_kv"]["step"] = {
+            "ms_per_step": round(ms_fs, 4), "over_two_pass_step": round(ms_fs / ms_step, 4),
+            "stage_ms": {n: round(v, 4) for n, v in st_fs.items()},
+            "srsu_plus_kv_ms": round(st_fs["kv_source_map"] + st_fs["srsu_self_fused"], 4),
+            "two_pass_srsu_plus_kv_ms": round(stage_ms["kv_assemble"] + stage_ms["srsu_self"], 4),
+            "srsu_bitwise_equal_to_two_pass": bool(torch.equal(o_srsu_fused.view(torch.int16), o_srsu.view(torch.int16)))}
         out["sw_cfg"] = sw_cfg_lines(sq, acc, wl, args.sigma, k)
         out["hbm_measured"] = hbm_measured(sq, out)
         out["midt"] = midt_lines(sq, q, kx, vx, mask, idx, stage_ms, tf)

@@ -276,9 +276,7 @@ int safe_kv_source_map(const safe_kv_args* a, int32_t* kv_src, void* stream);
  *               from the ascending index list of S.  The result is attention on the
  *               assembled K/V (bit for bit where safe_attn_plan reports the same schedule
  *               for both calls; the split of long key ranges may differ).  Not combinable with kv_len or a mask
- *               (SAFE_ERR_UNSUPPORTED); n_fresh < 2^24, fresh_stride[1] < 2^23 and
- *               n_fresh * fresh_stride[1] * 2 + 2 d <= 2^32 bytes, else SAFE_ERR_UNSUPPORTED.
- *               NULL: k and v are read as given.
+ *               (SAFE_ERR_UNSUPPORTED).  NULL: k and v are read as given.
  */
 typedef struct {
   int32_t B, H, Nq, Nk, d;

@@ -161,10 +161,6 @@ static int check_attn_call(const safe_attn_args* a) {
     const bool fresh = work && a->Nk > 0 && a->n_fresh > 0;
     if ((st = check_bnhd(a->k_fresh, a->fresh_stride, fresh)) != SAFE_OK) return st;
     if ((st = check_bnhd(a->v_fresh, a->fresh_stride, fresh)) != SAFE_OK) return st;
-    // a fresh row is addressed with a 32-bit byte offset from a 24-bit product (row x row bytes)
-    if (a->n_fresh >= (1 << 24) || a->fresh_stride[1] >= (1 << 23) ||
-        (int64_t)a->n_fresh * a->fresh_stride[1] * 2 + 2 * (int64_t)a->d > ((int64_t)1 << 32))
-      return SAFE_ERR_UNSUPPORTED;
   }
   if (!work) return SAFE_OK;
   // key/value token strides: the kernel addresses a 64-key tile with 32-bit byte offsets

@@ -16,24 +16,24 @@ hipError_t dispatch_two_blocks(const AttnParams& p, bool gather, hipStream_t s) 
   return gather ? launch<D, true, false, kMaskNone, 2>(p, s) : launch<D, false, false, kMaskNone, 2>(p, s);
 }
 
-// Fused global K/V (a per-token source map, Eq. 14/16 without the assembly pass): one row
-// block per wave, no key lengths, no mask.
-template <int D>
+// Fused global K/V (a per-token source map, Eq. 14/16 without the assembly pass): no key
+// lengths, no mask; one row block per wave, or two where the mask-free kernel has them.
+template <int D, int RB>
 hipError_t dispatch_map(const AttnParams& p, bool gather, hipStream_t s) {
-  return gather ? launch<D, true, false, kMaskNone, 1, true>(p, s) : launch<D, false, false, kMaskNone, 1, true>(p, s);
+  return gather ? launch<D, true, false, kMaskNone, RB, true>(p, s) : launch<D, false, false, kMaskNone, RB, true>(p, s);
 }
-template <int D>
+template <int D, int RB>
 int resident_map_d(bool gather) {
-  return gather ? resident_workgroups<D, true, false, kMaskNone, 1, true>()
-                : resident_workgroups<D, false, false, kMaskNone, 1, true>();
+  return gather ? resident_workgroups<D, true, false, kMaskNone, RB, true>()
+                : resident_workgroups<D, false, false, kMaskNone, RB, true>();
 }
-int resident_map(int d, bool gather) {
+int resident_map(int d, bool gather, int rb) {
   switch (d) {
-    case 32: return resident_map_d<32>(gather);
-    case 64: return resident_map_d<64>(gather);
-    case 72: return resident_map_d<72>(gather);
-    case 96: return resident_map_d<96>(gather);
-    case 128: return resident_map_d<128>(gather);
+    case 32: return resident_map_d<32, 1>(gather);
+    case 64: return resident_map_d<64, 1>(gather);
+    case 72: return rb == 2 ? resident_map_d<72, 2>(gather) : resident_map_d<72, 1>(gather);
+    case 96: return rb == 2 ? resident_map_d<96, 2>(gather) : resident_map_d<96, 1>(gather);
+    case 128: return resident_map_d<128, 1>(gather);
     default: return 0;
   }
 }
@@ -133,13 +133,13 @@ Choice choose(const safe_attn_args* a, bool allow_split) {
   Choice best;
   double best_t = 0.0;
   const bool map = a->kv_src != nullptr;
-  const int max_rb = (mt == kMaskNone && a->kv_len == nullptr && !map && two_blocks_available(a->d)) ? 2 : 1;
+  const int max_rb = (mt == kMaskNone && a->kv_len == nullptr && two_blocks_available(a->d)) ? 2 : 1;
   for (int rb = 1; rb <= max_rb; ++rb) {
     Choice c;
     c.rb = rb;
     c.rows = tile_rows(rb);
     c.tiles = (int64_t)((a->n_rows + c.rows - 1) / c.rows) * a->H * a->B;
-    const int S = map ? resident_map(a->d, gather)
+    const int S = map ? resident_map(a->d, gather, rb)
                       : (mt == kMaskNone ? resident_for(a->d, gather, rb) : attn_masked_resident(a->d, gather, mt));
     if (rb > 1 && S <= 0) break;
     const double round_s = S > 0 ? (double)S * c.rows * row_flops / (kRate * (rb > 1 ? kTwoBlockSpeed : 1.0)) : 0.0;
@@ -243,11 +243,11 @@ int attn_fwd_launch(const safe_attn_args* a, float scale, hipStream_t stream) {
   hipError_t e;
   if (p.kv_src != nullptr) {
     switch (a->d) {
-      case 32: e = dispatch_map<32>(p, gather, stream); break;
-      case 64: e = dispatch_map<64>(p, gather, stream); break;
-      case 72: e = dispatch_map<72>(p, gather, stream); break;
-      case 96: e = dispatch_map<96>(p, gather, stream); break;
-      case 128: e = dispatch_map<128>(p, gather, stream); break;
+      case 32: e = dispatch_map<32, 1>(p, gather, stream); break;
+      case 64: e = dispatch_map<64, 1>(p, gather, stream); break;
+      case 72: e = c.rb == 2 ? dispatch_map<72, 2>(p, gather, stream) : dispatch_map<72, 1>(p, gather, stream); break;
+      case 96: e = c.rb == 2 ? dispatch_map<96, 2>(p, gather, stream) : dispatch_map<96, 1>(p, gather, stream); break;
+      case 128: e = dispatch_map<128, 1>(p, gather, stream); break;
       default: return SAFE_ERR_UNSUPPORTED;
     }
   } else if (mt != kMaskNone) {

@@ -300,13 +300,18 @@ void attn_fwd_kernel(AttnParams p) {
   const int64_t krow_b = p.ks1 * 2, vrow_b = p.vs1 * 2;   // bytes between consecutive keys
   const char* kfresh = nullptr;                             // fused global K/V: fresh rows of (b, h)
   const char* vfresh = nullptr;
-  if constexpr (KVMAP) {
-    kfresh = reinterpret_cast<const char*>(p.kf + (int64_t)b * p.fs0 + (int64_t)h * p.fs2);
-    vfresh = reinterpret_cast<const char*>(p.vf + (int64_t)b * p.fs0 + (int64_t)h * p.fs2);
+  if constexpr (KVMAP) {   // uniform, kept in scalar registers (the vector ones are all taken)
+    kfresh = uniform_ptr(reinterpret_cast<const char*>(p.kf + (int64_t)b * p.fs0 + (int64_t)h * p.fs2));
+    vfresh = uniform_ptr(reinterpret_cast<const char*>(p.vf + (int64_t)b * p.fs0 + (int64_t)h * p.fs2));
   }
-  uint32_t coff[T::PER_WAVE];                               // byte offset of this lane's chunk in a tile
-  uint32_t msel[KVMAP ? T::PER_WAVE : 1];                   // map byte offset of its row << 16 | chunk bytes
-  const uint32_t frow_b = KVMAP ? (uint32_t)p.fs1 * 2u : 0u;   // fresh row stride in bytes (< 2^24)
+  // This lane's copy plan, per copy: the byte offset of its chunk in a tile, or for the fused
+  // global K/V, the byte offset of its row's K or V source address in a tile's address table
+  // (below) << 16 | the chunk's bytes.  The fused form with two row blocks keeps the plan in
+  // LDS (plan[wave][m][lane]), read back when a tile's copies issue: there the registers are
+  // all taken by the products.
+  constexpr bool PLAN_LDS = KVMAP && RB > 1;
+  uint32_t coff[PLAN_LDS ? 1 : T::PER_WAVE];
+  __shared__ __attribute__((aligned(256))) uint32_t planbuf[PLAN_LDS ? NWAVES * T::PER_WAVE * 64 : 1];
 #pragma unroll
   for (int m = 0; m < T::PER_WAVE; ++m) {
     const int c = wave + NWAVES * m;
@@ -316,78 +321,87 @@ void attn_fwd_kernel(AttnParams p) {
     const int row = sigma / slots;
     int chunk = sigma % slots;
     if (chunk >= T::CH) chunk = 0;
-    coff[m] = (uint32_t)(row * (isk ? krow_b : vrow_b) + chunk * 16);
-    if constexpr (KVMAP) msel[m] = ((uint32_t)row * 4u << 16) | (uint32_t)(chunk * 16);
+    uint32_t e = (uint32_t)(row * (isk ? krow_b : vrow_b) + chunk * 16);
+    if constexpr (KVMAP) e = ((uint32_t)((row & (BN - 1)) * 16 + (isk ? 0 : 8)) << 16) | (uint32_t)(chunk * 16);
+    if constexpr (PLAN_LDS) planbuf[(wave * T::PER_WAVE + m) * 64 + lane] = e;
+    else coff[m] = e;
   }
-  // Fused global K/V: each copy reads its key's row from the fresh rows or the cache, as
-  // the source map says.  A tile's 64 map entries reach LDS one tile ahead (one dword copy
-  // by wave 0, issued with the copies of the tile before), so the wait for a tile's copies
-  // covers them and no map value is held in registers across a tile.  Slot s of mapbuf
-  // holds the map of the tiles staged in stage s.  Rows past the valid keys use row 0.
+  // Fused global K/V: each copy reads its key's row from the fresh rows or the cache, as the
+  // source map says.  One wave (wave t % 4 for tile t, so the work rotates over the SIMDs)
+  // turns a tile's 64 map entries into a table of the 64 keys' K and V source addresses
+  // (addr[slot][row] = {K, V}, 16 bytes), two tiles ahead; a copy then costs one LDS read of
+  // its row's address and one add.  The map of tile t reaches LDS (one dword copy) at step
+  // t-3 into map slot t % 2, becomes table slot t % 2 at step t-2, and is read by every wave
+  // for the copies of tile t at step t-1: each handover is ordered by a step's wait-and-
+  // barrier, and a slot is rewritten only after the barrier that follows its last read.  Rows
+  // past the valid keys take the tile's first key.
   __shared__ __attribute__((aligned(256))) int mapbuf[KVMAP ? 2 * BN : 1];
-  const int32_t* smap = KVMAP ? p.kv_src + (int64_t)b * p.src_bs : nullptr;
-  auto load_map = [&](int j0, int slot) {
-    if (wave == 0) {
-      const int r = lane < nkeys - j0 ? lane : 0;
-      __builtin_amdgcn_global_load_lds(reinterpret_cast<const char*>(smap + j0 + r),
-                                       (lds_void*)(mapbuf + slot * BN), 4, 0, 0);
+  __shared__ __attribute__((aligned(256))) char addrbuf[KVMAP ? 2 * BN * 16 : 1];
+  const int32_t* smap =
+      KVMAP ? reinterpret_cast<const int32_t*>(uniform_ptr(reinterpret_cast<const char*>(p.kv_src + (int64_t)b * p.src_bs)))
+            : nullptr;
+  auto load_map = [&](int t) {   // map entries of tile t (one wave)
+    const int j0 = kb0 + t * BN;
+    const int r = lane < nkeys - j0 ? lane : 0;
+    __builtin_amdgcn_global_load_lds(reinterpret_cast<const char*>(smap + j0 + r),
+                                     (lds_void*)(mapbuf + (t & 1) * BN), 4, 0, 0);
+  };
+  auto store_table = [&](int t, int src) {   // source addresses of tile t from its map entries (one wave)
+    const int j0 = kb0 + t * BN;
+    const int key = j0 + (lane < nkeys - j0 ? lane : 0);
+    const bool fresh = (unsigned)src < (unsigned)p.nsel;
+    const int64_t fo = (int64_t)src * p.fs1 * 2;
+    u64x2 a;
+    a[0] = reinterpret_cast<uint64_t>(fresh ? kfresh + fo : kbase + (int64_t)key * krow_b);
+    a[1] = reinterpret_cast<uint64_t>(fresh ? vfresh + fo : vbase + (int64_t)key * vrow_b);
+    *reinterpret_cast<u64x2*>(addrbuf + ((t & 1) * BN + lane) * 16) = a;
+  };
+  // A tile's copies through the table: every plan entry, then every address, is read before
+  // the first copy issues (a copy writes LDS, so a read placed after one waits for it), and
+  // the reads can be issued well before the copies.
+  struct SrcPlan {
+    uint32_t e[KVMAP ? T::PER_WAVE : 1];
+    const char* from[KVMAP ? T::PER_WAVE : 1];
+  };
+  auto fetch_sources = [&](int j0, SrcPlan& sp) {
+    const char* table = addrbuf + (((j0 - kb0) / BN) & 1) * BN * 16;
+    // the plan's address redefined each tile, so no plan entry is hoisted into a register
+    uint32_t pa = (uint32_t)((wave * T::PER_WAVE * 64 + lane) * 4);
+    asm volatile("" : "+v"(pa));
+    const char* plan = reinterpret_cast<const char*>(planbuf) + pa;
+#pragma unroll
+    for (int m = 0; m < T::PER_WAVE; ++m) {
+      if (m < FULL || wave + NWAVES * m < T::NCOPY) {
+        if constexpr (PLAN_LDS) {
+          sp.e[m] = *reinterpret_cast<const uint32_t*>(plan + m * 256);
+        } else {
+          asm volatile("" : "+v"(coff[m]));
+          sp.e[m] = coff[m];
+        }
+      }
     }
+#pragma unroll
+    for (int m = 0; m < T::PER_WAVE; ++m)
+      if (m < FULL || wave + NWAVES * m < T::NCOPY) sp.from[m] = *reinterpret_cast<const char* const*>(table + (sp.e[m] >> 16));
+  };
+  auto issue_sources = [&](const SrcPlan& sp, char* stage) {
+    int wlds = __builtin_amdgcn_readfirstlane(wave * 1024);
+    asm volatile("" : "+s"(wlds));
+#pragma unroll
+    for (int m = 0; m < T::PER_WAVE; ++m)
+      if (m < FULL || wave + NWAVES * m < T::NCOPY)
+        copy16_to_lds(sp.from[m] + (sp.e[m] & 0xffffu), stage + wlds + m * NWAVES * 1024);
   };
   auto issue_tile = [&](int j0, char* stage) {
     const char* kb = kbase + (int64_t)j0 * krow_b;
     const char* vb = vbase + (int64_t)j0 * vrow_b;
     const int nrow_valid = nkeys - j0;
     if constexpr (KVMAP) {
-      const int slot = stage == stage0 ? 0 : 1;
-      if (nrow_valid >= BN) {
-        // full tile: the cache copy keeps the scalar-base form with this lane's 32-bit
-        // offset; lanes whose key is fresh copy instead from the fresh rows' base, offset
-        // src * row bytes (24-bit product) + chunk
-        int wlds = __builtin_amdgcn_readfirstlane(wave * 1024);
-        asm volatile("" : "+s"(wlds));
-        const char* mslot = reinterpret_cast<const char*>(mapbuf) + slot * BN * 4;
-#pragma unroll
-        for (int m = 0; m < T::PER_WAVE; ++m) {
-          const int c = wave + NWAVES * m;
-          const bool all_k = NWAVES * m + NWAVES - 1 < T::K_SLOTS;
-          const bool all_v = NWAVES * m >= T::K_SLOTS;
-          const bool ck = all_k || (!all_v && c < T::K_SLOTS);
-          asm volatile("" : "+v"(coff[m]), "+v"(msel[m]));
-          if (m < FULL || c < T::NCOPY) {
-            const int src = *reinterpret_cast<const int*>(mslot + (msel[m] >> 16));
-            char* dst = stage + wlds + m * NWAVES * 1024;
-            if ((unsigned)src < (unsigned)p.nsel)
-              copy16_to_lds((ck ? kfresh : vfresh) + (__umul24((unsigned)src, frow_b) + (msel[m] & 0xffffu)), dst);
-            else
-              copy16_to_lds((ck ? kb : vb) + coff[m], dst);
-          }
-        }
-        if (j0 + BN < kend) load_map(j0 + BN, slot ^ 1);
-        return;
-      }
-      const int* mrow = mapbuf + slot * BN;
-      // laundered so that no per-copy offset is hoisted into registers live across the loop
-      int ln = lane, wv = wave;
-      asm volatile("" : "+v"(ln), "+v"(wv));
-#pragma unroll
-      for (int m = 0; m < T::PER_WAVE; ++m) {
-        const int c = wv + NWAVES * m;
-        if (m < FULL || c < T::NCOPY) {
-          const bool isk = c < T::K_SLOTS;
-          const int slots = isk ? T::K_SLOTS : T::V_SLOTS;
-          const int sigma = (isk ? c : c - T::K_SLOTS) * 64 + ln;
-          int row = sigma / slots;
-          int chunk = sigma - row * slots;
-          if (chunk >= T::CH) chunk = 0;
-          if (row >= nrow_valid) row = 0;
-          const int src = mrow[row];
-          const char* from = (unsigned)src < (unsigned)p.nsel
-              ? (isk ? kfresh : vfresh) + (int64_t)src * p.fs1 * 2
-              : (isk ? kb : vb) + (int64_t)row * (isk ? krow_b : vrow_b);
-          copy16_to_lds(from + chunk * 16, stage + c * 1024);
-        }
-      }
-      if (j0 + BN < kend) load_map(j0 + BN, slot ^ 1);
+      // every copy from its row's source address in the tile's table (rows past the valid
+      // keys hold the first key's), plus the chunk's bytes
+      SrcPlan sp;
+      fetch_sources(j0, sp);
+      issue_sources(sp, stage);
       return;
     }
     if (nrow_valid >= BN) {
@@ -607,11 +621,14 @@ void attn_fwd_kernel(AttnParams p) {
   // bracket is one basic block, so the scheduler interleaves the MFMAs of one half
   // with the VALU work of the other; the rare reference moves sit between them.
   // MASKED is the partial last tile: it loads its own mask runs, masks by length and
-  // issues no copies.
+  // issues no copies.  The fused global K/V reads the next tile's source addresses at the
+  // top and issues its copies after S^T half 0, so the two LDS round trips of those reads
+  // are hidden behind products instead of delaying them.
   auto tile_step = [&](auto masked, int it, const char* cur, char* nxt, MRun (&mc)[8], MRun (&mn)[8],
                        MStage& sc_, MStage& sn_) {
     constexpr bool MASKED = decltype(masked)::value;
     const int j0 = kb0 + it * BN;
+    SrcPlan sp;       // fused global K/V: the next tile's sources
     __builtin_amdgcn_s_waitcnt(0x0F70);  // vmcnt(0): this wave's copies of tile `it` landed
     __syncthreads();                     // ... everyone's, and tile it-1 is no longer read
     if constexpr (!MASKED) {
@@ -620,12 +637,23 @@ void attn_fwd_kernel(AttnParams p) {
       // flight, the more of the tile hides their latency (+1-2%)
       __builtin_amdgcn_s_setprio(2);
       if (it + 1 < ntiles) {
-        issue_tile(j0 + BN, nxt);
+        // the fused global K/V reads its sources here and copies after the first products
+        if constexpr (KVMAP) fetch_sources(j0 + BN, sp);
+        else issue_tile(j0 + BN, nxt);
         if constexpr (HAS_MASK) {
           if (j0 + 2 * BN <= kend) {
             if constexpr (STAGED) stage_load(j0 + BN, sn_);
             else load_runs(j0 + BN, mn);
           }
+        }
+      }
+      if constexpr (KVMAP) {
+        // one wave, in turn: the table of tile it+2 from its map (landed before this step's
+        // barrier), then the map of tile it+3 into the slot that the map of tile it+1 left
+        // (read in the step before, so no wait)
+        if (wave == ((it + 2) & (NWAVES - 1)) && it + 2 < ntiles) {
+          store_table(it + 2, mapbuf[((it + 2) & 1) * BN + lane]);
+          if (it + 3 < ntiles) load_map(it + 3);
         }
       }
     } else if constexpr (HAS_MASK) {
@@ -639,6 +667,9 @@ void attn_fwd_kernel(AttnParams p) {
     bf16x8 pb0[RB][2], pb1[RB][2];
     float ts0[RB], ts1[RB];
     s_half(Kt, 0, s0);
+    if constexpr (KVMAP && !MASKED) {   // the sources were read at the top: no wait here
+      if (it + 1 < ntiles) issue_sources(sp, nxt);
+    }
 #pragma unroll
     for (int rb = 0; rb < RB; ++rb) {
       fold_half(s0[rb], 0, mc);
@@ -681,10 +712,21 @@ void attn_fwd_kernel(AttnParams p) {
   MStage sA, sB;            // staged mask loads of the even / odd tiles (unused unless STAGED)
   const int nfull = (kend - kb0) / BN;   // tiles whose 64 keys are all valid
   if constexpr (KVMAP) {
+    // the tables of tiles 0 and 1, and the map of tile 2, before the first copies
     if (ntiles > 0) {
-      load_map(kb0, 0);
-      __builtin_amdgcn_s_waitcnt(0x0F70);  // vmcnt(0): the first tile's map landed
+      if (wave == 0) {
+        load_map(0);
+        if (ntiles > 1) load_map(1);
+      }
+      __builtin_amdgcn_s_waitcnt(0x0F70);  // vmcnt(0): the maps landed
       __syncthreads();
+      if (wave == 0) {
+        store_table(0, mapbuf[lane]);
+        if (ntiles > 1) store_table(1, mapbuf[BN + lane]);
+        __builtin_amdgcn_s_waitcnt(0xC07F);   // lgkmcnt(0): map slot 0 has been read
+        if (ntiles > 2) load_map(2);
+      }
+      __syncthreads();                       // the tables are visible
     }
   }
   if (ntiles > 0) issue_tile(kb0, stage0);

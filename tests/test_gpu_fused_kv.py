@@ -94,6 +94,36 @@ def test_fused_matches_assembled_and_oracle(d, gather):
         assert_lse_close(l_f.cpu()[:, :, sel], ref_lse, f"fused lse d={d} gather={gather} ws={ws}")
 
 
+@pytest.mark.parametrize("d", [72, 96])
+@pytest.mark.parametrize("gather", [False, True])
+def test_fused_two_row_blocks(d, gather):
+    """Shapes large enough for 256-row tiles (two row blocks per wave, the copy plan in LDS):
+    ragged N, per-sample S, a split tail; bitwise against the two-pass path, the oracle on
+    sampled rows."""
+    B, N, H = 2, 16040, 8
+    nsel = 8017
+    rng, q, ck, cv, fk, fv, S = _case(B, N, H, d, nsel, seed=170 + d + gather)
+    qd, ckd, cvd, fkd, fvd = (to_dev_bf16(t) for t in (q, ck, cv, fk, fv))
+    Sd = to_dev(S)
+    src = sq.kv_source_map(Sd, N, check=True)
+    rows = Sd if gather else None
+    plan = sq.attn_plan(qd, ckd, q_rows=rows, kv_src=src)
+    assert plan["rows_per_tile"] == 256, plan
+    o_f, l_f = sq.attn_fwd(qd, ckd, cvd, q_rows=rows, return_lse=True, kv_src=src, k_fresh=fkd, v_fresh=fvd)
+    ko, vo = sq.kv_assemble(fkd, fvd, Sd, ckd, cvd)
+    o_a, l_a = sq.attn_fwd(qd, ko, vo, q_rows=rows, return_lse=True)
+    assert _plans_match(qd, ckd, rows, src, "auto")
+    assert torch.equal(o_f.view(torch.int16), o_a.view(torch.int16)), (d, gather)
+    assert torch.equal(l_f, l_a), (d, gather)
+    kg, vg = _oracle_global(fk, fv, S, ck, cv)
+    n_out = nsel if gather else N
+    samp = np.unique(np.concatenate([[0, n_out - 1], rng.choice(n_out, 20, replace=False)]))
+    ref, ref_lse = oracle.sdpa(q.value, kg, vg, q_rows=S[:, samp] if gather else samp)
+    sel = torch.from_numpy(samp).long()
+    assert_attn_close(o_f[:, sel], ref, f"fused two row blocks d={d} gather={gather}")
+    assert_lse_close(l_f.cpu()[:, :, sel], ref_lse, f"fused two row blocks lse d={d} gather={gather}")
+
+
 def test_fused_edge_sets_and_shared_map():
     """S empty (all keys from the cache), S = every token (all keys fresh), one map shared
     by the batch."""
