@@ -75,6 +75,31 @@ def test_noalloc_with_a_split_larger_than_the_array_runs_unsplit():
     assert torch.equal(_noalloc(q, k, v), ref)
 
 
+def test_noalloc_fused_global_kv_read():
+    """The fused global K/V read (source map, fresh rows over the cache) through the
+    no-alloc entry point: bit for bit what attn_fwd gives with a workspace of the array's size."""
+    B, N, H, d, nsel = 2, 3000, 4, 96, 900
+    q, kc, vc = W.attention_inputs(B, N, N, H, d, seed=93)
+    kf, vf, _ = W.attention_inputs(B, nsel, nsel, H, d, seed=94)
+    S = np.stack([W.random_rows(np.random.default_rng(95 + b), N, nsel) for b in range(B)])
+    qd, kcd, vcd, kfd, vfd = (to_dev_bf16(t) for t in (q, kc, vc, kf, vf))
+    Sd = to_dev(S)
+    src = sq.kv_source_map(Sd, N)
+    need = sq.attn_workspace_bytes(qd, kcd, q_rows=Sd, kv_src=src)
+    ws = torch.empty(SCRATCH, dtype=torch.uint8, device="cuda") if 0 < need <= SCRATCH else None
+    ref = sq.attn_fwd(qd, kcd, vcd, q_rows=Sd, workspace=ws, kv_src=src, k_fresh=kfd, v_fresh=vfd)
+    a, got, _ = sq._attn_call(qd, kcd, vcd, Sd, None, None, None, False, False, False, None, src, kfd, vfd)
+    st = sq.lib.safe_attn_fwd_noalloc(ctypes.byref(a), int(torch.cuda.current_stream().cuda_stream))
+    assert st == 0, sq.lib.safe_status_str(st).decode()
+    torch.cuda.synchronize()
+    assert torch.equal(got, ref)
+    kg = oracle.kv_assemble(kf.value, S, kc.value)
+    vg = oracle.kv_assemble(vf.value, S, vc.value)
+    samp = np.array([0, 1, 450, nsel - 1])
+    r, _ = oracle.sdpa(q.value, kg, vg, q_rows=S[:, samp])
+    assert_attn_close(got[:, torch.from_numpy(samp).long()], r, "no-alloc fused read")
+
+
 def test_noalloc_refuses_a_workspace_and_the_check_flag():
     q, k, v = W.attention_inputs(1, 256, 256, 2, 64, seed=94)
     qd, kd, vd = to_dev_bf16(q), to_dev_bf16(k), to_dev_bf16(v)
