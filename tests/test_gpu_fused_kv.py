@@ -124,6 +124,27 @@ def test_fused_two_row_blocks(d, gather):
     assert_lse_close(l_f.cpu()[:, :, sel], ref_lse, f"fused two row blocks lse d={d} gather={gather}")
 
 
+@pytest.mark.parametrize("N", [40, 64, 100, 150, 192, 250])
+def test_fused_few_key_tiles(N):
+    """One to four 64-key tiles (full and partial): the source-address tables of the first
+    tiles are built before the loop, later ones inside it; bitwise against the two passes,
+    the oracle on sampled rows."""
+    B, H, d = 2, 3, 96
+    nsel = max(1, N // 3)
+    rng, q, ck, cv, fk, fv, S = _case(B, N, H, d, nsel, seed=190 + N)
+    qd, ckd, cvd, fkd, fvd = (to_dev_bf16(t) for t in (q, ck, cv, fk, fv))
+    Sd = to_dev(S)
+    src = sq.kv_source_map(Sd, N, check=True)
+    ko, vo = sq.kv_assemble(fkd, fvd, Sd, ckd, cvd)
+    o_a = sq.attn_fwd(qd, ko, vo, workspace=None)
+    o_f = sq.attn_fwd(qd, ckd, cvd, workspace=None, kv_src=src, k_fresh=fkd, v_fresh=fvd)
+    assert torch.equal(o_f.view(torch.int16), o_a.view(torch.int16)), N
+    kg, vg = _oracle_global(fk, fv, S, ck, cv)
+    samp = np.unique(np.array([0, N // 2, N - 1]))
+    ref, _ = oracle.sdpa(q.value, kg, vg, q_rows=samp)
+    assert_attn_close(o_f[:, torch.from_numpy(samp).long()], ref, f"fused N={N}")
+
+
 def test_fused_edge_sets_and_shared_map():
     """S empty (all keys from the cache), S = every token (all keys fresh), one map shared
     by the batch."""
