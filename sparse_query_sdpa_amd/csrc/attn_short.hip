@@ -350,9 +350,13 @@ bool attn_short_applies(const safe_attn_args* a) {
          (int64_t)SBN * a->k_stride[1] * 2 < two_gib && (int64_t)SBN * a->v_stride[1] * 2 < two_gib;
 }
 
-// Heads per workgroup: enough workgroups for about two rounds of the resident ones, and at
-// least two heads per workgroup where that still leaves a full round (the next head's
-// query rows then load while the current head computes).
+// Heads per workgroup: several heads per workgroup (the next head's query rows then load
+// while the current head computes) only where that still leaves about two full rounds of
+// the resident workgroups.  Samples usually differ in key length (the conditional and the
+// unconditional prompt of a guidance pair), so a workgroup's time differs by sample and
+// more, shorter workgroups balance the CUs: at the 160x160 workload with key lengths
+// (195, 32) one head per workgroup takes 43 us against 52 us with two; with equal
+// lengths (195, 195) it costs 59 against 56 us.
 hipError_t attn_short_launch(const AttnParams& p, int d, hipStream_t s) {
   ShortParams sp;
   sp.a = p;
@@ -368,7 +372,7 @@ hipError_t attn_short_launch(const AttnParams& p, int d, hipStream_t s) {
   const int64_t items = (int64_t)sp.row_tiles * p.B;
   int hpg = 1;
   if (resident > 0 && items > 0) {
-    while (hpg < p.H && items * ((p.H + 2 * hpg - 1) / (2 * hpg)) >= resident) hpg *= 2;
+    while (hpg < p.H && items * ((p.H + 2 * hpg - 1) / (2 * hpg)) >= 2 * (int64_t)resident) hpg *= 2;
   }
   hpg = std::min(hpg, std::max(p.H, 1));
   sp.heads_per_group = hpg;

@@ -92,7 +92,7 @@ def test_short_keys_strided_views_and_many_heads():
 def test_short_keys_several_heads_per_workgroup(H):
     """Enough rows that each workgroup walks several heads (the next head's query rows
     prefetched during the current one), with a head count the groups do not divide evenly
-    (H = 7: groups of 4 and 3): the oracle on sampled rows of every sample and head."""
+    (H = 7): the oracle on sampled rows of every sample and head."""
     B, Nq, Nk, d = 4, 16384, 300, 64
     q, k, v = W.attention_inputs(B, Nq, Nk, H, d, seed=123 + H)
     kv = np.array([300, 1, 64, 211], dtype=np.int32)
