@@ -309,7 +309,9 @@ __global__ __launch_bounds__(256) void pcsp_reduce_kernel(const float* part, flo
   acc[x] += s;
 }
 
-// Head groups for the accumulation: enough workgroups to fill the GPU several times.
+// Head groups for the accumulation: enough workgroups (about 4800) to fill the GPU several
+// times, which also evens out samples whose text lengths differ (2400 ran 3-7% slower at the
+// 160x160 workload, 9600 as fast as 2400).
 struct AccPlan {
   int groups = 1, heads_per_group = 0;
 };
@@ -318,7 +320,7 @@ AccPlan plan_accum(const safe_pcsp_args* a) {
   pl.heads_per_group = a->H;
   const int64_t items = (int64_t)a->B * ((a->N + ABM - 1) / ABM);
   if (items <= 0 || a->H <= 1) return pl;
-  const int64_t want = (2400 + items - 1) / items;
+  const int64_t want = (4800 + items - 1) / items;
   if (want <= 1) return pl;
   const int g = (int)std::min<int64_t>(want, a->H);
   pl.heads_per_group = (a->H + g - 1) / g;
